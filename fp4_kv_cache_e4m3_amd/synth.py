@@ -1,0 +1,232 @@
+"""Seeded synthetic inputs for the CSA2 hot path (shared by tests, smoke and bench).
+
+This module only *draws* inputs: shapes, value distributions and seeds.  It
+holds none of the method's arithmetic (no quantisation, scoring, selection or
+attention), so both the HIP path and the oracle can consume what it produces.
+
+Workloads mirror the shapes of the CSA2 decode/prefill path described on the
+DeepSeek-V4.1-Flash pages (ai-maestro.online, section "Compressed Sparse
+Attention 2": Top-512, 2,048 blocks x 8 tokens, 128-token sliding window; FP4
+main KV with one E4M3 scale per 16 channels, section "FP4 KV, Bounded Replay,
+and other extensions").  Because the pages publish no activations, every
+tensor is drawn from a fixed distribution:
+
+* main-KV source rows: fp32 N(0, 1), later quantised to FP4;
+* indexer q / k: integers uniform in [-r, r] (int8), head weights integers
+  uniform in [1, w_max] stored as fp32 -- so every indexer score is an exact
+  integer in fp32;
+* attention Q and SWA rows: N(0, 1) rounded to bf16 (round-to-nearest-even).
+
+Seeds: ``SeedSequence([0xC5A2, workload_id, tensor_id, layer, chunk])``.
+Large tensors are drawn in fixed-size row chunks so any chunk can be redrawn
+on its own.
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+
+import numpy as np
+
+SEED_ROOT = 0xC5A2
+
+# tensor ids used in the seed tuple
+T_KV_SRC = 1      # fp32 source rows of the main KV cache
+T_IK = 2          # indexer keys, int8
+T_IQ = 3          # indexer queries, int8 (per layer)
+T_IW = 4          # indexer head weights (per layer)
+T_Q = 5           # attention queries, bf16 (per layer)
+T_SWA = 6         # sliding-window rows, bf16 (per layer)
+T_NEW = 7         # fp32 rows of the tokens appended this step
+T_IQ_POOL = 8     # indexer q of the Full layer that produced a Reindex pool
+T_IW_POOL = 9
+
+KV_CHUNK_ROWS = 4096   # rows per independently seeded chunk of the KV source / ik
+
+
+@dataclass(frozen=True)
+class Workload:
+    """Shape and distribution of one synthetic CSA2 workload."""
+
+    name: str
+    wid: int                 # id folded into every seed
+    batch: int               # B sequences
+    q_per_seq: int           # Qn query tokens per sequence (1 for decode)
+    kv_len: int              # T compressed main-KV entries per sequence
+    dim: int                 # d, main KV / Q / SWA row width
+    heads: int               # H attention heads
+    window: int              # W sliding-window rows per query
+    idx_heads: int           # H_I indexer heads
+    idx_dim: int             # D_I indexer dim
+    idx_range: int           # indexer q/k integers uniform in [-r, r]
+    w_max: int               # indexer head weights integers uniform in [1, w_max]
+    layers: tuple = ("full",)  # CSA2 layer modes of the group
+    ratio: int = 1           # tokens per compressed entry (context only)
+    note: str = ""
+
+    @property
+    def nq(self) -> int:
+        return self.batch * self.q_per_seq
+
+    @property
+    def swa_rows(self) -> int:
+        return self.window - 1 + self.q_per_seq
+
+    def replace(self, **kw) -> "Workload":
+        d = {f: getattr(self, f) for f in self.__dataclass_fields__}
+        d.update(kw)
+        return Workload(**d)
+
+
+# The five workloads (shapes and distributions of the pages' decode/prefill path).
+C1 = Workload("full_decode_t4096_d128", 1, batch=1, q_per_seq=1, kv_len=4096, dim=128,
+              heads=8, window=128, idx_heads=2, idx_dim=64, idx_range=4, w_max=4,
+              layers=("full",), note="one Full layer decode step, single sequence")
+C2 = Workload("decode_group_full_reuse3_b32_t65536", 2, batch=32, q_per_seq=1, kv_len=65536,
+              dim=512, heads=64, window=128, idx_heads=8, idx_dim=128, idx_range=8, w_max=8,
+              layers=("full", "reuse", "reuse", "reuse"),
+              note="decoder group 1: Full + 3 Reuse, batch 32, 64K entries")
+C3 = Workload("decode_group_reindex_reuse3_b32_t65536", 3, batch=32, q_per_seq=1, kv_len=65536,
+              dim=512, heads=64, window=128, idx_heads=8, idx_dim=128, idx_range=8, w_max=8,
+              layers=("reindex", "reuse", "reuse", "reuse"),
+              note="decoder groups 2-5: Reindex + 3 Reuse")
+C4 = Workload("prefill_group_full_reuse5_q4096_t65536", 4, batch=1, q_per_seq=4096, kv_len=65536,
+              dim=512, heads=64, window=128, idx_heads=8, idx_dim=128, idx_range=8, w_max=8,
+              layers=("full",) + ("reuse",) * 5, ratio=2,
+              note="encoder prefill chunk, 4096 queries over 65536 compressed entries")
+C5 = Workload("verify_group_full_reuse3_b8_q6_t1m", 5, batch=8, q_per_seq=6, kv_len=1 << 20,
+              dim=512, heads=64, window=128, idx_heads=8, idx_dim=128, idx_range=8, w_max=8,
+              layers=("full", "reuse", "reuse", "reuse"),
+              note="1M-entry decode with 1 + 5 draft queries per sequence")
+
+WORKLOADS = {w.name: w for w in (C1, C2, C3, C4, C5)}
+
+
+def _rng(w: Workload, tensor: int, layer: int = 0, chunk: int = 0) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence([SEED_ROOT, w.wid, tensor, layer, chunk]))
+
+
+def _threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+# ---------------------------------------------------------------- bf16 helpers
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 to the nearest bf16 (ties to even); returns uint16 bit patterns.
+
+    Used only to *draw* bf16 inputs.  Inputs here are finite."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    rounding = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return ((u + rounding) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+# ---------------------------------------------------------------- generators
+def kv_source_rows(w: Workload, b: int, row0: int, nrows: int, layer: int = 0) -> np.ndarray:
+    """fp32 N(0,1) source rows [row0, row0+nrows) of sequence b's main KV (before FP4)."""
+    out = np.empty((nrows, w.dim), dtype=np.float32)
+    c0 = row0 // KV_CHUNK_ROWS
+    c1 = (row0 + nrows - 1) // KV_CHUNK_ROWS if nrows else c0 - 1
+
+    def one(c):
+        rows = min(KV_CHUNK_ROWS, w.kv_len - c * KV_CHUNK_ROWS)
+        g = _rng(w, T_KV_SRC, layer, b * 100003 + c)
+        chunk = g.standard_normal((rows, w.dim), dtype=np.float32)
+        lo = max(row0, c * KV_CHUNK_ROWS)
+        hi = min(row0 + nrows, c * KV_CHUNK_ROWS + rows)
+        out[lo - row0:hi - row0] = chunk[lo - c * KV_CHUNK_ROWS:hi - c * KV_CHUNK_ROWS]
+
+    chunks = list(range(c0, c1 + 1))
+    if len(chunks) > 2:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(one, chunks))
+    else:
+        for c in chunks:
+            one(c)
+    return out
+
+
+def kv_source(w: Workload, b: int, layer: int = 0) -> np.ndarray:
+    return kv_source_rows(w, b, 0, w.kv_len, layer)
+
+
+def new_rows(w: Workload, step: int = 0) -> np.ndarray:
+    """fp32 N(0,1) rows of the B tokens appended in one decode step, [B, d]."""
+    return _rng(w, T_NEW, step).standard_normal((w.batch, w.dim), dtype=np.float32)
+
+
+def index_k_rows(w: Workload, b: int, row0: int, nrows: int) -> np.ndarray:
+    """int8 indexer keys of sequence b, rows [row0, row0+nrows), values in [-r, r]."""
+    out = np.empty((nrows, w.idx_dim), dtype=np.int8)
+    c0 = row0 // KV_CHUNK_ROWS
+    c1 = (row0 + nrows - 1) // KV_CHUNK_ROWS if nrows else c0 - 1
+    for c in range(c0, c1 + 1):
+        rows = min(KV_CHUNK_ROWS, w.kv_len - c * KV_CHUNK_ROWS)
+        g = _rng(w, T_IK, 0, b * 100003 + c)
+        chunk = g.integers(-w.idx_range, w.idx_range + 1, size=(rows, w.idx_dim), dtype=np.int8)
+        lo = max(row0, c * KV_CHUNK_ROWS)
+        hi = min(row0 + nrows, c * KV_CHUNK_ROWS + rows)
+        out[lo - row0:hi - row0] = chunk[lo - c * KV_CHUNK_ROWS:hi - c * KV_CHUNK_ROWS]
+    return out
+
+
+def index_k(w: Workload, b: int) -> np.ndarray:
+    return index_k_rows(w, b, 0, w.kv_len)
+
+
+def index_k_all(w: Workload) -> np.ndarray:
+    """[B, T, D_I] int8."""
+    out = np.empty((w.batch, w.kv_len, w.idx_dim), dtype=np.int8)
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(lambda b: out.__setitem__(b, index_k(w, b)), range(w.batch)))
+    return out
+
+
+def index_q(w: Workload, layer: int = 0, pool_source: bool = False) -> np.ndarray:
+    """[nq, H_I, D_I] int8 indexer queries of one layer."""
+    t = T_IQ_POOL if pool_source else T_IQ
+    return _rng(w, t, layer).integers(-w.idx_range, w.idx_range + 1,
+                                      size=(w.nq, w.idx_heads, w.idx_dim), dtype=np.int8)
+
+
+def index_w(w: Workload, layer: int = 0, pool_source: bool = False) -> np.ndarray:
+    """[nq, H_I] fp32 integer-valued head weights in [1, w_max]."""
+    t = T_IW_POOL if pool_source else T_IW
+    return _rng(w, t, layer).integers(1, w.w_max + 1, size=(w.nq, w.idx_heads)).astype(np.float32)
+
+
+def attn_q_bf16(w: Workload, layer: int = 0) -> np.ndarray:
+    """[nq, H, d] bf16 bit patterns of N(0,1) queries."""
+    x = _rng(w, T_Q, layer).standard_normal((w.nq, w.heads, w.dim), dtype=np.float32)
+    return f32_to_bf16_bits(x)
+
+
+def swa_bf16(w: Workload, layer: int = 0) -> np.ndarray:
+    """[B, W-1+Qn, d] bf16 bit patterns of N(0,1) sliding-window rows."""
+    x = _rng(w, T_SWA, layer).standard_normal((w.batch, w.swa_rows, w.dim), dtype=np.float32)
+    return f32_to_bf16_bits(x)
+
+
+@dataclass
+class Small:
+    """Helper for ad-hoc small shapes in tests (not one of the named workloads)."""
+    batch: int = 1
+    q_per_seq: int = 1
+    kv_len: int = 64
+    dim: int = 128
+    heads: int = 8
+    window: int = 128
+    idx_heads: int = 2
+    idx_dim: int = 64
+    idx_range: int = 4
+    w_max: int = 4
+    layers: tuple = field(default=("full",))
+
+    def workload(self, wid: int = 99, name: str = "small") -> Workload:
+        return Workload(name, wid, self.batch, self.q_per_seq, self.kv_len, self.dim, self.heads,
+                        self.window, self.idx_heads, self.idx_dim, self.idx_range, self.w_max,
+                        self.layers)
