@@ -1,0 +1,186 @@
+#!/usr/bin/env python3
+"""Decode throughput of one CSA2 layer group on one MI355X.
+
+Default workload: the decoder's first group at 64K context, batch 32 -- a Full
+layer (quantise the 32 new tokens' main-KV rows to FP4, scan all 65,536
+indexer keys per sequence, pool of 2,048 blocks, Top-512) followed by three
+Reuse layers (own Q and 128-row SWA window, same Top-512).  One step = the
+whole group over one batch; inputs are synthetic, seeded, and resident in HBM
+before timing starts.
+
+Prints one JSON line: query-tokens/s, achieved HBM GB/s of the group, the
+roofline of the dominant kernel (the indexer scan) from HIP events recorded
+around it inside the timed region, and the FP64 oracle timed on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak (AMD spec)
+
+
+def group_bytes(w) -> dict:
+    """Algorithmic bytes of one group step (what the method must move)."""
+    nq, T = w.nq, w.kv_len
+    row = w.dim // 2 + w.dim // 16                         # FP4 row: codes + scales
+    scan = w.batch * T * w.idx_dim + nq * w.idx_heads * (w.idx_dim + 4)
+    select = nq * (2048 * 4 + 512 * 4)                     # pool + topk written
+    quant = w.batch * (w.dim * 4 + row)
+    attn_layer = (nq * (512 * row + w.heads * w.dim * 2 + w.heads * w.dim * 4 + 512 * 4)
+                  + w.batch * w.swa_rows * w.dim * 2)
+    reindex = nq * (2048 * 4 + 16384 * w.idx_dim + w.idx_heads * (w.idx_dim + 4) + 512 * 4)
+    layers = len(w.layers)
+    if w.layers[0] == "full":
+        total = quant + scan + select + layers * attn_layer
+    else:
+        total = reindex + layers * attn_layer
+    return dict(scan=scan, select=select, quant=quant, attn_layer=attn_layer, reindex=reindex,
+                total=total)
+
+
+def cpu_baseline(w, n_seq: int) -> dict:
+    """The FP64 oracle on the first n_seq sequences of the same workload (one full
+    group step each: new-row quantisation, Full index over all T positions,
+    every layer's attention).  Input generation is not timed."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from fp4_kv_cache_e4m3_amd import synth
+    from oracle import attention as oattn
+    from oracle import indexer as oidx
+    from oracle import quant as oquant
+
+    T = w.kv_len
+    iq, iw = synth.index_q(w)[:n_seq * w.q_per_seq], synth.index_w(w)[:n_seq * w.q_per_seq]
+    ik = np.stack([synth.index_k(w, b) for b in range(n_seq)])
+    newr = synth.new_rows(w)[:n_seq]
+    qs = [synth.bf16_bits_to_f32(synth.attn_q_bf16(w, l)[:n_seq * w.q_per_seq]).astype(np.float64)
+          for l in range(len(w.layers))]
+    sws = [synth.bf16_bits_to_f32(synth.swa_bf16(w, l)[:n_seq]).astype(np.float64)
+           for l in range(len(w.layers))]
+    srcs = [synth.kv_source(w, b) for b in range(n_seq)]
+    t0 = time.perf_counter()
+    oquant.quantize_rows(newr)
+    _, topk = oidx.index_full(iq, iw, ik, w.q_per_seq)
+    for qi in range(n_seq * w.q_per_seq):
+        b = qi // w.q_per_seq
+        pos = topk[qi][topk[qi] >= 0]
+        codes, scales = oquant.quantize_rows(srcs[b][pos])     # the selected cache rows
+        for l in range(len(w.layers)):
+            keys = oattn.query_entries(qi % w.q_per_seq, w.q_per_seq, len(pos), np.arange(len(pos)),
+                                       codes, scales, sws[l][b:b + 1], w.window)
+            oattn.attend(qs[l][qi], keys, 1.0 / np.sqrt(w.dim))
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    nq = n_seq * w.q_per_seq
+    return {"value": nq / dt, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_seq} of {w.batch} sequences ({nq} query tokens), full group step "
+                      f"({'+'.join(w.layers)}), T={T}; {dt:.2f} s wall"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode_group_full_reuse3_b32_t65536")
+    ap.add_argument("--cpu-seqs", type=int, default=32, help="sequences in the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; the multi-GPU design is "
+                                   "described in DESIGN.md and not executed", "n_gpus": args.gpus}))
+        return 2
+
+    import torch
+
+    import fp4_kv_cache_e4m3_amd as csa2
+    from fp4_kv_cache_e4m3_amd import synth
+
+    w = synth.WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    csa2.load()
+    g = csa2.DecodeGroup(w)
+    stream = torch.cuda.current_stream()
+    nl = len(w.layers)
+    full = w.layers[0] == "full"
+
+    def step(ev=None):
+        # ev: list of events recorded between the calls (timing only; no sync)
+        if full:
+            csa2.quantize_kv(g.new_rows, g.new_codes, g.new_scales, stream)
+            if ev is not None: ev[0].record(stream)
+            csa2.index_scan(g.iargs, g.iws, stream)
+            if ev is not None: ev[1].record(stream)
+            csa2.index_select(g.iargs, g.pool, g.topk, g.iws, stream)
+        else:
+            if ev is not None: ev[0].record(stream)
+            csa2.index_reindex(g.iargs, g.pool, g.topk, g.iws, stream)
+            if ev is not None: ev[1].record(stream)
+        if ev is not None: ev[2].record(stream)
+        for l in range(nl):
+            csa2.sparse_attn(g.aargs[l], g.aws, stream)
+        if ev is not None: ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for k in range(args.steps):
+        step(evs[k])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = start.elapsed_time(stop) / args.steps
+    scan_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    sel_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    attn_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+
+    nbytes = group_bytes(w)
+    value = w.nq / (ms / 1e3)
+    scan_bytes = nbytes["scan"] if full else nbytes["reindex"]
+    achieved = scan_bytes / (scan_ms / 1e3) / 1e9
+    out = {
+        "metric": "decode query-tokens/s per CSA2 layer group at 64K ctx + achieved HBM GB/s",
+        "value": round(value, 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp4e2m1+e4m3/int8/fp16-mfma",
+        "data": "synthetic (seeded numpy; N(0,1) KV/Q/SWA, integer indexer inputs)",
+        "config": {"workload": w.name, "batch": w.batch, "q_per_seq": w.q_per_seq,
+                   "kv_len": w.kv_len, "dim": w.dim, "heads": w.heads, "window": w.window,
+                   "idx_heads": w.idx_heads, "idx_dim": w.idx_dim, "layers": list(w.layers)},
+        "hbm_gbs_group": round(nbytes["total"] / (ms / 1e3) / 1e9, 1),
+        "hbm_frac_group": round(nbytes["total"] / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+        "breakdown_ms": {"index_scan" if full else "reindex": round(scan_ms, 4),
+                         "index_select" if full else "-": round(sel_ms, 4),
+                         f"attention_x{nl}": round(attn_ms, 4)},
+        "roofline": {"kernel": "k_index_scan" if full else "k_reindex_score+select",
+                     "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "bytes_per_launch": scan_bytes, "traffic": None},
+        "wall_s_timed": round(t_wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, min(args.cpu_seqs, w.batch))
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,188 @@
+"""ctypes binding of libcsa2.so (include/csa2.h).
+
+Argument marshalling only: every function passes device pointers, sizes and
+the current HIP stream to the C ABI and turns a non-zero status into
+``CSA2Error``.  All computation happens in the library's gfx950 kernels.
+PyTorch supplies device memory and the stream; nothing here falls back to the
+CPU -- if the library is missing, ``load()`` raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa2.so")
+
+TOPK = 512
+BLOCK = 8
+POOL_BLOCKS = 2048
+WINDOW = 128
+SCALE_GROUP = 16
+
+EXPORTS = (
+    "csa2_status_string", "csa2_version", "csa2_quantize_kv", "csa2_dequantize_kv",
+    "csa2_index_workspace_size", "csa2_index_full", "csa2_index_scan", "csa2_index_select",
+    "csa2_index_reindex",
+    "csa2_attn_workspace_size", "csa2_sparse_attn",
+)
+
+
+class CSA2Error(RuntimeError):
+    pass
+
+
+class IndexArgs(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("q_per_seq", ctypes.c_int32), ("kv_len", ctypes.c_int64),
+        ("heads", ctypes.c_int32), ("dim", ctypes.c_int32),
+        ("q", ctypes.c_void_p), ("w", ctypes.c_void_p), ("k", ctypes.c_void_p),
+        ("n_visible", ctypes.c_void_p),
+    ]
+
+
+class AttnArgs(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("q_per_seq", ctypes.c_int32), ("kv_len", ctypes.c_int64),
+        ("heads", ctypes.c_int32), ("dim", ctypes.c_int32),
+        ("q", ctypes.c_void_p),
+        ("codes", ctypes.c_void_p), ("codes_stride", ctypes.c_int64),
+        ("scales", ctypes.c_void_p), ("scales_stride", ctypes.c_int64),
+        ("topk", ctypes.c_void_p), ("topk_k", ctypes.c_int32),
+        ("swa", ctypes.c_void_p), ("window", ctypes.c_int32),
+        ("swa_len", ctypes.c_void_p),
+        ("sm_scale", ctypes.c_float),
+        ("out", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libcsa2.so once; raises if it was not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise CSA2Error(f"{path} is missing: build it with `python -m fp4_kv_cache_e4m3_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.csa2_status_string.restype = ctypes.c_char_p
+    lib.csa2_status_string.argtypes = [ctypes.c_int]
+    lib.csa2_version.restype = ctypes.c_int
+    lib.csa2_quantize_kv.restype = ctypes.c_int
+    lib.csa2_quantize_kv.argtypes = [vp, i64, i64, i32, vp, i64, vp, i64, vp]
+    lib.csa2_dequantize_kv.restype = ctypes.c_int
+    lib.csa2_dequantize_kv.argtypes = [vp, i64, vp, i64, i64, i32, vp, i64, vp]
+    lib.csa2_index_workspace_size.restype = sz
+    lib.csa2_index_workspace_size.argtypes = [ctypes.POINTER(IndexArgs)]
+    lib.csa2_index_full.restype = ctypes.c_int
+    lib.csa2_index_full.argtypes = [ctypes.POINTER(IndexArgs), vp, vp, vp, sz, vp]
+    lib.csa2_index_scan.restype = ctypes.c_int
+    lib.csa2_index_scan.argtypes = [ctypes.POINTER(IndexArgs), vp, sz, vp]
+    lib.csa2_index_select.restype = ctypes.c_int
+    lib.csa2_index_select.argtypes = [ctypes.POINTER(IndexArgs), vp, vp, vp, sz, vp]
+    lib.csa2_index_reindex.restype = ctypes.c_int
+    lib.csa2_index_reindex.argtypes = [ctypes.POINTER(IndexArgs), vp, vp, vp, sz, vp]
+    lib.csa2_attn_workspace_size.restype = sz
+    lib.csa2_attn_workspace_size.argtypes = [ctypes.POINTER(AttnArgs)]
+    lib.csa2_sparse_attn.restype = ctypes.c_int
+    lib.csa2_sparse_attn.argtypes = [ctypes.POINTER(AttnArgs), vp, sz, vp]
+    _lib = lib
+    return lib
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise CSA2Error(load().csa2_status_string(status).decode())
+
+
+def status_string(status: int) -> str:
+    return load().csa2_status_string(status).decode()
+
+
+# ------------------------------------------------------------------ quantise
+def quantize_kv(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, stream=None) -> None:
+    """FP4-quantise fp32 rows x [rows, d] into codes [rows, >=d/2] / scales [rows, >=d/16]
+    (row strides taken from the tensors, so views into a larger cache work)."""
+    rows, dim = x.shape
+    _check(load().csa2_quantize_kv(_ptr(x), x.stride(0), rows, dim, _ptr(codes), codes.stride(0),
+                                   _ptr(scales), scales.stride(0), _stream(stream)))
+
+
+def dequantize_kv(codes: torch.Tensor, scales: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    rows, dim = out.shape
+    _check(load().csa2_dequantize_kv(_ptr(codes), codes.stride(0), _ptr(scales), scales.stride(0),
+                                     rows, dim, _ptr(out), out.stride(0), _stream(stream)))
+
+
+# ------------------------------------------------------------------ indexer
+def index_args(iq, iw, ik, q_per_seq: int, n_visible=None) -> IndexArgs:
+    """iq int8 [nq, H_I, D_I], iw fp32 [nq, H_I], ik int8 [B, T, D_I]."""
+    nq, heads, dim = iq.shape
+    B, T = ik.shape[0], ik.shape[1]
+    return IndexArgs(B, q_per_seq, T, heads, dim, _ptr(iq), _ptr(iw), _ptr(ik), _ptr(n_visible))
+
+
+def index_workspace_size(args: IndexArgs) -> int:
+    return int(load().csa2_index_workspace_size(ctypes.byref(args)))
+
+
+def index_full(args: IndexArgs, pool, topk, ws, stream=None) -> None:
+    _check(load().csa2_index_full(ctypes.byref(args), _ptr(pool), _ptr(topk), _ptr(ws),
+                                  ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream)))
+
+
+def index_scan(args: IndexArgs, ws, stream=None) -> None:
+    _check(load().csa2_index_scan(ctypes.byref(args), _ptr(ws), ws.numel() * ws.element_size(),
+                                  _stream(stream)))
+
+
+def index_select(args: IndexArgs, pool, topk, ws, stream=None) -> None:
+    _check(load().csa2_index_select(ctypes.byref(args), _ptr(pool), _ptr(topk), _ptr(ws),
+                                    ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def index_reindex(args: IndexArgs, pool, topk, ws, stream=None) -> None:
+    _check(load().csa2_index_reindex(ctypes.byref(args), _ptr(pool), _ptr(topk), _ptr(ws),
+                                     ws.numel() * ws.element_size() if ws is not None else 0,
+                                     _stream(stream)))
+
+
+# ------------------------------------------------------------------ attention
+def attn_args(q, codes, scales, topk, swa, out, q_per_seq: int, kv_len: int, window: int = WINDOW,
+              swa_len=None, sm_scale: float = 0.0) -> AttnArgs:
+    """q bf16-as-int16/uint16 [nq, H, d]; codes [B*T, >=d/2]; scales [B*T, >=d/16];
+    topk int32 [nq, k]; swa bf16 [B, window-1+Qn, d]; out fp32 [nq, H, d]."""
+    nq, heads, dim = q.shape
+    return AttnArgs(nq // q_per_seq, q_per_seq, kv_len, heads, dim, _ptr(q),
+                    _ptr(codes), codes.stride(0) if codes is not None else dim // 2,
+                    _ptr(scales), scales.stride(0) if scales is not None else dim // 16,
+                    _ptr(topk), topk.shape[1] if topk is not None else 0,
+                    _ptr(swa), window, _ptr(swa_len), float(sm_scale), _ptr(out))
+
+
+def attn_workspace_size(args: AttnArgs) -> int:
+    return int(load().csa2_attn_workspace_size(ctypes.byref(args)))
+
+
+def sparse_attn(args: AttnArgs, ws=None, stream=None) -> None:
+    _check(load().csa2_sparse_attn(ctypes.byref(args), _ptr(ws),
+                                   ws.numel() * ws.element_size() if ws is not None else 0,
+                                   _stream(stream)))

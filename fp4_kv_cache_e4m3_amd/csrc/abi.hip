@@ -1,0 +1,234 @@
+// C ABI of the CSA2 library: host-side validation, workspace sizing and
+// dispatch to the gfx950 kernels.  Declarations and contracts: include/csa2.h.
+#include <cmath>
+#include <cstdlib>
+
+#include "../../include/csa2.h"
+#include "common.h"
+
+namespace {
+
+using namespace csa2;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+constexpr int64_t kMaxKvLen = 1 << 20;           // 131,072 blocks per query in the pool select
+
+int check_index(const csa2_index_args* a) {
+  if (!a) return CSA2_ERR_NULL;
+  if (a->batch < 0 || a->q_per_seq < 1 || a->kv_len < 0 || a->kv_len > kMaxKvLen) return CSA2_ERR_SHAPE;
+  if (!(a->heads == 2 || a->heads == 4 || a->heads == 8 || a->heads == 16)) return CSA2_ERR_SHAPE;
+  if (!(a->dim == 64 || a->dim == 128)) return CSA2_ERR_SHAPE;
+  if ((int64_t)a->q_per_seq * a->heads > 64) return CSA2_ERR_SHAPE;
+  const int64_t nq = (int64_t)a->batch * a->q_per_seq;
+  if (nq > 0 && (!a->q || !a->w)) return CSA2_ERR_NULL;
+  if (nq > 0 && a->kv_len > 0 && !a->k) return CSA2_ERR_NULL;
+  if (!aligned(a->q, 16) || !aligned(a->k, 16) || !aligned(a->w, 4)) return CSA2_ERR_ALIGN;
+  return CSA2_OK;
+}
+
+struct IndexLayout {
+  int64_t nq, tk_stride, bk_stride, full_bytes, reindex_bytes, total;
+};
+
+IndexLayout index_layout(const csa2_index_args* a) {
+  IndexLayout L{};
+  L.nq = (int64_t)a->batch * a->q_per_seq;
+  L.tk_stride = round_up(a->kv_len, 16);
+  L.bk_stride = round_up((a->kv_len + kBlock - 1) / kBlock, 16);
+  L.full_bytes = L.nq * (L.tk_stride + L.bk_stride) * 4;
+  L.reindex_bytes = L.nq * kPoolPositions * 4;
+  L.total = round_up(L.full_bytes > L.reindex_bytes ? L.full_bytes : L.reindex_bytes, 256);
+  return L;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_ERR_HIP; }
+
+// Splits of the attention tile list over workgroups: aim for >= 256 workgroups
+// while keeping >= 8 tiles (2 per wave) in each split.
+int attn_splits(int64_t nq, int heads, int n_tiles) {
+  const int64_t base = nq * ((heads + 15) / 16);
+  int s = 1;
+  if (const char* e = std::getenv("CSA2_ATTN_SPLITS")) {
+    s = std::atoi(e);
+  } else if (base > 0) {
+    s = (int)((256 + base - 1) / base);
+    const int cap = n_tiles / 8 > 1 ? n_tiles / 8 : 1;
+    if (s > cap) s = cap;
+  }
+  if (s < 1) s = 1;
+  if (s > n_tiles && n_tiles > 0) s = n_tiles;
+  if (n_tiles == 0) s = 1;
+  const int tps = n_tiles > 0 ? (n_tiles + s - 1) / s : 1;
+  return n_tiles > 0 ? (n_tiles + tps - 1) / tps : 1;
+}
+
+struct AttnLayout {
+  int64_t nq;
+  int n_sparse_tiles, n_tiles, splits, tps, swa_rows;
+  int64_t ws_bytes;
+};
+
+AttnLayout attn_layout(const csa2_attn_args* a) {
+  AttnLayout L{};
+  L.nq = (int64_t)a->batch * a->q_per_seq;
+  L.n_sparse_tiles = a->kv_len > 0 ? (a->topk_k + 15) / 16 : 0;
+  L.swa_rows = a->window > 0 ? a->window - 1 + a->q_per_seq : 0;
+  L.n_tiles = L.n_sparse_tiles + (a->window + 15) / 16;
+  L.splits = attn_splits(L.nq, a->heads, L.n_tiles);
+  L.tps = L.n_tiles > 0 ? (L.n_tiles + L.splits - 1) / L.splits : 1;
+  L.ws_bytes = 0;
+  if (L.splits > 1) {
+    const int64_t parts = L.nq * L.splits * a->heads;
+    L.ws_bytes = round_up(parts * a->dim * 4, 256) + round_up(parts * 2 * 4, 256);
+  }
+  return L;
+}
+
+int check_attn(const csa2_attn_args* a) {
+  if (!a) return CSA2_ERR_NULL;
+  if (a->batch < 0 || a->q_per_seq < 1 || a->kv_len < 0 || a->kv_len > (int64_t)1 << 31) return CSA2_ERR_SHAPE;
+  if (a->heads < 1 || a->heads > 128) return CSA2_ERR_SHAPE;
+  if (!(a->dim == 128 || a->dim == 512)) return CSA2_ERR_SHAPE;
+  if (a->topk_k < 0 || a->topk_k > 2048 || a->window < 0 || a->window > 1024) return CSA2_ERR_SHAPE;
+  const int64_t nq = (int64_t)a->batch * a->q_per_seq;
+  if (nq == 0) return CSA2_OK;
+  if (!a->q || !a->out) return CSA2_ERR_NULL;
+  if (a->kv_len > 0 && a->topk_k > 0 && (!a->codes || !a->scales || !a->topk)) return CSA2_ERR_NULL;
+  if (a->window > 0 && !a->swa) return CSA2_ERR_NULL;
+  if (a->codes_stride < a->dim / 2 || a->scales_stride < a->dim / 16) return CSA2_ERR_SHAPE;
+  if (!aligned(a->q, 16) || !aligned(a->codes, 16) || !aligned(a->scales, 8) || !aligned(a->swa, 16) ||
+      !aligned(a->out, 16) || !aligned(a->topk, 4) || (a->codes_stride % 16) || (a->scales_stride % 8))
+    return CSA2_ERR_ALIGN;
+  return CSA2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* csa2_status_string(int s) {
+  switch (s) {
+    case CSA2_OK: return "CSA2_OK";
+    case CSA2_ERR_NULL: return "CSA2_ERR_NULL: a required pointer is NULL";
+    case CSA2_ERR_SHAPE: return "CSA2_ERR_SHAPE: unsupported or inconsistent size";
+    case CSA2_ERR_ALIGN: return "CSA2_ERR_ALIGN: pointer or stride misaligned";
+    case CSA2_ERR_WORKSPACE: return "CSA2_ERR_WORKSPACE: workspace missing or too small";
+    case CSA2_ERR_HIP: return "CSA2_ERR_HIP: the HIP runtime reported an error";
+    default: return "unknown csa2 status";
+  }
+}
+
+int csa2_version(void) { return (1 << 16) | 0; }
+
+int csa2_quantize_kv(const float* x, int64_t x_stride, int64_t rows, int32_t dim, uint8_t* codes,
+                     int64_t codes_stride, uint8_t* scales, int64_t scales_stride, hipStream_t stream) {
+  if (rows < 0 || dim < 32 || dim > 4096 || dim % 32) return CSA2_ERR_SHAPE;
+  if (rows == 0) return CSA2_OK;
+  if (!x || !codes || !scales) return CSA2_ERR_NULL;
+  if (x_stride < dim || codes_stride < dim / 2 || scales_stride < dim / 16) return CSA2_ERR_SHAPE;
+  if (!aligned(x, 16) || x_stride % 4 || !aligned(codes, 8) || codes_stride % 8) return CSA2_ERR_ALIGN;
+  return hip_status(launch_quantize(x, x_stride, rows, dim, codes, codes_stride, scales, scales_stride, stream));
+}
+
+int csa2_dequantize_kv(const uint8_t* codes, int64_t codes_stride, const uint8_t* scales,
+                       int64_t scales_stride, int64_t rows, int32_t dim, float* out, int64_t out_stride,
+                       hipStream_t stream) {
+  if (rows < 0 || dim < 32 || dim > 4096 || dim % 32) return CSA2_ERR_SHAPE;
+  if (rows == 0) return CSA2_OK;
+  if (!out || !codes || !scales) return CSA2_ERR_NULL;
+  if (out_stride < dim || codes_stride < dim / 2 || scales_stride < dim / 16) return CSA2_ERR_SHAPE;
+  if (!aligned(out, 16) || out_stride % 4 || !aligned(codes, 8) || codes_stride % 8) return CSA2_ERR_ALIGN;
+  return hip_status(launch_dequantize(codes, codes_stride, scales, scales_stride, rows, dim, out, out_stride, stream));
+}
+
+size_t csa2_index_workspace_size(const csa2_index_args* a) {
+  if (check_index(a) != CSA2_OK) return 0;
+  return (size_t)index_layout(a).total;
+}
+
+int csa2_index_scan(const csa2_index_args* a, void* ws, size_t ws_size, hipStream_t stream) {
+  int st = check_index(a);
+  if (st != CSA2_OK) return st;
+  const IndexLayout L = index_layout(a);
+  if (L.nq == 0) return CSA2_OK;
+  if (!aligned(a->n_visible, 4)) return CSA2_ERR_ALIGN;
+  if (!ws || ws_size < (size_t)L.total || !aligned(ws, 256)) return CSA2_ERR_WORKSPACE;
+  uint32_t* tkeys = static_cast<uint32_t*>(ws);
+  uint32_t* bkeys = tkeys + L.nq * L.tk_stride;
+  ScanParams sp{a->q, a->w, a->k, a->n_visible, a->batch, a->q_per_seq, a->kv_len, 1024,
+                tkeys, L.tk_stride, bkeys, L.bk_stride};
+  return hip_status(launch_index_scan(sp, a->heads, a->dim, stream));
+}
+
+int csa2_index_select(const csa2_index_args* a, int32_t* pool, int32_t* topk, const void* ws,
+                      size_t ws_size, hipStream_t stream) {
+  int st = check_index(a);
+  if (st != CSA2_OK) return st;
+  const IndexLayout L = index_layout(a);
+  if (L.nq == 0) return CSA2_OK;
+  if (!topk) return CSA2_ERR_NULL;
+  if (!aligned(a->n_visible, 4) || !aligned(pool, 4) || !aligned(topk, 4)) return CSA2_ERR_ALIGN;
+  if (!ws || ws_size < (size_t)L.total || !aligned(ws, 256)) return CSA2_ERR_WORKSPACE;
+  const uint32_t* tkeys = static_cast<const uint32_t*>(ws);
+  const uint32_t* bkeys = tkeys + L.nq * L.tk_stride;
+  SelectParams sel{tkeys, L.tk_stride, bkeys, L.bk_stride, a->n_visible, a->kv_len, pool, topk};
+  return hip_status(launch_select_full(sel, (int)L.nq, (a->kv_len + kBlock - 1) / kBlock, stream));
+}
+
+int csa2_index_full(const csa2_index_args* a, int32_t* pool, int32_t* topk, void* ws, size_t ws_size,
+                    hipStream_t stream) {
+  int st = check_index(a);
+  if (st != CSA2_OK) return st;
+  if ((int64_t)a->batch * a->q_per_seq > 0 && !topk) return CSA2_ERR_NULL;
+  st = csa2_index_scan(a, ws, ws_size, stream);
+  if (st != CSA2_OK) return st;
+  return csa2_index_select(a, pool, topk, ws, ws_size, stream);
+}
+
+int csa2_index_reindex(const csa2_index_args* a, const int32_t* pool, int32_t* topk, void* ws,
+                       size_t ws_size, hipStream_t stream) {
+  int st = check_index(a);
+  if (st != CSA2_OK) return st;
+  const IndexLayout L = index_layout(a);
+  if (L.nq == 0) return CSA2_OK;
+  if (!topk || !pool) return CSA2_ERR_NULL;
+  if (!aligned(a->n_visible, 4) || !aligned(pool, 4)) return CSA2_ERR_ALIGN;
+  if (!ws || ws_size < (size_t)L.total || !aligned(ws, 256)) return CSA2_ERR_WORKSPACE;
+  ReindexParams rp{a->q, a->w, a->k, a->n_visible, pool, a->q_per_seq, a->kv_len,
+                   static_cast<uint32_t*>(ws), topk};
+  return hip_status(launch_reindex(rp, (int)L.nq, a->heads, a->dim, stream));
+}
+
+size_t csa2_attn_workspace_size(const csa2_attn_args* a) {
+  if (check_attn(a) != CSA2_OK) return 0;
+  return (size_t)attn_layout(a).ws_bytes;
+}
+
+int csa2_sparse_attn(const csa2_attn_args* a, void* ws, size_t ws_size, hipStream_t stream) {
+  int st = check_attn(a);
+  if (st != CSA2_OK) return st;
+  const AttnLayout L = attn_layout(a);
+  if (L.nq == 0) return CSA2_OK;
+  if (L.ws_bytes > 0 && (!ws || ws_size < (size_t)L.ws_bytes || !aligned(ws, 256))) return CSA2_ERR_WORKSPACE;
+  if (!aligned(a->swa_len, 4)) return CSA2_ERR_ALIGN;
+  AttnParams p{};
+  p.q = a->q; p.codes = a->codes; p.scales = a->scales; p.topk = a->topk; p.swa = a->swa;
+  p.swa_len = a->swa_len; p.out = a->out;
+  p.opart = static_cast<float*>(ws);
+  p.mlpart = L.ws_bytes > 0 ? reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                                         round_up(L.nq * L.splits * a->heads * a->dim * 4, 256))
+                            : nullptr;
+  p.T = a->kv_len; p.codes_stride = a->codes_stride; p.scales_stride = a->scales_stride;
+  p.qn = a->q_per_seq; p.heads = a->heads; p.topk_k = a->topk_k; p.window = a->window;
+  p.swa_rows = L.swa_rows; p.splits = L.splits; p.tiles_per_split = L.tps;
+  p.n_sparse_tiles = L.n_sparse_tiles; p.n_tiles = L.n_tiles;
+  const float sm = a->sm_scale > 0.0f ? a->sm_scale : 1.0f / std::sqrt((float)a->dim);
+  p.qscale = sm * 1.4426950408889634f;
+  // With no tile at all the kernel still runs: every head ends with an empty
+  // softmax and writes zeros (no memset node, so the call stays graph-safe).
+  return hip_status(launch_attn(p, (int)L.nq, a->dim, stream));
+}
+
+}  // extern "C"

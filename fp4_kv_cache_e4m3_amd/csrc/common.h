@@ -1,0 +1,118 @@
+// Internal definitions shared by the CSA2 gfx950 kernels (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+
+#define CSA2_DEV __device__ __forceinline__
+
+namespace csa2 {
+
+constexpr int kTopK = 512;
+constexpr int kBlock = 8;
+constexpr int kPoolBlocks = 2048;
+constexpr int kPoolPositions = kPoolBlocks * kBlock;
+
+// ---------------------------------------------------------------- ranking key
+// Order-preserving map of an fp32 score to uint32: larger score -> larger key.
+// -0.0 ranks with +0.0; every finite score maps to a key >= 1, so key 0 is
+// free to mark "not a candidate".
+CSA2_DEV uint32_t score_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---------------------------------------------------------------- FP4 decode
+// fp16 value of byte `sel` (a constant 0..3) of an E4M3FN word: the gfx950
+// fp8 -> f32 convert decodes OCP E4M3FN exactly (0x7F / 0xFF -> NaN) and every
+// finite E4M3 value is exact in fp16.
+template <int SEL>
+CSA2_DEV _Float16 e4m3_to_half(uint32_t word) {
+  return (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)word, SEL);
+}
+
+// Eight E2M1 codes of one dword (channel 8w+i in nibble i, even channel in the
+// low nibble of each byte) times one scale, as eight fp16 values in channel
+// order.  The gfx950 FP4 -> fp16 convert applies only the power-of-two part of
+// its fp32 scale operand, so it runs with scale 1.0 (exact E2M1 values) and
+// one packed fp16 multiply applies the E4M3 scale.  E2M1 x E4M3 products have
+// <= 6 significant bits and magnitudes in [2^-10, 2688], so every value and
+// product is exact in fp16.
+CSA2_DEV v8h fp4x8_to_half(uint32_t x, _Float16 s) {
+  const v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 0);
+  const v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 1);
+  const v2h c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 2);
+  const v2h d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 3);
+  const v8h v = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+  const v8h sv = {s, s, s, s, s, s, s, s};
+  return v * sv;
+}
+
+// bf16 bits -> fp32 (exact)
+CSA2_DEV float bf16_to_float(uint32_t b) { return __uint_as_float(b << 16); }
+
+// eight bf16 (two per dword) -> eight fp16, round to nearest even
+CSA2_DEV v8h bf16x8_to_half(u4 w) {
+  v8h r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r[2 * i] = (_Float16)__uint_as_float(w[i] << 16);
+    r[2 * i + 1] = (_Float16)__uint_as_float(w[i] & 0xFFFF0000u);
+  }
+  return r;
+}
+
+// ---------------------------------------------------------------- wave helpers
+CSA2_DEV float wave_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+}  // namespace csa2
+
+// ---------------------------------------------------------------- launchers
+namespace csa2 {
+
+struct ScanParams {
+  const int8_t* iq; const float* iw; const int8_t* ik; const int32_t* nvis;
+  int32_t batch, qn; int64_t T; int32_t chunk;          // tokens per workgroup
+  uint32_t* tkeys; int64_t tk_stride;                    // [nq, tk_stride]
+  uint32_t* bkeys; int64_t bk_stride;                    // [nq, bk_stride]
+};
+struct SelectParams {
+  const uint32_t* tkeys; int64_t tk_stride;
+  const uint32_t* bkeys; int64_t bk_stride;
+  const int32_t* nvis; int64_t T;
+  int32_t* pool; int32_t* topk;
+};
+struct ReindexParams {
+  const int8_t* iq; const float* iw; const int8_t* ik; const int32_t* nvis;
+  const int32_t* pool; int32_t qn; int64_t T;
+  uint32_t* ckeys;                                       // [nq, 16384]
+  int32_t* topk;
+};
+struct AttnParams {
+  const uint16_t* q; const uint8_t* codes; const uint8_t* scales;
+  const int32_t* topk; const uint16_t* swa; const int32_t* swa_len;
+  float* out; float* opart; float* mlpart;
+  int64_t T, codes_stride, scales_stride;
+  int32_t qn, heads, topk_k, window, swa_rows, splits, tiles_per_split, n_sparse_tiles, n_tiles;
+  float qscale;                                          // sm_scale * log2(e)
+};
+
+hipError_t launch_quantize(const float* x, int64_t xs, int64_t rows, int dim, uint8_t* codes,
+                           int64_t cs, uint8_t* scales, int64_t ss, hipStream_t st);
+hipError_t launch_dequantize(const uint8_t* codes, int64_t cs, const uint8_t* scales, int64_t ss,
+                             int64_t rows, int dim, float* out, int64_t os, hipStream_t st);
+hipError_t launch_index_scan(const ScanParams& p, int heads, int dim, hipStream_t st);
+hipError_t launch_select_full(const SelectParams& p, int nq, int64_t max_blocks, hipStream_t st);
+hipError_t launch_reindex(const ReindexParams& p, int nq, int heads, int dim, hipStream_t st);
+hipError_t launch_attn(const AttnParams& p, int nq, int dim, hipStream_t st);
+
+}  // namespace csa2

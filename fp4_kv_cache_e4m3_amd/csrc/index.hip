@@ -1,0 +1,520 @@
+// Hierarchical sparse indexer of CSA2 for gfx950: Full-layer scan, block /
+// pool / Top-512 selection, and Reindex rescoring of the pool.
+//
+// Method: DeepSeek-V4.1-Flash pages, ai-maestro.online section "Compressed
+// Sparse Attention 2": a Full layer scores the context with its indexer and
+// selects fresh Top-512 indices; its hierarchical indexer keeps a candidate
+// pool of up to 16,384 positions (2,048 blocks of eight tokens), which later
+// Reindex layers rescore with their own indexer Q instead of the whole
+// context.  Score s(q,t) = sum_h w[q,h] * relu(q_h . k_t); block score = max
+// over its tokens; ranking by (score desc, index asc).
+//
+// Design (gfx950, wave64):
+//  * Scan: the indexer keys stream once from HBM.  Each wave takes 16-token
+//    tiles: an int8 MFMA 16x16x64 contracts the 16 token rows (B operand,
+//    one token per lane column) with up to 16 score rows (A operand: the
+//    sequence's query heads, Qn * H_I rows, padded), so the dot products are
+//    exact int32.  ReLU, head weights and the head sum run on the 4
+//    accumulator rows a lane holds plus one cross-lane add; the 8-token block
+//    maximum is three DPP max steps inside each 16-lane row.  Token keys and
+//    block keys (order-preserving uint32 of the fp32 score) go to workspace.
+//  * Select: one 1024-thread workgroup per query.  A 3-pass radix select
+//    (12-, 12- and 8-bit digits; all histograms cleared once up front; DPP
+//    wave scans; the digit search walks each thread's bins in registers)
+//    finds the K-th largest key and how many keys equal to it must be taken;
+//    a single packed block scan (count above, count equal) then emits the
+//    winners in ascending index order, ties to the lowest index.  Atomics
+//    only count, never decide membership, so the output is deterministic.
+//  * Reindex: the same MFMA scoring on gathered pool blocks (2 blocks = one
+//    16-token tile), then the same selection.
+#include "common.h"
+
+namespace csa2 {
+
+// ============================================================== scan
+// HI: indexer heads (2, 4, 8, 16); DI: indexer dim (64, 128).
+template <int DI, int HI>
+__global__ __launch_bounds__(256) void k_index_scan(ScanParams p) {
+  constexpr int KK = DI / 64;                 // MFMAs per tile
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int b = blockIdx.y;
+  const int64_t t0 = (int64_t)blockIdx.x * p.chunk;
+  const int rows_used = p.qn * HI;            // score rows of this sequence
+  const int MT = (rows_used + 15) >> 4;       // M tiles (<= 4)
+
+  // furthest visible position over the sequence's queries
+  int64_t vmax = p.T;
+  if (p.nvis) {
+    vmax = 0;
+    for (int j = 0; j < p.qn; ++j) vmax = max(vmax, (int64_t)p.nvis[b * p.qn + j]);
+    vmax = min(vmax, p.T);
+  }
+  if (t0 >= vmax) return;
+  const int64_t tend = min(t0 + (int64_t)p.chunk, vmax);
+
+  // A operands (score rows) and weights of the 4 output rows each lane holds
+  v4i a[4][KK];
+  float wv[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int r = 16 * mt + n;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      v4i z = {0, 0, 0, 0};
+      if (mt < MT && r < rows_used) {
+        const int j = r / HI, h = r % HI;
+        z = *reinterpret_cast<const v4i*>(p.iq + ((int64_t)(b * p.qn + j) * HI + h) * DI + g * (DI / 4) + kk * 16);
+      }
+      a[mt][kk] = z;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r2 = 16 * mt + 4 * g + i;
+      float w = 0.0f;
+      if (mt < MT && r2 < rows_used) w = p.iw[(int64_t)(b * p.qn + r2 / HI) * HI + r2 % HI];
+      wv[mt][i] = w;
+    }
+  }
+  int nvq[4];   // visibility of the queries whose rows this lane's group holds (HI >= 4 case)
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int j = (16 * mt + 4 * g) / HI;
+    nvq[mt] = (int)min((int64_t)(p.nvis && j < p.qn ? p.nvis[b * p.qn + j] : p.T), p.T);
+  }
+
+  const int8_t* ikb = p.ik + (int64_t)b * p.T * DI;
+  const int ntile = (int)((tend - t0 + 15) >> 4);
+
+  // score one 16-token tile whose indexer-key fragments are in bf
+  auto process = [&](int it, const v4i (&bf)[KK]) {
+    const int64_t t = t0 + 16 * it + n;
+    const bool tok_ok = t < tend;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      if (mt >= MT) break;
+      v4i acc = {0, 0, 0, 0};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mt][kk], bf[kk], acc, 0, 0, 0);
+      float val[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) val[i] = wv[mt][i] * (float)max(acc[i], 0);
+      if constexpr (HI >= 4) {
+        float tot = ((val[0] + val[1]) + val[2]) + val[3];
+        if constexpr (HI >= 8) tot = tot + __shfl_xor(tot, 16, 64);
+        if constexpr (HI >= 16) tot = tot + __shfl_xor(tot, 32, 64);
+        const int j = (16 * mt + 4 * g) / HI;     // query within the sequence
+        const uint32_t key = (tok_ok && t < nvq[mt] && j < p.qn) ? score_key(tot) : 0u;
+        // 8-token block max inside each half of the 16-lane row
+        uint32_t m = key;
+        m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false));  // xor 1
+        m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, false));  // xor 2
+        m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x141, 0xF, 0xF, false)); // half-row mirror
+        const bool writer = (HI == 4) || (HI == 8 && (g & 1) == 0) || (HI == 16 && g == 0);
+        if (writer && j < p.qn && tok_ok) {
+          const int64_t q = (int64_t)b * p.qn + j;
+          p.tkeys[q * p.tk_stride + t] = key;
+          if ((n & 7) == 0) p.bkeys[q * p.bk_stride + (t >> 3)] = m;
+        }
+      } else {  // HI == 2: rows (i0,i1) and (i2,i3) are two queries
+#pragma unroll
+        for (int hq = 0; hq < 2; ++hq) {
+          const float tot = val[2 * hq] + val[2 * hq + 1];
+          const int j = (16 * mt + 4 * g) / 2 + hq;
+          const int nv = (int)min((int64_t)(p.nvis && j < p.qn ? p.nvis[b * p.qn + j] : p.T), p.T);
+          const uint32_t key = (tok_ok && t < nv && j < p.qn) ? score_key(tot) : 0u;
+          uint32_t m = key;
+          m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false));
+          m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, false));
+          m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x141, 0xF, 0xF, false));
+          if (j < p.qn && tok_ok) {
+            const int64_t q = (int64_t)b * p.qn + j;
+            p.tkeys[q * p.tk_stride + t] = key;
+            if ((n & 7) == 0) p.bkeys[q * p.bk_stride + (t >> 3)] = m;
+          }
+        }
+      }
+    }
+  };
+
+  // U tiles per wave and iteration: all their loads are issued before the
+  // first MFMA so several KiB per wave are in flight
+  constexpr int U = 4;
+  for (int it0 = wave; it0 < ntile; it0 += 4 * U) {
+    v4i bf[U][KK];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t t = t0 + 16 * (it0 + 4 * u) + n;
+      const int64_t row = t < tend ? t : t0;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        bf[u][kk] = *reinterpret_cast<const v4i*>(ikb + row * DI + g * (DI / 4) + kk * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (it0 + 4 * u < ntile) process(it0 + 4 * u, bf[u]);
+  }
+}
+
+// ============================================================== select
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kDigitBins = 4096;                 // 12-bit digits: bits 31..20, 19..8, then 7..0
+constexpr int kSelHists = 6;                     // 3 passes x 2 selections, cleared once
+
+struct SelShared {
+  alignas(16) uint32_t hist[kSelHists][kDigitBins];
+  uint32_t bc[4];
+  uint32_t wsum[kSelWaves];
+  int32_t pool[kPoolBlocks];
+};
+
+// inclusive prefix sum over the 64 lanes with DPP (row shifts inside 16-lane
+// rows, then row broadcasts across rows); no LDS traffic
+CSA2_DEV uint32_t wave_incl_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);   // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);   // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);   // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);   // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return x;
+}
+
+// exclusive prefix sum over the workgroup (thread order)
+CSA2_DEV uint32_t block_excl_scan(uint32_t v, SelShared& sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t incl = wave_incl_scan(v);
+  if (lane == 63) sh.wsum[wave] = incl;
+  __syncthreads();
+  if (wave == 0) {
+    const uint32_t x = lane < kSelWaves ? sh.wsum[lane] : 0u;
+    const uint32_t xi = wave_incl_scan(x);
+    if (lane < kSelWaves) sh.wsum[lane] = xi - x;
+  }
+  __syncthreads();
+  const uint32_t r = sh.wsum[wave] + incl - v;
+  __syncthreads();
+  return r;
+}
+
+CSA2_DEV uint32_t block_sum(uint32_t v, SelShared& sh) {
+  const uint32_t ex = block_excl_scan(v, sh);
+  if (threadIdx.x == kSelThreads - 1) sh.bc[0] = ex + v;
+  __syncthreads();
+  const uint32_t t = sh.bc[0];
+  __syncthreads();
+  return t;
+}
+
+// +1 on counter `bin`.  When every active lane of the wave hits the same bin
+// (ties, concentrated scores) one lane adds the whole count, so a repeated
+// digit does not serialise 64 LDS atomics on one address.
+CSA2_DEV void hist_inc(uint32_t* hist, uint32_t bin, bool active) {
+  const uint64_t act = __ballot(active);
+  if (act == 0) return;
+  const int leader = __ffsll((unsigned long long)act) - 1;
+  const uint32_t lb = __shfl(bin, leader, 64);
+  const uint64_t same = __ballot(active && bin == lb);
+  if (same == act) {
+    if ((int)(threadIdx.x & 63) == leader) atomicAdd(&hist[lb], (uint32_t)__popcll(act));
+  } else if (active) {
+    atomicAdd(&hist[bin], 1u);
+  }
+}
+
+// Digit d of an NB-bin histogram with  above(d) < k <= above(d) + count(d),
+// where above(d) counts larger digits.  Thread t owns the BPT bins
+// [NB - BPT (t+1), NB - BPT t), so thread order is descending digit order;
+// the owning thread walks its bins in registers.
+template <int NB>
+CSA2_DEV void hist_find(const uint32_t* hist, uint32_t k, SelShared& sh, uint32_t& digit, uint32_t& above) {
+  constexpr int BPT = NB >= kSelThreads ? NB / kSelThreads : 1;
+  constexpr int OWNERS = NB / BPT;
+  const int t = threadIdx.x;
+  uint32_t c[BPT];
+  uint32_t sum = 0;
+  const int lo_bin = NB - BPT * (t + 1);
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) {
+    c[i] = t < OWNERS ? hist[lo_bin + i] : 0u;
+    sum += c[i];
+  }
+  const uint32_t ex = block_excl_scan(sum, sh);
+  if (t < OWNERS && ex < k && k <= ex + sum) {
+    uint32_t run = ex;
+#pragma unroll
+    for (int i = BPT - 1; i >= 0; --i) {
+      if (run + c[i] >= k) { sh.bc[0] = (uint32_t)(lo_bin + i); sh.bc[1] = run; break; }
+      run += c[i];
+    }
+  }
+  __syncthreads();
+  digit = sh.bc[0];
+  above = sh.bc[1];
+  __syncthreads();
+}
+
+// K-th largest key among nonzero keys (1 <= K <= #nonzero): returns the key
+// value tau and how many keys equal to tau belong to the top K.  Three radix
+// passes (12, 12 and 8 bits) on pre-cleared histograms h[0..2].  get(j)
+// returns this thread's j-th key (j < KPT); small KPT keeps keys in
+// registers, large KPT re-reads them each pass.
+template <int KPT, typename Get>
+CSA2_DEV void radix_select(Get get, uint32_t K, SelShared& sh, uint32_t (*h)[kDigitBins], uint32_t& tau,
+                           uint32_t& need) {
+#pragma unroll 16
+  for (int j = 0; j < KPT; ++j) {
+    const uint32_t k = get(j);
+    hist_inc(h[0], k >> 20, k != 0u);
+  }
+  __syncthreads();
+  uint32_t d1, a1;
+  hist_find<kDigitBins>(h[0], K, sh, d1, a1);
+  const uint32_t k2 = K - a1;
+#pragma unroll 16
+  for (int j = 0; j < KPT; ++j) {
+    const uint32_t k = get(j);
+    hist_inc(h[1], (k >> 8) & 0xFFFu, k != 0u && (k >> 20) == d1);
+  }
+  __syncthreads();
+  uint32_t d2, a2;
+  hist_find<kDigitBins>(h[1], k2, sh, d2, a2);
+  const uint32_t k3 = k2 - a2;
+  const uint32_t pre = (d1 << 12) | d2;
+#pragma unroll 16
+  for (int j = 0; j < KPT; ++j) {
+    const uint32_t k = get(j);
+    hist_inc(h[2], k & 0xFFu, k != 0u && (k >> 8) == pre);
+  }
+  __syncthreads();
+  uint32_t d3, a3;
+  hist_find<256>(h[2], k3, sh, d3, a3);
+  tau = (pre << 8) | d3;
+  need = k3 - a3;
+}
+
+CSA2_DEV void hists_clear(SelShared& sh) {
+  u4* hp = reinterpret_cast<u4*>(&sh.hist[0][0]);
+  constexpr int n4 = kSelHists * kDigitBins / 4;
+  for (int i = threadIdx.x; i < n4; i += kSelThreads) hp[i] = u4{0u, 0u, 0u, 0u};
+}
+
+// Emit the indices of the top-K keys in ascending index order.  Thread t owns
+// indices [t*KPT, t*KPT + KPT); emit(o, j) writes output slot o for local j.
+template <int KPT, typename Get, typename Emit>
+CSA2_DEV void compact_topk(Get get, uint32_t tau, uint32_t need, SelShared& sh, Emit emit) {
+  uint32_t ngt = 0, neq = 0;
+#pragma unroll 16
+  for (int j = 0; j < KPT; ++j) {
+    const uint32_t k = get(j);
+    ngt += k > tau ? 1u : 0u;
+    neq += k == tau ? 1u : 0u;
+  }
+  const uint32_t ex = block_excl_scan((ngt << 16) | neq, sh);
+  const uint32_t gt_before = ex >> 16, eq_before = ex & 0xFFFFu;
+  uint32_t pos = gt_before + min(eq_before, need);
+  uint32_t r = eq_before;
+#pragma unroll 16
+  for (int j = 0; j < KPT; ++j) {
+    const uint32_t k = get(j);
+    if (k > tau) {
+      emit(pos++, j);
+    } else if (k == tau) {
+      if (r < need) emit(pos++, j);
+      ++r;
+    }
+  }
+}
+
+// Candidate step shared by Full and Reindex: candidate c = 8*slot + r refers
+// to position 8*pool[slot] + r; keys[c] is its score key (0 = not a candidate).
+template <int KPT2>
+CSA2_DEV void select_positions(const uint32_t (&key)[KPT2], SelShared& sh, const int32_t* pool_slots,
+                               int32_t* topk_out) {
+  uint32_t nvalid = 0;
+#pragma unroll
+  for (int j = 0; j < KPT2; ++j) nvalid += key[j] != 0u ? 1u : 0u;
+  nvalid = block_sum(nvalid, sh);
+  const uint32_t K2 = min(nvalid, (uint32_t)kTopK);
+  if (K2 > 0) {
+    uint32_t tau, need;
+    auto get = [&](int j) { return key[j]; };
+    radix_select<KPT2>(get, K2, sh, &sh.hist[3], tau, need);
+    const int base = threadIdx.x * KPT2;
+    compact_topk<KPT2>(get, tau, need, sh, [&](uint32_t o, int j) {
+      const int c = base + j;
+      topk_out[o] = pool_slots[c >> 3] * kBlock + (c & 7);
+    });
+  }
+  for (int i = K2 + threadIdx.x; i < kTopK; i += kSelThreads) topk_out[i] = -1;
+}
+
+// Full layer: pool of top-2048 blocks, then Top-512 of the pool's positions.
+template <int KPT1>
+__global__ __launch_bounds__(kSelThreads) void k_select_full(SelectParams p) {
+  constexpr int KPT2 = kPoolPositions / kSelThreads;   // 16
+  __shared__ SelShared sh;
+  const int64_t q = blockIdx.x;
+  hists_clear(sh);
+  __syncthreads();
+  int64_t nv = p.nvis ? (int64_t)p.nvis[q] : p.T;
+  nv = max((int64_t)0, min(nv, p.T));
+  const int64_t nb = (nv + kBlock - 1) / kBlock;
+  const uint32_t K1 = (uint32_t)min(nb, (int64_t)kPoolBlocks);
+
+  // ---- step 1: top blocks (keys in registers when they fit, else re-read)
+  const int64_t base1 = (int64_t)threadIdx.x * KPT1;
+  const uint32_t* bk = p.bkeys + q * p.bk_stride;
+  if constexpr (KPT1 <= 16) {
+    uint32_t bkey[KPT1];
+#pragma unroll
+    for (int j = 0; j < KPT1; ++j) bkey[j] = base1 + j < nb ? bk[base1 + j] : 0u;
+    auto get = [&](int j) { return bkey[j]; };
+    if (K1 > 0) {
+      uint32_t tau, need;
+      radix_select<KPT1>(get, K1, sh, &sh.hist[0], tau, need);
+      compact_topk<KPT1>(get, tau, need, sh, [&](uint32_t o, int j) { sh.pool[o] = (int32_t)(base1 + j); });
+    }
+  } else {
+    auto get = [&](int j) { return base1 + j < nb ? bk[base1 + j] : 0u; };
+    if (K1 > 0) {
+      uint32_t tau, need;
+      radix_select<KPT1>(get, K1, sh, &sh.hist[0], tau, need);
+      compact_topk<KPT1>(get, tau, need, sh, [&](uint32_t o, int j) { sh.pool[o] = (int32_t)(base1 + j); });
+    }
+  }
+  for (int i = K1 + threadIdx.x; i < kPoolBlocks; i += kSelThreads) sh.pool[i] = -1;
+  __syncthreads();
+  if (p.pool)
+    for (int i = threadIdx.x; i < kPoolBlocks; i += kSelThreads) p.pool[q * kPoolBlocks + i] = sh.pool[i];
+
+  // ---- step 2: Top-512 positions of the pool
+  uint32_t key[KPT2];
+  const int base2 = threadIdx.x * KPT2;
+#pragma unroll
+  for (int j = 0; j < KPT2; ++j) {
+    const int c = base2 + j;
+    const int32_t blk = sh.pool[c >> 3];
+    const int64_t pos = (int64_t)blk * kBlock + (c & 7);
+    key[j] = (blk >= 0 && pos < nv) ? p.tkeys[q * p.tk_stride + pos] : 0u;
+  }
+  select_positions<KPT2>(key, sh, sh.pool, p.topk + q * kTopK);
+}
+
+// ============================================================== reindex
+// Score the pool positions of one query: grid (2048 / 256 slots, nq).
+template <int DI, int HI>
+__global__ __launch_bounds__(256) void k_reindex_score(ReindexParams p) {
+  constexpr int KK = DI / 64;
+  constexpr int kSlotsPerWG = 256;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int64_t q = blockIdx.y;
+  const int64_t b = q / p.qn;
+  int64_t nv = p.nvis ? (int64_t)p.nvis[q] : p.T;
+  nv = max((int64_t)0, min(nv, p.T));
+  const int64_t nb = (nv + kBlock - 1) / kBlock;
+
+  v4i a[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    v4i z = {0, 0, 0, 0};
+    if (n < HI) z = *reinterpret_cast<const v4i*>(p.iq + (q * HI + n) * DI + g * (DI / 4) + kk * 16);
+    a[kk] = z;
+  }
+  float wv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) wv[i] = (4 * g + i < HI) ? p.iw[q * HI + 4 * g + i] : 0.0f;
+
+  const int8_t* ikb = p.ik + b * p.T * DI;
+  const int32_t* pool = p.pool + q * kPoolBlocks;
+  uint32_t* ck = p.ckeys + q * kPoolPositions;
+  const int slot0 = blockIdx.x * kSlotsPerWG;
+  for (int it = wave; it < kSlotsPerWG / 2; it += 4) {
+    const int slot = slot0 + 2 * it + (n >> 3);
+    const int32_t blk = pool[slot];
+    const int64_t pos = (int64_t)blk * kBlock + (n & 7);
+    const bool ok = blk >= 0 && (int64_t)blk < nb && pos < nv;
+    v4i bf[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      v4i z = {0, 0, 0, 0};
+      if (ok) z = *reinterpret_cast<const v4i*>(ikb + pos * DI + g * (DI / 4) + kk * 16);
+      bf[kk] = z;
+    }
+    v4i acc = {0, 0, 0, 0};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[kk], bf[kk], acc, 0, 0, 0);
+    float val[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) val[i] = wv[i] * (float)max(acc[i], 0);
+    float tot;
+    if constexpr (HI == 2) {
+      tot = val[0] + val[1];
+    } else {
+      tot = ((val[0] + val[1]) + val[2]) + val[3];
+      if constexpr (HI >= 8) tot = tot + __shfl_xor(tot, 16, 64);
+      if constexpr (HI >= 16) tot = tot + __shfl_xor(tot, 32, 64);
+    }
+    if (g == 0) ck[slot * kBlock + (n & 7)] = ok ? score_key(tot) : 0u;
+  }
+}
+
+__global__ __launch_bounds__(kSelThreads) void k_select_reindex(ReindexParams p) {
+  constexpr int KPT2 = kPoolPositions / kSelThreads;
+  __shared__ SelShared sh;
+  const int64_t q = blockIdx.x;
+  hists_clear(sh);
+  for (int i = threadIdx.x; i < kPoolBlocks; i += kSelThreads) sh.pool[i] = p.pool[q * kPoolBlocks + i];
+  __syncthreads();
+  uint32_t key[KPT2];
+  const int base = threadIdx.x * KPT2;
+#pragma unroll
+  for (int j = 0; j < KPT2; ++j) key[j] = p.ckeys[q * kPoolPositions + base + j];
+  __syncthreads();
+  select_positions<KPT2>(key, sh, sh.pool, p.topk + q * kTopK);
+}
+
+// ============================================================== launchers
+template <int DI, int HI>
+static void launch_scan_t(const ScanParams& p, hipStream_t st) {
+  const int64_t chunks = (p.T + p.chunk - 1) / p.chunk;
+  hipLaunchKernelGGL((k_index_scan<DI, HI>), dim3((unsigned)chunks, (unsigned)p.batch), dim3(256), 0, st, p);
+}
+
+hipError_t launch_index_scan(const ScanParams& p, int heads, int dim, hipStream_t st) {
+  if (p.T == 0 || p.batch == 0) return hipSuccess;
+#define CSA2_SCAN_CASE(D, H) if (dim == D && heads == H) { launch_scan_t<D, H>(p, st); return hipGetLastError(); }
+  CSA2_SCAN_CASE(64, 2) CSA2_SCAN_CASE(64, 4) CSA2_SCAN_CASE(64, 8) CSA2_SCAN_CASE(64, 16)
+  CSA2_SCAN_CASE(128, 2) CSA2_SCAN_CASE(128, 4) CSA2_SCAN_CASE(128, 8) CSA2_SCAN_CASE(128, 16)
+#undef CSA2_SCAN_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_select_full(const SelectParams& p, int nq, int64_t max_blocks, hipStream_t st) {
+  if (nq == 0) return hipSuccess;
+  if (max_blocks <= 8 * kSelThreads)
+    hipLaunchKernelGGL((k_select_full<8>), dim3(nq), dim3(kSelThreads), 0, st, p);
+  else if (max_blocks <= 128 * kSelThreads)
+    hipLaunchKernelGGL((k_select_full<128>), dim3(nq), dim3(kSelThreads), 0, st, p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_reindex(const ReindexParams& p, int nq, int heads, int dim, hipStream_t st) {
+  if (nq == 0) return hipSuccess;
+  const dim3 grid(kPoolBlocks / 256, nq);
+#define CSA2_RX_CASE(D, H) if (dim == D && heads == H) { hipLaunchKernelGGL((k_reindex_score<D, H>), grid, dim3(256), 0, st, p); } else
+  CSA2_RX_CASE(64, 2) CSA2_RX_CASE(64, 4) CSA2_RX_CASE(64, 8) CSA2_RX_CASE(64, 16)
+  CSA2_RX_CASE(128, 2) CSA2_RX_CASE(128, 4) CSA2_RX_CASE(128, 8) CSA2_RX_CASE(128, 16)
+  { return hipErrorInvalidValue; }
+#undef CSA2_RX_CASE
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_select_reindex, dim3(nq), dim3(kSelThreads), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace csa2

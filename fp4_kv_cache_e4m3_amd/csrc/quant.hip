@@ -1,0 +1,134 @@
+// FP4 (E2M1 codes, one E4M3 scale per 16 channels) quantise / dequantise of
+// main-KV rows for gfx950.
+//
+// Method: DeepSeek-V4.1-Flash pages, ai-maestro.online section "FP4 KV,
+// Bounded Replay, and other extensions": the main KV quantises to E2M1 with
+// one E4M3 scale per 16 channels, NVFP4 without its global scale.  The scale
+// of a group is E4M3(amax / 6) and each element is E2M1(x / scale), both
+// rounded to nearest with ties to the even code and saturating (448 and 6).
+//
+// Exactness: neither quotient is ever formed.  Rounding y = amax/6 to the
+// E4M3 grid only needs the sign of amax - 6*mu for midpoints mu between
+// neighbouring grid values, and 6*mu (<= 7 significant bits) is exact in
+// fp32; likewise |x| / s against the E2M1 midpoints 0.25 .. 5 compares
+// |x| with m*s, exact in fp32 (<= 7 significant bits).  So every decision is
+// the exact-arithmetic one.
+//
+// One thread handles one 16-channel group: 64 B of fp32 in, 8 code bytes and
+// 1 scale byte out.  This kernel is not bandwidth critical in the decode step
+// (B rows per step); bulk quantisation of a cache is a one-off.
+#include "common.h"
+
+namespace csa2 {
+
+// value of non-negative finite E4M3 code c (0..126) as fp32 (exact)
+CSA2_DEV float e4m3_pos(uint32_t c) {
+  const uint32_t e = c >> 3, m = c & 7u;
+  return e == 0 ? (float)m * 0x1p-9f : __builtin_ldexpf((float)(8u + m), (int)e - 10);
+}
+
+// E4M3 code of amax/6: nearest, ties to even, saturating at 448 (0x7E).
+CSA2_DEV uint32_t scale_code(float amax) {
+  // count midpoints mu_c (c = 0..125) with 6*mu_c < amax  (lower bound)
+  uint32_t lo = 0, hi = 126;
+  while (lo < hi) {
+    const uint32_t mid = (lo + hi) >> 1;
+    const float t = 3.0f * (e4m3_pos(mid) + e4m3_pos(mid + 1));   // 6 * midpoint, exact
+    if (t < amax) lo = mid + 1; else hi = mid;
+  }
+  uint32_t c = lo;
+  if (c < 126u) {
+    const float t = 3.0f * (e4m3_pos(c) + e4m3_pos(c + 1));
+    if (t == amax && (c & 1u)) c += 1;                             // tie -> even code
+  }
+  return c;
+}
+
+// E2M1 code of x / s for s > 0: nearest, ties to even, saturating at 6.
+CSA2_DEV uint32_t element_code(float x, float s) {
+  const float a = fabsf(x);
+  const float mids[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
+  uint32_t cnt = 0;
+  bool tie = false;
+#pragma unroll
+  for (int j = 0; j < 7; ++j) {
+    const float t = mids[j] * s;                                   // exact
+    cnt += (t < a) ? 1u : 0u;
+    tie |= (t == a);
+  }
+  const uint32_t mag = cnt + ((tie && (cnt & 1u)) ? 1u : 0u);
+  return mag | ((__float_as_uint(x) >> 28) & 8u);
+}
+
+__global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ x, int64_t xs, int64_t rows,
+                                                  int groups, uint8_t* __restrict__ codes, int64_t cs,
+                                                  uint8_t* __restrict__ scales, int64_t ss) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= rows * groups) return;
+  const int64_t r = gid / groups;
+  const int g = (int)(gid - r * groups);
+  const float4* src = reinterpret_cast<const float4*>(x + r * xs + 16 * g);
+  float v[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 f = src[i];
+    v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const uint32_t sc = scale_code(amax);
+  const float s = e4m3_pos(sc);
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t c = (s == 0.0f) ? ((__float_as_uint(v[i]) >> 28) & 8u) : element_code(v[i], s);
+    if (i < 8) lo |= c << (4 * i); else hi |= c << (4 * (i - 8));
+  }
+  *reinterpret_cast<u2*>(codes + r * cs + 8 * g) = u2{lo, hi};
+  scales[r * ss + g] = (uint8_t)sc;
+}
+
+// One thread per 16 channels: 8 code bytes + 1 scale -> 16 fp32 values.
+__global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ codes, int64_t cs,
+                                                    const uint8_t* __restrict__ scales, int64_t ss,
+                                                    int64_t rows, int groups, float* __restrict__ out,
+                                                    int64_t os) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= rows * groups) return;
+  const int64_t r = gid / groups;
+  const int g = (int)(gid - r * groups);
+  const u2 c = *reinterpret_cast<const u2*>(codes + r * cs + 8 * g);
+  const _Float16 s = e4m3_to_half<0>(scales[r * ss + g]);
+  const v8h a = fp4x8_to_half(c[0], s);
+  const v8h b = fp4x8_to_half(c[1], s);
+  float4* dst = reinterpret_cast<float4*>(out + r * os + 16 * g);
+  dst[0] = make_float4((float)a[0], (float)a[1], (float)a[2], (float)a[3]);
+  dst[1] = make_float4((float)a[4], (float)a[5], (float)a[6], (float)a[7]);
+  dst[2] = make_float4((float)b[0], (float)b[1], (float)b[2], (float)b[3]);
+  dst[3] = make_float4((float)b[4], (float)b[5], (float)b[6], (float)b[7]);
+}
+
+hipError_t launch_quantize(const float* x, int64_t xs, int64_t rows, int dim, uint8_t* codes,
+                           int64_t cs, uint8_t* scales, int64_t ss, hipStream_t st) {
+  const int groups = dim / 16;
+  const int64_t n = rows * groups;
+  if (n == 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(k_quantize, dim3((unsigned)blocks), dim3(256), 0, st, x, xs, rows, groups, codes,
+                     cs, scales, ss);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequantize(const uint8_t* codes, int64_t cs, const uint8_t* scales, int64_t ss,
+                             int64_t rows, int dim, float* out, int64_t os, hipStream_t st) {
+  const int groups = dim / 16;
+  const int64_t n = rows * groups;
+  if (n == 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(k_dequantize, dim3((unsigned)blocks), dim3(256), 0, st, codes, cs, scales, ss, rows,
+                     groups, out, os);
+  return hipGetLastError();
+}
+
+}  // namespace csa2

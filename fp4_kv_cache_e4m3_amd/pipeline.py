@@ -1,0 +1,93 @@
+"""One CSA2 layer group on the device: staging of a synthetic workload and the
+ordered library calls of one decode / prefill step.
+
+The call order follows the pages' layer schedule (ai-maestro.online,
+"Compressed Sparse Attention 2"): a group starts with a Full layer (own FP4
+main KV, fresh indexer scan, pool + Top-512) or a Reindex layer (rescore the
+last Full layer's pool with its own indexer Q), followed by Reuse layers that
+attend with their own Q and sliding window over the latest Top-K.  Every
+step's computation runs in libcsa2.so; this module only allocates buffers and
+issues the C-ABI calls.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import _binding as B
+from . import synth
+
+
+def _dev(a: np.ndarray, device) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    return t.to(device, non_blocking=False)
+
+
+class DecodeGroup:
+    """Device state of one synthetic layer group and its step.
+
+    ``w.layers`` names the group, e.g. ("full", "reuse", "reuse", "reuse") or
+    ("reindex", "reuse", ...).  For a Reindex group the Full layer's pool is
+    produced once at set-up (from the pool-source indexer Q) and is an input
+    of every step, as it would be when the Full layer ran earlier."""
+
+    def __init__(self, w: synth.Workload, device: str = "cuda", kv_rows=None):
+        self.w = w
+        self.device = device
+        dev = device
+        B_, T, d = w.batch, w.kv_len, w.dim
+        # ---- FP4 main KV cache: quantised on the device from seeded fp32 rows
+        self.codes = torch.empty((B_ * T, d // 2), dtype=torch.uint8, device=dev)
+        self.scales = torch.empty((B_ * T, d // 16), dtype=torch.uint8, device=dev)
+        chunk = 65536
+        for b in range(B_):
+            for r0 in range(0, T, chunk):
+                n = min(chunk, T - r0)
+                src = _dev(synth.kv_source_rows(w, b, r0, n), dev)
+                base = b * T + r0
+                B.quantize_kv(src, self.codes[base:base + n], self.scales[base:base + n])
+                del src
+        # ---- indexer keys [B, T, D_I]
+        self.ik = torch.empty((B_, T, w.idx_dim), dtype=torch.int8, device=dev)
+        for b in range(B_):
+            self.ik[b].copy_(torch.from_numpy(synth.index_k(w, b)))
+        # ---- per-step inputs
+        self.new_rows = _dev(synth.new_rows(w), dev)                       # [B, d] fp32
+        self.iq = _dev(synth.index_q(w, 0), dev)
+        self.iw = _dev(synth.index_w(w, 0), dev)
+        nl = len(w.layers)
+        self.q = [_dev(synth.attn_q_bf16(w, l).view(np.int16), dev) for l in range(nl)]
+        self.swa = [_dev(synth.swa_bf16(w, l).view(np.int16), dev) for l in range(nl)]
+        # ---- outputs and workspaces
+        nq = w.nq
+        self.pool = torch.full((nq, B.POOL_BLOCKS), -1, dtype=torch.int32, device=dev)
+        self.topk = torch.full((nq, B.TOPK), -1, dtype=torch.int32, device=dev)
+        self.out = [torch.empty((nq, w.heads, d), dtype=torch.float32, device=dev) for _ in range(nl)]
+        self.iargs = B.index_args(self.iq, self.iw, self.ik, w.q_per_seq)
+        self.iws = torch.empty(max(256, B.index_workspace_size(self.iargs)), dtype=torch.uint8, device=dev)
+        self.aargs = [B.attn_args(self.q[l], self.codes, self.scales, self.topk, self.swa[l], self.out[l],
+                                  w.q_per_seq, T, w.window) for l in range(nl)]
+        aws = max(B.attn_workspace_size(a) for a in self.aargs)
+        self.aws = torch.empty(max(256, aws), dtype=torch.uint8, device=dev) if aws > 0 else None
+        # new tokens land in the last slot of each sequence: rows b*T + T-1
+        self.new_codes = self.codes[T - 1::T]
+        self.new_scales = self.scales[T - 1::T]
+        if w.layers[0] == "reindex":
+            iq0 = _dev(synth.index_q(w, 0, pool_source=True), dev)
+            iw0 = _dev(synth.index_w(w, 0, pool_source=True), dev)
+            pa = B.index_args(iq0, iw0, self.ik, w.q_per_seq)
+            scratch = torch.empty_like(self.topk)
+            B.index_full(pa, self.pool, scratch, self.iws)
+            self._pool_src = (iq0, iw0)
+        torch.cuda.synchronize()
+
+    # one pass of the whole group
+    def step(self, stream=None) -> None:
+        w = self.w
+        if w.layers[0] == "full":
+            B.quantize_kv(self.new_rows, self.new_codes, self.new_scales, stream)
+            B.index_full(self.iargs, self.pool, self.topk, self.iws, stream)
+        elif w.layers[0] == "reindex":
+            B.index_reindex(self.iargs, self.pool, self.topk, self.iws, stream)
+        for l in range(len(w.layers)):
+            B.sparse_attn(self.aargs[l], self.aws, stream)

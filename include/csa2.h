@@ -1,0 +1,217 @@
+/*
+ * csa2.h -- C ABI of the CSA2 hot path over an FP4 (E2M1 + E4M3/16) KV cache,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Method: DeepSeek-V4.1-Flash pages.
+ *   - Layer modes Full / Reindex / Reuse and the hierarchical indexer
+ *     (candidate pool of 2,048 blocks x 8 tokens = 16,384 positions, fresh
+ *     Top-512): ai-maestro.online, section "Compressed Sparse Attention 2";
+ *     wpnews.pro, "What is Compressed Sparse Attention 2 CSA2?".
+ *   - FP4 main KV: E2M1 codes with one E4M3 scale per 16 channels, NVFP4
+ *     without its global scale: ai-maestro.online, "FP4 KV, Bounded Replay,
+ *     and other extensions".
+ *   - 128-token sliding window in every layer, own Q and SWA cache per layer:
+ *     ai-maestro.online, "Causal Encoder-Decoder architecture" and
+ *     "Compressed Sparse Attention 2".
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library never allocates device memory and never synchronises the host.
+ *   - Work is enqueued on `stream` (NULL = the default stream) and runs
+ *     asynchronously; outputs are valid once the stream reaches that point.
+ *   - Arguments are validated on the host first.  On any error nothing is
+ *     launched and no output or workspace byte is written.  CSA2_ERR_HIP is
+ *     returned when the HIP runtime rejects a launch (hipGetLastError).
+ *   - Results are deterministic: the same inputs give bit-identical outputs.
+ *   - Calls that share a workspace must be ordered on one stream; calls with
+ *     distinct workspaces may run concurrently.
+ *   - Reuse layers have no entry point: they pass the latest Top-K buffer to
+ *     csa2_sparse_attn (ai-maestro.online, "Compressed Sparse Attention 2":
+ *     Reuse skips the indexer entirely).
+ */
+#ifndef CSA2_H_
+#define CSA2_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA2_TOPK 512          /* fresh Top-512 per query token              */
+#define CSA2_BLOCK 8           /* tokens per indexer block                   */
+#define CSA2_POOL_BLOCKS 2048  /* blocks in the Full layer's candidate pool  */
+#define CSA2_WINDOW 128        /* sliding-window rows per query              */
+#define CSA2_SCALE_GROUP 16    /* channels sharing one E4M3 scale            */
+
+typedef enum {
+  CSA2_OK = 0,
+  CSA2_ERR_NULL = 1,       /* a required pointer is NULL                     */
+  CSA2_ERR_SHAPE = 2,      /* unsupported or inconsistent size               */
+  CSA2_ERR_ALIGN = 3,      /* pointer or stride not aligned as documented    */
+  CSA2_ERR_WORKSPACE = 4,  /* workspace NULL or smaller than the query says  */
+  CSA2_ERR_HIP = 5         /* the HIP runtime reported a launch error        */
+} csa2_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* csa2_status_string(int status);
+
+/* ABI version, (major << 16) | minor. */
+int csa2_version(void);
+
+/*
+ * csa2_quantize_kv -- FP4 quantisation of main-KV rows.
+ * Source: ai-maestro.online, "FP4 KV, Bounded Replay, and other extensions".
+ *
+ * For every row r < rows and every 16-channel group g of x[r, 0:dim):
+ *   amax  = max |x|;  scale = E4M3(amax / 6), round to nearest, ties to the
+ *   even code, saturating at 448 (code 0x7E), never NaN;
+ *   code_i = E2M1(x_i / scale), nearest, ties to even, saturating at 6, sign
+ *   bit = sign bit of x_i; a zero scale gives signed-zero codes.
+ * Both roundings are decided exactly (threshold compares, no rounded
+ * quotient), so the result equals the exact-arithmetic definition.
+ *
+ *   x           fp32, row r at x + r * x_stride (elements); 16-byte aligned,
+ *               x_stride % 4 == 0.  Finite inputs; NaN/Inf give unspecified
+ *               (but deterministic) codes.
+ *   rows        >= 0 (0 is a no-op).
+ *   dim         % 32 == 0, 32 .. 4096.
+ *   codes       out, row r at codes + r * codes_stride (bytes): dim/2 bytes,
+ *               byte j = code[2j] | code[2j+1] << 4.  8-byte aligned,
+ *               codes_stride % 8 == 0, codes_stride >= dim/2.
+ *   scales      out, row r at scales + r * scales_stride: dim/16 E4M3FN bytes.
+ *               scales_stride >= dim/16.
+ * Strided rows let the caller write new tokens straight into their slots of
+ * a [B, T] cache (row stride T * row bytes).
+ */
+int csa2_quantize_kv(const float* x, int64_t x_stride, int64_t rows, int32_t dim,
+                     uint8_t* codes, int64_t codes_stride,
+                     uint8_t* scales, int64_t scales_stride, hipStream_t stream);
+
+/*
+ * csa2_dequantize_kv -- values of FP4 rows as fp32 (code value x E4M3 scale,
+ * exact).  Same row layout and alignment as csa2_quantize_kv; out is fp32
+ * [rows, dim] at out + r * out_stride (elements), 16-byte aligned,
+ * out_stride % 4 == 0.  Uses the same device decoder as csa2_sparse_attn.
+ */
+int csa2_dequantize_kv(const uint8_t* codes, int64_t codes_stride,
+                       const uint8_t* scales, int64_t scales_stride,
+                       int64_t rows, int32_t dim, float* out, int64_t out_stride,
+                       hipStream_t stream);
+
+/*
+ * Indexer arguments (Full and Reindex layers).
+ * Source: ai-maestro.online, "Compressed Sparse Attention 2".
+ * The pages do not print the score; the library computes, per query q and
+ * visible position t,
+ *     s(q, t) = sum_h w[q, h] * max(0, sum_c iq[q, h, c] * ik[b, t, c])
+ * with b = q / q_per_seq, the dot products in exact int32 and the weighted
+ * sum in fp32 (heads in ascending order).  Scores are exact whenever w is
+ * integer-valued and all partial sums stay below 2^24.  Ranking is by
+ * (score descending, position ascending): ties go to the lower position.
+ */
+typedef struct {
+  int32_t batch;             /* B sequences                                   */
+  int32_t q_per_seq;         /* Qn query tokens per sequence; nq = B * Qn    */
+  int64_t kv_len;            /* T rows per sequence in ik (row b * T + t)     */
+  int32_t heads;             /* H_I: 2, 4, 8 or 16                            */
+  int32_t dim;               /* D_I: 64 or 128                                */
+  const int8_t* q;           /* iq [nq, H_I, D_I], 16-byte aligned            */
+  const float* w;            /* iw [nq, H_I]                                  */
+  const int8_t* k;           /* ik [B, T, D_I] contiguous, 16-byte aligned    */
+  const int32_t* n_visible;  /* [nq] in [0, T] or NULL (= T): query q sees
+                                positions [0, n_visible[q])                  */
+} csa2_index_args;
+
+/* Bytes of workspace csa2_index_full / csa2_index_reindex need (0 on bad args). */
+size_t csa2_index_workspace_size(const csa2_index_args* args);
+
+/*
+ * csa2_index_full -- Full layer: score every visible position, take each
+ * 8-token block's maximum (blocks aligned at position 0; a partial block
+ * uses its visible positions), keep the top min(2048, #blocks) blocks by
+ * (block score desc, block id asc) as the pool, and select the top
+ * min(512, #pool positions) pool positions by (score desc, position asc).
+ * This equals the Top-512 over all visible positions.
+ *   pool   out [nq, 2048] int32 block ids, ascending, padded with -1
+ *          (may be NULL when no Reindex layer will consume it).
+ *   topk   out [nq, 512] int32 positions, ascending, padded with -1.
+ *   ws     workspace of csa2_index_workspace_size(args) bytes, 256-B aligned.
+ * Supports Qn * H_I <= 64.
+ */
+int csa2_index_full(const csa2_index_args* args, int32_t* pool, int32_t* topk,
+                    void* ws, size_t ws_size, hipStream_t stream);
+
+/*
+ * The two stages of csa2_index_full, for callers that schedule them apart
+ * (e.g. to time or overlap the scan).  csa2_index_scan streams the indexer
+ * keys once and writes every visible position's score key and every 8-token
+ * block's maximum into `ws`; csa2_index_select then forms the pool and the
+ * Top-512 from that workspace.  Both must get the same `args` and `ws`, in
+ * this order on one stream; together they equal csa2_index_full.
+ */
+int csa2_index_scan(const csa2_index_args* args, void* ws, size_t ws_size, hipStream_t stream);
+int csa2_index_select(const csa2_index_args* args, int32_t* pool, int32_t* topk,
+                      const void* ws, size_t ws_size, hipStream_t stream);
+
+/*
+ * csa2_index_reindex -- Reindex layer: rescore only the positions of the last
+ * Full layer's pool with this layer's own iq / iw and select the top
+ * min(512, #positions) by (score desc, position asc).
+ *   pool   in [nq, 2048] block ids as written by csa2_index_full for the
+ *          same query tokens: ascending, -1 only as trailing padding.
+ *          Ids outside [0, ceil(T/8)) are treated as empty.
+ *   topk   out [nq, 512], ascending, padded with -1.
+ */
+int csa2_index_reindex(const csa2_index_args* args, const int32_t* pool, int32_t* topk,
+                       void* ws, size_t ws_size, hipStream_t stream);
+
+/*
+ * Sparse + sliding-window attention of one CSA2 layer.
+ * Source: ai-maestro.online, "Compressed Sparse Attention 2" (own main Q and
+ * SWA cache per layer; Top-K indices from the Full/Reindex layer) and
+ * "Causal Encoder-Decoder architecture" (128-token window).
+ * For query q (sequence b = q / Qn, index j = q % Qn) and head h:
+ *   entries = { FP4 row b*T + t : t in topk[q], 0 <= t < T }  followed by
+ *             { swa[b, r] : j <= r < j + window, r >= swa_rows - swa_len[b] },
+ *   out[q, h] = sum_e softmax_e(sm_scale * Q[q,h] . e) * e   (key = value)
+ * in one softmax; a query with no entry gets zeros.
+ * Arithmetic: Q and SWA rows are converted bf16 -> fp16, exact for
+ * magnitudes in [2^-14, 65504] (smaller ones lose at most 2^-25 absolute);
+ * FP4 values are exact in fp16.  QK^T and PV run on fp16 MFMA with fp32
+ * accumulation, sm_scale is applied to the fp32 logits, probabilities are
+ * rounded to fp16 and normalised by the sum of the rounded values.
+ * Requires |Q| and |SWA| below 65504.
+ */
+typedef struct {
+  int32_t batch;               /* B                                            */
+  int32_t q_per_seq;           /* Qn; nq = B * Qn                              */
+  int64_t kv_len;              /* T rows per sequence in the FP4 cache         */
+  int32_t heads;               /* H: 8 or a multiple of 16, <= 128             */
+  int32_t dim;                 /* d: 128 or 512                                */
+  const uint16_t* q;           /* bf16 [nq, H, d], 16-byte aligned             */
+  const uint8_t* codes;        /* FP4 codes, row b*T+t at codes + row*codes_stride;
+                                  16-byte aligned rows                         */
+  int64_t codes_stride;        /* bytes, % 16 == 0, >= d/2                     */
+  const uint8_t* scales;       /* E4M3 scales, row at scales + row*scales_stride */
+  int64_t scales_stride;       /* bytes, % 8 == 0, >= d/16                     */
+  const int32_t* topk;         /* [nq, topk_k] positions, -1 = empty           */
+  int32_t topk_k;              /* entries per Top-K row, 0 .. 2048             */
+  const uint16_t* swa;         /* bf16 [B, swa_rows, d], swa_rows = window-1+Qn */
+  int32_t window;              /* 0 .. 1024 (128 on the pages)                 */
+  const int32_t* swa_len;      /* [B] valid trailing SWA rows, or NULL (= all) */
+  float sm_scale;              /* <= 0 selects 1/sqrt(d)                       */
+  float* out;                  /* fp32 [nq, H, d]                              */
+} csa2_attn_args;
+
+/* Bytes of workspace csa2_sparse_attn needs for these arguments (may be 0). */
+size_t csa2_attn_workspace_size(const csa2_attn_args* args);
+
+int csa2_sparse_attn(const csa2_attn_args* args, void* ws, size_t ws_size, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA2_H_ */

@@ -1,0 +1,92 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host (no launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import fp4_kv_cache_e4m3_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        pytest.skip("libcsa2.so not built (run __graft_entry__.build())")
+    return m.load()
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "csa2.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa2_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    import fp4_kv_cache_e4m3_amd as m
+    names = header_functions()
+    assert names == sorted(m.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    import fp4_kv_cache_e4m3_amd as m
+    for s in range(6):
+        assert m.status_string(s).startswith("CSA2_")
+    assert lib.csa2_version() >> 16 == 1
+
+
+def test_quantize_rejects(lib):
+    f = lib.csa2_quantize_kv
+    assert f(None, 512, 4, 33, None, 256, None, 32, None) == 2            # dim % 32
+    assert f(None, 512, 4, 512, None, 256, None, 32, None) == 1           # NULL x
+    assert f(16, 512, 4, 512, 16, 100, 16, 32, None) == 2                 # codes stride < d/2
+    assert f(8, 512, 4, 512, 16, 256, 16, 32, None) == 3                  # x misaligned
+    assert f(None, 512, 0, 512, None, 256, None, 32, None) == 0           # empty: no-op
+
+
+def test_index_rejects(lib):
+    import fp4_kv_cache_e4m3_amd as m
+    a = m.IndexArgs(1, 1, 100, 3, 64, 16, 16, 16, None)                    # 3 heads
+    assert lib.csa2_index_full(ctypes.byref(a), None, 16, None, 0, None) == 2
+    assert lib.csa2_index_workspace_size(ctypes.byref(a)) == 0
+    a = m.IndexArgs(1, 9, 100, 8, 64, 16, 16, 16, None)                    # Qn*H_I > 64
+    assert lib.csa2_index_full(ctypes.byref(a), None, 16, None, 0, None) == 2
+    a = m.IndexArgs(1, 1, 100, 8, 64, 16, 16, 16, None)
+    ws = lib.csa2_index_workspace_size(ctypes.byref(a))
+    assert ws > 0 and ws % 256 == 0
+    assert lib.csa2_index_full(ctypes.byref(a), None, 16, 256, ws - 1, None) == 4
+    assert lib.csa2_index_full(ctypes.byref(a), None, 16, None, ws, None) == 4
+    assert lib.csa2_index_full(ctypes.byref(a), None, None, 256, ws, None) == 1
+    a = m.IndexArgs(1, 1, 100, 8, 64, 17, 16, 16, None)                    # iq misaligned
+    assert lib.csa2_index_full(ctypes.byref(a), None, 16, 256, ws, None) == 3
+    assert lib.csa2_index_reindex(ctypes.byref(m.IndexArgs(1, 1, 100, 8, 64, 16, 16, 16, None)),
+                                  None, 16, 256, ws, None) == 1            # no pool
+    a = m.IndexArgs(1, 1, (1 << 20) + 1, 8, 64, 16, 16, 16, None)          # T too long
+    assert lib.csa2_index_workspace_size(ctypes.byref(a)) == 0
+
+
+def test_attn_rejects(lib):
+    import fp4_kv_cache_e4m3_amd as m
+
+    def args(**kw):
+        base = dict(batch=2, q_per_seq=1, kv_len=64, heads=16, dim=512, q=256, codes=256,
+                    codes_stride=256, scales=256, scales_stride=32, topk=256, topk_k=512, swa=256,
+                    window=128, swa_len=None, sm_scale=0.0, out=256)
+        base.update(kw)
+        return m.AttnArgs(**base)
+
+    sa = lib.csa2_sparse_attn
+    assert sa(ctypes.byref(args(dim=256)), None, 0, None) == 2
+    assert sa(ctypes.byref(args(topk_k=4096)), None, 0, None) == 2
+    assert sa(ctypes.byref(args(q=None)), None, 0, None) == 1
+    assert sa(ctypes.byref(args(codes_stride=200)), None, 0, None) == 2
+    assert sa(ctypes.byref(args(codes_stride=264)), None, 0, None) == 3
+    assert sa(ctypes.byref(args(out=260)), None, 0, None) == 3
+    a = args()
+    need = lib.csa2_attn_workspace_size(ctypes.byref(a))
+    assert need > 0                                   # 2 queries x 4 head groups -> split
+    assert sa(ctypes.byref(a), None, 0, None) == 4
+    assert sa(ctypes.byref(a), 256, need - 1, None) == 4

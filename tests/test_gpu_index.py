@@ -1,0 +1,134 @@
+"""GPU parity of csa2_index_full / csa2_index_reindex against the oracle:
+bit-exact pools and Top-512 lists (including the -1 padding), at small ragged
+shapes, at the single-sequence T=4096 workload and at the full batch-32,
+64K-entry decode workload."""
+import numpy as np
+import pytest
+import torch
+
+import fp4_kv_cache_e4m3_amd as csa2
+from fp4_kv_cache_e4m3_amd import synth
+from oracle import indexer as oidx
+from tests.parity import dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def run_full(iq, iw, ik, qn, n_visible=None, with_pool=True):
+    iq_d, iw_d, ik_d = dev(iq), dev(iw), dev(ik)
+    nv_d = dev(np.asarray(n_visible, dtype=np.int32)) if n_visible is not None else None
+    nq = iq.shape[0]
+    pool = torch.full((nq, 2048), -7, dtype=torch.int32, device="cuda")
+    topk = torch.full((nq, 512), -7, dtype=torch.int32, device="cuda")
+    args = csa2.index_args(iq_d, iw_d, ik_d, qn, nv_d)
+    ws = torch.empty(max(256, csa2.index_workspace_size(args)), dtype=torch.uint8, device="cuda")
+    csa2.index_full(args, pool if with_pool else None, topk, ws)
+    return host(pool), host(topk)
+
+
+def run_reindex(iq, iw, ik, qn, pool, n_visible=None):
+    iq_d, iw_d, ik_d = dev(iq), dev(iw), dev(ik)
+    nv_d = dev(np.asarray(n_visible, dtype=np.int32)) if n_visible is not None else None
+    topk = torch.full((iq.shape[0], 512), -7, dtype=torch.int32, device="cuda")
+    args = csa2.index_args(iq_d, iw_d, ik_d, qn, nv_d)
+    ws = torch.empty(max(256, csa2.index_workspace_size(args)), dtype=torch.uint8, device="cuda")
+    csa2.index_reindex(args, dev(pool.astype(np.int32)), topk, ws)
+    return host(topk)
+
+
+def inputs(seed, B, Qn, T, HI, DI, r, wmax):
+    rng = np.random.default_rng(seed)
+    iq = rng.integers(-r, r + 1, size=(B * Qn, HI, DI), dtype=np.int8)
+    iw = rng.integers(1, wmax + 1, size=(B * Qn, HI)).astype(np.float32)
+    ik = rng.integers(-r, r + 1, size=(B, T, DI), dtype=np.int8)
+    return iq, iw, ik
+
+
+CASES = [  # (B, Qn, T, H_I, D_I, r, wmax)
+    (1, 1, 1, 2, 64, 4, 4),
+    (2, 1, 9, 2, 64, 4, 4),
+    (1, 1, 4096, 2, 64, 4, 4),
+    (3, 1, 5003, 8, 128, 8, 8),
+    (2, 6, 20011, 8, 128, 8, 8),      # several queries per sequence, pool drops blocks
+    (2, 4, 17003, 16, 64, 2, 2),
+    (2, 3, 16400, 4, 128, 1, 1),      # heavy ties
+    (1, 5, 300, 2, 64, 1, 3),
+    (2, 1, 33000, 8, 64, 0, 1),       # all scores equal
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}Q{}T{}H{}D{}".format(*c[:5]))
+def test_index_full_matches_oracle(case):
+    B, Qn, T, HI, DI, r, wmax = case
+    iq, iw, ik = inputs(hash(case) % 1000, B, Qn, T, HI, DI, r, wmax)
+    pool, topk = run_full(iq, iw, ik, Qn)
+    rpool, rtopk = oidx.index_full(iq, iw, ik, Qn)
+    np.testing.assert_array_equal(pool, rpool)
+    np.testing.assert_array_equal(topk, rtopk)
+
+
+def test_index_full_n_visible_ragged():
+    B, Qn, T = 3, 4, 21000
+    iq, iw, ik = inputs(11, B, Qn, T, 8, 128, 3, 5)
+    nv = np.array([T, 0, 1, 7, 8, 9, 16, 17, 513, 16385, 20999, 12345], dtype=np.int32)
+    pool, topk = run_full(iq, iw, ik, Qn, nv)
+    rpool, rtopk = oidx.index_full(iq, iw, ik, Qn, nv)
+    np.testing.assert_array_equal(pool, rpool)
+    np.testing.assert_array_equal(topk, rtopk)
+
+
+def test_index_full_without_pool_output():
+    iq, iw, ik = inputs(3, 2, 1, 3000, 8, 128, 8, 8)
+    _, topk = run_full(iq, iw, ik, 1, with_pool=False)
+    _, rtopk = oidx.index_full(iq, iw, ik, 1)
+    np.testing.assert_array_equal(topk, rtopk)
+
+
+def test_index_full_single_sequence_t4096():
+    w = synth.C1
+    iq, iw, ik = synth.index_q(w), synth.index_w(w), synth.index_k_all(w)
+    pool, topk = run_full(iq, iw, ik, 1)
+    rpool, rtopk = oidx.index_full(iq, iw, ik, 1)
+    np.testing.assert_array_equal(pool, rpool)
+    np.testing.assert_array_equal(topk, rtopk)
+
+
+@pytest.fixture(scope="module")
+def c2_inputs():
+    w = synth.C2
+    return w, synth.index_q(w), synth.index_w(w), synth.index_k_all(w)
+
+
+def test_index_full_batch32_t65536(c2_inputs):
+    w, iq, iw, ik = c2_inputs
+    pool, topk = run_full(iq, iw, ik, 1)
+    rpool, rtopk = oidx.index_full(iq, iw, ik, 1)
+    np.testing.assert_array_equal(pool, rpool)
+    np.testing.assert_array_equal(topk, rtopk)
+    # repeat: bit-identical
+    pool2, topk2 = run_full(iq, iw, ik, 1)
+    np.testing.assert_array_equal(pool, pool2)
+    np.testing.assert_array_equal(topk, topk2)
+
+
+def test_index_reindex_batch32_t65536(c2_inputs):
+    w, _, _, ik = c2_inputs
+    iq0, iw0 = synth.index_q(w, 0, pool_source=True), synth.index_w(w, 0, pool_source=True)
+    rpool, rtopk0 = oidx.index_full(iq0, iw0, ik, 1)
+    iq, iw = synth.index_q(w, 1), synth.index_w(w, 1)
+    topk = run_reindex(iq, iw, ik, 1, rpool)
+    np.testing.assert_array_equal(topk, oidx.index_reindex(iq, iw, ik, 1, rpool))
+    # invariant: rescoring with the Full layer's own q reproduces its Top-512
+    np.testing.assert_array_equal(run_reindex(iq0, iw0, ik, 1, rpool), rtopk0)
+
+
+@pytest.mark.parametrize("case", CASES[3:7], ids=lambda c: "B{}Q{}T{}H{}D{}".format(*c[:5]))
+def test_index_reindex_matches_oracle(case):
+    B, Qn, T, HI, DI, r, wmax = case
+    iq, iw, ik = inputs(hash(case) % 997, B, Qn, T, HI, DI, r, wmax)
+    rpool, _ = oidx.index_full(iq, iw, ik, Qn)
+    iq2, iw2, _ = inputs(hash(case) % 991 + 1, B, Qn, T, HI, DI, r, wmax)
+    nv = np.full(B * Qn, T, dtype=np.int32)
+    nv[0] = T // 2
+    topk = run_reindex(iq2, iw2, ik, Qn, rpool, nv)
+    np.testing.assert_array_equal(topk, oidx.index_reindex(iq2, iw2, ik, Qn, rpool, nv))
