@@ -45,28 +45,39 @@ IndexLayout index_layout(const csa2_index_args* a) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_ERR_HIP; }
 
-// Splits of the attention tile list over workgroups: aim for >= 256 workgroups
-// while keeping >= 8 tiles (2 per wave) in each split.
-int attn_splits(int64_t nq, int heads, int n_tiles) {
+int env_int(const char* name, int dflt) {
+  const char* e = std::getenv(name);
+  return e ? std::atoi(e) : dflt;
+}
+
+// Work split of one attention layer.  A workgroup owns (query, 16 heads, a
+// contiguous range of 16-entry tiles); its NW waves take every NW-th tile.
+// With few (query, head-group) pairs, 8 waves per workgroup (two per SIMD)
+// keep the whole tile list in one workgroup; with many pairs, 4 waves.
+// Splits of the tile list over workgroups are used only when the grid would
+// otherwise leave most CUs idle; their partial states are merged by a second
+// kernel.  CSA2_ATTN_WAVES / CSA2_ATTN_SPLITS override the choice (tuning).
+void attn_plan(int64_t nq, int heads, int n_tiles, int& waves, int& splits) {
   const int64_t base = nq * ((heads + 15) / 16);
-  int s = 1;
-  if (const char* e = std::getenv("CSA2_ATTN_SPLITS")) {
-    s = std::atoi(e);
-  } else if (base > 0) {
-    s = (int)((256 + base - 1) / base);
-    const int cap = n_tiles / 8 > 1 ? n_tiles / 8 : 1;
-    if (s > cap) s = cap;
+  waves = env_int("CSA2_ATTN_WAVES", base <= 512 ? 8 : 4);
+  if (waves != 4 && waves != 8) waves = 4;
+  int dflt = 1;
+  if (base > 0 && base < 128) {            // fewer than half the CUs busy: split
+    dflt = (int)((256 + base - 1) / base);
+    const int cap = n_tiles / (2 * waves) > 1 ? n_tiles / (2 * waves) : 1;
+    if (dflt > cap) dflt = cap;
   }
+  int s = env_int("CSA2_ATTN_SPLITS", dflt);
   if (s < 1) s = 1;
-  if (s > n_tiles && n_tiles > 0) s = n_tiles;
   if (n_tiles == 0) s = 1;
+  if (s > n_tiles && n_tiles > 0) s = n_tiles;
   const int tps = n_tiles > 0 ? (n_tiles + s - 1) / s : 1;
-  return n_tiles > 0 ? (n_tiles + tps - 1) / tps : 1;
+  splits = n_tiles > 0 ? (n_tiles + tps - 1) / tps : 1;
 }
 
 struct AttnLayout {
   int64_t nq;
-  int n_sparse_tiles, n_tiles, splits, tps, swa_rows;
+  int n_sparse_tiles, n_tiles, splits, tps, swa_rows, waves;
   int64_t ws_bytes;
 };
 
@@ -76,7 +87,7 @@ AttnLayout attn_layout(const csa2_attn_args* a) {
   L.n_sparse_tiles = a->kv_len > 0 ? (a->topk_k + 15) / 16 : 0;
   L.swa_rows = a->window > 0 ? a->window - 1 + a->q_per_seq : 0;
   L.n_tiles = L.n_sparse_tiles + (a->window + 15) / 16;
-  L.splits = attn_splits(L.nq, a->heads, L.n_tiles);
+  attn_plan(L.nq, a->heads, L.n_tiles, L.waves, L.splits);
   L.tps = L.n_tiles > 0 ? (L.n_tiles + L.splits - 1) / L.splits : 1;
   L.ws_bytes = 0;
   if (L.splits > 1) {
@@ -228,7 +239,7 @@ int csa2_sparse_attn(const csa2_attn_args* a, void* ws, size_t ws_size, hipStrea
   p.qscale = sm * 1.4426950408889634f;
   // With no tile at all the kernel still runs: every head ends with an empty
   // softmax and writes zeros (no memset node, so the call stays graph-safe).
-  return hip_status(launch_attn(p, (int)L.nq, a->dim, stream));
+  return hip_status(launch_attn(p, (int)L.nq, a->dim, L.waves, stream));
 }
 
 }  // extern "C"

@@ -53,6 +53,16 @@ CSA2_DEV v4h lds_read_tr16(const _Float16* p) {
   return __builtin_bit_cast(v4h, r);
 }
 
+// max over lanes {l, l^16, l^32, l^48}: gfx950 permlane swaps (no LDS traffic);
+// permlane16_swap(x, x) yields the values of lanes l and l^16, the 32 variant
+// those of l and l^32
+CSA2_DEV float max_over_quarters(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 template <int SEL>
 CSA2_DEV _Float16 scale_half(uint32_t w) { return e4m3_to_half<SEL>(w); }
 
@@ -93,28 +103,28 @@ CSA2_DEV bool load_fp4(const AttnParams& p, int32_t pos, int64_t b, int g, Fp4Ra
   return valid;
 }
 
-// LDS tiles are D halves per row with 16-byte chunks XOR-swizzled per row
-// (chunk c of row r lives at chunk c ^ sw(r)) instead of padded, so four
-// per-wave V tiles plus the Q tile take exactly 80 KiB and two workgroups fit
-// on a CU.  V rows use sw(r) = 2r mod 16: a transposing read of 32 lanes
-// (rows 4G + r, 8-byte column groups) then hits 64 distinct banks.  Q rows use
-// sw(h) = h mod 16: 16 lanes reading the same chunk of 16 rows hit 16
-// distinct 16-byte bank groups.
+// LDS tiles are padded rows of D + 8 halves: consecutive rows start 4 banks
+// apart, so the 16-byte staging writes and Q reads (16 rows, same column) and
+// the transposing V reads stay within a few bank groups, and every address is
+// a per-lane base plus a compile-time offset.
 template <int D, typename KV>
-CSA2_DEV void attend_tile(const AttnParams& p, KV kvf, bool valid, const _Float16* qrow, int qsw,
-                          _Float16* wrow, int wsw, int wchunk0, const _Float16* vrow, int vsw, int vq, int g,
-                          v4f (&o)[D / 16], float& m_run, float& l_run) {
+CSA2_DEV void attend_tile(const AttnParams& p, KV kvf, bool valid, const _Float16* qbase, _Float16* wbase,
+                          const _Float16* vbase, int g, v4f (&o)[D / 16], float& m_run, float& l_run) {
   constexpr int KS = D / 32, NT = D / 16;
-  v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  constexpr int NA = KS >= 4 ? 4 : KS;      // independent MFMA accumulation chains
+  v4f accs[NA];
+#pragma unroll
+  for (int a = 0; a < NA; ++a) accs[a] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     const v8h kv = kvf(ks);
-    const v8h qv = *reinterpret_cast<const v8h*>(qrow + (((wchunk0 + ks) ^ qsw) << 3));
-    if (ks & 1) acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, qv, acc1, 0, 0, 0);
-    else        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, qv, acc0, 0, 0, 0);
-    *reinterpret_cast<v8h*>(wrow + (((wchunk0 + ks) ^ wsw) << 3)) = kv;
+    const v8h qv = *reinterpret_cast<const v8h*>(qbase + 8 * ks);
+    accs[ks % NA] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, qv, accs[ks % NA], 0, 0, 0);
+    *reinterpret_cast<v8h*>(wbase + 8 * ks) = kv;
   }
-  const v4f acc = acc0 + acc1;
+  v4f acc = accs[0];
+#pragma unroll
+  for (int a = 1; a < NA; ++a) acc += accs[a];
 
   // online softmax (head = lane % 16, entries 4g..4g+3).  The reference max
   // only moves when a tile's max exceeds it by more than 2^8, so O is rarely
@@ -127,19 +137,18 @@ CSA2_DEV void attend_tile(const AttnParams& p, KV kvf, bool valid, const _Float1
     s4[i] = ((vm >> (4 * g + i)) & 1ull) ? acc[i] * p.qscale : -__builtin_inff();
     tmax = fmaxf(tmax, s4[i]);
   }
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+  tmax = max_over_quarters(tmax);
   const bool grow = tmax > m_run + 8.0f;
   float alpha = 1.0f;
   if (grow) {
-    alpha = exp2f(m_run - tmax);
+    alpha = __builtin_amdgcn_exp2f(m_run - tmax);
     m_run = tmax;
   }
   v4h pa;
   float psum = 0.0f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const _Float16 ph = (s4[i] == -__builtin_inff()) ? (_Float16)0.0f : (_Float16)exp2f(s4[i] - m_run);
+    const _Float16 ph = (s4[i] == -__builtin_inff()) ? (_Float16)0.0f : (_Float16)__builtin_amdgcn_exp2f(s4[i] - m_run);
     pa[i] = ph;
     psum += (float)ph;          // normalise with the probabilities actually used
   }
@@ -159,16 +168,17 @@ CSA2_DEV void attend_tile(const AttnParams& p, KV kvf, bool valid, const _Float1
   wave_lds_sync();
 #pragma unroll
   for (int t = 0; t < NT; ++t)
-    o[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, lds_read_tr16(vrow + ((((2 * t) ^ vsw) << 3) | vq)), o[t], 0, 0, 0);
+    o[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, lds_read_tr16(vbase + 16 * t), o[t], 0, 0, 0);
   wave_lds_sync();
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void k_attn(AttnParams p) {
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void k_attn(AttnParams p) {
   constexpr int KS = D / 32;        // QK k-steps; each lane holds 8*KS = D/4 channels
   constexpr int NT = D / 16;        // PV output tiles of 16 channels
-  __shared__ __attribute__((aligned(16))) _Float16 vt[4 * 16 * D];   // per-wave V tiles
-  __shared__ __attribute__((aligned(16))) _Float16 qs[16 * D];       // Q of the 16 heads
+  constexpr int PITCH = D + 8;      // LDS row pitch in halves
+  __shared__ __attribute__((aligned(16))) _Float16 vt[NW * 16 * PITCH];  // per-wave V tiles
+  __shared__ __attribute__((aligned(16))) _Float16 qs[16 * PITCH];       // Q of the 16 heads
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
@@ -187,11 +197,11 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
   // Q staging so the latencies overlap (a tile's gather then needs no
   // dependent index load)
   constexpr int PB = 8;                             // FP4 tiles per position batch
-  const int n_fp4 = tile < sp_end ? (sp_end - tile + 3) / 4 : 0;
+  const int n_fp4 = tile < sp_end ? (sp_end - tile + NW - 1) / NW : 0;
   auto load_positions = [&](int first, int32_t (&pos)[PB]) {
 #pragma unroll
     for (int i = 0; i < PB; ++i) {
-      const int ti = tile + 4 * (first + i);
+      const int ti = tile + NW * (first + i);
       const int slot = ti * 16 + n;
       pos[i] = (first + i < n_fp4 && slot < p.topk_k) ? p.topk[q * p.topk_k + slot] : -1;
     }
@@ -200,18 +210,27 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
   load_positions(0, pos);
 
   // ---- stage Q (16 heads x D, bf16 -> fp16 unscaled, exact in fp16's normal
-  // range) in LDS; every wave reads its B operand from there
-  {
-    constexpr int PER = 16 * D / 256;               // halves per thread
-    const int hr = threadIdx.x / (D / PER), c0 = (threadIdx.x % (D / PER)) * PER;
-    const int h = h0 + hr;
-    const uint16_t* src = p.q + (q * p.heads + (h < p.heads ? h : 0)) * D + c0;
+  // range) in LDS; every wave reads its B operand from there.  The Q loads and
+  // the first FP4 gather are both in flight before either is waited on.
+  constexpr int QCH = 16 * D / 8;                 // 8-half chunks of the Q tile
+  constexpr int QPT = (QCH + 64 * NW - 1) / (64 * NW);
+  u4 qraw[QPT];
 #pragma unroll
-    for (int i = 0; i < PER / 8; ++i) {
-      v8h f = bf16x8_to_half(*reinterpret_cast<const u4*>(src + 8 * i));
-      if (h >= p.heads) f = v8h{0, 0, 0, 0, 0, 0, 0, 0};
-      *reinterpret_cast<v8h*>(qs + hr * D + ((((c0 >> 3) + i) ^ (hr & 15)) << 3)) = f;
-    }
+  for (int i = 0; i < QPT; ++i) {
+    const int c = threadIdx.x + 64 * NW * i;
+    const int hr = c / (D / 8), h = h0 + hr;
+    if (c < QCH) qraw[i] = *reinterpret_cast<const u4*>(p.q + (q * p.heads + (h < p.heads ? h : 0)) * D +
+                                                         (c % (D / 8)) * 8);
+  }
+  Fp4Raw<D> raw;
+  bool valid = n_fp4 > 0 ? load_fp4<D>(p, pos[0], b, g, raw) : false;
+#pragma unroll
+  for (int i = 0; i < QPT; ++i) {
+    const int c = threadIdx.x + 64 * NW * i;
+    const int hr = c / (D / 8);
+    v8h f = bf16x8_to_half(qraw[i]);
+    if (h0 + hr >= p.heads) f = v8h{0, 0, 0, 0, 0, 0, 0, 0};
+    if (c < QCH) *reinterpret_cast<v8h*>(qs + hr * PITCH + (c % (D / 8)) * 8) = f;
   }
   __syncthreads();
 
@@ -220,25 +239,19 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
   for (int t = 0; t < NT; ++t) o[t] = v4f{0.f, 0.f, 0.f, 0.f};
   float m_run = -__builtin_inff(), l_run = 0.0f;
 
-  _Float16* my = vt + wave * 16 * D;
-  // staging: lane writes entry n, chunks D/32*g + ks (8 halves each)
-  _Float16* wrow = my + n * D;
-  const int wsw = (2 * n) & 15, wchunk0 = (D / 32) * g;
-  // transposing PV read: lane reads row 4g + n/4, halves 16t + 4(n%4) .. +4
-  const int vr = 4 * g + (n >> 2);
-  const _Float16* vrow = my + vr * D;
-  const int vsw = (2 * vr) & 15, vq = 4 * (n & 3);
-  // QK B operand: head n, same chunks as the staging write
-  const _Float16* qrow = qs + n * D;
-  const int qsw = n & 15;
+  _Float16* my = vt + wave * 16 * PITCH;
+  _Float16* wbase = my + n * PITCH + (D / 4) * g;                  // staging: entry n, quarter g
+  const _Float16* vbase = my + (4 * g + (n >> 2)) * PITCH + 4 * (n & 3);   // transposing PV read
+  const _Float16* qbase = qs + n * PITCH + (D / 4) * g;            // QK B operand: head n
   const v8h zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
 
   // ---- FP4 tiles: positions in batches of PB, next gather in flight while
   // the current tile is processed
   for (int first = 0; first < n_fp4; first += PB) {
-    if (first > 0) load_positions(first, pos);
-    Fp4Raw<D> raw;
-    bool valid = load_fp4<D>(p, pos[0], b, g, raw);
+    if (first > 0) {
+      load_positions(first, pos);
+      valid = load_fp4<D>(p, pos[0], b, g, raw);
+    }
     const int cnt = min(PB, n_fp4 - first);
 #pragma unroll 1
     for (int i = 0; i < cnt; ++i) {
@@ -247,18 +260,17 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
       const Fp4Raw<D> cur = raw;
       const bool cur_valid = valid;
       if (i + 1 < cnt) valid = load_fp4<D>(p, pos[0], b, g, raw);
+      // an empty slot gets scale 0: finite zeros in V, and its logits are masked
       _Float16 sc[KS / 2];
 #pragma unroll
-      for (int gi = 0; gi < KS / 2; ++gi) sc[gi] = scale_sel(cur.s[gi >> 2], gi & 3);
-      attend_tile<D>(p, [&](int ks) {
-        const v8h v = fp4x8_to_half(cur.c[ks >> 2][ks & 3], sc[ks >> 1]);
-        return cur_valid ? v : zero8;
-      }, cur_valid, qrow, qsw, wrow, wsw, wchunk0, vrow, vsw, vq, g, o, m_run, l_run);
+      for (int gi = 0; gi < KS / 2; ++gi) sc[gi] = cur_valid ? scale_sel(cur.s[gi >> 2], gi & 3) : (_Float16)0.0f;
+      attend_tile<D>(p, [&](int ks) { return fp4x8_to_half(cur.c[ks >> 2][ks & 3], sc[ks >> 1]); },
+                     cur_valid, qbase, wbase, vbase, g, o, m_run, l_run);
     }
   }
-  tile += 4 * n_fp4;
+  tile += NW * n_fp4;
   // ---- sliding-window tiles (bf16 rows)
-  for (; tile < t_end; tile += 4) {
+  for (; tile < t_end; tile += NW) {
     const int wr = (tile - p.n_sparse_tiles) * 16 + n;
     const int r = j + wr;
     const bool v = wr < p.window && r >= first_swa && r < p.swa_rows;
@@ -266,11 +278,11 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
     u4 w[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) w[ks] = *reinterpret_cast<const u4*>(rp + 8 * ks);
-    attend_tile<D>(p, [&](int ks) { return v ? bf16x8_to_half(w[ks]) : zero8; }, v, qrow, qsw, wrow, wsw,
-                   wchunk0, vrow, vsw, vq, g, o, m_run, l_run);
+    attend_tile<D>(p, [&](int ks) { return v ? bf16x8_to_half(w[ks]) : zero8; }, v, qbase, wbase, vbase, g,
+                   o, m_run, l_run);
   }
 
-  // ---- merge the 4 waves: M = max m_w, L = sum f_w l_w, O = sum f_w O_w
+  // ---- merge the NW waves: M = max m_w, L = sum f_w l_w, O = sum f_w O_w
   float l_tot = l_run + __shfl_xor(l_run, 16, 64);
   l_tot = l_tot + __shfl_xor(l_tot, 32, 64);
   __syncthreads();                                  // every wave is done with the Q tile
@@ -283,10 +295,10 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
     const int hh = 4 * g + i;
     float mx = -__builtin_inff();
 #pragma unroll
-    for (int w = 0; w < 4; ++w) mx = fmaxf(mx, ml[w][hh][0]);
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, ml[w][hh][0]);
     float ls = 0.0f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float mw = ml[w][hh][0];
       ls += (mw == -__builtin_inff()) ? 0.0f : exp2f(mw - mx) * ml[w][hh][1];
     }
@@ -300,33 +312,25 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[t][i] *= fme[i];
 
-  float* fb = reinterpret_cast<float*>(vt);     // [2][16][D] fp32, reuses the tile buffers
-  if (wave >= 2) {
+  // pairwise tree in a fixed order through a lane-major fp32 buffer
+  // (element (slot, t, lane) holds o[t] of one wave); reuses the tile buffers
+  v4f* fb = reinterpret_cast<v4f*>(vt);
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+  for (int r = 1; r < NW; r <<= 1) {
+    if ((wave & (2 * r - 1)) == r) {
+      const int slot = wave / (2 * r);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) fb[(wave - 2) * 16 * D + (4 * g + i) * D + 16 * t + n] = o[t][i];
+      for (int t = 0; t < NT; ++t) fb[(slot * NT + t) * 64 + lane] = o[t];
+    }
+    __syncthreads();
+    if ((wave & (2 * r - 1)) == 0) {
+      const int slot = wave / (2 * r);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) o[t] += fb[(slot * NT + t) * 64 + lane];
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  if (wave < 2) {
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[t][i] += fb[wave * 16 * D + (4 * g + i) * D + 16 * t + n];
-  }
-  __syncthreads();
-  if (wave == 1) {
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) fb[(4 * g + i) * D + 16 * t + n] = o[t][i];
-  }
-  __syncthreads();
   if (wave != 0) return;
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o[t][i] += fb[(4 * g + i) * D + 16 * t + n];
 
   if (p.splits == 1) {
 #pragma unroll
@@ -375,20 +379,19 @@ __global__ __launch_bounds__(D / 4) void k_attn_combine(AttnParams p) {
       make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
 }
 
-hipError_t launch_attn(const AttnParams& p, int nq, int dim, hipStream_t st) {
+hipError_t launch_attn(const AttnParams& p, int nq, int dim, int waves, hipStream_t st) {
   if (nq == 0) return hipSuccess;
   const int ngroups = (p.heads + 15) / 16;
   const dim3 grid(ngroups * p.splits, nq);
-  if (dim == 512) {
-    hipLaunchKernelGGL(k_attn<512>, grid, dim3(256), 0, st, p);
-    if (p.splits > 1) hipLaunchKernelGGL(k_attn_combine<512>, dim3(nq * p.heads), dim3(128), 0, st, p);
-  } else if (dim == 128) {
-    hipLaunchKernelGGL(k_attn<128>, grid, dim3(256), 0, st, p);
-    if (p.splits > 1) hipLaunchKernelGGL(k_attn_combine<128>, dim3(nq * p.heads), dim3(32), 0, st, p);
-  } else {
-    return hipErrorInvalidValue;
+#define CSA2_ATTN_CASE(D, NW)                                                                 \
+  if (dim == D && waves == NW) {                                                              \
+    hipLaunchKernelGGL((k_attn<D, NW>), grid, dim3(64 * NW), 0, st, p);                       \
+    if (p.splits > 1) hipLaunchKernelGGL(k_attn_combine<D>, dim3(nq * p.heads), dim3(D / 4), 0, st, p); \
+    return hipGetLastError();                                                                 \
   }
-  return hipGetLastError();
+  CSA2_ATTN_CASE(512, 4) CSA2_ATTN_CASE(512, 8) CSA2_ATTN_CASE(128, 4) CSA2_ATTN_CASE(128, 8)
+#undef CSA2_ATTN_CASE
+  return hipErrorInvalidValue;
 }
 
 }  // namespace csa2

@@ -113,6 +113,6 @@ hipError_t launch_dequantize(const uint8_t* codes, int64_t cs, const uint8_t* sc
 hipError_t launch_index_scan(const ScanParams& p, int heads, int dim, hipStream_t st);
 hipError_t launch_select_full(const SelectParams& p, int nq, int64_t max_blocks, hipStream_t st);
 hipError_t launch_reindex(const ReindexParams& p, int nq, int heads, int dim, hipStream_t st);
-hipError_t launch_attn(const AttnParams& p, int nq, int dim, hipStream_t st);
+hipError_t launch_attn(const AttnParams& p, int nq, int dim, int waves, hipStream_t st);
 
 }  // namespace csa2
