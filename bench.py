@@ -95,8 +95,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; the multi-GPU design is "
-                                   "described in DESIGN.md and not executed", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "only --gpus 1 is supported: the path runs on one GPU and "
+                                   "its multi-GPU sharding is not implemented", "n_gpus": args.gpus}))
         return 2
 
     import torch

@@ -22,8 +22,8 @@ What it computes, and where the pages say so (DeepSeek-V4.1-Flash pages):
   Encoder-Decoder architecture" for the window, "Compressed Sparse
   Attention 2" for the per-layer Q and SWA).
 
-Readings of points the pages leave open are listed in the design doc's readings
-table and repeated next to the code that takes them.
+Each reading of a point the pages leave open is stated next to the code that
+takes it, numbered R1..R25.
 
 Pins (tests/test_oracle_*.py, run with ``-m "not gpu"``): bit-field decoders
 against torch's float8_e4m3fn cast and the E2M1 value fixture; the quantiser

@@ -9,7 +9,7 @@ Encoder-Decoder architecture"); Full/Reindex layers attend over fresh Top-512
 indices, Reuse layers over the latest ones; the main KV is stored as FP4
 (E2M1 with one E4M3 scale per 16 channels).
 
-Readings (readings table):
+Readings taken for what the pages leave open:
 
 * R14  one d-vector per entry is both key and value (main cache and SWA);
 * R15  query j of a sequence sees SWA buffer rows j .. j+W-1, i.e. the W

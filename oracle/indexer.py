@@ -13,7 +13,7 @@ wpnews.pro "What is Compressed Sparse Attention 2 CSA2?"; kongchang.com
 "Three Core Innovations", where "16,000 blocks" is a garble of 16,384
 positions.)
 
-Readings (readings table) for what the pages leave open:
+Readings taken for what the pages leave open:
 
 * R9   score s(q, t) = sum_h w[q, h] * max(0, q_h . k_t): one indexer key per
        position shared by all indexer heads, one weight per query and head;

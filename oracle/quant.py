@@ -8,7 +8,7 @@ Replay, and other extensions"; wpnews.pro, "What is Compressed Sparse
 Attention 2 CSA2?": one E4M3 scaling factor per 16 channels; cutthecrap,
 "Architectural Breakthroughs": one scale for every 16 values).
 
-The pages give no formula; readings (readings table):
+The pages give no formula; the readings taken for what they leave open:
 
 * R2  a scale group is 16 consecutive channels of one entry;
 * R3  scale = E4M3(amax / 6) rounded to nearest, ties to the even code
