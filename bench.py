@@ -93,6 +93,9 @@ def main() -> int:
     ap.add_argument("--workload", default="decode_group_full_reuse3_b32_t65536")
     ap.add_argument("--cpu-seqs", type=int, default=32, help="sequences in the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB three times (the "
+                         "reference for scaling HBM byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "only --gpus 1 is supported: the path runs on one GPU and "
@@ -100,6 +103,16 @@ def main() -> int:
         return 2
 
     import torch
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+        return 0
 
     import fp4_kv_cache_e4m3_amd as csa2
     from fp4_kv_cache_e4m3_amd import synth

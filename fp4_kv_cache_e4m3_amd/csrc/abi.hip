@@ -50,16 +50,16 @@ int env_int(const char* name, int dflt) {
   return e ? std::atoi(e) : dflt;
 }
 
-// Work split of one attention layer.  A workgroup owns (query, 16 heads, a
-// contiguous range of 16-entry tiles); its NW waves take every NW-th tile.
-// With few (query, head-group) pairs, 8 waves per workgroup (two per SIMD)
-// keep the whole tile list in one workgroup; with many pairs, 4 waves.
-// Splits of the tile list over workgroups are used only when the grid would
-// otherwise leave most CUs idle; their partial states are merged by a second
-// kernel.  CSA2_ATTN_WAVES / CSA2_ATTN_SPLITS override the choice (tuning).
+// Work split of one attention layer.  A workgroup owns (query, 16 heads, one
+// column half of the output channels, a contiguous range of 16-entry tiles);
+// its NW waves take every NW-th tile.  With few workgroups, 8 waves (two per
+// SIMD) keep the whole tile list in one workgroup; with many, 4.  Splits of
+// the tile list over workgroups are used only when the grid would otherwise
+// leave most CUs idle; their partial states are merged by a second kernel.
+// CSA2_ATTN_WAVES / CSA2_ATTN_SPLITS override the choice (tuning).
 void attn_plan(int64_t nq, int heads, int n_tiles, int& waves, int& splits) {
-  const int64_t base = nq * ((heads + 15) / 16);
-  waves = env_int("CSA2_ATTN_WAVES", base <= 512 ? 8 : 4);
+  const int64_t base = 2 * nq * ((heads + 15) / 16);
+  waves = env_int("CSA2_ATTN_WAVES", base <= 1024 ? 8 : 4);
   if (waves != 4 && waves != 8) waves = 4;
   int dflt = 1;
   if (base > 0 && base < 128) {            // fewer than half the CUs busy: split
@@ -231,7 +231,7 @@ int csa2_sparse_attn(const csa2_attn_args* a, void* ws, size_t ws_size, hipStrea
   p.mlpart = L.ws_bytes > 0 ? reinterpret_cast<float*>(static_cast<char*>(ws) +
                                                          round_up(L.nq * L.splits * a->heads * a->dim * 4, 256))
                             : nullptr;
-  p.T = a->kv_len; p.codes_stride = a->codes_stride; p.scales_stride = a->scales_stride;
+  p.T = a->kv_len; p.codes_stride = a->codes_stride; p.scales_stride = a->scales_stride; p.nq = L.nq;
   p.qn = a->q_per_seq; p.heads = a->heads; p.topk_k = a->topk_k; p.window = a->window;
   p.swa_rows = L.swa_rows; p.splits = L.splits; p.tiles_per_split = L.tps;
   p.n_sparse_tiles = L.n_sparse_tiles; p.n_tiles = L.n_tiles;

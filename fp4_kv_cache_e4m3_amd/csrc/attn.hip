@@ -11,23 +11,29 @@
 // both key and value.
 //
 // Work decomposition (wave64, MFMA):
-//  * workgroup = (query, group of 16 heads, split of the tile list); its 4
-//    waves take every 4th 16-entry tile of the split and merge their
-//    (max, sum, O) states through LDS at the end.  When the tile list is split
+//  * workgroup = (query, group of 16 heads, split of the tile list, column
+//    half of the output channels).  Both halves of a (query, head group)
+//    compute the same logits over all D channels; each stages and multiplies
+//    only its own D/2 value channels, so no partial outputs are exchanged.
+//    The two halves get workgroup ids 8 apart, which the dispatcher places on
+//    one XCD, so the second gather of the same rows hits that XCD's L2.
+//  * NW waves per workgroup take every NW-th 16-entry tile and merge their
+//    (max, sum, O) states through LDS at the end; when the tile list is split
 //    over several workgroups, a second kernel merges the partial states.
-//  * per tile a wave gathers 16 entries: lane (e = lane % 16, quarter =
-//    lane / 16) loads entry e's channels [D/4*quarter, D/4*(quarter+1)):
-//    D/8 FP4 code bytes + D/64 E4M3 scales, or D/4 bf16 SWA values, and
-//    turns them into fp16 in registers (FP4 values are exact in fp16).
+//  * per tile a wave gathers 16 entries: lane (e = lane % 16, g = lane / 16)
+//    loads D/8 channels of entry e from each column half ([g*D/8, (g+1)*D/8)
+//    within the half): FP4 codes + E4M3 scales, or bf16 SWA values, and turns
+//    them into fp16 in registers (FP4 values are exact in fp16).
 //  * QK^T: MFMA 16x16x32 f16 with the entries as A rows and the 16 heads as
-//    B columns; each lane's own dequantised channels are its A fragment (the
-//    contraction only needs A and B to agree on the channel order, and Q is
-//    loaded in the same order).  The result holds entries 4*(lane/16)+i of
-//    head lane%16 -- exactly the A-operand layout of the PV MFMA, so the
-//    probabilities never leave registers.
-//  * PV: MFMA 16x16x16 f16 over the 16 entries; the V operand needs 4 entries
-//    of one channel per lane, which one transposing LDS read per 16 channels
-//    delivers from the wave's fp16 tile.
+//    B columns (Q lives in registers, in the same channel order as K).  Each
+//    half's k-steps accumulate separately and the two sums are added last;
+//    fp32 addition commutes, so both column halves get bit-identical logits
+//    whichever half they process first.  The result holds entries
+//    4*(lane/16)+i of head lane%16 -- the A-operand layout of the PV MFMA, so
+//    the probabilities never leave registers.
+//  * PV: MFMA 16x16x16 f16 over the 16 entries; the V operand (4 entries of
+//    one channel per lane) comes from one transposing LDS read per 16
+//    channels of the wave's own fp16 half-tile.
 //  * the next tile's gather is issued before the current tile is processed.
 // Q and SWA rows go bf16 -> fp16 unscaled, which is exact for magnitudes in
 // [2^-14, 65504] (bf16 carries 8 significant bits, fp16 11), so QK^T is exact
@@ -63,68 +69,132 @@ CSA2_DEV float max_over_quarters(float x) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-template <int SEL>
-CSA2_DEV _Float16 scale_half(uint32_t w) { return e4m3_to_half<SEL>(w); }
-
 CSA2_DEV _Float16 scale_sel(uint32_t w, int sel) {
   switch (sel & 3) {            // sel is a constant after unrolling
-    case 0: return scale_half<0>(w);
-    case 1: return scale_half<1>(w);
-    case 2: return scale_half<2>(w);
-    default: return scale_half<3>(w);
+    case 0: return e4m3_to_half<0>(w);
+    case 1: return e4m3_to_half<1>(w);
+    case 2: return e4m3_to_half<2>(w);
+    default: return e4m3_to_half<3>(w);
   }
 }
 
-// FP4 tile data of this lane (entry lane%16, channel quarter lane/16):
-// D/8 code bytes and D/64 scale bytes.
+// Geometry of one lane's share of a 16-entry tile for head dim D.
+template <int D>
+struct Geo {
+  static constexpr int HALF = D / 2;       // channels per column half
+  static constexpr int CPL = D / 8;        // channels per lane per half
+  static constexpr int KH = CPL / 8;       // 32-channel k-steps per half (8 channels per lane each)
+  static constexpr int NT = HALF / 16;     // 16-channel PV tiles per half
+  static constexpr int PITCH = HALF + 8;   // LDS row pitch of a half-tile, in halves
+};
+
+// Lane -> channel maps of a half (a lane holds 8 channels per 32-channel
+// k-step j; lanes g = 0..3 of an entry share the k-step).  The QK contraction
+// does not care about the channel order as long as K and Q use the same map,
+// so each data type gets the map that coalesces its loads:
+//  * FP4 codes ("runs"): lane g holds two runs of CPL/2 channels, at
+//    g*CPL/2 and HALF/2 + g*CPL/2; the 4 lanes of an entry read one contiguous
+//    stretch of code bytes per load.
+//  * bf16 window rows ("interleaved"): k-step j, lane g holds channels
+//    32j + 8g .. +7; the 4 lanes of an entry read 64 contiguous bytes per load.
+// off(j) + LANE * g is the channel within the half.
+template <int D>
+struct RunsMap {
+  static constexpr int LANE = Geo<D>::CPL / 2;
+  static constexpr int off(int j) { return (j / (Geo<D>::KH / 2)) * (Geo<D>::HALF / 2) + 8 * (j % (Geo<D>::KH / 2)); }
+};
+template <int D>
+struct InterMap {
+  static constexpr int LANE = 8;
+  static constexpr int off(int j) { return 32 * j; }
+};
+
+// FP4 data of one entry for this lane (RunsMap): code words w[h][j] of k-step
+// j and, per run, a scale word whose byte (jj / 2) is the E4M3 scale of
+// k-step jj of that run (D = 512) or whose byte 0 is the run's scale (D = 128);
+// index h = 0 is the workgroup's own half.
 template <int D>
 struct Fp4Raw {
-  u4 c[D / 128];
-  uint32_t s[2];
+  uint32_t w[2][Geo<D>::KH];
+  uint32_t s[2][2];
+};
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer over [base, base + bytes): loads past the end return zeros.
+CSA2_DEV rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// One sequence's FP4 rows as buffers, plus this lane's fixed offsets.  A row
+// offset at or past `oob` lies outside both buffers, so an empty Top-K slot
+// reads zero codes and zero scales.
+struct Fp4Src {
+  rsrc_t codes, scales;
+  uint32_t cstride, sstride, oob;
+  int hcb[2], hsb[2];          // code / scale byte offset of each half (0 = own)
+  uint32_t lcb, lsb, lsh;      // per-lane code offset, scale word offset, scale shift
 };
 
 template <int D>
-CSA2_DEV bool load_fp4(const AttnParams& p, int32_t pos, int64_t b, int g, Fp4Raw<D>& r) {
-  constexpr int CB = D / 8, SB = D / 64;
-  const bool valid = pos >= 0 && (int64_t)pos < p.T;
-  const int64_t row = b * p.T + (valid ? pos : 0);
-  const uint8_t* cp = p.codes + row * p.codes_stride + CB * g;
-  const uint8_t* sp = p.scales + row * p.scales_stride + SB * g;
+CSA2_DEV bool load_fp4(const Fp4Src& src, int32_t pos, uint32_t T, Fp4Raw<D>& r) {
+  using G = Geo<D>;
+  const bool valid = pos >= 0 && (uint32_t)pos < T;
+  const uint32_t rc = valid ? __umul24((uint32_t)pos, src.cstride) : src.oob;
+  const uint32_t rs = valid ? __umul24((uint32_t)pos, src.sstride) : src.oob;
 #pragma unroll
-  for (int c = 0; c < D / 128; ++c) r.c[c] = *reinterpret_cast<const u4*>(cp + 16 * c);
-  if constexpr (SB == 8) {
-    const u2 w = *reinterpret_cast<const u2*>(sp);
-    r.s[0] = w[0];
-    r.s[1] = w[1];
-  } else {
-    r.s[0] = *reinterpret_cast<const uint16_t*>(sp);
-    r.s[1] = 0u;
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int run = 0; run < 2; ++run) {
+      if constexpr (G::KH == 8) {
+        const u4 c = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                src.codes, rc + src.lcb + run * (G::HALF / 4), src.hcb[h], 0));
+        r.w[h][4 * run + 0] = c[0]; r.w[h][4 * run + 1] = c[1];
+        r.w[h][4 * run + 2] = c[2]; r.w[h][4 * run + 3] = c[3];
+        r.s[h][run] = __builtin_amdgcn_raw_buffer_load_b32(src.scales, rs + src.lsb + run * 8, src.hsb[h], 0) >> src.lsh;
+      } else {
+        static_assert(G::KH == 2, "D must be 128 or 512");
+        r.w[h][run] = __builtin_amdgcn_raw_buffer_load_b32(src.codes, rc + src.lcb + run * (G::HALF / 4), src.hcb[h], 0);
+        if (run == 0) r.s[h][0] = __builtin_amdgcn_raw_buffer_load_b32(src.scales, rs, src.hsb[h], 0);
+        else r.s[h][1] = r.s[h][0] >> (src.lsh + 16);
+        if (run == 1) r.s[h][0] >>= src.lsh;
+      }
+    }
   }
   return valid;
 }
 
-// LDS tiles are padded rows of D + 8 halves: consecutive rows start 4 banks
-// apart, so the 16-byte staging writes and Q reads (16 rows, same column) and
-// the transposing V reads stay within a few bank groups, and every address is
-// a per-lane base plus a compile-time offset.
-template <int D, typename KV>
-CSA2_DEV void attend_tile(const AttnParams& p, KV kvf, bool valid, const _Float16* qbase, _Float16* wbase,
-                          const _Float16* vbase, int g, v4f (&o)[D / 16], float& m_run, float& l_run) {
-  constexpr int KS = D / 32, NT = D / 16;
-  constexpr int NA = KS >= 4 ? 4 : KS;      // independent MFMA accumulation chains
-  v4f accs[NA];
+// One 16-entry tile: logits, online-softmax update, O += P V for the own half.
+// kvf(h, j) gives this lane's 8 fp16 channels of k-step j of half h under
+// channel map M; wrow points at this lane's LDS staging row plus M::LANE * g.
+template <int D, typename M, typename KV>
+CSA2_DEV void attend_tile(const AttnParams& p, KV kvf, bool valid, const v8h (&qf)[2][Geo<D>::KH],
+                          _Float16* wrow, const _Float16* vbase, int g, v4f (&o)[Geo<D>::NT], float& m_run,
+                          float& l_run) {
+  constexpr int KH = Geo<D>::KH, NT = Geo<D>::NT;
+  constexpr int NC = KH >= 2 ? 2 : 1;      // accumulation chains per half
+  v4f acc[2][NC];
 #pragma unroll
-  for (int a = 0; a < NA; ++a) accs[a] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int h = 0; h < 2; ++h)
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const v8h kv = kvf(ks);
-    const v8h qv = *reinterpret_cast<const v8h*>(qbase + 8 * ks);
-    accs[ks % NA] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, qv, accs[ks % NA], 0, 0, 0);
-    *reinterpret_cast<v8h*>(wbase + 8 * ks) = kv;
+    for (int c = 0; c < NC; ++c) acc[h][c] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int j = 0; j < KH; ++j) {
+      const v8h kv = kvf(h, j);
+      acc[h][j % NC] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, qf[h][j], acc[h][j % NC], 0, 0, 0);
+      if (h == 0) *reinterpret_cast<v8h*>(wrow + M::off(j)) = kv;
+    }
   }
-  v4f acc = accs[0];
+  v4f part[2];
 #pragma unroll
-  for (int a = 1; a < NA; ++a) acc += accs[a];
+  for (int h = 0; h < 2; ++h) {
+    part[h] = acc[h][0];
+#pragma unroll
+    for (int c = 1; c < NC; ++c) part[h] += acc[h][c];
+  }
+  const v4f s_acc = part[0] + part[1];      // commutative: same bits in both halves
 
   // online softmax (head = lane % 16, entries 4g..4g+3).  The reference max
   // only moves when a tile's max exceeds it by more than 2^8, so O is rarely
@@ -134,7 +204,7 @@ CSA2_DEV void attend_tile(const AttnParams& p, KV kvf, bool valid, const _Float1
   float tmax = -__builtin_inff();
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    s4[i] = ((vm >> (4 * g + i)) & 1ull) ? acc[i] * p.qscale : -__builtin_inff();
+    s4[i] = ((vm >> (4 * g + i)) & 1ull) ? s_acc[i] * p.qscale : -__builtin_inff();
     tmax = fmaxf(tmax, s4[i]);
   }
   tmax = max_over_quarters(tmax);
@@ -173,64 +243,114 @@ CSA2_DEV void attend_tile(const AttnParams& p, KV kvf, bool valid, const _Float1
 }
 
 template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) void k_attn(AttnParams p) {
-  constexpr int KS = D / 32;        // QK k-steps; each lane holds 8*KS = D/4 channels
-  constexpr int NT = D / 16;        // PV output tiles of 16 channels
-  constexpr int PITCH = D + 8;      // LDS row pitch in halves
-  __shared__ __attribute__((aligned(16))) _Float16 vt[NW * 16 * PITCH];  // per-wave V tiles
-  __shared__ __attribute__((aligned(16))) _Float16 qs[16 * PITCH];       // Q of the 16 heads
+__global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
+  using G = Geo<D>;
+  constexpr int KH = G::KH, NT = G::NT, PITCH = G::PITCH, HALF = G::HALF;
+  constexpr int NH = NW / 2;                                     // waves holding O after the first merge level
+  constexpr int TILE_HALVES = 16 * PITCH;
+  __shared__ __attribute__((aligned(16))) _Float16 vt[NW * TILE_HALVES];  // per-wave V half-tiles / merge buffer
+  static_assert(NH * NT * 64 * 16 <= NW * TILE_HALVES * 2, "merge buffer must fit in the tile buffers");
+  constexpr int QPITCH = D + 8;
+  __shared__ __attribute__((aligned(16))) _Float16 qs[16 * QPITCH];        // Q of the 16 heads
+  __shared__ float ml[NW][16][2];
+  __shared__ float mlh[16][2];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
+
+  // workgroup id -> (query, head group, split, column half).  The dispatcher
+  // deals consecutive ids round-robin to the 8 XCDs; all P workgroups of one
+  // query get ids that are equal mod 8, so they share that XCD's L2 for the
+  // query's rows, window and Q.  Ids past the last query exit at once.
   const int ngroups = (p.heads + 15) >> 4;
-  const int hg = blockIdx.x % ngroups, split = blockIdx.x / ngroups;
-  const int64_t q = blockIdx.y;
+  const int P = 2 * ngroups * p.splits;
+  const int xcd = (int)(blockIdx.x & 7), slot = (int)(blockIdx.x >> 3);
+  const int64_t q = (int64_t)(slot / P) * 8 + xcd;
+  if (q >= p.nq) return;
+  const int idx = slot % P;
+  const int c0 = idx & 1;
+  const int split = (idx >> 1) % p.splits;
+  const int hg = (idx >> 1) / p.splits;
   const int64_t b = q / p.qn;
   const int j = (int)(q - b * p.qn);
   const int h0 = hg * 16;
   const int first_swa = p.swa_len ? p.swa_rows - p.swa_len[b] : 0;
   const int t_end = min(p.n_tiles, (split + 1) * p.tiles_per_split);
   const int sp_end = min(t_end, p.n_sparse_tiles);
-  int tile = split * p.tiles_per_split + wave;
+  const int tile0 = split * p.tiles_per_split + wave;
+  const int hb[2] = {c0 * HALF, (1 - c0) * HALF};                // first channel of each half (0 = own)
 
-  // Top-K positions of this wave's first batch of FP4 tiles go out before the
-  // Q staging so the latencies overlap (a tile's gather then needs no
-  // dependent index load)
-  constexpr int PB = 8;                             // FP4 tiles per position batch
-  const int n_fp4 = tile < sp_end ? (sp_end - tile + NW - 1) / NW : 0;
+  // Top-K positions of this wave's first batch of FP4 tiles go out first: the
+  // first gather depends on them
+  constexpr int PB = 4;                             // FP4 tiles per position batch (even)
+  const int n_fp4 = tile0 < sp_end ? (sp_end - tile0 + NW - 1) / NW : 0;
+  const int32_t* tk = p.topk + q * p.topk_k;
   auto load_positions = [&](int first, int32_t (&pos)[PB]) {
 #pragma unroll
     for (int i = 0; i < PB; ++i) {
-      const int ti = tile + NW * (first + i);
-      const int slot = ti * 16 + n;
-      pos[i] = (first + i < n_fp4 && slot < p.topk_k) ? p.topk[q * p.topk_k + slot] : -1;
+      const int slot_i = (tile0 + NW * (first + i)) * 16 + n;
+      pos[i] = (first + i < n_fp4 && slot_i < p.topk_k) ? tk[slot_i] : -1;
     }
   };
   int32_t pos[PB];
   load_positions(0, pos);
 
-  // ---- stage Q (16 heads x D, bf16 -> fp16 unscaled, exact in fp16's normal
-  // range) in LDS; every wave reads its B operand from there.  The Q loads and
-  // the first FP4 gather are both in flight before either is waited on.
-  constexpr int QCH = 16 * D / 8;                 // 8-half chunks of the Q tile
+  // ---- Q of the 16 heads, loaded once per workgroup (bf16 -> fp16, heads past
+  // H are zero) into LDS; each wave reads its QK B operand from there
+  constexpr int QCH = 16 * D / 8;                   // 8-channel chunks of the Q tile
   constexpr int QPT = (QCH + 64 * NW - 1) / (64 * NW);
   u4 qraw[QPT];
 #pragma unroll
   for (int i = 0; i < QPT; ++i) {
     const int c = threadIdx.x + 64 * NW * i;
     const int hr = c / (D / 8), h = h0 + hr;
-    if (c < QCH) qraw[i] = *reinterpret_cast<const u4*>(p.q + (q * p.heads + (h < p.heads ? h : 0)) * D +
-                                                         (c % (D / 8)) * 8);
+    if (c < QCH) qraw[i] = *reinterpret_cast<const u4*>(p.q + (q * p.heads + (h < p.heads ? h : 0)) * D + (c % (D / 8)) * 8);
   }
-  Fp4Raw<D> raw;
-  bool valid = n_fp4 > 0 ? load_fp4<D>(p, pos[0], b, g, raw) : false;
+
+  // ---- the window tiles come first: their rows are known without the Top-K
+  // list, so their loads overlap the position loads and the Q staging
+  const int swa_first = tile0 + NW * n_fp4;
+  u4 w[2][KH];
+  bool swa_valid = false;
+  constexpr uint32_t kOob = 0xFFFFF000u;            // row offset past every buffer
+  const rsrc_t swa_buf = make_rsrc(p.swa + b * p.swa_rows * D, (uint32_t)(p.swa_rows * D * 2));
+  const uint32_t swa_lane = 2u * InterMap<D>::LANE * g;
+  auto load_swa = [&](int t) {
+    const int wr = (t - p.n_sparse_tiles) * 16 + n;
+    const int r = j + wr;
+    swa_valid = wr < p.window && r >= first_swa && r < p.swa_rows;
+    const uint32_t ro = (swa_valid ? (uint32_t)r * (2u * D) : kOob) + swa_lane;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int k = 0; k < KH; ++k)
+        w[hh][k] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(swa_buf, ro + 2 * InterMap<D>::off(k), 2 * hb[hh], 0));
+  };
+  if (swa_first < t_end) load_swa(swa_first);
+
+  Fp4Src src;
+  src.codes = make_rsrc(p.codes + b * p.T * p.codes_stride, (uint32_t)(p.T * p.codes_stride));
+  src.scales = make_rsrc(p.scales + b * p.T * p.scales_stride, (uint32_t)(p.T * p.scales_stride));
+  src.cstride = (uint32_t)p.codes_stride;
+  src.sstride = (uint32_t)p.scales_stride;
+  src.oob = kOob;
+  src.hcb[0] = hb[0] / 2; src.hcb[1] = hb[1] / 2;
+  src.hsb[0] = hb[0] / 16; src.hsb[1] = hb[1] / 16;
+  src.lcb = (uint32_t)(g * RunsMap<D>::LANE / 2);
+  src.lsb = KH == 8 ? 4u * (uint32_t)(g >> 1) : 0u;
+  src.lsh = KH == 8 ? 16u * (uint32_t)(g & 1) : 8u * (uint32_t)(g >> 1);
+  const uint32_t T32 = (uint32_t)p.T;
+  Fp4Raw<D> raw[2];
+  bool vld[2] = {false, false};
+  if (n_fp4 > 0) vld[0] = load_fp4<D>(src, pos[0], T32, raw[0]);
+  const v8h zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
   for (int i = 0; i < QPT; ++i) {
     const int c = threadIdx.x + 64 * NW * i;
     const int hr = c / (D / 8);
     v8h f = bf16x8_to_half(qraw[i]);
-    if (h0 + hr >= p.heads) f = v8h{0, 0, 0, 0, 0, 0, 0, 0};
-    if (c < QCH) *reinterpret_cast<v8h*>(qs + hr * PITCH + (c % (D / 8)) * 8) = f;
+    if (h0 + hr >= p.heads) f = zero8;
+    if (c < QCH) *reinterpret_cast<v8h*>(qs + hr * QPITCH + (c % (D / 8)) * 8) = f;
   }
   __syncthreads();
 
@@ -239,119 +359,136 @@ __global__ __launch_bounds__(64 * NW) void k_attn(AttnParams p) {
   for (int t = 0; t < NT; ++t) o[t] = v4f{0.f, 0.f, 0.f, 0.f};
   float m_run = -__builtin_inff(), l_run = 0.0f;
 
-  _Float16* my = vt + wave * 16 * PITCH;
-  _Float16* wbase = my + n * PITCH + (D / 4) * g;                  // staging: entry n, quarter g
+  _Float16* my = vt + wave * TILE_HALVES;
   const _Float16* vbase = my + (4 * g + (n >> 2)) * PITCH + 4 * (n & 3);   // transposing PV read
-  const _Float16* qbase = qs + n * PITCH + (D / 4) * g;            // QK B operand: head n
-  const v8h zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+  v8h qf[2][KH];
+  auto load_qf = [&](auto map) {
+    using M = decltype(map);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int k = 0; k < KH; ++k)
+        qf[hh][k] = *reinterpret_cast<const v8h*>(qs + n * QPITCH + hb[hh] + M::off(k) + M::LANE * g);
+  };
 
-  // ---- FP4 tiles: positions in batches of PB, next gather in flight while
-  // the current tile is processed
-  for (int first = 0; first < n_fp4; first += PB) {
-    if (first > 0) {
-      load_positions(first, pos);
-      valid = load_fp4<D>(p, pos[0], b, g, raw);
-    }
-    const int cnt = min(PB, n_fp4 - first);
-#pragma unroll 1
-    for (int i = 0; i < cnt; ++i) {
-#pragma unroll
-      for (int k = 0; k + 1 < PB; ++k) pos[k] = pos[k + 1];   // pos[0] = next tile
-      const Fp4Raw<D> cur = raw;
-      const bool cur_valid = valid;
-      if (i + 1 < cnt) valid = load_fp4<D>(p, pos[0], b, g, raw);
-      // an empty slot gets scale 0: finite zeros in V, and its logits are masked
-      _Float16 sc[KS / 2];
-#pragma unroll
-      for (int gi = 0; gi < KS / 2; ++gi) sc[gi] = cur_valid ? scale_sel(cur.s[gi >> 2], gi & 3) : (_Float16)0.0f;
-      attend_tile<D>(p, [&](int ks) { return fp4x8_to_half(cur.c[ks >> 2][ks & 3], sc[ks >> 1]); },
-                     cur_valid, qbase, wbase, vbase, g, o, m_run, l_run);
+  // ---- sliding-window tiles (bf16 rows, interleaved channel map)
+  if (swa_first < t_end) {
+    load_qf(InterMap<D>{});
+    _Float16* wrow = my + n * PITCH + InterMap<D>::LANE * g;
+    for (int t = swa_first; t < t_end; t += NW) {
+      const bool v = swa_valid;
+      attend_tile<D, InterMap<D>>(p, [&](int hh, int k) { return v ? bf16x8_to_half(w[hh][k]) : zero8; }, v, qf,
+                                  wrow, vbase, g, o, m_run, l_run);
+      if (t + NW < t_end) load_swa(t + NW);
     }
   }
-  tile += NW * n_fp4;
-  // ---- sliding-window tiles (bf16 rows)
-  for (; tile < t_end; tile += NW) {
-    const int wr = (tile - p.n_sparse_tiles) * 16 + n;
-    const int r = j + wr;
-    const bool v = wr < p.window && r >= first_swa && r < p.swa_rows;
-    const uint16_t* rp = p.swa + ((b * p.swa_rows + (v ? r : 0)) * D + (D / 4) * g);
-    u4 w[KS];
+
+  // ---- FP4 tiles (runs channel map): positions in batches of PB, the next
+  // tile's gather in flight while the current one is processed (ping-pong)
+  if (n_fp4 > 0) {
+    load_qf(RunsMap<D>{});
+    _Float16* wrow = my + n * PITCH + RunsMap<D>::LANE * g;
+    for (int first = 0; first < n_fp4; first += PB) {
+      int32_t nxt[PB];
+      load_positions(first + PB, nxt);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) w[ks] = *reinterpret_cast<const u4*>(rp + 8 * ks);
-    attend_tile<D>(p, [&](int ks) { return v ? bf16x8_to_half(w[ks]) : zero8; }, v, qbase, wbase, vbase, g,
-                   o, m_run, l_run);
+      for (int i = 0; i < PB; ++i) {
+        if (first + i < n_fp4) {
+          const int cur = i & 1;
+          if (first + i + 1 < n_fp4) vld[cur ^ 1] = load_fp4<D>(src, i + 1 < PB ? pos[i + 1] : nxt[0], T32, raw[cur ^ 1]);
+          // an empty slot read zero codes and scales: finite zeros in V; its
+          // logits are masked
+          _Float16 sc[2][2][(KH / 2 + 1) / 2];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int run = 0; run < 2; ++run)
+#pragma unroll
+              for (int k = 0; k < (KH / 2 + 1) / 2; ++k) sc[hh][run][k] = scale_sel(raw[cur].s[hh][run], k);
+          attend_tile<D, RunsMap<D>>(
+              p,
+              [&](int hh, int k) {
+                constexpr int HK = KH / 2;
+                return fp4x8_to_half(raw[cur].w[hh][k], sc[hh][k / HK][(k % HK) / 2]);
+              },
+              vld[cur], qf, wrow, vbase, g, o, m_run, l_run);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < PB; ++i) pos[i] = nxt[i];
+    }
   }
 
   // ---- merge the NW waves: M = max m_w, L = sum f_w l_w, O = sum f_w O_w
   float l_tot = l_run + __shfl_xor(l_run, 16, 64);
   l_tot = l_tot + __shfl_xor(l_tot, 32, 64);
-  __syncthreads();                                  // every wave is done with the Q tile
-  float (*ml)[16][2] = reinterpret_cast<float (*)[16][2]>(qs);
   if (g == 0) { ml[wave][n][0] = m_run; ml[wave][n][1] = l_tot; }
-  __syncthreads();
-  float M[4], L[4], fme[4];
+  __syncthreads();                                  // also: every wave is done with its tile buffer
+  float fme[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int hh = 4 * g + i;
     float mx = -__builtin_inff();
 #pragma unroll
     for (int w = 0; w < NW; ++w) mx = fmaxf(mx, ml[w][hh][0]);
-    float ls = 0.0f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float mw = ml[w][hh][0];
-      ls += (mw == -__builtin_inff()) ? 0.0f : exp2f(mw - mx) * ml[w][hh][1];
-    }
     const float mme = ml[wave][hh][0];
-    M[i] = mx;
-    L[i] = ls;
     fme[i] = (mme == -__builtin_inff()) ? 0.0f : exp2f(mme - mx);
+    if (wave == 0 && n == 0) {
+      float ls = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float mw = ml[w][hh][0];
+        ls += (mw == -__builtin_inff()) ? 0.0f : exp2f(mw - mx) * ml[w][hh][1];
+      }
+      mlh[hh][0] = mx;
+      mlh[hh][1] = ls;
+    }
   }
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[t][i] *= fme[i];
 
-  // pairwise tree in a fixed order through a lane-major fp32 buffer
-  // (element (slot, t, lane) holds o[t] of one wave); reuses the tile buffers
+  // two levels in a fixed order through a lane-major fp32 buffer (element
+  // (slot, t, lane) holds o[t] of one wave): waves NH.. add into waves 0..NH-1,
+  // which then leave their sums for a cooperative final pass
   v4f* fb = reinterpret_cast<v4f*>(vt);
+  if (wave >= NH) {
 #pragma unroll
-  for (int r = 1; r < NW; r <<= 1) {
-    if ((wave & (2 * r - 1)) == r) {
-      const int slot = wave / (2 * r);
-#pragma unroll
-      for (int t = 0; t < NT; ++t) fb[(slot * NT + t) * 64 + lane] = o[t];
-    }
-    __syncthreads();
-    if ((wave & (2 * r - 1)) == 0) {
-      const int slot = wave / (2 * r);
-#pragma unroll
-      for (int t = 0; t < NT; ++t) o[t] += fb[(slot * NT + t) * 64 + lane];
-    }
-    __syncthreads();
+    for (int t = 0; t < NT; ++t) fb[((wave - NH) * NT + t) * 64 + lane] = o[t];
   }
-  if (wave != 0) return;
+  __syncthreads();
+  if (wave < NH) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) o[t] += fb[(wave * NT + t) * 64 + lane];
+  }
+  __syncthreads();
+  if (wave < NH) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) fb[(wave * NT + t) * 64 + lane] = o[t];
+  }
+  __syncthreads();
 
-  if (p.splits == 1) {
+  // one item = (16-channel tile t, lane l): the v4f of lane l holds channel
+  // 16t + l%16 of heads 4*(l/16) .. 4*(l/16)+3
+  for (int it = threadIdx.x; it < NT * 64; it += 64 * NW) {
+    const int t = it >> 6, l = it & 63;
+    v4f sum = fb[t * 64 + l];
+#pragma unroll
+    for (int w = 1; w < NH; ++w) sum += fb[(w * NT + t) * 64 + l];
+    const int chg = c0 * HALF + 16 * t + (l & 15);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int hh = h0 + 4 * g + i;
-      if (hh >= p.heads) continue;
-      const float inv = L[i] > 0.0f ? 1.0f / L[i] : 0.0f;
-      float* dst = p.out + (q * p.heads + hh) * D + n;
-#pragma unroll
-      for (int t = 0; t < NT; ++t) dst[16 * t] = o[t][i] * inv;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int hh = h0 + 4 * g + i;
-      if (hh >= p.heads) continue;
-      const int64_t pr = (q * p.splits + split) * p.heads + hh;
-      float* dst = p.opart + pr * D + n;
-#pragma unroll
-      for (int t = 0; t < NT; ++t) dst[16 * t] = o[t][i];
-      if (n == 0) { p.mlpart[2 * pr] = M[i]; p.mlpart[2 * pr + 1] = L[i]; }
+      const int hh = 4 * (l >> 4) + i, hglob = h0 + hh;
+      if (hglob >= p.heads) continue;
+      if (p.splits == 1) {
+        const float Lh = mlh[hh][1];
+        p.out[(q * p.heads + hglob) * D + chg] = Lh > 0.0f ? sum[i] / Lh : 0.0f;
+      } else {
+        const int64_t pr = (q * p.splits + split) * p.heads + hglob;
+        p.opart[pr * D + chg] = sum[i];
+        if (c0 == 0 && t == 0 && (l & 15) == 0) { p.mlpart[2 * pr] = mlh[hh][0]; p.mlpart[2 * pr + 1] = mlh[hh][1]; }
+      }
     }
   }
 }
@@ -381,11 +518,12 @@ __global__ __launch_bounds__(D / 4) void k_attn_combine(AttnParams p) {
 
 hipError_t launch_attn(const AttnParams& p, int nq, int dim, int waves, hipStream_t st) {
   if (nq == 0) return hipSuccess;
-  const int ngroups = (p.heads + 15) / 16;
-  const dim3 grid(ngroups * p.splits, nq);
+  const int64_t ngroups = (p.heads + 15) / 16;
+  const int64_t blocks = 8 * (((int64_t)nq + 7) / 8) * 2 * ngroups * p.splits;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
 #define CSA2_ATTN_CASE(D, NW)                                                                 \
   if (dim == D && waves == NW) {                                                              \
-    hipLaunchKernelGGL((k_attn<D, NW>), grid, dim3(64 * NW), 0, st, p);                       \
+    hipLaunchKernelGGL((k_attn<D, NW>), dim3((unsigned)blocks), dim3(64 * NW), 0, st, p);     \
     if (p.splits > 1) hipLaunchKernelGGL(k_attn_combine<D>, dim3(nq * p.heads), dim3(D / 4), 0, st, p); \
     return hipGetLastError();                                                                 \
   }

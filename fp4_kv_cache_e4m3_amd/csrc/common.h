@@ -101,7 +101,7 @@ struct AttnParams {
   const uint16_t* q; const uint8_t* codes; const uint8_t* scales;
   const int32_t* topk; const uint16_t* swa; const int32_t* swa_len;
   float* out; float* opart; float* mlpart;
-  int64_t T, codes_stride, scales_stride;
+  int64_t T, codes_stride, scales_stride, nq;
   int32_t qn, heads, topk_k, window, swa_rows, splits, tiles_per_split, n_sparse_tiles, n_tiles;
   float qscale;                                          // sm_scale * log2(e)
 };
