@@ -166,64 +166,59 @@ CSA2_DEV bool load_fp4(const Fp4Src& src, int32_t pos, uint32_t T, Fp4Raw<D>& r)
 
 // One 16-entry tile: logits, online-softmax update, O += P V for the own half.
 // kvf(h, j) gives this lane's 8 fp16 channels of k-step j of half h under
-// channel map M; wrow points at this lane's LDS staging row plus M::LANE * g.
-template <int D, typename M, typename KV>
-CSA2_DEV void attend_tile(const AttnParams& p, KV kvf, bool valid, const v8h (&qf)[2][Geo<D>::KH],
+// channel map M; wrow points at this lane's LDS staging row plus M::LANE * g;
+// after_qk() runs once the raw tile data has been consumed.
+template <int D, typename M, typename KV, typename AfterQK>
+CSA2_DEV void attend_tile(const AttnParams& p, KV kvf, AfterQK after_qk, bool valid, const v8h (&qf)[2][Geo<D>::KH],
                           _Float16* wrow, const _Float16* vbase, int g, v4f (&o)[Geo<D>::NT], float& m_run,
                           float& l_run) {
   constexpr int KH = Geo<D>::KH, NT = Geo<D>::NT;
-  constexpr int NC = KH >= 2 ? 2 : 1;      // accumulation chains per half
-  v4f acc[2][NC];
+  // one accumulation chain per half (the two halves interleave); the half sums
+  // are added last
+  v4f part[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
+  for (int j = 0; j < KH; ++j) {
 #pragma unroll
-    for (int c = 0; c < NC; ++c) acc[h][c] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-#pragma unroll
-    for (int j = 0; j < KH; ++j) {
+    for (int h = 0; h < 2; ++h) {
       const v8h kv = kvf(h, j);
-      acc[h][j % NC] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, qf[h][j], acc[h][j % NC], 0, 0, 0);
+      part[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, qf[h][j], part[h], 0, 0, 0);
       if (h == 0) *reinterpret_cast<v8h*>(wrow + M::off(j)) = kv;
     }
   }
-  v4f part[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    part[h] = acc[h][0];
-#pragma unroll
-    for (int c = 1; c < NC; ++c) part[h] += acc[h][c];
-  }
   const v4f s_acc = part[0] + part[1];      // commutative: same bits in both halves
+  after_qk();                               // the tile's raw data is dead from here on
 
   // online softmax (head = lane % 16, entries 4g..4g+3).  The reference max
   // only moves when a tile's max exceeds it by more than 2^8, so O is rarely
-  // rescaled; probabilities stay <= 256, fine for fp16.
+  // rescaled; probabilities stay <= 256, fine for fp16.  Masked entries get
+  // -inf logits (probability exactly 0).
   const uint64_t vm = __ballot(valid);
   float s4[4];
-  float tmax = -__builtin_inff();
+  if (vm == ~0ull) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    s4[i] = ((vm >> (4 * g + i)) & 1ull) ? s_acc[i] * p.qscale : -__builtin_inff();
-    tmax = fmaxf(tmax, s4[i]);
+    for (int i = 0; i < 4; ++i) s4[i] = s_acc[i] * p.qscale;
+  } else {
+    const uint32_t bits = (uint32_t)(vm >> (4 * g));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s4[i] = ((bits >> i) & 1u) ? s_acc[i] * p.qscale : -__builtin_inff();
   }
+  float tmax = fmaxf(fmaxf(s4[0], s4[1]), fmaxf(s4[2], s4[3]));
   tmax = max_over_quarters(tmax);
   const bool grow = tmax > m_run + 8.0f;
+  // a wave's first entries only set the reference (O and l are still zero)
+  const bool rescale = grow && m_run != -__builtin_inff();
   float alpha = 1.0f;
-  if (grow) {
-    alpha = __builtin_amdgcn_exp2f(m_run - tmax);
-    m_run = tmax;
-  }
+  if (rescale) alpha = __builtin_amdgcn_exp2f(m_run - tmax);
+  if (grow) m_run = tmax;
+  const float mref = m_run == -__builtin_inff() ? 0.0f : m_run;   // all masked so far: exp2(-inf) = 0
   v4h pa;
-  float psum = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const _Float16 ph = (s4[i] == -__builtin_inff()) ? (_Float16)0.0f : (_Float16)__builtin_amdgcn_exp2f(s4[i] - m_run);
-    pa[i] = ph;
-    psum += (float)ph;          // normalise with the probabilities actually used
-  }
+  for (int i = 0; i < 4; ++i) pa[i] = (_Float16)__builtin_amdgcn_exp2f(s4[i] - mref);
+  // normalise with the probabilities actually used (fp16 products with 1 are exact)
+  const v2h one2 = {(_Float16)1.0f, (_Float16)1.0f};
+  const float psum = __builtin_amdgcn_fdot2(v2h{pa[2], pa[3]}, one2, __builtin_amdgcn_fdot2(v2h{pa[0], pa[1]}, one2, 0.0f, false), false);
   l_run = l_run * alpha + psum;
-  if (__any(grow)) {
+  if (__any(rescale)) {
     float ai[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, 4 * g + i, 64);
@@ -307,8 +302,8 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
     if (c < QCH) qraw[i] = *reinterpret_cast<const u4*>(p.q + (q * p.heads + (h < p.heads ? h : 0)) * D + (c % (D / 8)) * 8);
   }
 
-  // ---- the window tiles come first: their rows are known without the Top-K
-  // list, so their loads overlap the position loads and the Q staging
+  // ---- window rows (bf16): loaded through a buffer over this sequence's
+  // window; rows outside the window read zeros
   const int swa_first = tile0 + NW * n_fp4;
   u4 w[2][KH];
   bool swa_valid = false;
@@ -326,8 +321,9 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
       for (int k = 0; k < KH; ++k)
         w[hh][k] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(swa_buf, ro + 2 * InterMap<D>::off(k), 2 * hb[hh], 0));
   };
-  if (swa_first < t_end) load_swa(swa_first);
 
+  // ---- FP4 rows: the first two gathers go out as soon as their positions
+  // are known
   Fp4Src src;
   src.codes = make_rsrc(p.codes + b * p.T * p.codes_stride, (uint32_t)(p.T * p.codes_stride));
   src.scales = make_rsrc(p.scales + b * p.T * p.scales_stride, (uint32_t)(p.T * p.scales_stride));
@@ -343,6 +339,8 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
   Fp4Raw<D> raw[2];
   bool vld[2] = {false, false};
   if (n_fp4 > 0) vld[0] = load_fp4<D>(src, pos[0], T32, raw[0]);
+  if (n_fp4 > 1) vld[1] = load_fp4<D>(src, pos[1], T32, raw[1]);
+
   const v8h zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
   for (int i = 0; i < QPT; ++i) {
@@ -371,20 +369,9 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
         qf[hh][k] = *reinterpret_cast<const v8h*>(qs + n * QPITCH + hb[hh] + M::off(k) + M::LANE * g);
   };
 
-  // ---- sliding-window tiles (bf16 rows, interleaved channel map)
-  if (swa_first < t_end) {
-    load_qf(InterMap<D>{});
-    _Float16* wrow = my + n * PITCH + InterMap<D>::LANE * g;
-    for (int t = swa_first; t < t_end; t += NW) {
-      const bool v = swa_valid;
-      attend_tile<D, InterMap<D>>(p, [&](int hh, int k) { return v ? bf16x8_to_half(w[hh][k]) : zero8; }, v, qf,
-                                  wrow, vbase, g, o, m_run, l_run);
-      if (t + NW < t_end) load_swa(t + NW);
-    }
-  }
-
-  // ---- FP4 tiles (runs channel map): positions in batches of PB, the next
-  // tile's gather in flight while the current one is processed (ping-pong)
+  // ---- FP4 tiles (runs channel map): positions in batches of PB; two tiles'
+  // gathers are in flight at all times: tile i + 2 goes into tile i's buffer as
+  // soon as tile i's logits are done with it
   if (n_fp4 > 0) {
     load_qf(RunsMap<D>{});
     _Float16* wrow = my + n * PITCH + RunsMap<D>::LANE * g;
@@ -394,8 +381,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
 #pragma unroll
       for (int i = 0; i < PB; ++i) {
         if (first + i < n_fp4) {
-          const int cur = i & 1;
-          if (first + i + 1 < n_fp4) vld[cur ^ 1] = load_fp4<D>(src, i + 1 < PB ? pos[i + 1] : nxt[0], T32, raw[cur ^ 1]);
+          Fp4Raw<D>& cur = raw[i & 1];
           // an empty slot read zero codes and scales: finite zeros in V; its
           // logits are masked
           _Float16 sc[2][2][(KH / 2 + 1) / 2];
@@ -404,18 +390,36 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
 #pragma unroll
             for (int run = 0; run < 2; ++run)
 #pragma unroll
-              for (int k = 0; k < (KH / 2 + 1) / 2; ++k) sc[hh][run][k] = scale_sel(raw[cur].s[hh][run], k);
+              for (int k = 0; k < (KH / 2 + 1) / 2; ++k) sc[hh][run][k] = scale_sel(cur.s[hh][run], k);
+          const bool v = vld[i & 1];
           attend_tile<D, RunsMap<D>>(
               p,
               [&](int hh, int k) {
                 constexpr int HK = KH / 2;
-                return fp4x8_to_half(raw[cur].w[hh][k], sc[hh][k / HK][(k % HK) / 2]);
+                return fp4x8_to_half(cur.w[hh][k], sc[hh][k / HK][(k % HK) / 2]);
               },
-              vld[cur], qf, wrow, vbase, g, o, m_run, l_run);
+              [&]() {
+                if (first + i + 2 < n_fp4)
+                  vld[i & 1] = load_fp4<D>(src, i + 2 < PB ? pos[i + 2] : nxt[i + 2 - PB], T32, cur);
+              },
+              v, qf, wrow, vbase, g, o, m_run, l_run);
         }
       }
 #pragma unroll
       for (int i = 0; i < PB; ++i) pos[i] = nxt[i];
+    }
+  }
+
+  // ---- sliding-window tiles (bf16 rows, interleaved channel map)
+  if (swa_first < t_end) {
+    load_swa(swa_first);
+    load_qf(InterMap<D>{});
+    _Float16* wrow = my + n * PITCH + InterMap<D>::LANE * g;
+    for (int t = swa_first; t < t_end; t += NW) {
+      const bool v = swa_valid;
+      attend_tile<D, InterMap<D>>(p, [&](int hh, int k) { return v ? bf16x8_to_half(w[hh][k]) : zero8; }, [] {}, v,
+                                  qf, wrow, vbase, g, o, m_run, l_run);
+      if (t + NW < t_end) load_swa(t + NW);
     }
   }
 
@@ -432,13 +436,13 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
 #pragma unroll
     for (int w = 0; w < NW; ++w) mx = fmaxf(mx, ml[w][hh][0]);
     const float mme = ml[wave][hh][0];
-    fme[i] = (mme == -__builtin_inff()) ? 0.0f : exp2f(mme - mx);
+    fme[i] = (mme == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mme - mx);
     if (wave == 0 && n == 0) {
       float ls = 0.0f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
         const float mw = ml[w][hh][0];
-        ls += (mw == -__builtin_inff()) ? 0.0f : exp2f(mw - mx) * ml[w][hh][1];
+        ls += (mw == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mw - mx) * ml[w][hh][1];
       }
       mlh[hh][0] = mx;
       mlh[hh][1] = ls;
@@ -506,7 +510,7 @@ __global__ __launch_bounds__(D / 4) void k_attn_combine(AttnParams p) {
   for (int s = 0; s < S; ++s) {
     const int64_t pr = (q * S + s) * p.heads + h;
     const float ms = p.mlpart[2 * pr];
-    const float f = (ms == -__builtin_inff()) ? 0.0f : exp2f(ms - mx);
+    const float f = (ms == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(ms - mx);
     L += f * p.mlpart[2 * pr + 1];
     const float4 v = reinterpret_cast<const float4*>(p.opart + pr * D)[threadIdx.x];
     acc.x += f * v.x; acc.y += f * v.y; acc.z += f * v.z; acc.w += f * v.w;
