@@ -166,6 +166,8 @@ struct SelShared {
   alignas(16) uint32_t hist[kSelHists][kDigitBins];
   uint32_t bc[4];
   uint32_t wsum[kSelWaves];
+  uint32_t wmin[kSelWaves];
+  uint32_t wcnt[kSelWaves];
   int32_t pool[kPoolBlocks];
 };
 
@@ -209,17 +211,19 @@ CSA2_DEV uint32_t block_sum(uint32_t v, SelShared& sh) {
 
 // +1 on counter `bin`.  When every active lane of the wave hits the same bin
 // (ties, concentrated scores) one lane adds the whole count, so a repeated
-// digit does not serialise 64 LDS atomics on one address.
+// digit does not serialise 64 LDS atomics on one address.  The leader's bin
+// comes from readfirstlane (a scalar register), not a cross-lane LDS shuffle.
 CSA2_DEV void hist_inc(uint32_t* hist, uint32_t bin, bool active) {
-  const uint64_t act = __ballot(active);
-  if (act == 0) return;
-  const int leader = __ffsll((unsigned long long)act) - 1;
-  const uint32_t lb = __shfl(bin, leader, 64);
-  const uint64_t same = __ballot(active && bin == lb);
-  if (same == act) {
-    if ((int)(threadIdx.x & 63) == leader) atomicAdd(&hist[lb], (uint32_t)__popcll(act));
-  } else if (active) {
-    atomicAdd(&hist[bin], 1u);
+  if (active) {
+    const uint32_t lb = __builtin_amdgcn_readfirstlane(bin);
+    const uint64_t act = __ballot(1);
+    const uint64_t same = __ballot(bin == lb);
+    if (same == act) {
+      const uint32_t lane = __builtin_amdgcn_mbcnt_hi((uint32_t)(act >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)act, 0u));
+      if (lane == 0) atomicAdd(&hist[lb], (uint32_t)__popcll(act));
+    } else {
+      atomicAdd(&hist[bin], 1u);
+    }
   }
 }
 
@@ -255,43 +259,104 @@ CSA2_DEV void hist_find(const uint32_t* hist, uint32_t k, SelShared& sh, uint32_
   __syncthreads();
 }
 
-// K-th largest key among nonzero keys (1 <= K <= #nonzero): returns the key
-// value tau and how many keys equal to tau belong to the top K.  Three radix
-// passes (12, 12 and 8 bits) on pre-cleared histograms h[0..2].  get(j)
-// returns this thread's j-th key (j < KPT); small KPT keeps keys in
-// registers, large KPT re-reads them each pass.
+// inclusive max-scan over the 64 lanes with DPP (lanes outside a row read 0,
+// which is neutral for unsigned max)
+CSA2_DEV uint32_t wave_incl_max(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true));   // row_shr:1
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true));   // row_shr:2
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true));   // row_shr:4
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true));   // row_shr:8
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false));  // row_bcast:15
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false));  // row_bcast:31
+  return x;
+}
+
+// Largest and smallest nonzero key and the number of nonzero keys over the
+// workgroup (kmin = ~0, kmax = 0 when there is none); the smallest is taken as
+// the largest complement.
 template <int KPT, typename Get>
-CSA2_DEV void radix_select(Get get, uint32_t K, SelShared& sh, uint32_t (*h)[kDigitBins], uint32_t& tau,
-                           uint32_t& need) {
+CSA2_DEV void key_stats(Get get, SelShared& sh, uint32_t& kmin, uint32_t& kmax, uint32_t& count) {
+  uint32_t mx = 0u, mnc = 0u, cnt = 0u;
 #pragma unroll 16
   for (int j = 0; j < KPT; ++j) {
     const uint32_t k = get(j);
-    hist_inc(h[0], k >> 20, k != 0u);
+    mx = max(mx, k);
+    mnc = max(mnc, k != 0u ? ~k : 0u);
+    cnt += k != 0u ? 1u : 0u;
+  }
+  mx = __builtin_amdgcn_readlane(wave_incl_max(mx), 63);
+  mnc = __builtin_amdgcn_readlane(wave_incl_max(mnc), 63);
+  cnt = __builtin_amdgcn_readlane(wave_incl_scan(cnt), 63);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) { sh.wsum[wave] = mx; sh.wmin[wave] = mnc; sh.wcnt[wave] = cnt; }
+  __syncthreads();
+  mx = 0u; mnc = 0u; cnt = 0u;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) { mx = max(mx, sh.wsum[w]); mnc = max(mnc, sh.wmin[w]); cnt += sh.wcnt[w]; }
+  __syncthreads();
+  kmax = mx;
+  kmin = ~mnc;
+  count = cnt;
+}
+
+// K-th largest key among nonzero keys (1 <= K <= #nonzero): returns the key
+// value tau and how many keys equal to tau belong to the top K.  kmin / kmax
+// are the smallest / largest nonzero key.  Radix passes run on the offset
+// r = key - kmin, whose width w is known from the key range:
+// the first pass takes its top 12 bits (so the keys spread over all 4096 bins
+// whatever their magnitude, and equal digits rarely collide in the LDS
+// atomics), a second pass the next up to 12 bits, a third the remaining up
+// to 8.  Histograms h[0..2] are pre-cleared.  get(j) returns this thread's
+// j-th key (j < KPT); small KPT keeps keys in registers, large KPT re-reads
+// them each pass.
+template <int KPT, typename Get>
+CSA2_DEV void radix_select(Get get, uint32_t K, uint32_t kmin, uint32_t kmax, SelShared& sh,
+                           uint32_t (*h)[kDigitBins], uint32_t& tau, uint32_t& need) {
+  const uint32_t range = kmax - kmin;
+  const int width = range == 0u ? 0 : 32 - __builtin_clz(range);
+  const int s1 = width > 12 ? width - 12 : 0;                 // bits below the first digit
+  const int b2 = s1 > 12 ? 12 : s1;                            // second digit width
+  const int s2 = s1 - b2;                                      // bits below the second digit (<= 8)
+#pragma unroll 16
+  for (int j = 0; j < KPT; ++j) {
+    const uint32_t k = get(j);
+    hist_inc(h[0], (k - kmin) >> s1, k != 0u);
   }
   __syncthreads();
   uint32_t d1, a1;
   hist_find<kDigitBins>(h[0], K, sh, d1, a1);
-  const uint32_t k2 = K - a1;
+  uint32_t kk = K - a1;
+  uint32_t pre = d1;                                           // known high bits of the offset
+  if (b2 > 0) {
+    const uint32_t m2 = (1u << b2) - 1u;
 #pragma unroll 16
-  for (int j = 0; j < KPT; ++j) {
-    const uint32_t k = get(j);
-    hist_inc(h[1], (k >> 8) & 0xFFFu, k != 0u && (k >> 20) == d1);
+    for (int j = 0; j < KPT; ++j) {
+      const uint32_t k = get(j);
+      const uint32_t r = k - kmin;
+      hist_inc(h[1], (r >> s2) & m2, k != 0u && (r >> s1) == d1);
+    }
+    __syncthreads();
+    uint32_t d2, a2;
+    hist_find<kDigitBins>(h[1], kk, sh, d2, a2);
+    kk -= a2;
+    pre = (pre << b2) | d2;
   }
-  __syncthreads();
-  uint32_t d2, a2;
-  hist_find<kDigitBins>(h[1], k2, sh, d2, a2);
-  const uint32_t k3 = k2 - a2;
-  const uint32_t pre = (d1 << 12) | d2;
+  if (s2 > 0) {
+    const uint32_t m3 = (1u << s2) - 1u;
 #pragma unroll 16
-  for (int j = 0; j < KPT; ++j) {
-    const uint32_t k = get(j);
-    hist_inc(h[2], k & 0xFFu, k != 0u && (k >> 8) == pre);
+    for (int j = 0; j < KPT; ++j) {
+      const uint32_t k = get(j);
+      const uint32_t r = k - kmin;
+      hist_inc(h[2], r & m3, k != 0u && (r >> s2) == pre);
+    }
+    __syncthreads();
+    uint32_t d3, a3;
+    hist_find<256>(h[2], kk, sh, d3, a3);
+    kk -= a3;
+    pre = (pre << s2) | d3;
   }
-  __syncthreads();
-  uint32_t d3, a3;
-  hist_find<256>(h[2], k3, sh, d3, a3);
-  tau = (pre << 8) | d3;
-  need = k3 - a3;
+  tau = kmin + pre;
+  need = kk;
 }
 
 CSA2_DEV void hists_clear(SelShared& sh) {
@@ -332,15 +397,13 @@ CSA2_DEV void compact_topk(Get get, uint32_t tau, uint32_t need, SelShared& sh, 
 template <int KPT2>
 CSA2_DEV void select_positions(const uint32_t (&key)[KPT2], SelShared& sh, const int32_t* pool_slots,
                                int32_t* topk_out) {
-  uint32_t nvalid = 0;
-#pragma unroll
-  for (int j = 0; j < KPT2; ++j) nvalid += key[j] != 0u ? 1u : 0u;
-  nvalid = block_sum(nvalid, sh);
+  auto get = [&](int j) { return key[j]; };
+  uint32_t kmin, kmax, nvalid;
+  key_stats<KPT2>(get, sh, kmin, kmax, nvalid);
   const uint32_t K2 = min(nvalid, (uint32_t)kTopK);
   if (K2 > 0) {
     uint32_t tau, need;
-    auto get = [&](int j) { return key[j]; };
-    radix_select<KPT2>(get, K2, sh, &sh.hist[3], tau, need);
+    radix_select<KPT2>(get, K2, kmin, kmax, sh, &sh.hist[3], tau, need);
     const int base = threadIdx.x * KPT2;
     compact_topk<KPT2>(get, tau, need, sh, [&](uint32_t o, int j) {
       const int c = base + j;
@@ -368,19 +431,29 @@ __global__ __launch_bounds__(kSelThreads) void k_select_full(SelectParams p) {
   const uint32_t* bk = p.bkeys + q * p.bk_stride;
   if constexpr (KPT1 <= 16) {
     uint32_t bkey[KPT1];
+    if (base1 + KPT1 <= nb) {                 // whole run visible: 16-byte loads
 #pragma unroll
-    for (int j = 0; j < KPT1; ++j) bkey[j] = base1 + j < nb ? bk[base1 + j] : 0u;
+      for (int j = 0; j < KPT1; j += 4) {
+        const u4 v = *reinterpret_cast<const u4*>(bk + base1 + j);
+        bkey[j] = v[0]; bkey[j + 1] = v[1]; bkey[j + 2] = v[2]; bkey[j + 3] = v[3];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < KPT1; ++j) bkey[j] = base1 + j < nb ? bk[base1 + j] : 0u;
+    }
     auto get = [&](int j) { return bkey[j]; };
     if (K1 > 0) {
-      uint32_t tau, need;
-      radix_select<KPT1>(get, K1, sh, &sh.hist[0], tau, need);
+      uint32_t tau, need, kmin, kmax, cnt;
+      key_stats<KPT1>(get, sh, kmin, kmax, cnt);
+      radix_select<KPT1>(get, K1, kmin, kmax, sh, &sh.hist[0], tau, need);
       compact_topk<KPT1>(get, tau, need, sh, [&](uint32_t o, int j) { sh.pool[o] = (int32_t)(base1 + j); });
     }
   } else {
     auto get = [&](int j) { return base1 + j < nb ? bk[base1 + j] : 0u; };
     if (K1 > 0) {
-      uint32_t tau, need;
-      radix_select<KPT1>(get, K1, sh, &sh.hist[0], tau, need);
+      uint32_t tau, need, kmin, kmax, cnt;
+      key_stats<KPT1>(get, sh, kmin, kmax, cnt);
+      radix_select<KPT1>(get, K1, kmin, kmax, sh, &sh.hist[0], tau, need);
       compact_topk<KPT1>(get, tau, need, sh, [&](uint32_t o, int j) { sh.pool[o] = (int32_t)(base1 + j); });
     }
   }
@@ -393,11 +466,19 @@ __global__ __launch_bounds__(kSelThreads) void k_select_full(SelectParams p) {
   uint32_t key[KPT2];
   const int base2 = threadIdx.x * KPT2;
 #pragma unroll
-  for (int j = 0; j < KPT2; ++j) {
-    const int c = base2 + j;
-    const int32_t blk = sh.pool[c >> 3];
-    const int64_t pos = (int64_t)blk * kBlock + (c & 7);
-    key[j] = (blk >= 0 && pos < nv) ? p.tkeys[q * p.tk_stride + pos] : 0u;
+  for (int jb = 0; jb < KPT2; jb += kBlock) {           // one pool block = 8 keys, 32 aligned bytes
+    const int32_t blk = sh.pool[(base2 + jb) >> 3];
+    const int64_t pos0 = (int64_t)blk * kBlock;
+    if (blk >= 0 && pos0 + kBlock <= nv) {
+      const u4* kp = reinterpret_cast<const u4*>(p.tkeys + q * p.tk_stride + pos0);
+      const u4 v0 = kp[0], v1 = kp[1];
+      key[jb + 0] = v0[0]; key[jb + 1] = v0[1]; key[jb + 2] = v0[2]; key[jb + 3] = v0[3];
+      key[jb + 4] = v1[0]; key[jb + 5] = v1[1]; key[jb + 6] = v1[2]; key[jb + 7] = v1[3];
+    } else {
+#pragma unroll
+      for (int r = 0; r < kBlock; ++r)
+        key[jb + r] = (blk >= 0 && pos0 + r < nv) ? p.tkeys[q * p.tk_stride + pos0 + r] : 0u;
+    }
   }
   select_positions<KPT2>(key, sh, sh.pool, p.topk + q * kTopK);
 }
