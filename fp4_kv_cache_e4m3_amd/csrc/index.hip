@@ -32,6 +32,20 @@
 namespace csa2 {
 
 // ============================================================== scan
+// x + (x of lane l ^ 16), resp. l ^ 32, with the gfx950 permlane swaps (no LDS
+// traffic); fp32 addition commutes, so both lanes get the same bits.
+CSA2_DEV float sum_swap16(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
+CSA2_DEV float sum_swap32(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
+
+// Channel order of the int8 operands: lane group g takes, in k-step kk, the 16
+// channels 16g + 64kk .. +15, so the 4 lanes of a key row read 64 contiguous
+// bytes per load (the contraction only needs both operands to agree).
 // HI: indexer heads (2, 4, 8, 16); DI: indexer dim (64, 128).
 template <int DI, int HI>
 __global__ __launch_bounds__(256) void k_index_scan(ScanParams p) {
@@ -39,7 +53,6 @@ __global__ __launch_bounds__(256) void k_index_scan(ScanParams p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int b = blockIdx.y;
-  const int64_t t0 = (int64_t)blockIdx.x * p.chunk;
   const int rows_used = p.qn * HI;            // score rows of this sequence
   const int MT = (rows_used + 15) >> 4;       // M tiles (<= 4)
 
@@ -50,8 +63,7 @@ __global__ __launch_bounds__(256) void k_index_scan(ScanParams p) {
     for (int j = 0; j < p.qn; ++j) vmax = max(vmax, (int64_t)p.nvis[b * p.qn + j]);
     vmax = min(vmax, p.T);
   }
-  if (t0 >= vmax) return;
-  const int64_t tend = min(t0 + (int64_t)p.chunk, vmax);
+  const int64_t t0 = 0, tend = vmax;
 
   // A operands (score rows) and weights of the 4 output rows each lane holds
   v4i a[4][KK];
@@ -64,7 +76,7 @@ __global__ __launch_bounds__(256) void k_index_scan(ScanParams p) {
       v4i z = {0, 0, 0, 0};
       if (mt < MT && r < rows_used) {
         const int j = r / HI, h = r % HI;
-        z = *reinterpret_cast<const v4i*>(p.iq + ((int64_t)(b * p.qn + j) * HI + h) * DI + g * (DI / 4) + kk * 16);
+        z = *reinterpret_cast<const v4i*>(p.iq + ((int64_t)(b * p.qn + j) * HI + h) * DI + g * 16 + kk * 64);
       }
       a[mt][kk] = z;
     }
@@ -101,8 +113,8 @@ __global__ __launch_bounds__(256) void k_index_scan(ScanParams p) {
       for (int i = 0; i < 4; ++i) val[i] = wv[mt][i] * (float)max(acc[i], 0);
       if constexpr (HI >= 4) {
         float tot = ((val[0] + val[1]) + val[2]) + val[3];
-        if constexpr (HI >= 8) tot = tot + __shfl_xor(tot, 16, 64);
-        if constexpr (HI >= 16) tot = tot + __shfl_xor(tot, 32, 64);
+        if constexpr (HI >= 8) tot = sum_swap16(tot);
+        if constexpr (HI >= 16) tot = sum_swap32(tot);
         const int j = (16 * mt + 4 * g) / HI;     // query within the sequence
         const uint32_t key = (tok_ok && t < nvq[mt] && j < p.qn) ? score_key(tot) : 0u;
         // 8-token block max inside each half of the 16-lane row
@@ -137,22 +149,25 @@ __global__ __launch_bounds__(256) void k_index_scan(ScanParams p) {
     }
   };
 
-  // U tiles per wave and iteration: all their loads are issued before the
-  // first MFMA so several KiB per wave are in flight
+  // The workgroups of a sequence sweep its keys together: in each round they
+  // take 16 consecutive tiles each out of one contiguous stretch of
+  // 16 * gridDim.x tiles, so the requests in flight across the GPU stay close
+  // in memory.  Wave w takes tiles 4u + w of its workgroup's 16; all U loads
+  // are issued before the first MFMA so several KiB per wave are in flight.
   constexpr int U = 4;
-  for (int it0 = wave; it0 < ntile; it0 += 4 * U) {
+  for (int64_t base = 16 * (int64_t)blockIdx.x; base < ntile; base += 16 * (int64_t)gridDim.x) {
     v4i bf[U][KK];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t t = t0 + 16 * (it0 + 4 * u) + n;
-      const int64_t row = t < tend ? t : t0;
+      const int64_t t = 16 * (base + 4 * u + wave) + n;
+      const int64_t row = t < tend ? t : 0;
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
-        bf[u][kk] = *reinterpret_cast<const v4i*>(ikb + row * DI + g * (DI / 4) + kk * 16);
+        bf[u][kk] = *reinterpret_cast<const v4i*>(ikb + row * DI + g * 16 + kk * 64);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if (it0 + 4 * u < ntile) process(it0 + 4 * u, bf[u]);
+      if (base + 4 * u + wave < ntile) process((int)(base + 4 * u + wave), bf[u]);
   }
 }
 
@@ -501,7 +516,7 @@ __global__ __launch_bounds__(256) void k_reindex_score(ReindexParams p) {
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
     v4i z = {0, 0, 0, 0};
-    if (n < HI) z = *reinterpret_cast<const v4i*>(p.iq + (q * HI + n) * DI + g * (DI / 4) + kk * 16);
+    if (n < HI) z = *reinterpret_cast<const v4i*>(p.iq + (q * HI + n) * DI + g * 16 + kk * 64);
     a[kk] = z;
   }
   float wv[4];
@@ -521,7 +536,7 @@ __global__ __launch_bounds__(256) void k_reindex_score(ReindexParams p) {
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       v4i z = {0, 0, 0, 0};
-      if (ok) z = *reinterpret_cast<const v4i*>(ikb + pos * DI + g * (DI / 4) + kk * 16);
+      if (ok) z = *reinterpret_cast<const v4i*>(ikb + pos * DI + g * 16 + kk * 64);
       bf[kk] = z;
     }
     v4i acc = {0, 0, 0, 0};
@@ -535,8 +550,8 @@ __global__ __launch_bounds__(256) void k_reindex_score(ReindexParams p) {
       tot = val[0] + val[1];
     } else {
       tot = ((val[0] + val[1]) + val[2]) + val[3];
-      if constexpr (HI >= 8) tot = tot + __shfl_xor(tot, 16, 64);
-      if constexpr (HI >= 16) tot = tot + __shfl_xor(tot, 32, 64);
+      if constexpr (HI >= 8) tot = sum_swap16(tot);
+      if constexpr (HI >= 16) tot = sum_swap32(tot);
     }
     if (g == 0) ck[slot * kBlock + (n & 7)] = ok ? score_key(tot) : 0u;
   }
