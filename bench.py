@@ -25,6 +25,23 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak (AMD spec)
 
+# HBM bytes per k_index_scan launch measured with rocprofv3 FETCH_SIZE and
+# WRITE_SIZE (each scaled by what the counter reads for a plain 1 GiB copy) on
+# the workload and kernel source named here; reported only while both match.
+SCAN_TRAFFIC = {"workload": "decode_group_full_reuse3_b32_t65536",
+                "source_sha256": "ba675ecea58dc4d17d5d7f19ef74a9a147cc04593b8d2f6c77ff1da0cc579c44",
+                "bytes": 268827648 + 9526579}
+
+
+def scan_traffic(w):
+    import hashlib
+    src = os.path.join(ROOT, "fp4_kv_cache_e4m3_amd", "csrc", "index.hip")
+    with open(src, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if w.name == SCAN_TRAFFIC["workload"] and sha == SCAN_TRAFFIC["source_sha256"]:
+        return SCAN_TRAFFIC["bytes"]
+    return None
+
 
 def group_bytes(w) -> dict:
     """Algorithmic bytes of one group step (what the method must move)."""
@@ -186,7 +203,7 @@ def main() -> int:
         "roofline": {"kernel": "k_index_scan" if full else "k_reindex_score+select",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "bytes_per_launch": scan_bytes, "traffic": None},
+                     "bytes_per_launch": scan_bytes, "traffic": scan_traffic(w) if full else None},
         "wall_s_timed": round(t_wall, 3),
     }
     if not args.no_cpu_baseline:
