@@ -15,15 +15,15 @@
 //    half of the output channels).  Both halves of a (query, head group)
 //    compute the same logits over all D channels; each stages and multiplies
 //    only its own D/2 value channels, so no partial outputs are exchanged.
-//    The two halves get workgroup ids 8 apart, which the dispatcher places on
-//    one XCD, so the second gather of the same rows hits that XCD's L2.
+//    All workgroups of one query get ids that are equal mod 8, which the
+//    dispatcher places on one XCD, so they share its L2 for the query's rows.
 //  * NW waves per workgroup take every NW-th 16-entry tile and merge their
 //    (max, sum, O) states through LDS at the end; when the tile list is split
 //    over several workgroups, a second kernel merges the partial states.
-//  * per tile a wave gathers 16 entries: lane (e = lane % 16, g = lane / 16)
-//    loads D/8 channels of entry e from each column half ([g*D/8, (g+1)*D/8)
-//    within the half): FP4 codes + E4M3 scales, or bf16 SWA values, and turns
-//    them into fp16 in registers (FP4 values are exact in fp16).
+//  * per tile a wave gathers 16 entries (lane % 16 = entry; the 4 lanes of an
+//    entry split its channels) through buffer loads, FP4 codes + E4M3 scales
+//    or bf16 window rows, and turns them into fp16 in registers (FP4 values
+//    are exact in fp16).  Two FP4 gathers are in flight per wave.
 //  * QK^T: MFMA 16x16x32 f16 with the entries as A rows and the 16 heads as
 //    B columns (Q lives in registers, in the same channel order as K).  Each
 //    half's k-steps accumulate separately and the two sums are added last;
@@ -34,7 +34,6 @@
 //  * PV: MFMA 16x16x16 f16 over the 16 entries; the V operand (4 entries of
 //    one channel per lane) comes from one transposing LDS read per 16
 //    channels of the wave's own fp16 half-tile.
-//  * the next tile's gather is issued before the current tile is processed.
 // Q and SWA rows go bf16 -> fp16 unscaled, which is exact for magnitudes in
 // [2^-14, 65504] (bf16 carries 8 significant bits, fp16 11), so QK^T is exact
 // up to fp32 accumulation; sm_scale * log2(e) multiplies the fp32 logits and
