@@ -48,8 +48,8 @@ def group_bytes(w) -> dict:
     nq, T = w.nq, w.kv_len
     row = w.dim // 2 + w.dim // 16                         # FP4 row: codes + scales
     scan = w.batch * T * w.idx_dim + nq * w.idx_heads * (w.idx_dim + 4)
-    select = nq * (2048 * 4 + 512 * 4)                     # pool + topk written
-    quant = w.batch * (w.dim * 4 + row)
+    select = nq * ((0 if w.encoder else 2048 * 4) + 512 * 4)   # pool (decoder groups) + topk written
+    quant = w.batch * w.new_per_seq * (w.dim * 4 + row)
     attn_layer = (nq * (512 * row + w.heads * w.dim * 2 + w.heads * w.dim * 4 + 512 * 4)
                   + w.batch * w.swa_rows * w.dim * 2)
     reindex = nq * (2048 * 4 + 16384 * w.idx_dim + w.idx_heads * (w.idx_dim + 4) + 512 * 4)
@@ -62,10 +62,11 @@ def group_bytes(w) -> dict:
                 total=total)
 
 
-def cpu_baseline(w, n_seq: int) -> dict:
-    """The FP64 oracle on the first n_seq sequences of the same workload (one full
-    group step each: new-row quantisation, Full index over all T positions,
-    every layer's attention).  Input generation is not timed."""
+def cpu_baseline(w, max_queries: int) -> dict:
+    """The FP64 oracle on the first max_queries query tokens of the same
+    workload (one full group step each: new-entry quantisation of their
+    sequences, Full index over all T positions, every layer's attention).
+    Input generation is not timed."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -74,32 +75,32 @@ def cpu_baseline(w, n_seq: int) -> dict:
     from oracle import indexer as oidx
     from oracle import quant as oquant
 
-    T = w.kv_len
-    iq, iw = synth.index_q(w)[:n_seq * w.q_per_seq], synth.index_w(w)[:n_seq * w.q_per_seq]
-    ik = np.stack([synth.index_k(w, b) for b in range(n_seq)])
-    newr = synth.new_rows(w)[:n_seq]
-    qs = [synth.bf16_bits_to_f32(synth.attn_q_bf16(w, l)[:n_seq * w.q_per_seq]).astype(np.float64)
+    T, qn = w.kv_len, w.q_per_seq
+    nqs = min(w.nq, max_queries)
+    n_seq = (nqs + qn - 1) // qn
+    iq, iw = synth.index_q(w)[:nqs], synth.index_w(w)[:nqs]
+    ik = [synth.index_k(w, b) for b in range(n_seq)]
+    newr = synth.new_rows(w)[:n_seq * w.new_per_seq]
+    qs = [synth.bf16_bits_to_f32(synth.attn_q_bf16(w, l)[:nqs]).astype(np.float64)
           for l in range(len(w.layers))]
     sws = [synth.bf16_bits_to_f32(synth.swa_bf16(w, l)[:n_seq]).astype(np.float64)
            for l in range(len(w.layers))]
     srcs = [synth.kv_source(w, b) for b in range(n_seq)]
     t0 = time.perf_counter()
     oquant.quantize_rows(newr)
-    _, topk = oidx.index_full(iq, iw, ik, w.q_per_seq)
-    for qi in range(n_seq * w.q_per_seq):
-        b = qi // w.q_per_seq
-        pos = topk[qi][topk[qi] >= 0]
+    for qi in range(nqs):
+        b = qi // qn
+        _, pos, _ = oidx.full_query(iq[qi], iw[qi], ik[b], T)
         codes, scales = oquant.quantize_rows(srcs[b][pos])     # the selected cache rows
         for l in range(len(w.layers)):
-            keys = oattn.query_entries(qi % w.q_per_seq, w.q_per_seq, len(pos), np.arange(len(pos)),
-                                       codes, scales, sws[l][b:b + 1], w.window)
+            keys = oattn.query_entries(qi % qn, qn, len(pos), np.arange(len(pos)), codes, scales,
+                                       sws[l][b:b + 1], w.window)
             oattn.attend(qs[l][qi], keys, 1.0 / np.sqrt(w.dim))
     dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    nq = n_seq * w.q_per_seq
-    return {"value": nq / dt, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n_seq} of {w.batch} sequences ({nq} query tokens), full group step "
-                      f"({'+'.join(w.layers)}), T={T}; {dt:.2f} s wall"}
+    return {"value": nqs / dt, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {nqs} of {w.nq} query tokens ({n_seq} of {w.batch} sequences), full group "
+                      f"step ({'+'.join(w.layers)}), T={T}; {dt:.2f} s wall"}
 
 
 def main() -> int:
@@ -108,7 +109,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode_group_full_reuse3_b32_t65536")
-    ap.add_argument("--cpu-seqs", type=int, default=32, help="sequences in the oracle sample")
+    ap.add_argument("--cpu-queries", type=int, default=32, help="query tokens in the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (the "
@@ -145,11 +146,11 @@ def main() -> int:
     def step(ev=None):
         # ev: list of events recorded between the calls (timing only; no sync)
         if full:
-            csa2.quantize_kv(g.new_rows, g.new_codes, g.new_scales, stream)
+            g.quantize_new(stream)
             if ev is not None: ev[0].record(stream)
             csa2.index_scan(g.iargs, g.iws, stream)
             if ev is not None: ev[1].record(stream)
-            csa2.index_select(g.iargs, g.pool, g.topk, g.iws, stream)
+            csa2.index_select(g.iargs, g.pool_out(), g.topk, g.iws, stream)
         else:
             if ev is not None: ev[0].record(stream)
             csa2.index_reindex(g.iargs, g.pool, g.topk, g.iws, stream)
@@ -207,7 +208,7 @@ def main() -> int:
         "wall_s_timed": round(t_wall, 3),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, min(args.cpu_seqs, w.batch))
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_queries)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -14,13 +14,14 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 constexpr int64_t kMaxKvLen = 1 << 20;           // 131,072 blocks per query in the pool select
+constexpr int64_t kMaxScoreRows = 64 * 65535;    // Qn * H_I: 64 score rows per scan workgroup
 
 int check_index(const csa2_index_args* a) {
   if (!a) return CSA2_ERR_NULL;
   if (a->batch < 0 || a->q_per_seq < 1 || a->kv_len < 0 || a->kv_len > kMaxKvLen) return CSA2_ERR_SHAPE;
   if (!(a->heads == 2 || a->heads == 4 || a->heads == 8 || a->heads == 16)) return CSA2_ERR_SHAPE;
   if (!(a->dim == 64 || a->dim == 128)) return CSA2_ERR_SHAPE;
-  if ((int64_t)a->q_per_seq * a->heads > 64) return CSA2_ERR_SHAPE;
+  if ((int64_t)a->q_per_seq * a->heads > kMaxScoreRows) return CSA2_ERR_SHAPE;
   const int64_t nq = (int64_t)a->batch * a->q_per_seq;
   if (nq > 0 && (!a->q || !a->w)) return CSA2_ERR_NULL;
   if (nq > 0 && a->kv_len > 0 && !a->k) return CSA2_ERR_NULL;
@@ -109,6 +110,13 @@ int check_attn(const csa2_attn_args* a) {
   if (a->kv_len > 0 && a->topk_k > 0 && (!a->codes || !a->scales || !a->topk)) return CSA2_ERR_NULL;
   if (a->window > 0 && !a->swa) return CSA2_ERR_NULL;
   if (a->codes_stride < a->dim / 2 || a->scales_stride < a->dim / 16) return CSA2_ERR_SHAPE;
+  // one sequence's rows are addressed through 32-bit buffer offsets (24-bit
+  // row multiplies)
+  constexpr int64_t kBufMax = 0xFFFFE000ll;
+  if (a->kv_len >= (1 << 24) || a->codes_stride >= (1 << 24) || a->scales_stride >= (1 << 24) ||
+      a->kv_len * a->codes_stride > kBufMax || a->kv_len * a->scales_stride > kBufMax ||
+      ((int64_t)a->window - 1 + a->q_per_seq) * a->dim * 2 > kBufMax)
+    return CSA2_ERR_SHAPE;
   if (!aligned(a->q, 16) || !aligned(a->codes, 16) || !aligned(a->scales, 8) || !aligned(a->swa, 16) ||
       !aligned(a->out, 16) || !aligned(a->topk, 4) || (a->codes_stride % 16) || (a->scales_stride % 8))
     return CSA2_ERR_ALIGN;

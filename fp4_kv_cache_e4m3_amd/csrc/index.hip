@@ -12,8 +12,9 @@
 // Design (gfx950, wave64):
 //  * Scan: the indexer keys stream once from HBM.  Each wave takes 16-token
 //    tiles: an int8 MFMA 16x16x64 contracts the 16 token rows (B operand,
-//    one token per lane column) with up to 16 score rows (A operand: the
-//    sequence's query heads, Qn * H_I rows, padded), so the dot products are
+//    one token per lane column) with up to 64 score rows (A operand: 64 of
+//    the sequence's Qn * H_I query-head rows; more rows take more
+//    workgroups, so prefill chunks reuse the keys from L2), so the dot products are
 //    exact int32.  ReLU, head weights and the head sum run on the 4
 //    accumulator rows a lane holds plus one cross-lane add; the 8-token block
 //    maximum is three DPP max steps inside each 16-lane row.  Token keys and
@@ -53,14 +54,18 @@ __global__ __launch_bounds__(256) void k_index_scan(ScanParams p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int b = blockIdx.y;
-  const int rows_used = p.qn * HI;            // score rows of this sequence
-  const int MT = (rows_used + 15) >> 4;       // M tiles (<= 4)
+  // score rows (query j, head h) -> row j*HI + h; this workgroup takes rows
+  // [r0, r0 + rows_used) of its sequence, at most 64 (4 M tiles)
+  const int r0 = 64 * (int)blockIdx.z;
+  const int rows_used = min(64, p.qn * HI - r0);
+  const int MT = (rows_used + 15) >> 4;
+  const int j_lo = r0 / HI, j_hi = (r0 + rows_used - 1) / HI;
 
-  // furthest visible position over the sequence's queries
+  // furthest visible position over the workgroup's queries
   int64_t vmax = p.T;
   if (p.nvis) {
     vmax = 0;
-    for (int j = 0; j < p.qn; ++j) vmax = max(vmax, (int64_t)p.nvis[b * p.qn + j]);
+    for (int j = j_lo; j <= j_hi; ++j) vmax = max(vmax, (int64_t)p.nvis[b * p.qn + j]);
     vmax = min(vmax, p.T);
   }
   const int64_t t0 = 0, tend = vmax;
@@ -75,7 +80,7 @@ __global__ __launch_bounds__(256) void k_index_scan(ScanParams p) {
     for (int kk = 0; kk < KK; ++kk) {
       v4i z = {0, 0, 0, 0};
       if (mt < MT && r < rows_used) {
-        const int j = r / HI, h = r % HI;
+        const int j = (r0 + r) / HI, h = (r0 + r) % HI;
         z = *reinterpret_cast<const v4i*>(p.iq + ((int64_t)(b * p.qn + j) * HI + h) * DI + g * 16 + kk * 64);
       }
       a[mt][kk] = z;
@@ -84,14 +89,14 @@ __global__ __launch_bounds__(256) void k_index_scan(ScanParams p) {
     for (int i = 0; i < 4; ++i) {
       const int r2 = 16 * mt + 4 * g + i;
       float w = 0.0f;
-      if (mt < MT && r2 < rows_used) w = p.iw[(int64_t)(b * p.qn + r2 / HI) * HI + r2 % HI];
+      if (mt < MT && r2 < rows_used) w = p.iw[(int64_t)(b * p.qn + (r0 + r2) / HI) * HI + (r0 + r2) % HI];
       wv[mt][i] = w;
     }
   }
   int nvq[4];   // visibility of the queries whose rows this lane's group holds (HI >= 4 case)
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
-    const int j = (16 * mt + 4 * g) / HI;
+    const int j = (r0 + 16 * mt + 4 * g) / HI;
     nvq[mt] = (int)min((int64_t)(p.nvis && j < p.qn ? p.nvis[b * p.qn + j] : p.T), p.T);
   }
 
@@ -115,7 +120,7 @@ __global__ __launch_bounds__(256) void k_index_scan(ScanParams p) {
         float tot = ((val[0] + val[1]) + val[2]) + val[3];
         if constexpr (HI >= 8) tot = sum_swap16(tot);
         if constexpr (HI >= 16) tot = sum_swap32(tot);
-        const int j = (16 * mt + 4 * g) / HI;     // query within the sequence
+        const int j = (r0 + 16 * mt + 4 * g) / HI;   // query within the sequence
         const uint32_t key = (tok_ok && t < nvq[mt] && j < p.qn) ? score_key(tot) : 0u;
         // 8-token block max inside each half of the 16-lane row
         uint32_t m = key;
@@ -132,7 +137,7 @@ __global__ __launch_bounds__(256) void k_index_scan(ScanParams p) {
 #pragma unroll
         for (int hq = 0; hq < 2; ++hq) {
           const float tot = val[2 * hq] + val[2 * hq + 1];
-          const int j = (16 * mt + 4 * g) / 2 + hq;
+          const int j = (r0 + 16 * mt + 4 * g) / 2 + hq;
           const int nv = (int)min((int64_t)(p.nvis && j < p.qn ? p.nvis[b * p.qn + j] : p.T), p.T);
           const uint32_t key = (tok_ok && t < nv && j < p.qn) ? score_key(tot) : 0u;
           uint32_t m = key;
@@ -576,7 +581,9 @@ __global__ __launch_bounds__(kSelThreads) void k_select_reindex(ReindexParams p)
 template <int DI, int HI>
 static void launch_scan_t(const ScanParams& p, hipStream_t st) {
   const int64_t chunks = (p.T + p.chunk - 1) / p.chunk;
-  hipLaunchKernelGGL((k_index_scan<DI, HI>), dim3((unsigned)chunks, (unsigned)p.batch), dim3(256), 0, st, p);
+  const int64_t groups = ((int64_t)p.qn * HI + 63) / 64;    // 64 score rows per workgroup
+  hipLaunchKernelGGL((k_index_scan<DI, HI>), dim3((unsigned)chunks, (unsigned)p.batch, (unsigned)groups), dim3(256),
+                     0, st, p);
 }
 
 hipError_t launch_index_scan(const ScanParams& p, int heads, int dim, hipStream_t st) {

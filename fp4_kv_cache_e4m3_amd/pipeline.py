@@ -52,7 +52,7 @@ class DecodeGroup:
         for b in range(B_):
             self.ik[b].copy_(torch.from_numpy(synth.index_k(w, b)))
         # ---- per-step inputs
-        self.new_rows = _dev(synth.new_rows(w), dev)                       # [B, d] fp32
+        self.new_rows = _dev(synth.new_rows(w), dev)           # [B * new_per_seq, d] fp32
         self.iq = _dev(synth.index_q(w, 0), dev)
         self.iw = _dev(synth.index_w(w, 0), dev)
         nl = len(w.layers)
@@ -69,9 +69,20 @@ class DecodeGroup:
                                   w.q_per_seq, T, w.window) for l in range(nl)]
         aws = max(B.attn_workspace_size(a) for a in self.aargs)
         self.aws = torch.empty(max(256, aws), dtype=torch.uint8, device=dev) if aws > 0 else None
-        # new tokens land in the last slot of each sequence: rows b*T + T-1
-        self.new_codes = self.codes[T - 1::T]
-        self.new_scales = self.scales[T - 1::T]
+        # a step's new entries land in the last new_per_seq slots of each
+        # sequence (rows b*T + T - n + i); one strided quantise call per
+        # sequence or per slot index, whichever is fewer
+        n = w.new_per_seq
+        self._new_calls = []
+        if n == 1:
+            self._new_calls.append((self.new_rows, self.codes[T - 1::T], self.scales[T - 1::T]))
+        elif B_ <= n:
+            for b in range(B_):
+                r = slice(b * T + T - n, b * T + T)
+                self._new_calls.append((self.new_rows[b * n:(b + 1) * n], self.codes[r], self.scales[r]))
+        else:
+            for i in range(n):
+                self._new_calls.append((self.new_rows[i::n], self.codes[T - n + i::T], self.scales[T - n + i::T]))
         if w.layers[0] == "reindex":
             iq0 = _dev(synth.index_q(w, 0, pool_source=True), dev)
             iw0 = _dev(synth.index_w(w, 0, pool_source=True), dev)
@@ -81,12 +92,21 @@ class DecodeGroup:
             self._pool_src = (iq0, iw0)
         torch.cuda.synchronize()
 
+    # the stages of one step (bench.py times them apart)
+    def quantize_new(self, stream=None) -> None:
+        for x, c, s in self._new_calls:
+            B.quantize_kv(x, c, s, stream)
+
+    def pool_out(self):
+        """The pool buffer, or None for an encoder group (no Reindex consumes it)."""
+        return None if self.w.encoder else self.pool
+
     # one pass of the whole group
     def step(self, stream=None) -> None:
         w = self.w
         if w.layers[0] == "full":
-            B.quantize_kv(self.new_rows, self.new_codes, self.new_scales, stream)
-            B.index_full(self.iargs, self.pool, self.topk, self.iws, stream)
+            self.quantize_new(stream)
+            B.index_full(self.iargs, self.pool_out(), self.topk, self.iws, stream)
         elif w.layers[0] == "reindex":
             B.index_reindex(self.iargs, self.pool, self.topk, self.iws, stream)
         for l in range(len(w.layers)):

@@ -62,7 +62,8 @@ class Workload:
     idx_range: int           # indexer q/k integers uniform in [-r, r]
     w_max: int               # indexer head weights integers uniform in [1, w_max]
     layers: tuple = ("full",)  # CSA2 layer modes of the group
-    ratio: int = 1           # tokens per compressed entry (context only)
+    ratio: int = 1           # tokens per compressed entry
+    encoder: bool = False    # encoder (prefill) group: no Reindex layer consumes the pool
     note: str = ""
 
     @property
@@ -72,6 +73,11 @@ class Workload:
     @property
     def swa_rows(self) -> int:
         return self.window - 1 + self.q_per_seq
+
+    @property
+    def new_per_seq(self) -> int:
+        """Main-KV entries a step appends per sequence (its query tokens / ratio)."""
+        return max(1, self.q_per_seq // self.ratio)
 
     def replace(self, **kw) -> "Workload":
         d = {f: getattr(self, f) for f in self.__dataclass_fields__}
@@ -93,7 +99,7 @@ C3 = Workload("decode_group_reindex_reuse3_b32_t65536", 3, batch=32, q_per_seq=1
               note="decoder groups 2-5: Reindex + 3 Reuse")
 C4 = Workload("prefill_group_full_reuse5_q4096_t65536", 4, batch=1, q_per_seq=4096, kv_len=65536,
               dim=512, heads=64, window=128, idx_heads=8, idx_dim=128, idx_range=8, w_max=8,
-              layers=("full",) + ("reuse",) * 5, ratio=2,
+              layers=("full",) + ("reuse",) * 5, ratio=2, encoder=True,
               note="encoder prefill chunk, 4096 queries over 65536 compressed entries")
 C5 = Workload("verify_group_full_reuse3_b8_q6_t1m", 5, batch=8, q_per_seq=6, kv_len=1 << 20,
               dim=512, heads=64, window=128, idx_heads=8, idx_dim=128, idx_range=8, w_max=8,
@@ -155,8 +161,10 @@ def kv_source(w: Workload, b: int, layer: int = 0) -> np.ndarray:
 
 
 def new_rows(w: Workload, step: int = 0) -> np.ndarray:
-    """fp32 N(0,1) rows of the B tokens appended in one decode step, [B, d]."""
-    return _rng(w, T_NEW, step).standard_normal((w.batch, w.dim), dtype=np.float32)
+    """fp32 N(0,1) rows of the main-KV entries one step appends,
+    [B * new_per_seq, d]; row b * new_per_seq + i lands in slot
+    T - new_per_seq + i of sequence b."""
+    return _rng(w, T_NEW, step).standard_normal((w.batch * w.new_per_seq, w.dim), dtype=np.float32)
 
 
 def index_k_rows(w: Workload, b: int, row0: int, nrows: int) -> np.ndarray:

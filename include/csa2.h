@@ -139,7 +139,7 @@ size_t csa2_index_workspace_size(const csa2_index_args* args);
  *          (may be NULL when no Reindex layer will consume it).
  *   topk   out [nq, 512] int32 positions, ascending, padded with -1.
  *   ws     workspace of csa2_index_workspace_size(args) bytes, 256-B aligned.
- * Supports Qn * H_I <= 64.
+ * Supports Qn * H_I <= 4,194,240 (prefill chunks included).
  */
 int csa2_index_full(const csa2_index_args* args, int32_t* pool, int32_t* topk,
                     void* ws, size_t ws_size, hipStream_t stream);
@@ -188,7 +188,9 @@ int csa2_index_reindex(const csa2_index_args* args, const int32_t* pool, int32_t
 typedef struct {
   int32_t batch;               /* B                                            */
   int32_t q_per_seq;           /* Qn; nq = B * Qn                              */
-  int64_t kv_len;              /* T rows per sequence in the FP4 cache         */
+  int64_t kv_len;              /* T rows per sequence in the FP4 cache, < 2^24;
+                                  T * codes_stride and T * scales_stride must
+                                  stay below 4 GiB - 8 KiB                      */
   int32_t heads;               /* H: 8 or a multiple of 16, <= 128             */
   int32_t dim;                 /* d: 128 or 512                                */
   const uint16_t* q;           /* bf16 [nq, H, d], 16-byte aligned             */

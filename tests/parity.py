@@ -45,7 +45,8 @@ def oracle_index_full(w: synth.Workload, iq, iw, ik, n_visible=None):
 
 def oracle_kv_rows(w: synth.Workload, b: int, positions: np.ndarray, with_new_rows: bool = True):
     """Oracle FP4 codes/scales of sequence b's rows ``positions`` as the cache
-    holds them after one step (row T-1 = the step's new token)."""
+    holds them after one step (rows T - new_per_seq .. T - 1 = the step's new
+    entries)."""
     positions = np.asarray(positions, dtype=np.int64)
     src = np.empty((len(positions), w.dim), dtype=np.float32)
     order = np.argsort(positions)
@@ -60,8 +61,10 @@ def oracle_kv_rows(w: synth.Workload, b: int, positions: np.ndarray, with_new_ro
     for i, p in zip(order, sp):
         src[i] = buf[int(p // synth.KV_CHUNK_ROWS)][int(p % synth.KV_CHUNK_ROWS)]
     if with_new_rows:
-        nr = synth.new_rows(w)[b]
-        src[positions == w.kv_len - 1] = nr
+        n = w.new_per_seq
+        nr = synth.new_rows(w)[b * n:(b + 1) * n]
+        sel = positions >= w.kv_len - n
+        src[sel] = nr[positions[sel] - (w.kv_len - n)]
     return oquant.quantize_rows(src)
 
 

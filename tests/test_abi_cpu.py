@@ -52,7 +52,7 @@ def test_index_rejects(lib):
     a = m.IndexArgs(1, 1, 100, 3, 64, 16, 16, 16, None)                    # 3 heads
     assert lib.csa2_index_full(ctypes.byref(a), None, 16, None, 0, None) == 2
     assert lib.csa2_index_workspace_size(ctypes.byref(a)) == 0
-    a = m.IndexArgs(1, 9, 100, 8, 64, 16, 16, 16, None)                    # Qn*H_I > 64
+    a = m.IndexArgs(1, 262141, 100, 16, 64, 16, 16, 16, None)              # Qn*H_I > 64*65535
     assert lib.csa2_index_full(ctypes.byref(a), None, 16, None, 0, None) == 2
     a = m.IndexArgs(1, 1, 100, 8, 64, 16, 16, 16, None)
     ws = lib.csa2_index_workspace_size(ctypes.byref(a))

@@ -132,3 +132,18 @@ def test_index_reindex_matches_oracle(case):
     nv[0] = T // 2
     topk = run_reindex(iq2, iw2, ik, Qn, rpool, nv)
     np.testing.assert_array_equal(topk, oidx.index_reindex(iq2, iw2, ik, Qn, rpool, nv))
+
+
+def test_index_full_verify_1m_entries():
+    """1,048,576 entries per sequence, 1 + 5 draft queries per sequence: the
+    131,072-block pool select that streams its block keys from memory.  The
+    oracle checks the first and the last sequence (12 of the 48 queries)."""
+    w = synth.C5
+    iq, iw = synth.index_q(w), synth.index_w(w)
+    ik = synth.index_k_all(w)
+    pool, topk = run_full(iq, iw, ik, w.q_per_seq)
+    for b in (0, w.batch - 1):
+        sl = slice(b * w.q_per_seq, (b + 1) * w.q_per_seq)
+        rpool, rtopk = oidx.index_full(iq[sl], iw[sl], ik[b:b + 1], w.q_per_seq)
+        np.testing.assert_array_equal(pool[sl], rpool)
+        np.testing.assert_array_equal(topk[sl], rtopk)
