@@ -189,6 +189,7 @@ struct SelShared {
   uint32_t wmin[kSelWaves];
   uint32_t wcnt[kSelWaves];
   int32_t pool[kPoolBlocks];
+  int32_t sbpool[kPoolBlocks];                   // chosen super-blocks (large pools only)
 };
 
 // inclusive prefix sum over the 64 lanes with DPP (row shifts inside 16-lane
@@ -469,12 +470,70 @@ __global__ __launch_bounds__(kSelThreads) void k_select_full(SelectParams p) {
       compact_topk<KPT1>(get, tau, need, sh, [&](uint32_t o, int j) { sh.pool[o] = (int32_t)(base1 + j); });
     }
   } else {
-    auto get = [&](int j) { return base1 + j < nb ? bk[base1 + j] : 0u; };
-    if (K1 > 0) {
+    // More than 16 blocks per thread: rank super-blocks of 8 blocks by their
+    // maximum first.  The top 2,048 blocks lie in the top 2,048 super-blocks
+    // (ranked by (max desc, id asc)): every super-block ranked above a chosen
+    // block's super-block holds a distinct block that outranks that block.
+    // Their 16,384 member blocks are then ranked exactly.
+    constexpr int SPT = kPoolPositions / kSelThreads;   // 16 super-blocks per thread
+    const int64_t nsb = (nb + 7) / 8;
+    const int64_t sb0 = (int64_t)threadIdx.x * SPT;
+    uint32_t skey[SPT];
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) {
+      const int64_t b0 = (sb0 + j) * 8;
+      uint32_t m = 0u;
+      if (b0 + 8 <= nb) {
+        const u4* kp = reinterpret_cast<const u4*>(bk + b0);
+        const u4 v0 = kp[0], v1 = kp[1];
+        m = max(max(max(v0[0], v0[1]), max(v0[2], v0[3])), max(max(v1[0], v1[1]), max(v1[2], v1[3])));
+      } else {
+        for (int r = 0; r < 8; ++r) m = max(m, b0 + r < nb ? bk[b0 + r] : 0u);
+      }
+      skey[j] = m;
+    }
+    const uint32_t Ks = (uint32_t)min(nsb, (int64_t)kPoolBlocks);
+    {
+      auto get = [&](int j) { return skey[j]; };
       uint32_t tau, need, kmin, kmax, cnt;
-      key_stats<KPT1>(get, sh, kmin, kmax, cnt);
-      radix_select<KPT1>(get, K1, kmin, kmax, sh, &sh.hist[0], tau, need);
-      compact_topk<KPT1>(get, tau, need, sh, [&](uint32_t o, int j) { sh.pool[o] = (int32_t)(base1 + j); });
+      key_stats<SPT>(get, sh, kmin, kmax, cnt);
+      radix_select<SPT>(get, Ks, kmin, kmax, sh, &sh.hist[0], tau, need);
+      compact_topk<SPT>(get, tau, need, sh, [&](uint32_t o, int j) { sh.sbpool[o] = (int32_t)(sb0 + j); });
+    }
+    for (int i = Ks + threadIdx.x; i < kPoolBlocks; i += kSelThreads) sh.sbpool[i] = -1;
+    __syncthreads();
+    // member blocks of the chosen super-blocks: thread t takes slots 2t, 2t+1
+    uint32_t ckey[2 * 8];
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int32_t sb = sh.sbpool[2 * threadIdx.x + jj];
+      const int64_t b0 = (int64_t)sb * 8;
+      if (sb >= 0 && b0 + 8 <= nb) {
+        const u4* kp = reinterpret_cast<const u4*>(bk + b0);
+        const u4 v0 = kp[0], v1 = kp[1];
+        ckey[8 * jj + 0] = v0[0]; ckey[8 * jj + 1] = v0[1]; ckey[8 * jj + 2] = v0[2]; ckey[8 * jj + 3] = v0[3];
+        ckey[8 * jj + 4] = v1[0]; ckey[8 * jj + 5] = v1[1]; ckey[8 * jj + 6] = v1[2]; ckey[8 * jj + 7] = v1[3];
+      } else {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) ckey[8 * jj + r] = (sb >= 0 && b0 + r < nb) ? bk[b0 + r] : 0u;
+      }
+    }
+    {
+      auto get = [&](int j) { return ckey[j]; };
+      uint32_t tau, need, kmin, kmax, cnt;
+      key_stats<16>(get, sh, kmin, kmax, cnt);
+      radix_select<16>(get, K1, kmin, kmax, sh, &sh.hist[3], tau, need);
+      const int c0 = threadIdx.x * 16;
+      compact_topk<16>(get, tau, need, sh, [&](uint32_t o, int j) {
+        const int c = c0 + j;
+        sh.pool[o] = sh.sbpool[c >> 3] * 8 + (c & 7);
+      });
+    }
+    // the position select below needs clean histograms
+    __syncthreads();
+    {
+      u4* hp = reinterpret_cast<u4*>(&sh.hist[3][0]);
+      for (int i = threadIdx.x; i < 3 * kDigitBins / 4; i += kSelThreads) hp[i] = u4{0u, 0u, 0u, 0u};
     }
   }
   for (int i = K1 + threadIdx.x; i < kPoolBlocks; i += kSelThreads) sh.pool[i] = -1;

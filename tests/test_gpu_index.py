@@ -54,6 +54,9 @@ CASES = [  # (B, Qn, T, H_I, D_I, r, wmax)
     (2, 3, 16400, 4, 128, 1, 1),      # heavy ties
     (1, 5, 300, 2, 64, 1, 3),
     (2, 1, 33000, 8, 64, 0, 1),       # all scores equal
+    (1, 2, 100003, 8, 128, 8, 8),     # more than 8,192 blocks: super-block pre-selection
+    (1, 3, 300001, 8, 64, 1, 2),      # ... with heavy ties
+    (1, 1, 262144, 2, 64, 0, 1),      # ... all scores equal
 ]
 
 
@@ -71,6 +74,16 @@ def test_index_full_n_visible_ragged():
     B, Qn, T = 3, 4, 21000
     iq, iw, ik = inputs(11, B, Qn, T, 8, 128, 3, 5)
     nv = np.array([T, 0, 1, 7, 8, 9, 16, 17, 513, 16385, 20999, 12345], dtype=np.int32)
+    pool, topk = run_full(iq, iw, ik, Qn, nv)
+    rpool, rtopk = oidx.index_full(iq, iw, ik, Qn, nv)
+    np.testing.assert_array_equal(pool, rpool)
+    np.testing.assert_array_equal(topk, rtopk)
+
+
+def test_index_full_n_visible_ragged_large():
+    B, Qn, T = 1, 6, 150001
+    iq, iw, ik = inputs(12, B, Qn, T, 8, 128, 2, 3)
+    nv = np.array([T, 65537, 65535, 131073, 8, 149999], dtype=np.int32)
     pool, topk = run_full(iq, iw, ik, Qn, nv)
     rpool, rtopk = oidx.index_full(iq, iw, ik, Qn, nv)
     np.testing.assert_array_equal(pool, rpool)
