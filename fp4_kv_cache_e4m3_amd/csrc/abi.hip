@@ -106,6 +106,7 @@ int check_attn(const csa2_attn_args* a) {
   if (a->topk_k < 0 || a->topk_k > 2048 || a->window < 0 || a->window > 1024) return CSA2_ERR_SHAPE;
   const int64_t nq = (int64_t)a->batch * a->q_per_seq;
   if (nq == 0) return CSA2_OK;
+  if (nq > 0x7FFFFFF8ll) return CSA2_ERR_SHAPE;
   if (!a->q || !a->out) return CSA2_ERR_NULL;
   if (a->kv_len > 0 && a->topk_k > 0 && (!a->codes || !a->scales || !a->topk)) return CSA2_ERR_NULL;
   if (a->window > 0 && !a->swa) return CSA2_ERR_NULL;
@@ -240,6 +241,9 @@ int csa2_sparse_attn(const csa2_attn_args* a, void* ws, size_t ws_size, hipStrea
                                                          round_up(L.nq * L.splits * a->heads * a->dim * 4, 256))
                             : nullptr;
   p.T = a->kv_len; p.codes_stride = a->codes_stride; p.scales_stride = a->scales_stride; p.nq = L.nq;
+  p.qn_shift = -1;
+  for (int sh = 0; sh < 31; ++sh)
+    if ((1 << sh) == a->q_per_seq) p.qn_shift = sh;
   p.qn = a->q_per_seq; p.heads = a->heads; p.topk_k = a->topk_k; p.window = a->window;
   p.swa_rows = L.swa_rows; p.splits = L.splits; p.tiles_per_split = L.tps;
   p.n_sparse_tiles = L.n_sparse_tiles; p.n_tiles = L.n_tiles;

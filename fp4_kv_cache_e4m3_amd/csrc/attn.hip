@@ -252,21 +252,17 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
 
-  // workgroup id -> (query, head group, split, column half).  The dispatcher
-  // deals consecutive ids round-robin to the 8 XCDs; all P workgroups of one
-  // query get ids that are equal mod 8, so they share that XCD's L2 for the
-  // query's rows, window and Q.  Ids past the last query exit at once.
-  const int ngroups = (p.heads + 15) >> 4;
-  const int P = 2 * ngroups * p.splits;
-  const int xcd = (int)(blockIdx.x & 7), slot = (int)(blockIdx.x >> 3);
-  const int64_t q = (int64_t)(slot / P) * 8 + xcd;
+  // grid (8 * 2 * head groups, ceil(nq / 8), splits): blockIdx.x = 8 * (2 * hg
+  // + c0) + xcd and q = 8 * blockIdx.y + xcd.  The dispatcher deals linear
+  // workgroup ids round-robin to the 8 XCDs and gridDim.x is a multiple of 8,
+  // so all workgroups of one query share an XCD (and its L2 for the query's
+  // rows, window and Q).  No division: queries past nq exit at once.
+  const int xcd = (int)(blockIdx.x & 7), idx = (int)(blockIdx.x >> 3);
+  const int q = (int)blockIdx.y * 8 + xcd;
   if (q >= p.nq) return;
-  const int idx = slot % P;
-  const int c0 = idx & 1;
-  const int split = (idx >> 1) % p.splits;
-  const int hg = (idx >> 1) / p.splits;
-  const int64_t b = q / p.qn;
-  const int j = (int)(q - b * p.qn);
+  const int c0 = idx & 1, hg = idx >> 1, split = (int)blockIdx.z;
+  const int b = p.qn_shift >= 0 ? q >> p.qn_shift : q / p.qn;
+  const int j = q - b * p.qn;
   const int h0 = hg * 16;
   const int first_swa = p.swa_len ? p.swa_rows - p.swa_len[b] : 0;
   const int t_end = min(p.n_tiles, (split + 1) * p.tiles_per_split);
@@ -278,7 +274,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
   // first gather depends on them
   constexpr int PB = 4;                             // FP4 tiles per position batch (even)
   const int n_fp4 = tile0 < sp_end ? (sp_end - tile0 + NW - 1) / NW : 0;
-  const int32_t* tk = p.topk + q * p.topk_k;
+  const int32_t* tk = p.topk + (int64_t)q * p.topk_k;
   auto load_positions = [&](int first, int32_t (&pos)[PB]) {
 #pragma unroll
     for (int i = 0; i < PB; ++i) {
@@ -289,25 +285,13 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
   int32_t pos[PB];
   load_positions(0, pos);
 
-  // ---- Q of the 16 heads, loaded once per workgroup (bf16 -> fp16, heads past
-  // H are zero) into LDS; each wave reads its QK B operand from there
-  constexpr int QCH = 16 * D / 8;                   // 8-channel chunks of the Q tile
-  constexpr int QPT = (QCH + 64 * NW - 1) / (64 * NW);
-  u4 qraw[QPT];
-#pragma unroll
-  for (int i = 0; i < QPT; ++i) {
-    const int c = threadIdx.x + 64 * NW * i;
-    const int hr = c / (D / 8), h = h0 + hr;
-    if (c < QCH) qraw[i] = *reinterpret_cast<const u4*>(p.q + (q * p.heads + (h < p.heads ? h : 0)) * D + (c % (D / 8)) * 8);
-  }
-
   // ---- window rows (bf16): loaded through a buffer over this sequence's
   // window; rows outside the window read zeros
   const int swa_first = tile0 + NW * n_fp4;
   u4 w[2][KH];
   bool swa_valid = false;
   constexpr uint32_t kOob = 0xFFFFF000u;            // row offset past every buffer
-  const rsrc_t swa_buf = make_rsrc(p.swa + b * p.swa_rows * D, (uint32_t)(p.swa_rows * D * 2));
+  const rsrc_t swa_buf = make_rsrc(p.swa + (int64_t)b * p.swa_rows * D, (uint32_t)(p.swa_rows * D * 2));
   const uint32_t swa_lane = 2u * InterMap<D>::LANE * g;
   auto load_swa = [&](int t) {
     const int wr = (t - p.n_sparse_tiles) * 16 + n;
@@ -339,6 +323,20 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
   bool vld[2] = {false, false};
   if (n_fp4 > 0) vld[0] = load_fp4<D>(src, pos[0], T32, raw[0]);
   if (n_fp4 > 1) vld[1] = load_fp4<D>(src, pos[1], T32, raw[1]);
+
+  // ---- Q of the 16 heads (after the first gathers, which wait on the
+  // positions), loaded once per workgroup (bf16 -> fp16, heads past
+  // H are zero) into LDS; each wave reads its QK B operand from there
+  constexpr int QCH = 16 * D / 8;                   // 8-channel chunks of the Q tile
+  constexpr int QPT = (QCH + 64 * NW - 1) / (64 * NW);
+  u4 qraw[QPT];
+#pragma unroll
+  for (int i = 0; i < QPT; ++i) {
+    const int c = threadIdx.x + 64 * NW * i;
+    const int hr = c / (D / 8), h = h0 + hr;
+    if (c < QCH) qraw[i] = *reinterpret_cast<const u4*>(p.q + ((int64_t)q * p.heads + (h < p.heads ? h : 0)) * D + (c % (D / 8)) * 8);
+  }
+
 
   const v8h zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
@@ -486,9 +484,9 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
       if (hglob >= p.heads) continue;
       if (p.splits == 1) {
         const float Lh = mlh[hh][1];
-        p.out[(q * p.heads + hglob) * D + chg] = Lh > 0.0f ? sum[i] / Lh : 0.0f;
+        p.out[((int64_t)q * p.heads + hglob) * D + chg] = Lh > 0.0f ? sum[i] / Lh : 0.0f;
       } else {
-        const int64_t pr = (q * p.splits + split) * p.heads + hglob;
+        const int64_t pr = ((int64_t)q * p.splits + split) * p.heads + hglob;
         p.opart[pr * D + chg] = sum[i];
         if (c0 == 0 && t == 0 && (l & 15) == 0) { p.mlpart[2 * pr] = mlh[hh][0]; p.mlpart[2 * pr + 1] = mlh[hh][1]; }
       }
@@ -521,12 +519,11 @@ __global__ __launch_bounds__(D / 4) void k_attn_combine(AttnParams p) {
 
 hipError_t launch_attn(const AttnParams& p, int nq, int dim, int waves, hipStream_t st) {
   if (nq == 0) return hipSuccess;
-  const int64_t ngroups = (p.heads + 15) / 16;
-  const int64_t blocks = 8 * (((int64_t)nq + 7) / 8) * 2 * ngroups * p.splits;
-  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const int ngroups = (p.heads + 15) / 16;
+  const dim3 grid((unsigned)(16 * ngroups), (unsigned)((nq + 7) / 8), (unsigned)p.splits);
 #define CSA2_ATTN_CASE(D, NW)                                                                 \
   if (dim == D && waves == NW) {                                                              \
-    hipLaunchKernelGGL((k_attn<D, NW>), dim3((unsigned)blocks), dim3(64 * NW), 0, st, p);     \
+    hipLaunchKernelGGL((k_attn<D, NW>), grid, dim3(64 * NW), 0, st, p);                       \
     if (p.splits > 1) hipLaunchKernelGGL(k_attn_combine<D>, dim3(nq * p.heads), dim3(D / 4), 0, st, p); \
     return hipGetLastError();                                                                 \
   }

@@ -103,6 +103,7 @@ struct AttnParams {
   float* out; float* opart; float* mlpart;
   int64_t T, codes_stride, scales_stride, nq;
   int32_t qn, heads, topk_k, window, swa_rows, splits, tiles_per_split, n_sparse_tiles, n_tiles;
+  int32_t qn_shift;                                      // log2(qn) when qn is a power of two, else -1
   float qscale;                                          // sm_scale * log2(e)
 };
 
