@@ -103,7 +103,7 @@ int check_attn(const csa2_attn_args* a) {
   if (a->batch < 0 || a->q_per_seq < 1 || a->kv_len < 0 || a->kv_len > (int64_t)1 << 31) return CSA2_ERR_SHAPE;
   if (a->heads < 1 || a->heads > 128) return CSA2_ERR_SHAPE;
   if (!(a->dim == 128 || a->dim == 512)) return CSA2_ERR_SHAPE;
-  if (a->topk_k < 0 || a->topk_k > 2048 || a->window < 0 || a->window > 1024) return CSA2_ERR_SHAPE;
+  if (a->topk_k < 0 || a->topk_k > kMaxTopK || a->window < 0 || a->window > 1024) return CSA2_ERR_SHAPE;
   const int64_t nq = (int64_t)a->batch * a->q_per_seq;
   if (nq == 0) return CSA2_OK;
   if (nq > 0x7FFFFFF8ll) return CSA2_ERR_SHAPE;

@@ -109,9 +109,10 @@ struct InterMap {
 };
 
 // FP4 data of one entry for this lane (RunsMap): code words w[h][j] of k-step
-// j and, per run, a scale word whose byte (jj / 2) is the E4M3 scale of
-// k-step jj of that run (D = 512) or whose byte 0 is the run's scale (D = 128);
-// index h = 0 is the workgroup's own half.
+// j and the scale words as loaded (D = 512: one word per run, the run's
+// scales from byte lsh / 8 up; D = 128: one word for both runs, in s[h][0]);
+// index h = 0 is the workgroup's own half.  The words are shifted where they
+// are used, so issuing a gather never waits for its own data.
 template <int D>
 struct Fp4Raw {
   uint32_t w[2][Geo<D>::KH];
@@ -141,6 +142,9 @@ CSA2_DEV bool load_fp4(const Fp4Src& src, int32_t pos, uint32_t T, Fp4Raw<D>& r)
   const bool valid = pos >= 0 && (uint32_t)pos < T;
   const uint32_t rc = valid ? __umul24((uint32_t)pos, src.cstride) : src.oob;
   const uint32_t rs = valid ? __umul24((uint32_t)pos, src.sstride) : src.oob;
+  // the loads go out in one fixed order wherever a gather is issued, so the
+  // compiler's count of loads in flight is the same on every path into a tile
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -150,13 +154,15 @@ CSA2_DEV bool load_fp4(const Fp4Src& src, int32_t pos, uint32_t T, Fp4Raw<D>& r)
                                                 src.codes, rc + src.lcb + run * (G::HALF / 4), src.hcb[h], 0));
         r.w[h][4 * run + 0] = c[0]; r.w[h][4 * run + 1] = c[1];
         r.w[h][4 * run + 2] = c[2]; r.w[h][4 * run + 3] = c[3];
-        r.s[h][run] = __builtin_amdgcn_raw_buffer_load_b32(src.scales, rs + src.lsb + run * 8, src.hsb[h], 0) >> src.lsh;
+        __builtin_amdgcn_sched_barrier(0);
+        r.s[h][run] = __builtin_amdgcn_raw_buffer_load_b32(src.scales, rs + src.lsb + run * 8, src.hsb[h], 0);
+        __builtin_amdgcn_sched_barrier(0);
       } else {
         static_assert(G::KH == 2, "D must be 128 or 512");
         r.w[h][run] = __builtin_amdgcn_raw_buffer_load_b32(src.codes, rc + src.lcb + run * (G::HALF / 4), src.hcb[h], 0);
+        __builtin_amdgcn_sched_barrier(0);
         if (run == 0) r.s[h][0] = __builtin_amdgcn_raw_buffer_load_b32(src.scales, rs, src.hsb[h], 0);
-        else r.s[h][1] = r.s[h][0] >> (src.lsh + 16);
-        if (run == 1) r.s[h][0] >>= src.lsh;
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
@@ -165,10 +171,13 @@ CSA2_DEV bool load_fp4(const Fp4Src& src, int32_t pos, uint32_t T, Fp4Raw<D>& r)
 
 // One 16-entry tile: logits, online-softmax update, O += P V for the own half.
 // kvf(h, j) gives this lane's 8 fp16 channels of k-step j of half h under
-// channel map M; wrow points at this lane's LDS staging row plus M::LANE * g;
-// after_qk() runs once the raw tile data has been consumed.
+// channel map M; the matching Q channels are qf[j] (own half, registers) and
+// qo + M::off(j) (other half, LDS: read per k-step, which keeps the register
+// budget of two waves per SIMD); wrow points at this lane's LDS staging row
+// plus M::LANE * g; after_qk() runs once the raw tile data has been consumed.
 template <int D, typename M, typename KV, typename AfterQK>
-CSA2_DEV void attend_tile(const AttnParams& p, KV kvf, AfterQK after_qk, bool valid, const v8h (&qf)[2][Geo<D>::KH],
+CSA2_DEV void attend_tile(const AttnParams& p, KV kvf, AfterQK after_qk, bool valid, const v8h (&qf)[Geo<D>::KH],
+                          const _Float16* qo,
                           _Float16* wrow, const _Float16* vbase, int g, v4f (&o)[Geo<D>::NT], float& m_run,
                           float& l_run) {
   constexpr int KH = Geo<D>::KH, NT = Geo<D>::NT;
@@ -180,7 +189,8 @@ CSA2_DEV void attend_tile(const AttnParams& p, KV kvf, AfterQK after_qk, bool va
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const v8h kv = kvf(h, j);
-      part[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, qf[h][j], part[h], 0, 0, 0);
+      const v8h qv = h == 0 ? qf[j] : *reinterpret_cast<const v8h*>(qo + M::off(j));
+      part[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, qv, part[h], 0, 0, 0);
       if (h == 0) *reinterpret_cast<v8h*>(wrow + M::off(j)) = kv;
     }
   }
@@ -240,13 +250,17 @@ template <int D, int NW>
 __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
   using G = Geo<D>;
   constexpr int KH = G::KH, NT = G::NT, PITCH = G::PITCH, HALF = G::HALF;
-  constexpr int NH = NW / 2;                                     // waves holding O after the first merge level
   constexpr int TILE_HALVES = 16 * PITCH;
-  __shared__ __attribute__((aligned(16))) _Float16 vt[NW * TILE_HALVES];  // per-wave V half-tiles / merge buffer
-  static_assert(NH * NT * 64 * 16 <= NW * TILE_HALVES * 2, "merge buffer must fit in the tile buffers");
   constexpr int QPITCH = D + 8;
-  __shared__ __attribute__((aligned(16))) _Float16 qs[16 * QPITCH];        // Q of the 16 heads
-  __shared__ float ml[NW][16][2];
+  // one LDS arena: per-wave V half-tiles, Q of the 16 heads and this split's
+  // Top-K positions while the tiles run; the NW partial outputs at the merge
+  constexpr int VT_BYTES = NW * TILE_HALVES * 2, QS_BYTES = 16 * QPITCH * 2, SPOS_BYTES = kMaxTopK * 4;
+  constexpr int WORK_BYTES = VT_BYTES + QS_BYTES + SPOS_BYTES, FB_BYTES = NW * NT * 64 * 16;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[WORK_BYTES > FB_BYTES ? WORK_BYTES : FB_BYTES];
+  _Float16* const vt = reinterpret_cast<_Float16*>(smem);
+  _Float16* const qs = reinterpret_cast<_Float16*>(smem + VT_BYTES);
+  int32_t* const spos = reinterpret_cast<int32_t*>(smem + VT_BYTES + QS_BYTES);   // -1 = empty slot
+  __shared__ __attribute__((aligned(8))) float ml[NW][16][2];
   __shared__ float mlh[16][2];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -270,40 +284,51 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
   const int tile0 = split * p.tiles_per_split + wave;
   const int hb[2] = {c0 * HALF, (1 - c0) * HALF};                // first channel of each half (0 = own)
 
-  // Top-K positions of this wave's first batch of FP4 tiles go out first: the
-  // first gather depends on them
-  constexpr int PB = 4;                             // FP4 tiles per position batch (even)
+  // Every load below is issued unconditionally (slots, rows and heads that do
+  // not exist read zeros through out-of-range buffer offsets), so the compiler
+  // can count the loads in flight and waits only for the data it uses.
+  constexpr uint32_t kOob = 0xFFFFF000u;            // offset past every buffer
   const int n_fp4 = tile0 < sp_end ? (sp_end - tile0 + NW - 1) / NW : 0;
-  const int32_t* tk = p.topk + (int64_t)q * p.topk_k;
-  auto load_positions = [&](int first, int32_t (&pos)[PB]) {
+  const int slot0 = split * p.tiles_per_split * 16;                  // first Top-K slot of this split
+  const int n_slots = max(0, sp_end * 16 - slot0);                   // FP4 slots of this split
+  const rsrc_t tk_buf = make_rsrc(p.topk + (int64_t)q * p.topk_k, (uint32_t)p.topk_k * 4u);
+  // The positions of the wave's first two FP4 tiles go out first (the first
+  // gathers depend on them); the whole split's positions follow into LDS, from
+  // where each later gather takes its own.  The validity test is applied where
+  // a position is used, so nothing waits on these loads here.
+  int32_t pos0[2];
 #pragma unroll
-    for (int i = 0; i < PB; ++i) {
-      const int slot_i = (tile0 + NW * (first + i)) * 16 + n;
-      pos[i] = (first + i < n_fp4 && slot_i < p.topk_k) ? tk[slot_i] : -1;
-    }
+  for (int i = 0; i < 2; ++i) {
+    const int slot_i = (tile0 + NW * i) * 16 + n;
+    pos0[i] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(tk_buf, i < n_fp4 && slot_i < p.topk_k ? 4u * (uint32_t)slot_i : kOob, 0, 0);
+  }
+  auto first_position = [&](int i) {
+    const int slot_i = (tile0 + NW * i) * 16 + n;
+    return i < n_fp4 && slot_i < p.topk_k ? pos0[i] : -1;
   };
-  int32_t pos[PB];
-  load_positions(0, pos);
+  constexpr int SPT = (kMaxTopK + 64 * NW - 1) / (64 * NW);
+  int32_t sraw[SPT];
+#pragma unroll
+  for (int i = 0; i < SPT; ++i) {
+    const int sl = (int)threadIdx.x + 64 * NW * i;
+    sraw[i] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(tk_buf, sl < n_slots ? 4u * (uint32_t)(slot0 + sl) : kOob, 0, 0);
+  }
+  // position of the wave's FP4 tile i (slot n), from LDS
+  auto position = [&](int i) { return i < n_fp4 ? spos[(wave + NW * i) * 16 + n] : -1; };
 
-  // ---- window rows (bf16): loaded through a buffer over this sequence's
-  // window; rows outside the window read zeros
-  const int swa_first = tile0 + NW * n_fp4;
-  u4 w[2][KH];
-  bool swa_valid = false;
-  constexpr uint32_t kOob = 0xFFFFF000u;            // row offset past every buffer
-  const rsrc_t swa_buf = make_rsrc(p.swa + (int64_t)b * p.swa_rows * D, (uint32_t)(p.swa_rows * D * 2));
-  const uint32_t swa_lane = 2u * InterMap<D>::LANE * g;
-  auto load_swa = [&](int t) {
-    const int wr = (t - p.n_sparse_tiles) * 16 + n;
-    const int r = j + wr;
-    swa_valid = wr < p.window && r >= first_swa && r < p.swa_rows;
-    const uint32_t ro = (swa_valid ? (uint32_t)r * (2u * D) : kOob) + swa_lane;
+  // ---- Q of the 16 heads (bf16 -> fp16, heads past H read zeros): global
+  // loads now, converted into LDS once the first gathers are out; each wave
+  // then reads its QK B operand from there
+  constexpr int QCH = 16 * D / 8;                   // 8-channel chunks of the Q tile
+  constexpr int QPT = (QCH + 64 * NW - 1) / (64 * NW);
+  const rsrc_t q_buf = make_rsrc(p.q + ((int64_t)q * p.heads + h0) * D, (uint32_t)(min(16, p.heads - h0) * D * 2));
+  u4 qraw[QPT];
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int k = 0; k < KH; ++k)
-        w[hh][k] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(swa_buf, ro + 2 * InterMap<D>::off(k), 2 * hb[hh], 0));
-  };
+  for (int i = 0; i < QPT; ++i) {
+    const int c = threadIdx.x + 64 * NW * i;       // chunk c: head row c / (D / 8), 16 bytes each
+    qraw[i] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(q_buf, c < QCH ? 16u * (uint32_t)c : kOob, 0, 0));
+  }
+  __builtin_amdgcn_sched_barrier(0);                // positions and Q go out before the gathers
 
   // ---- FP4 rows: the first two gathers go out as soon as their positions
   // are known
@@ -320,32 +345,20 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
   src.lsh = KH == 8 ? 16u * (uint32_t)(g & 1) : 8u * (uint32_t)(g >> 1);
   const uint32_t T32 = (uint32_t)p.T;
   Fp4Raw<D> raw[2];
-  bool vld[2] = {false, false};
-  if (n_fp4 > 0) vld[0] = load_fp4<D>(src, pos[0], T32, raw[0]);
-  if (n_fp4 > 1) vld[1] = load_fp4<D>(src, pos[1], T32, raw[1]);
+  bool vld[2];
+  vld[0] = load_fp4<D>(src, first_position(0), T32, raw[0]);
+  vld[1] = load_fp4<D>(src, first_position(1), T32, raw[1]);
 
-  // ---- Q of the 16 heads (after the first gathers, which wait on the
-  // positions), loaded once per workgroup (bf16 -> fp16, heads past
-  // H are zero) into LDS; each wave reads its QK B operand from there
-  constexpr int QCH = 16 * D / 8;                   // 8-channel chunks of the Q tile
-  constexpr int QPT = (QCH + 64 * NW - 1) / (64 * NW);
-  u4 qraw[QPT];
-#pragma unroll
-  for (int i = 0; i < QPT; ++i) {
-    const int c = threadIdx.x + 64 * NW * i;
-    const int hr = c / (D / 8), h = h0 + hr;
-    if (c < QCH) qraw[i] = *reinterpret_cast<const u4*>(p.q + ((int64_t)q * p.heads + (h < p.heads ? h : 0)) * D + (c % (D / 8)) * 8);
-  }
-
-
-  const v8h zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
   for (int i = 0; i < QPT; ++i) {
     const int c = threadIdx.x + 64 * NW * i;
     const int hr = c / (D / 8);
-    v8h f = bf16x8_to_half(qraw[i]);
-    if (h0 + hr >= p.heads) f = zero8;
-    if (c < QCH) *reinterpret_cast<v8h*>(qs + hr * QPITCH + (c % (D / 8)) * 8) = f;
+    if (c < QCH) *reinterpret_cast<v8h*>(qs + hr * QPITCH + (c % (D / 8)) * 8) = bf16x8_to_half(qraw[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < SPT; ++i) {
+    const int sl = (int)threadIdx.x + 64 * NW * i;
+    if (sl < n_slots) spos[sl] = slot0 + sl < p.topk_k ? sraw[i] : -1;
   }
   __syncthreads();
 
@@ -356,67 +369,97 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
 
   _Float16* my = vt + wave * TILE_HALVES;
   const _Float16* vbase = my + (4 * g + (n >> 2)) * PITCH + 4 * (n & 3);   // transposing PV read
-  v8h qf[2][KH];
+  v8h qf[KH];
   auto load_qf = [&](auto map) {
     using M = decltype(map);
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int k = 0; k < KH; ++k)
-        qf[hh][k] = *reinterpret_cast<const v8h*>(qs + n * QPITCH + hb[hh] + M::off(k) + M::LANE * g);
+    for (int k = 0; k < KH; ++k) qf[k] = *reinterpret_cast<const v8h*>(qs + n * QPITCH + hb[0] + M::off(k) + M::LANE * g);
   };
 
-  // ---- FP4 tiles (runs channel map): positions in batches of PB; two tiles'
-  // gathers are in flight at all times: tile i + 2 goes into tile i's buffer as
-  // soon as tile i's logits are done with it
+  const int swa_first = tile0 + NW * n_fp4;          // the wave's first window tile
+  // ---- window rows (bf16), read through a buffer over this sequence's
+  // window (rows outside it read zeros); w holds one 16-row tile
+  const v8h zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+  u4 w[2][KH];
+  bool swa_valid = false;
+  const rsrc_t swa_buf = make_rsrc(p.swa + (int64_t)b * p.swa_rows * D, (uint32_t)(p.swa_rows * D * 2));
+  const uint32_t swa_lane = 2u * InterMap<D>::LANE * g;
+  auto swa_rows = [&](int t) {                      // this lane's row offset of window tile t
+    const int wr = (t - p.n_sparse_tiles) * 16 + n;
+    const int r = j + wr;
+    swa_valid = t < t_end && wr >= 0 && wr < p.window && r >= first_swa && r < p.swa_rows;
+    return (swa_valid ? (uint32_t)r * (2u * D) : kOob) + swa_lane;
+  };
+  auto load_swa_half = [&](uint32_t ro, int hh) {
+#pragma unroll
+    for (int k = 0; k < KH; ++k)
+      w[hh][k] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(swa_buf, ro + 2 * InterMap<D>::off(k),
+                                                                           __builtin_amdgcn_readfirstlane(2 * hb[hh]), 0));
+  };
+  auto load_swa = [&](int t) {
+    const uint32_t ro = swa_rows(t);
+    load_swa_half(ro, 0);
+    load_swa_half(ro, 1);
+  };
+  uint32_t swa_ro = kOob;
+
+  // ---- FP4 tiles (runs channel map), two at a time: two tiles' gathers are
+  // in flight at all times: tile i + 2 goes into tile i's buffer as soon as
+  // tile i's logits are done with it.  Past the wave's last tile the slots are
+  // empty: the loads read zeros and such a tile (the second of the last pair)
+  // is fully masked, so every pair issues the same loads and the compiler's
+  // wait counts stay exact.  The last pair loads the two halves of the wave's
+  // first window tile in place of gathers (the same number of loads).
   if (n_fp4 > 0) {
     load_qf(RunsMap<D>{});
     _Float16* wrow = my + n * PITCH + RunsMap<D>::LANE * g;
-    for (int first = 0; first < n_fp4; first += PB) {
-      int32_t nxt[PB];
-      load_positions(first + PB, nxt);
+    auto fp4_tile = [&](int u, auto after) {
+      Fp4Raw<D>& cur = raw[u];
+      // an empty slot read zero codes and scales: finite zeros in V; its
+      // logits are masked
+      _Float16 sc[2][2][(KH / 2 + 1) / 2];
 #pragma unroll
-      for (int i = 0; i < PB; ++i) {
-        if (first + i < n_fp4) {
-          Fp4Raw<D>& cur = raw[i & 1];
-          // an empty slot read zero codes and scales: finite zeros in V; its
-          // logits are masked
-          _Float16 sc[2][2][(KH / 2 + 1) / 2];
+      for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-          for (int hh = 0; hh < 2; ++hh)
+        for (int run = 0; run < 2; ++run)
 #pragma unroll
-            for (int run = 0; run < 2; ++run)
+          for (int k = 0; k < (KH / 2 + 1) / 2; ++k)
+            sc[hh][run][k] = scale_sel(KH == 8 ? cur.s[hh][run] >> src.lsh : cur.s[hh][0] >> (src.lsh + 16 * run), k);
+      const bool v = vld[u];
+      attend_tile<D, RunsMap<D>>(
+          p,
+          [&](int hh, int k) {
+            constexpr int HK = KH / 2;
+            return fp4x8_to_half(cur.w[hh][k], sc[hh][k / HK][(k % HK) / 2]);
+          },
+          after, v, qf, qs + n * QPITCH + hb[1] + RunsMap<D>::LANE * g, wrow, vbase, g, o, m_run, l_run);
+    };
+    int i0 = 0;
+    for (; i0 + 2 < n_fp4; i0 += 2) {
 #pragma unroll
-              for (int k = 0; k < (KH / 2 + 1) / 2; ++k) sc[hh][run][k] = scale_sel(cur.s[hh][run], k);
-          const bool v = vld[i & 1];
-          attend_tile<D, RunsMap<D>>(
-              p,
-              [&](int hh, int k) {
-                constexpr int HK = KH / 2;
-                return fp4x8_to_half(cur.w[hh][k], sc[hh][k / HK][(k % HK) / 2]);
-              },
-              [&]() {
-                if (first + i + 2 < n_fp4)
-                  vld[i & 1] = load_fp4<D>(src, i + 2 < PB ? pos[i + 2] : nxt[i + 2 - PB], T32, cur);
-              },
-              v, qf, wrow, vbase, g, o, m_run, l_run);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < PB; ++i) pos[i] = nxt[i];
+      for (int u = 0; u < 2; ++u) fp4_tile(u, [&]() { vld[u] = load_fp4<D>(src, position(i0 + u + 2), T32, raw[u]); });
     }
+    fp4_tile(0, [&]() {
+      swa_ro = swa_rows(swa_first);
+      load_swa_half(swa_ro, 0);
+    });
+    fp4_tile(1, [&]() { load_swa_half(swa_ro, 1); });
   }
 
-  // ---- sliding-window tiles (bf16 rows, interleaved channel map)
+  // ---- sliding-window tiles (bf16 rows, interleaved channel map); the
+  // first one was loaded during the last FP4 pair (or is loaded here when the
+  // wave has no FP4 tile), each next one as soon as the current one's logits
+  // are done
   if (swa_first < t_end) {
-    load_swa(swa_first);
+    if (n_fp4 == 0) load_swa(swa_first);
     load_qf(InterMap<D>{});
     _Float16* wrow = my + n * PITCH + InterMap<D>::LANE * g;
     for (int t = swa_first; t < t_end; t += NW) {
       const bool v = swa_valid;
-      attend_tile<D, InterMap<D>>(p, [&](int hh, int k) { return v ? bf16x8_to_half(w[hh][k]) : zero8; }, [] {}, v,
-                                  qf, wrow, vbase, g, o, m_run, l_run);
-      if (t + NW < t_end) load_swa(t + NW);
+      attend_tile<D, InterMap<D>>(
+          p, [&](int hh, int k) { return v ? bf16x8_to_half(w[hh][k]) : zero8; },
+          [&] { load_swa(t + NW); }, v, qf, qs + n * QPITCH + hb[1] + InterMap<D>::LANE * g, wrow, vbase, g, o,
+          m_run, l_run);
     }
   }
 
@@ -424,50 +467,38 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
   float l_tot = l_run + __shfl_xor(l_run, 16, 64);
   l_tot = l_tot + __shfl_xor(l_tot, 32, 64);
   if (g == 0) { ml[wave][n][0] = m_run; ml[wave][n][1] = l_tot; }
-  __syncthreads();                                  // also: every wave is done with its tile buffer
+  __syncthreads();                                  // also: every wave is done with the arena
+  // every lane merges head n over the NW waves (independent LDS reads, fixed
+  // order); o holds heads 4g + i, whose factors come from lanes 4g + i
+  float mw[NW], lw[NW];
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const float2 v = *reinterpret_cast<const float2*>(&ml[w][n][0]);
+    mw[w] = v.x;
+    lw[w] = v.y;
+  }
+  float mx = mw[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) mx = fmaxf(mx, mw[w]);
+  float ls = 0.0f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) ls += (mw[w] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mw[w] - mx) * lw[w];
+  if (wave == 0 && g == 0) { mlh[n][0] = mx; mlh[n][1] = ls; }
+  const float f_own = (m_run == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m_run - mx);
   float fme[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int hh = 4 * g + i;
-    float mx = -__builtin_inff();
-#pragma unroll
-    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, ml[w][hh][0]);
-    const float mme = ml[wave][hh][0];
-    fme[i] = (mme == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mme - mx);
-    if (wave == 0 && n == 0) {
-      float ls = 0.0f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const float mw = ml[w][hh][0];
-        ls += (mw == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mw - mx) * ml[w][hh][1];
-      }
-      mlh[hh][0] = mx;
-      mlh[hh][1] = ls;
-    }
-  }
+  for (int i = 0; i < 4; ++i) fme[i] = __shfl(f_own, 4 * g + i, 64);
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[t][i] *= fme[i];
 
-  // two levels in a fixed order through a lane-major fp32 buffer (element
-  // (slot, t, lane) holds o[t] of one wave): waves NH.. add into waves 0..NH-1,
-  // which then leave their sums for a cooperative final pass
-  v4f* fb = reinterpret_cast<v4f*>(vt);
-  if (wave >= NH) {
+  // every wave leaves its scaled O in a lane-major fp32 buffer over the arena
+  // (element (wave, t, lane) holds o[t]); one cooperative pass adds the NW
+  // partials in a fixed order
+  v4f* fb = reinterpret_cast<v4f*>(smem);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) fb[((wave - NH) * NT + t) * 64 + lane] = o[t];
-  }
-  __syncthreads();
-  if (wave < NH) {
-#pragma unroll
-    for (int t = 0; t < NT; ++t) o[t] += fb[(wave * NT + t) * 64 + lane];
-  }
-  __syncthreads();
-  if (wave < NH) {
-#pragma unroll
-    for (int t = 0; t < NT; ++t) fb[(wave * NT + t) * 64 + lane] = o[t];
-  }
+  for (int t = 0; t < NT; ++t) fb[(wave * NT + t) * 64 + lane] = o[t];
   __syncthreads();
 
   // one item = (16-channel tile t, lane l): the v4f of lane l holds channel
@@ -476,7 +507,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
     const int t = it >> 6, l = it & 63;
     v4f sum = fb[t * 64 + l];
 #pragma unroll
-    for (int w = 1; w < NH; ++w) sum += fb[(w * NT + t) * 64 + l];
+    for (int w = 1; w < NW; ++w) sum += fb[(w * NT + t) * 64 + l];
     const int chg = c0 * HALF + 16 * t + (l & 15);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {

@@ -17,6 +17,7 @@ typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 namespace csa2 {
 
 constexpr int kTopK = 512;
+constexpr int kMaxTopK = 2048;                   // largest Top-K row the attention kernel takes
 constexpr int kBlock = 8;
 constexpr int kPoolBlocks = 2048;
 constexpr int kPoolPositions = kPoolBlocks * kBlock;
