@@ -169,17 +169,24 @@ CSA2_DEV bool load_fp4(const Fp4Src& src, int32_t pos, uint32_t T, Fp4Raw<D>& r)
   return valid;
 }
 
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// QK^T k-step in the operands' own type (products exact, fp32 accumulation)
+CSA2_DEV v4f mfma_qk(v8h a, v8h b, v4f c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
+CSA2_DEV v4f mfma_qk(v8bf a, v8bf b, v4f c) { return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0); }
+
 // One 16-entry tile: logits, online-softmax update, O += P V for the own half.
-// kvf(h, j) gives this lane's 8 fp16 channels of k-step j of half h under
-// channel map M; the matching Q channels are qf[j] (own half, registers) and
+// kvf(h, j) gives this lane's 8 channels of k-step j of half h under channel
+// map M as a QK operand of type V8 (fp16 for FP4 rows, the raw bf16 for window
+// rows); the matching Q channels are qf[j] (own half, registers) and
 // qo + M::off(j) (other half, LDS: read per k-step, which keeps the register
-// budget of two waves per SIMD); wrow points at this lane's LDS staging row
-// plus M::LANE * g; after_qk() runs once the raw tile data has been consumed.
-template <int D, typename M, typename KV, typename AfterQK>
-CSA2_DEV void attend_tile(const AttnParams& p, KV kvf, AfterQK after_qk, bool valid, const v8h (&qf)[Geo<D>::KH],
-                          const _Float16* qo,
-                          _Float16* wrow, const _Float16* vbase, int g, v4f (&o)[Geo<D>::NT], float& m_run,
-                          float& l_run) {
+// budget of two waves per SIMD).  stage(kv) turns an own-half operand into the
+// fp16 V values staged at wrow (this lane's LDS row plus M::LANE * g) for PV;
+// after_qk() runs once the raw tile data has been consumed.
+template <int D, typename M, typename V8, typename KV, typename ST, typename AfterQK>
+CSA2_DEV void attend_tile(const AttnParams& p, KV kvf, ST stage, AfterQK after_qk, bool valid,
+                          const V8 (&qf)[Geo<D>::KH], const uint16_t* qo, _Float16* wrow, const _Float16* vbase, int g,
+                          v4f (&o)[Geo<D>::NT], float& m_run, float& l_run) {
   constexpr int KH = Geo<D>::KH, NT = Geo<D>::NT;
   // one accumulation chain per half (the two halves interleave); the half sums
   // are added last
@@ -188,10 +195,10 @@ CSA2_DEV void attend_tile(const AttnParams& p, KV kvf, AfterQK after_qk, bool va
   for (int j = 0; j < KH; ++j) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const v8h kv = kvf(h, j);
-      const v8h qv = h == 0 ? qf[j] : *reinterpret_cast<const v8h*>(qo + M::off(j));
-      part[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, qv, part[h], 0, 0, 0);
-      if (h == 0) *reinterpret_cast<v8h*>(wrow + M::off(j)) = kv;
+      const V8 kv = kvf(h, j);
+      const V8 qv = h == 0 ? qf[j] : *reinterpret_cast<const V8*>(qo + M::off(j));
+      part[h] = mfma_qk(kv, qv, part[h]);
+      if (h == 0) *reinterpret_cast<v8h*>(wrow + M::off(j)) = stage(kv);
     }
   }
   const v4f s_acc = part[0] + part[1];      // commutative: same bits in both halves
@@ -255,13 +262,13 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
   // one LDS arena: per-wave V half-tiles, Q of the 16 heads and this split's
   // Top-K positions while the tiles run; the NW partial outputs at the merge
   constexpr int VT_BYTES = NW * TILE_HALVES * 2, QS_BYTES = 16 * QPITCH * 2, SPOS_BYTES = kMaxTopK * 4;
-  constexpr int WORK_BYTES = VT_BYTES + QS_BYTES + SPOS_BYTES, FB_BYTES = NW * NT * 64 * 16;
+  constexpr int WORK_BYTES = VT_BYTES + 2 * QS_BYTES + SPOS_BYTES, FB_BYTES = NW * NT * 64 * 16;
   __shared__ __attribute__((aligned(16))) unsigned char smem[WORK_BYTES > FB_BYTES ? WORK_BYTES : FB_BYTES];
   _Float16* const vt = reinterpret_cast<_Float16*>(smem);
   _Float16* const qs = reinterpret_cast<_Float16*>(smem + VT_BYTES);
-  int32_t* const spos = reinterpret_cast<int32_t*>(smem + VT_BYTES + QS_BYTES);   // -1 = empty slot
+  __bf16* const qsb = reinterpret_cast<__bf16*>(smem + VT_BYTES + QS_BYTES);      // the same Q as bf16
+  int32_t* const spos = reinterpret_cast<int32_t*>(smem + VT_BYTES + 2 * QS_BYTES);   // -1 = empty slot
   __shared__ __attribute__((aligned(8))) float ml[NW][16][2];
-  __shared__ float mlh[16][2];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
@@ -353,7 +360,10 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
   for (int i = 0; i < QPT; ++i) {
     const int c = threadIdx.x + 64 * NW * i;
     const int hr = c / (D / 8);
-    if (c < QCH) *reinterpret_cast<v8h*>(qs + hr * QPITCH + (c % (D / 8)) * 8) = bf16x8_to_half(qraw[i]);
+    if (c < QCH) {
+      *reinterpret_cast<v8h*>(qs + hr * QPITCH + (c % (D / 8)) * 8) = bf16x8_to_half(qraw[i]);
+      *reinterpret_cast<u4*>(qsb + hr * QPITCH + (c % (D / 8)) * 8) = qraw[i];
+    }
   }
 #pragma unroll
   for (int i = 0; i < SPT; ++i) {
@@ -379,7 +389,6 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
   const int swa_first = tile0 + NW * n_fp4;          // the wave's first window tile
   // ---- window rows (bf16), read through a buffer over this sequence's
   // window (rows outside it read zeros); w holds one 16-row tile
-  const v8h zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
   u4 w[2][KH];
   bool swa_valid = false;
   const rsrc_t swa_buf = make_rsrc(p.swa + (int64_t)b * p.swa_rows * D, (uint32_t)(p.swa_rows * D * 2));
@@ -426,13 +435,15 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
           for (int k = 0; k < (KH / 2 + 1) / 2; ++k)
             sc[hh][run][k] = scale_sel(KH == 8 ? cur.s[hh][run] >> src.lsh : cur.s[hh][0] >> (src.lsh + 16 * run), k);
       const bool v = vld[u];
-      attend_tile<D, RunsMap<D>>(
+      attend_tile<D, RunsMap<D>, v8h>(
           p,
           [&](int hh, int k) {
             constexpr int HK = KH / 2;
             return fp4x8_to_half(cur.w[hh][k], sc[hh][k / HK][(k % HK) / 2]);
           },
-          after, v, qf, qs + n * QPITCH + hb[1] + RunsMap<D>::LANE * g, wrow, vbase, g, o, m_run, l_run);
+          [](v8h kv) { return kv; }, after, v, qf,
+          reinterpret_cast<const uint16_t*>(qs + n * QPITCH + hb[1] + RunsMap<D>::LANE * g), wrow, vbase, g, o, m_run,
+          l_run);
     };
     int i0 = 0;
     for (; i0 + 2 < n_fp4; i0 += 2) {
@@ -450,15 +461,22 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
   // first one was loaded during the last FP4 pair (or is loaded here when the
   // wave has no FP4 tile), each next one as soon as the current one's logits
   // are done
+  // QK runs on the bf16 rows and the bf16 Q as they are; only the own half
+  // becomes fp16 (exactly, inside fp16's range) for PV.  Rows outside the
+  // window read as zeros and their logits are masked.
   if (swa_first < t_end) {
     if (n_fp4 == 0) load_swa(swa_first);
-    load_qf(InterMap<D>{});
+    v8bf qfb[KH];
+#pragma unroll
+    for (int k = 0; k < KH; ++k)
+      qfb[k] = *reinterpret_cast<const v8bf*>(qsb + n * QPITCH + hb[0] + InterMap<D>::off(k) + InterMap<D>::LANE * g);
     _Float16* wrow = my + n * PITCH + InterMap<D>::LANE * g;
     for (int t = swa_first; t < t_end; t += NW) {
       const bool v = swa_valid;
-      attend_tile<D, InterMap<D>>(
-          p, [&](int hh, int k) { return v ? bf16x8_to_half(w[hh][k]) : zero8; },
-          [&] { load_swa(t + NW); }, v, qf, qs + n * QPITCH + hb[1] + InterMap<D>::LANE * g, wrow, vbase, g, o,
+      attend_tile<D, InterMap<D>, v8bf>(
+          p, [&](int hh, int k) { return __builtin_bit_cast(v8bf, w[hh][k]); },
+          [](v8bf kv) { return bf16x8_to_half(__builtin_bit_cast(u4, kv)); }, [&] { load_swa(t + NW); }, v, qfb,
+          reinterpret_cast<const uint16_t*>(qsb + n * QPITCH + hb[1] + InterMap<D>::LANE * g), wrow, vbase, g, o,
           m_run, l_run);
     }
   }
@@ -483,11 +501,14 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
   float ls = 0.0f;
 #pragma unroll
   for (int w = 0; w < NW; ++w) ls += (mw[w] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mw[w] - mx) * lw[w];
-  if (wave == 0 && g == 0) { mlh[n][0] = mx; mlh[n][1] = ls; }
   const float f_own = (m_run == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m_run - mx);
-  float fme[4];
+  const float inv_own = ls > 0.0f ? 1.0f / ls : 0.0f;
+  float fme[4], inv[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) fme[i] = __shfl(f_own, 4 * g + i, 64);
+  for (int i = 0; i < 4; ++i) {
+    fme[i] = __shfl(f_own, 4 * g + i, 64);
+    inv[i] = __shfl(inv_own, 4 * g + i, 64);
+  }
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -501,27 +522,31 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
   for (int t = 0; t < NT; ++t) fb[(wave * NT + t) * 64 + lane] = o[t];
   __syncthreads();
 
-  // one item = (16-channel tile t, lane l): the v4f of lane l holds channel
-  // 16t + l%16 of heads 4*(l/16) .. 4*(l/16)+3
-  for (int it = threadIdx.x; it < NT * 64; it += 64 * NW) {
-    const int t = it >> 6, l = it & 63;
-    v4f sum = fb[t * 64 + l];
+  // each thread sums the NW partials of tiles t = wave, wave + NW, ... at its
+  // own lane, i.e. channel 16t + n of heads 4g .. 4g + 3 (the o layout), so
+  // the per-head factors above apply directly
+  for (int t = wave; t < NT; t += NW) {
+    v4f sum = fb[t * 64 + lane];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) sum += fb[(w * NT + t) * 64 + l];
-    const int chg = c0 * HALF + 16 * t + (l & 15);
+    for (int w = 1; w < NW; ++w) sum += fb[(w * NT + t) * 64 + lane];
+    const int chg = c0 * HALF + 16 * t + n;
+    if (p.splits == 1) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int hh = 4 * (l >> 4) + i, hglob = h0 + hh;
-      if (hglob >= p.heads) continue;
-      if (p.splits == 1) {
-        const float Lh = mlh[hh][1];
-        p.out[((int64_t)q * p.heads + hglob) * D + chg] = Lh > 0.0f ? sum[i] / Lh : 0.0f;
-      } else {
-        const int64_t pr = ((int64_t)q * p.splits + split) * p.heads + hglob;
-        p.opart[pr * D + chg] = sum[i];
-        if (c0 == 0 && t == 0 && (l & 15) == 0) { p.mlpart[2 * pr] = mlh[hh][0]; p.mlpart[2 * pr + 1] = mlh[hh][1]; }
+      for (int i = 0; i < 4; ++i)
+        if (h0 + 4 * g + i < p.heads) p.out[((int64_t)q * p.heads + h0 + 4 * g + i) * D + chg] = sum[i] * inv[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t pr = ((int64_t)q * p.splits + split) * p.heads + h0 + 4 * g + i;
+        if (h0 + 4 * g + i < p.heads) p.opart[pr * D + chg] = sum[i];
       }
     }
+  }
+  // the split's (max, sum) per head: lane n of wave 0 holds head n's
+  if (p.splits > 1 && wave == 0 && g == 0 && c0 == 0 && h0 + n < p.heads) {
+    const int64_t pr = ((int64_t)q * p.splits + split) * p.heads + h0 + n;
+    p.mlpart[2 * pr] = mx;
+    p.mlpart[2 * pr + 1] = ls;
   }
 }
 
