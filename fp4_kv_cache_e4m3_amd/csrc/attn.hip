@@ -22,22 +22,27 @@
 //    over several workgroups, a second kernel merges the partial states.
 //  * per tile a wave gathers 16 entries (lane % 16 = entry; the 4 lanes of an
 //    entry split its channels) through buffer loads, FP4 codes + E4M3 scales
-//    or bf16 window rows, and turns them into fp16 in registers (FP4 values
-//    are exact in fp16).  Two FP4 gathers are in flight per wave.
-//  * QK^T: MFMA 16x16x32 f16 with the entries as A rows and the 16 heads as
-//    B columns (Q lives in registers, in the same channel order as K).  Each
-//    half's k-steps accumulate separately and the two sums are added last;
-//    fp32 addition commutes, so both column halves get bit-identical logits
-//    whichever half they process first.  The result holds entries
-//    4*(lane/16)+i of head lane%16 -- the A-operand layout of the PV MFMA, so
-//    the probabilities never leave registers.
+//    or bf16 window rows.  Every load is unconditional (absent data reads
+//    zeros through out-of-range offsets), so the compiler's wait counts are
+//    exact and two FP4 gathers stay in flight per wave; the last FP4 pair
+//    loads the wave's first window tile instead.
+//  * QK^T: MFMA 16x16x32 with the entries as A rows and the 16 heads as B
+//    columns.  FP4 rows become fp16 in registers (exact) against an fp16
+//    copy of Q; window rows stay bf16 against a bf16 copy of Q.  The own
+//    half of Q lives in registers, the other half is read from LDS per
+//    k-step.  Each half's k-steps accumulate separately and the two sums are
+//    added last; fp32 addition commutes, so both column halves get
+//    bit-identical logits whichever half they process first.  The result
+//    holds entries 4*(lane/16)+i of head lane%16 -- the A-operand layout of
+//    the PV MFMA, so the probabilities never leave registers.
 //  * PV: MFMA 16x16x16 f16 over the 16 entries; the V operand (4 entries of
 //    one channel per lane) comes from one transposing LDS read per 16
 //    channels of the wave's own fp16 half-tile.
-// Q and SWA rows go bf16 -> fp16 unscaled, which is exact for magnitudes in
-// [2^-14, 65504] (bf16 carries 8 significant bits, fp16 11), so QK^T is exact
-// up to fp32 accumulation; sm_scale * log2(e) multiplies the fp32 logits and
-// the softmax uses exp2.
+// Q goes bf16 -> fp16 unscaled for the FP4 tiles, which is exact for
+// magnitudes in [2^-14, 65504] (bf16 carries 8 significant bits, fp16 11);
+// products are exact in both MFMA types, so QK^T is exact up to fp32
+// accumulation.  sm_scale * log2(e) multiplies the fp32 logits and the
+// softmax uses exp2.
 #include "common.h"
 
 namespace csa2 {
@@ -68,13 +73,28 @@ CSA2_DEV float max_over_quarters(float x) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-CSA2_DEV _Float16 scale_sel(uint32_t w, int sel) {
-  switch (sel & 3) {            // sel is a constant after unrolling
-    case 0: return e4m3_to_half<0>(w);
-    case 1: return e4m3_to_half<1>(w);
-    case 2: return e4m3_to_half<2>(w);
-    default: return e4m3_to_half<3>(w);
-  }
+// Two E4M3 scale bytes of w (chosen by the v_perm selector sel, which puts
+// them at bytes 0 and 2) -> fp16 values scale * 2^-8.  A scale byte has sign
+// 0; shifted left by 7 it puts its 4 exponent and 3 mantissa bits in fp16's
+// fields, where the exponent bias is 15 instead of 7: the fp16 value is the
+// scale times 2^-8, subnormal scales included.
+CSA2_DEV v2h e4m3_pair_s8(uint32_t w, uint32_t sel) {
+  return __builtin_bit_cast(v2h, __builtin_amdgcn_perm(0u, w, sel) << 7);
+}
+
+// Eight FP4 codes -> fp16 times an E4M3 scale s, given s8 = s * 2^-8 in fp16:
+// the conversion scales the codes by 2^8 (a power of two: exact) and one
+// packed multiply applies s8.  code * 2^8 and s * 2^-8 are exact in fp16, and
+// so is their product code * s (at most 5 significant bits, inside fp16's
+// range), so the result equals the FP4 value times the scale exactly.
+CSA2_DEV v8h fp4x8_to_half_s8(uint32_t x, _Float16 s8) {
+  const v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 256.0f, 0);
+  const v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 256.0f, 1);
+  const v2h c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 256.0f, 2);
+  const v2h d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 256.0f, 3);
+  const v8h v = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+  const v8h sv = {s8, s8, s8, s8, s8, s8, s8, s8};
+  return v * sv;
 }
 
 // Geometry of one lane's share of a 16-entry tile for head dim D.
@@ -109,10 +129,10 @@ struct InterMap {
 };
 
 // FP4 data of one entry for this lane (RunsMap): code words w[h][j] of k-step
-// j and the scale words as loaded (D = 512: one word per run, the run's
-// scales from byte lsh / 8 up; D = 128: one word for both runs, in s[h][0]);
-// index h = 0 is the workgroup's own half.  The words are shifted where they
-// are used, so issuing a gather never waits for its own data.
+// j and the scale words as loaded (D = 512: one word per run; D = 128: one
+// word for both runs, in s[h][0]); index h = 0 is the workgroup's own half.
+// The scale bytes are picked out where they are used, so issuing a gather
+// never waits for its own data.
 template <int D>
 struct Fp4Raw {
   uint32_t w[2][Geo<D>::KH];
@@ -133,7 +153,8 @@ struct Fp4Src {
   rsrc_t codes, scales;
   uint32_t cstride, sstride, oob;
   int hcb[2], hsb[2];          // code / scale byte offset of each half (0 = own)
-  uint32_t lcb, lsb, lsh;      // per-lane code offset, scale word offset, scale shift
+  uint32_t lcb, lsb;           // per-lane code offset, scale word offset
+  uint32_t psel[2];            // per run: v_perm selector of its scale bytes in the scale word
 };
 
 template <int D>
@@ -349,7 +370,13 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
   src.hsb[0] = hb[0] / 16; src.hsb[1] = hb[1] / 16;
   src.lcb = (uint32_t)(g * RunsMap<D>::LANE / 2);
   src.lsb = KH == 8 ? 4u * (uint32_t)(g >> 1) : 0u;
-  src.lsh = KH == 8 ? 16u * (uint32_t)(g & 1) : 8u * (uint32_t)(g >> 1);
+  // D = 512: a run's two scales are bytes 2(g&1), 2(g&1)+1 of its word;
+  // D = 128: run r's scale is byte (g>>1) + 2r of the shared word
+  for (int r = 0; r < 2; ++r) {
+    const uint32_t b0 = KH == 8 ? 2u * (uint32_t)(g & 1) : (uint32_t)(g >> 1) + 2u * r;
+    const uint32_t b1 = KH == 8 ? b0 + 1u : 0x0Cu;               // 0x0C selects a zero byte
+    src.psel[r] = b0 | (0x0Cu << 8) | (b1 << 16) | (0x0Cu << 24);
+  }
   const uint32_t T32 = (uint32_t)p.T;
   Fp4Raw<D> raw[2];
   bool vld[2];
@@ -426,20 +453,18 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
       Fp4Raw<D>& cur = raw[u];
       // an empty slot read zero codes and scales: finite zeros in V; its
       // logits are masked
-      _Float16 sc[2][2][(KH / 2 + 1) / 2];
+      v2h sc[2][2];                // per half and run: its scales times 2^-8
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
         for (int run = 0; run < 2; ++run)
-#pragma unroll
-          for (int k = 0; k < (KH / 2 + 1) / 2; ++k)
-            sc[hh][run][k] = scale_sel(KH == 8 ? cur.s[hh][run] >> src.lsh : cur.s[hh][0] >> (src.lsh + 16 * run), k);
+          sc[hh][run] = e4m3_pair_s8(KH == 8 ? cur.s[hh][run] : cur.s[hh][0], src.psel[run]);
       const bool v = vld[u];
       attend_tile<D, RunsMap<D>, v8h>(
           p,
           [&](int hh, int k) {
             constexpr int HK = KH / 2;
-            return fp4x8_to_half(cur.w[hh][k], sc[hh][k / HK][(k % HK) / 2]);
+            return fp4x8_to_half_s8(cur.w[hh][k], sc[hh][k / HK][(k % HK) / 2]);
           },
           [](v8h kv) { return kv; }, after, v, qf,
           reinterpret_cast<const uint16_t*>(qs + n * QPITCH + hb[1] + RunsMap<D>::LANE * g), wrow, vbase, g, o, m_run,
