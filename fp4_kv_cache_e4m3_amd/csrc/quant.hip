@@ -14,12 +14,15 @@
 // |x| with m*s, exact in fp32 (<= 7 significant bits).  So every decision is
 // the exact-arithmetic one.
 //
-// One thread handles one 16-channel group: 64 B of fp32 in, 8 code bytes and
-// 1 scale byte out.  This kernel is not bandwidth critical in the decode step
-// (B rows per step); bulk quantisation of a cache is a one-off.
+// A decode step quantises B new rows (latency-bound): four lanes take one
+// 16-channel group there, 16 B of fp32 in and 2 code bytes out each.  Bulk
+// quantisation of a cache (a one-off) takes one thread per group.
 #include "common.h"
 
 namespace csa2 {
+
+// launches of at most this many 16-channel groups use four lanes per group
+constexpr int64_t kQuantQuadMaxGroups = 8192;
 
 // value of non-negative finite E4M3 code c (0..126) as fp32 (exact)
 CSA2_DEV float e4m3_pos(uint32_t c) {
@@ -28,15 +31,30 @@ CSA2_DEV float e4m3_pos(uint32_t c) {
 }
 
 // E4M3 code of amax/6: nearest, ties to even, saturating at 448 (0x7E).
+// The code is n = #{c in 0..125 : 6 * mu_c < amax} for the midpoints mu_c
+// between grid values c and c + 1, raised to the even neighbour on a tie.
+// An fp32 estimate y' of amax/6 (relative error ~2^-23, against a grid
+// spacing of at least 1/16) has grid floor ce within one code of the true
+// floor f, and n is f or f + 1; so every c <= ce - 2 counts, every
+// c >= ce + 2 does not, and only mu_{ce-2} .. mu_{ce+1} are compared, each
+// exactly (6 * mu is exact in fp32).
 CSA2_DEV uint32_t scale_code(float amax) {
-  // count midpoints mu_c (c = 0..125) with 6*mu_c < amax  (lower bound)
-  uint32_t lo = 0, hi = 126;
-  while (lo < hi) {
-    const uint32_t mid = (lo + hi) >> 1;
-    const float t = 3.0f * (e4m3_pos(mid) + e4m3_pos(mid + 1));   // 6 * midpoint, exact
-    if (t < amax) lo = mid + 1; else hi = mid;
+  const float yp = amax * (1.0f / 6.0f);
+  int ce;
+  if (!(yp < 448.0f)) ce = 126;
+  else if (yp < 0x1p-6f) ce = (int)(yp * 512.0f);                // subnormal grid, step 2^-9
+  else ce = ((int)((__float_as_uint(yp) >> 23) & 0xFFu) - 120) * 8 + (int)((__float_as_uint(yp) >> 20) & 7u);
+  const int base = ce - 2;
+  int n = base;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int c = base + k;
+    const bool below = c < 0 ? true
+                     : c > 125 ? false
+                               : 3.0f * (e4m3_pos((uint32_t)c) + e4m3_pos((uint32_t)c + 1)) < amax;   // 6 * mu_c, exact
+    n += below ? 1 : 0;
   }
-  uint32_t c = lo;
+  uint32_t c = (uint32_t)n;
   if (c < 126u) {
     const float t = 3.0f * (e4m3_pos(c) + e4m3_pos(c + 1));
     if (t == amax && (c & 1u)) c += 1;                             // tie -> even code
@@ -60,7 +78,8 @@ CSA2_DEV uint32_t element_code(float x, float s) {
   return mag | ((__float_as_uint(x) >> 28) & 8u);
 }
 
-__global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ x, int64_t xs, int64_t rows,
+// One thread per 16-channel group (bulk: every lane's VALU work is its own).
+__global__ __launch_bounds__(256) void k_quantize_group(const float* __restrict__ x, int64_t xs, int64_t rows,
                                                   int groups, uint8_t* __restrict__ codes, int64_t cs,
                                                   uint8_t* __restrict__ scales, int64_t ss) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -89,6 +108,40 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ x, i
   scales[r * ss + g] = (uint8_t)sc;
 }
 
+
+// Four lanes per 16-channel group, four channels each (small launches such
+// as a decode step's new rows, where latency rules): coalesced 16-byte loads,
+// the group's amax over the lane quad by DPP (max is exact and ignores NaN in
+// any order), then each lane writes its 4 codes (2 bytes) and the quad's
+// first lane the scale.
+__global__ __launch_bounds__(256) void k_quantize_quad(const float* __restrict__ x, int64_t xs, int64_t rows,
+                                                  int groups, uint8_t* __restrict__ codes, int64_t cs,
+                                                  uint8_t* __restrict__ scales, int64_t ss) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= rows * groups * 4) return;            // whole quads: the count is a multiple of 4
+  const int64_t grp = gid >> 2;
+  const int qtr = (int)(gid & 3);
+  const int64_t r = grp / groups;
+  const int g = (int)(grp - r * groups);
+  const float4 f = *reinterpret_cast<const float4*>(x + r * xs + 16 * g + 4 * qtr);
+  const float v[4] = {f.x, f.y, f.z, f.w};
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(amax), 0xB1, 0xF, 0xF, false)));  // xor 1
+  amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(amax), 0x4E, 0xF, 0xF, false)));  // xor 2
+  const uint32_t sc = scale_code(amax);
+  const float s = e4m3_pos(sc);
+  uint32_t bits = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t c = (s == 0.0f) ? ((__float_as_uint(v[i]) >> 28) & 8u) : element_code(v[i], s);
+    bits |= c << (4 * i);
+  }
+  *reinterpret_cast<uint16_t*>(codes + r * cs + 8 * g + 2 * qtr) = (uint16_t)bits;
+  if (qtr == 0) scales[r * ss + g] = (uint8_t)sc;
+}
+
 // One thread per 16 channels: 8 code bytes + 1 scale -> 16 fp32 values.
 __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ codes, int64_t cs,
                                                     const uint8_t* __restrict__ scales, int64_t ss,
@@ -114,9 +167,13 @@ hipError_t launch_quantize(const float* x, int64_t xs, int64_t rows, int dim, ui
   const int groups = dim / 16;
   const int64_t n = rows * groups;
   if (n == 0) return hipSuccess;
-  const int64_t blocks = (n + 255) / 256;
-  hipLaunchKernelGGL(k_quantize, dim3((unsigned)blocks), dim3(256), 0, st, x, xs, rows, groups, codes,
-                     cs, scales, ss);
+  if (n <= kQuantQuadMaxGroups) {                 // four lanes per group
+    hipLaunchKernelGGL(k_quantize_quad, dim3((unsigned)((4 * n + 255) / 256)), dim3(256), 0, st, x, xs, rows, groups,
+                       codes, cs, scales, ss);
+  } else {
+    hipLaunchKernelGGL(k_quantize_group, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, x, xs, rows, groups,
+                       codes, cs, scales, ss);
+  }
   return hipGetLastError();
 }
 

@@ -56,8 +56,11 @@ def exhaustive_groups() -> np.ndarray:
     return x.reshape(-1, 512)
 
 
-def test_quantize_exhaustive_bit_exact():
-    x = exhaustive_groups()
+@pytest.mark.parametrize("copies", [1, 8])
+def test_quantize_exhaustive_bit_exact(copies):
+    """The exhaustive groups once (a small launch: four lanes per group) and
+    tiled 8 times (past 8,192 groups: the one-thread-per-group kernel)."""
+    x = np.concatenate([exhaustive_groups()] * copies)
     c, s = gpu_quantize(x)
     rc, rs = quant.quantize_rows(x)
     np.testing.assert_array_equal(s, rs)
