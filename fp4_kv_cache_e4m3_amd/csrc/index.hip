@@ -440,8 +440,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_full(SelectParams p) {
   constexpr int KPT2 = kPoolPositions / kSelThreads;   // 16
   __shared__ SelShared sh;
   const int64_t q = blockIdx.x;
-  hists_clear(sh);
-  __syncthreads();
+  // the histograms are cleared while the first keys are in flight
   int64_t nv = p.nvis ? (int64_t)p.nvis[q] : p.T;
   nv = max((int64_t)0, min(nv, p.T));
   const int64_t nb = (nv + kBlock - 1) / kBlock;
@@ -462,6 +461,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select_full(SelectParams p) {
 #pragma unroll
       for (int j = 0; j < KPT1; ++j) bkey[j] = base1 + j < nb ? bk[base1 + j] : 0u;
     }
+    hists_clear(sh);
+    __syncthreads();
     auto get = [&](int j) { return bkey[j]; };
     if (K1 > 0) {
       uint32_t tau, need, kmin, kmax, cnt;
@@ -492,6 +493,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select_full(SelectParams p) {
       }
       skey[j] = m;
     }
+    hists_clear(sh);
+    __syncthreads();
     const uint32_t Ks = (uint32_t)min(nsb, (int64_t)kPoolBlocks);
     {
       auto get = [&](int j) { return skey[j]; };
@@ -625,13 +628,13 @@ __global__ __launch_bounds__(kSelThreads) void k_select_reindex(ReindexParams p)
   constexpr int KPT2 = kPoolPositions / kSelThreads;
   __shared__ SelShared sh;
   const int64_t q = blockIdx.x;
-  hists_clear(sh);
-  for (int i = threadIdx.x; i < kPoolBlocks; i += kSelThreads) sh.pool[i] = p.pool[q * kPoolBlocks + i];
-  __syncthreads();
+  // the candidate keys go out first; the histograms are cleared meanwhile
   uint32_t key[KPT2];
   const int base = threadIdx.x * KPT2;
 #pragma unroll
   for (int j = 0; j < KPT2; ++j) key[j] = p.ckeys[q * kPoolPositions + base + j];
+  hists_clear(sh);
+  for (int i = threadIdx.x; i < kPoolBlocks; i += kSelThreads) sh.pool[i] = p.pool[q * kPoolBlocks + i];
   __syncthreads();
   select_positions<KPT2>(key, sh, sh.pool, p.topk + q * kTopK);
 }
