@@ -62,6 +62,9 @@ CASES = [  # (B, Qn, T, d, H, W, k)
     (2, 2, 64, 128, 8, 0, 64),          # no window at all
     (1, 1, 0, 128, 8, 128, 512),        # empty main cache: window only
     (4, 1, 2000, 512, 128, 128, 512),   # 128 heads
+    (1, 1, 6000, 512, 32, 128, 2048),   # longest Top-K row: many FP4 tile pairs per wave
+    (2, 2, 3000, 512, 16, 64, 1000),    # odd number of FP4 tiles, shorter window
+    (1, 3, 900, 128, 16, 128, 17),      # one full FP4 tile and a one-entry tail
 ]
 
 
