@@ -157,22 +157,48 @@ __global__ __launch_bounds__(256) void k_index_scan(ScanParams p) {
   // The workgroups of a sequence sweep its keys together: in each round they
   // take 16 consecutive tiles each out of one contiguous stretch of
   // 16 * gridDim.x tiles, so the requests in flight across the GPU stay close
-  // in memory.  Wave w takes tiles 4u + w of its workgroup's 16; all U loads
-  // are issued before the first MFMA so several KiB per wave are in flight.
+  // in memory.  Wave w takes tiles 4u + w of its workgroup's 16.
+  //
+  // The keys go straight to LDS (global_load_lds_dwordx4): each instruction
+  // reads 1 KiB of whole key rows, lane l taking 16 bytes, and lands them in
+  // the wave's tile buffer in lane order.  A row-dependent XOR swizzle of the
+  // 16-byte chunk each lane fetches (chunk p of row r holds key chunk
+  // p ^ swz(r)) makes the operand reads below, row n and chunk g + 4kk per
+  // lane, hit 16 distinct bank groups per 16 lanes.  All U tiles are issued
+  // before the first MFMA.
   constexpr int U = 4;
+  constexpr int CPR = DI / 16;                 // 16-byte chunks per key row
+  constexpr int RPI = 1024 / DI;               // rows per 1 KiB load instruction
+  constexpr int NI = 16 * DI / 1024;           // load instructions per 16-row tile
+  constexpr int SWD = 16 / CPR;                // swz(r) = (r / SWD) % CPR
+  __shared__ __attribute__((aligned(16))) int8_t kbuf[4][U][16 * DI];
+  int8_t* const mybuf = &kbuf[wave][0][0];
   for (int64_t base = 16 * (int64_t)blockIdx.x; base < ntile; base += 16 * (int64_t)gridDim.x) {
-    v4i bf[U][KK];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t t = 16 * (base + 4 * u + wave) + n;
-      const int64_t row = t < tend ? t : 0;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int r = i * RPI + lane / CPR;
+        const int c = (lane % CPR) ^ ((r / SWD) % CPR);
+        const int64_t t = 16 * (base + 4 * u + wave) + r;
+        const int64_t row = t < tend ? t : 0;
+        __builtin_amdgcn_global_load_lds(ikb + row * DI + c * 16,
+                                         (__attribute__((address_space(3))) void*)(mybuf + u * 16 * DI + i * 1024),
+                                         16, 0, 0);
+      }
+    }
+    // s_waitcnt vmcnt(0) (expcnt, lgkmcnt left at their maximum): the tiles
+    // are in this wave's LDS buffer; the compiler does not order LDS-bound
+    // loads before the reads below by itself
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      v4i bf[KK];
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
-        bf[u][kk] = *reinterpret_cast<const v4i*>(ikb + row * DI + g * 16 + kk * 64);
+        bf[kk] = *reinterpret_cast<const v4i*>(mybuf + u * 16 * DI + n * DI + ((g + 4 * kk) ^ ((n / SWD) % CPR)) * 16);
+      if (base + 4 * u + wave < ntile) process((int)(base + 4 * u + wave), bf);
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (base + 4 * u + wave < ntile) process((int)(base + 4 * u + wave), bf[u]);
   }
 }
 
