@@ -68,18 +68,40 @@ def oracle_kv_rows(w: synth.Workload, b: int, positions: np.ndarray, with_new_ro
     return oquant.quantize_rows(src)
 
 
+def oracle_selected_rows(w: synth.Workload, topk, queries, with_new_rows=True) -> dict:
+    """Oracle FP4 codes/scales of the rows each query's Top-K names:
+    {query: (codes, scales)} in Top-K order.  The rows of one sequence are
+    quantised once over the union of its queries' positions, so the seeded
+    chunks are regenerated once per sequence (layers sharing a Top-K reuse
+    the result)."""
+    out = {}
+    by_seq = {}
+    for qi in queries:
+        by_seq.setdefault(qi // w.q_per_seq, []).append(qi)
+    for b, qis in by_seq.items():
+        allpos = np.unique(np.concatenate([topk[qi][topk[qi] >= 0].astype(np.int64) for qi in qis]))
+        codes, scales = oracle_kv_rows(w, b, allpos, with_new_rows)
+        for qi in qis:
+            idx = np.searchsorted(allpos, topk[qi][topk[qi] >= 0].astype(np.int64))
+            out[qi] = (codes[idx], scales[idx])
+    return out
+
+
 def oracle_attention(w: synth.Workload, q_bits, swa_bits, topk, with_new_rows=True, queries=None,
-                     swa_len=None):
-    """Oracle output of one layer for the given Top-K (oracle's own), [nq, H, d]."""
+                     swa_len=None, rows=None):
+    """Oracle output of one layer for the given Top-K (oracle's own), [nq, H, d].
+    rows: optional precomputed oracle_selected_rows for the same Top-K."""
     nq = w.nq
     qsel = range(nq) if queries is None else queries
     out = np.zeros((nq, w.heads, w.dim))
     qv = bf16_values(q_bits)
     sv = bf16_values(swa_bits)
+    if rows is None:
+        rows = oracle_selected_rows(w, topk, list(qsel), with_new_rows)
     for qi in qsel:
         b = qi // w.q_per_seq
         pos = topk[qi][topk[qi] >= 0].astype(np.int64)
-        codes, scales = oracle_kv_rows(w, b, pos, with_new_rows)
+        codes, scales = rows[qi]
         # local cache holding just these rows: row i <-> position pos[i]
         local_topk = np.arange(len(pos), dtype=np.int64)
         keys = oattn.query_entries(qi % w.q_per_seq, w.q_per_seq, len(pos), local_topk, codes, scales,

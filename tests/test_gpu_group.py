@@ -9,7 +9,7 @@ import torch
 
 from fp4_kv_cache_e4m3_amd import DecodeGroup, synth
 from oracle import indexer as oidx
-from tests.parity import ATTN_TOL, host, oracle_attention, oracle_kv_rows, rownorm_err
+from tests.parity import ATTN_TOL, host, oracle_attention, oracle_kv_rows, oracle_selected_rows, rownorm_err
 
 pytestmark = pytest.mark.gpu
 
@@ -52,10 +52,12 @@ def check_group(w, sample=None):
             rc, rs = oracle_kv_rows(w, b, np.arange(T - n, T), with_new_rows=True)
             np.testing.assert_array_equal(host(g.codes[b * T + T - n:b * T + T]), rc)
             np.testing.assert_array_equal(host(g.scales[b * T + T - n:b * T + T]), rs)
+    # every layer of the group attends over the same Top-K rows
+    rows = oracle_selected_rows(w, rtopk, qs, with_new_rows=(w.layers[0] == "full"))
     for l in range(len(w.layers)):
         got = host(g.out[l])
         ref = oracle_attention(w, synth.attn_q_bf16(w, l), synth.swa_bf16(w, l), rtopk,
-                               with_new_rows=(w.layers[0] == "full"), queries=qs)
+                               with_new_rows=(w.layers[0] == "full"), queries=qs, rows=rows)
         err = rownorm_err(got[qs], ref[qs])
         assert err <= ATTN_TOL, (l, err)
 
