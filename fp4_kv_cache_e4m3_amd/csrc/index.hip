@@ -216,6 +216,7 @@ struct SelShared {
   uint32_t wcnt[kSelWaves];
   int32_t pool[kPoolBlocks];
   int32_t sbpool[kPoolBlocks];                   // chosen super-blocks (large pools only)
+  int32_t cand[kSelThreads];                     // Top-512 candidate blocks (Full select, fast path)
 };
 
 // inclusive prefix sum over the 64 lanes with DPP (row shifts inside 16-lane
@@ -247,13 +248,23 @@ CSA2_DEV uint32_t block_excl_scan(uint32_t v, SelShared& sh) {
   return r;
 }
 
-CSA2_DEV uint32_t block_sum(uint32_t v, SelShared& sh) {
-  const uint32_t ex = block_excl_scan(v, sh);
-  if (threadIdx.x == kSelThreads - 1) sh.bc[0] = ex + v;
+// exclusive prefix sum over the workgroup plus the workgroup total
+CSA2_DEV uint32_t block_excl_scan_total(uint32_t v, SelShared& sh, uint32_t& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t incl = wave_incl_scan(v);
+  if (lane == 63) sh.wsum[wave] = incl;
   __syncthreads();
-  const uint32_t t = sh.bc[0];
+  if (wave == 0) {
+    const uint32_t x = lane < kSelWaves ? sh.wsum[lane] : 0u;
+    const uint32_t xi = wave_incl_scan(x);
+    if (lane < kSelWaves) sh.wsum[lane] = xi - x;
+    if (lane == kSelWaves - 1) sh.bc[3] = xi;
+  }
   __syncthreads();
-  return t;
+  const uint32_t r = sh.wsum[wave] + incl - v;
+  total = sh.bc[3];
+  __syncthreads();
+  return r;
 }
 
 // +1 on counter `bin`.  When every active lane of the wave hits the same bin
@@ -274,36 +285,50 @@ CSA2_DEV void hist_inc(uint32_t* hist, uint32_t bin, bool active) {
   }
 }
 
-// Digit d of an NB-bin histogram with  above(d) < k <= above(d) + count(d),
-// where above(d) counts larger digits.  Thread t owns the BPT bins
-// [NB - BPT (t+1), NB - BPT t), so thread order is descending digit order;
-// the owning thread walks its bins in registers.
+// Digit d of an NB-bin histogram (NB = 4096 or 256) with
+// above(d) < k <= above(d) + count(d), where above(d) counts larger digits;
+// 1 <= k <= the histogram's total.  One wave searches: lane l sums the NB/64
+// bins [NB - (NB/64)(l+1), NB - (NB/64) l), so lane order is descending digit
+// order; a DPP scan over the lane sums finds the lane whose bins hold the k-th
+// key, and a second scan over that lane's bins (one per lane, highest first)
+// finds the bin.
+template <int NB>
+CSA2_DEV void wave_hist_find(const uint32_t* hist, uint32_t k, uint32_t& digit, uint32_t& above) {
+  constexpr int BPL = NB / 64;
+  static_assert(BPL == 64 || BPL == 4, "4096- or 256-bin histograms");
+  const int lane = threadIdx.x & 63;
+  const u4* h4 = reinterpret_cast<const u4*>(hist + NB - BPL * (lane + 1));
+  uint32_t sum = 0;
+#pragma unroll
+  for (int i = 0; i < BPL / 4; ++i) {
+    const u4 v = h4[i];
+    sum += (v[0] + v[1]) + (v[2] + v[3]);
+  }
+  const uint32_t incl = wave_incl_scan(sum);
+  const uint32_t ex = incl - sum;
+  const int L = (int)__builtin_ctzll(__ballot(ex < k && k <= incl));
+  const uint32_t exL = (uint32_t)__builtin_amdgcn_readlane((int)ex, L);
+  const int bin = NB - BPL * L - 1 - min(lane, BPL - 1);
+  const uint32_t c = lane < BPL ? hist[bin] : 0u;
+  const uint32_t incl2 = exL + wave_incl_scan(c);
+  const int M = (int)__builtin_ctzll(__ballot(lane < BPL && incl2 - c < k && k <= incl2));
+  digit = (uint32_t)__builtin_amdgcn_readlane(bin, M);
+  above = (uint32_t)__builtin_amdgcn_readlane((int)(incl2 - c), M);
+}
+
+// wave_hist_find in wave 0, the result broadcast through LDS (the other waves
+// only wait at the barrier).  sh.bc is next written after the workgroup has
+// passed at least one more barrier, so one barrier suffices here.
 template <int NB>
 CSA2_DEV void hist_find(const uint32_t* hist, uint32_t k, SelShared& sh, uint32_t& digit, uint32_t& above) {
-  constexpr int BPT = NB >= kSelThreads ? NB / kSelThreads : 1;
-  constexpr int OWNERS = NB / BPT;
-  const int t = threadIdx.x;
-  uint32_t c[BPT];
-  uint32_t sum = 0;
-  const int lo_bin = NB - BPT * (t + 1);
-#pragma unroll
-  for (int i = 0; i < BPT; ++i) {
-    c[i] = t < OWNERS ? hist[lo_bin + i] : 0u;
-    sum += c[i];
-  }
-  const uint32_t ex = block_excl_scan(sum, sh);
-  if (t < OWNERS && ex < k && k <= ex + sum) {
-    uint32_t run = ex;
-#pragma unroll
-    for (int i = BPT - 1; i >= 0; --i) {
-      if (run + c[i] >= k) { sh.bc[0] = (uint32_t)(lo_bin + i); sh.bc[1] = run; break; }
-      run += c[i];
-    }
+  if (threadIdx.x < 64) {
+    uint32_t d, a;
+    wave_hist_find<NB>(hist, k, d, a);
+    if (threadIdx.x == 0) { sh.bc[0] = d; sh.bc[1] = a; }
   }
   __syncthreads();
   digit = sh.bc[0];
   above = sh.bc[1];
-  __syncthreads();
 }
 
 // inclusive max-scan over the 64 lanes with DPP (lanes outside a row read 0,
@@ -346,41 +371,67 @@ CSA2_DEV void key_stats(Get get, SelShared& sh, uint32_t& kmin, uint32_t& kmax, 
   count = cnt;
 }
 
-// K-th largest key among nonzero keys (1 <= K <= #nonzero): returns the key
-// value tau and how many keys equal to tau belong to the top K.  kmin / kmax
-// are the smallest / largest nonzero key.  Radix passes run on the offset
-// r = key - kmin, whose width w is known from the key range:
-// the first pass takes its top 12 bits (so the keys spread over all 4096 bins
-// whatever their magnitude, and equal digits rarely collide in the LDS
-// atomics), a second pass the next up to 12 bits, a third the remaining up
-// to 8.  Histograms h[0..2] are pre-cleared.  get(j) returns this thread's
-// j-th key (j < KPT); small KPT keeps keys in registers, large KPT re-reads
-// them each pass.
+// K-th largest key among nonzero keys (1 <= K <= #nonzero): tau, the key
+// value, and how many keys equal to tau belong to the top K.  kmin / kmax are
+// the smallest / largest nonzero key.  Radix passes run on the offset
+// r = key - kmin, whose width w is known from the key range: the first pass
+// takes its top 12 bits (so the keys spread over all 4096 bins whatever their
+// magnitude, and equal digits rarely collide in the LDS atomics), a second
+// pass the next up to 12 bits, a third the remaining up to 8.  Histograms
+// h[0..2] are pre-cleared.  get(j) returns this thread's j-th key (j < KPT);
+// small KPT keeps keys in registers, large KPT re-reads them each pass.
+// radix_first runs the first pass and, when kx > 0, also returns thr_x, the
+// smallest key whose first digit is that of the kx-th largest key: every key
+// ranked within the top kx is >= thr_x.  radix_rest finishes the select.
+struct RadixState {
+  uint32_t kmin;
+  int s1, b2, s2;           // bits below the first digit, second digit width, bits below it
+  uint32_t d1, kk;          // first digit, rank left inside it
+};
+
 template <int KPT, typename Get>
-CSA2_DEV void radix_select(Get get, uint32_t K, uint32_t kmin, uint32_t kmax, SelShared& sh,
-                           uint32_t (*h)[kDigitBins], uint32_t& tau, uint32_t& need) {
+CSA2_DEV RadixState radix_first(Get get, uint32_t K, uint32_t kmin, uint32_t kmax, SelShared& sh,
+                                uint32_t (*h)[kDigitBins], uint32_t kx, uint32_t& thr_x) {
+  RadixState st;
   const uint32_t range = kmax - kmin;
   const int width = range == 0u ? 0 : 32 - __builtin_clz(range);
-  const int s1 = width > 12 ? width - 12 : 0;                 // bits below the first digit
-  const int b2 = s1 > 12 ? 12 : s1;                            // second digit width
-  const int s2 = s1 - b2;                                      // bits below the second digit (<= 8)
+  st.kmin = kmin;
+  st.s1 = width > 12 ? width - 12 : 0;
+  st.b2 = st.s1 > 12 ? 12 : st.s1;
+  st.s2 = st.s1 - st.b2;
 #pragma unroll 16
   for (int j = 0; j < KPT; ++j) {
     const uint32_t k = get(j);
-    hist_inc(h[0], (k - kmin) >> s1, k != 0u);
+    hist_inc(h[0], (k - kmin) >> st.s1, k != 0u);
   }
   __syncthreads();
-  uint32_t d1, a1;
-  hist_find<kDigitBins>(h[0], K, sh, d1, a1);
-  uint32_t kk = K - a1;
-  uint32_t pre = d1;                                           // known high bits of the offset
+  if (threadIdx.x < 64) {
+    uint32_t d, a, dx = 0u, ax;
+    wave_hist_find<kDigitBins>(h[0], K, d, a);
+    if (kx > 0u) wave_hist_find<kDigitBins>(h[0], kx, dx, ax);
+    if (threadIdx.x == 0) { sh.bc[0] = d; sh.bc[1] = a; sh.bc[2] = dx; }
+  }
+  __syncthreads();
+  st.d1 = sh.bc[0];
+  st.kk = K - sh.bc[1];
+  thr_x = kmin + (sh.bc[2] << st.s1);
+  return st;
+}
+
+template <int KPT, typename Get>
+CSA2_DEV void radix_rest(Get get, const RadixState& st, SelShared& sh, uint32_t (*h)[kDigitBins], uint32_t& tau,
+                         uint32_t& need) {
+  const uint32_t kmin = st.kmin;
+  const int s1 = st.s1, b2 = st.b2, s2 = st.s2;
+  uint32_t kk = st.kk;
+  uint32_t pre = st.d1;                                        // known high bits of the offset
   if (b2 > 0) {
     const uint32_t m2 = (1u << b2) - 1u;
 #pragma unroll 16
     for (int j = 0; j < KPT; ++j) {
       const uint32_t k = get(j);
       const uint32_t r = k - kmin;
-      hist_inc(h[1], (r >> s2) & m2, k != 0u && (r >> s1) == d1);
+      hist_inc(h[1], (r >> s2) & m2, k != 0u && (r >> s1) == st.d1);
     }
     __syncthreads();
     uint32_t d2, a2;
@@ -404,6 +455,14 @@ CSA2_DEV void radix_select(Get get, uint32_t K, uint32_t kmin, uint32_t kmax, Se
   }
   tau = kmin + pre;
   need = kk;
+}
+
+template <int KPT, typename Get>
+CSA2_DEV void radix_select(Get get, uint32_t K, uint32_t kmin, uint32_t kmax, SelShared& sh,
+                           uint32_t (*h)[kDigitBins], uint32_t& tau, uint32_t& need) {
+  uint32_t unused;
+  const RadixState st = radix_first<KPT>(get, K, kmin, kmax, sh, h, 0u, unused);
+  radix_rest<KPT>(get, st, sh, h, tau, need);
 }
 
 CSA2_DEV void hists_clear(SelShared& sh) {
@@ -475,6 +534,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select_full(SelectParams p) {
   // ---- step 1: top blocks (keys in registers when they fit, else re-read)
   const int64_t base1 = (int64_t)threadIdx.x * KPT1;
   const uint32_t* bk = p.bkeys + q * p.bk_stride;
+  int ncand = -1;                       // >= 0: Top-512 candidates are sh.cand[0..ncand), keys in ckey
+  uint32_t ckey[kBlock] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
   if constexpr (KPT1 <= 16) {
     uint32_t bkey[KPT1];
     if (base1 + KPT1 <= nb) {                 // whole run visible: 16-byte loads
@@ -491,9 +552,38 @@ __global__ __launch_bounds__(kSelThreads) void k_select_full(SelectParams p) {
     __syncthreads();
     auto get = [&](int j) { return bkey[j]; };
     if (K1 > 0) {
-      uint32_t tau, need, kmin, kmax, cnt;
+      uint32_t tau, need, kmin, kmax, cnt, thr;
       key_stats<KPT1>(get, sh, kmin, kmax, cnt);
-      radix_select<KPT1>(get, K1, kmin, kmax, sh, &sh.hist[0], tau, need);
+      const RadixState st = radix_first<KPT1>(get, K1, kmin, kmax, sh, &sh.hist[0], min(K1, (uint32_t)kTopK), thr);
+      // Top-512 candidates: every block ranked above the block of a selected
+      // position holds a position ranked above it, so the Top-512 positions
+      // lie in the top 512 blocks, and those have keys >= thr.  When at most
+      // one block per thread passes, their ids (ascending) go to sh.cand and
+      // their token keys are gathered now, while the pool select finishes.
+      uint32_t mine = 0, ntot;
+#pragma unroll
+      for (int j = 0; j < KPT1; ++j) mine += bkey[j] >= thr ? 1u : 0u;     // thr >= kmin >= 1: key 0 fails
+      uint32_t o = block_excl_scan_total(mine, sh, ntot);
+      if (ntot <= (uint32_t)kSelThreads) {
+#pragma unroll
+        for (int j = 0; j < KPT1; ++j)
+          if (bkey[j] >= thr) sh.cand[o++] = (int32_t)(base1 + j);
+        __syncthreads();
+        ncand = (int)ntot;
+        if ((int)threadIdx.x < ncand) {
+          const int64_t pos0 = (int64_t)sh.cand[threadIdx.x] * kBlock;
+          if (pos0 + kBlock <= nv) {
+            const u4* kp = reinterpret_cast<const u4*>(p.tkeys + q * p.tk_stride + pos0);
+            const u4 v0 = kp[0], v1 = kp[1];
+            ckey[0] = v0[0]; ckey[1] = v0[1]; ckey[2] = v0[2]; ckey[3] = v0[3];
+            ckey[4] = v1[0]; ckey[5] = v1[1]; ckey[6] = v1[2]; ckey[7] = v1[3];
+          } else {
+#pragma unroll
+            for (int r = 0; r < kBlock; ++r) ckey[r] = pos0 + r < nv ? p.tkeys[q * p.tk_stride + pos0 + r] : 0u;
+          }
+        }
+      }
+      radix_rest<KPT1>(get, st, sh, &sh.hist[0], tau, need);
       compact_topk<KPT1>(get, tau, need, sh, [&](uint32_t o, int j) { sh.pool[o] = (int32_t)(base1 + j); });
     }
   } else {
@@ -570,7 +660,11 @@ __global__ __launch_bounds__(kSelThreads) void k_select_full(SelectParams p) {
   if (p.pool)
     for (int i = threadIdx.x; i < kPoolBlocks; i += kSelThreads) p.pool[q * kPoolBlocks + i] = sh.pool[i];
 
-  // ---- step 2: Top-512 positions of the pool
+  // ---- step 2: Top-512 positions of the candidate blocks, or of the pool
+  if (ncand >= 0) {
+    select_positions<kBlock>(ckey, sh, sh.cand, p.topk + q * kTopK);
+    return;
+  }
   uint32_t key[KPT2];
   const int base2 = threadIdx.x * KPT2;
 #pragma unroll

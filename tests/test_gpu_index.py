@@ -57,6 +57,9 @@ CASES = [  # (B, Qn, T, H_I, D_I, r, wmax)
     (1, 2, 100003, 8, 128, 8, 8),     # more than 8,192 blocks: super-block pre-selection
     (1, 3, 300001, 8, 64, 1, 2),      # ... with heavy ties
     (1, 1, 262144, 2, 64, 0, 1),      # ... all scores equal
+    (1, 1, 8192, 2, 64, 0, 1),        # all equal, 1,024 blocks: every block a Top-512 candidate
+    (1, 1, 8200, 2, 64, 0, 1),        # all equal, 1,025 candidate blocks: the pool is searched
+    (2, 1, 12000, 2, 64, 1, 1),       # ties spread over the candidate threshold
 ]
 
 
