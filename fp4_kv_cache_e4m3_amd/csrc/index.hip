@@ -211,7 +211,7 @@ constexpr int kSelHists = 6;                     // 3 passes x 2 selections, cle
 struct SelShared {
   alignas(16) uint32_t hist[kSelHists][kDigitBins];
   uint32_t bc[4];
-  uint32_t wsum[kSelWaves];
+  alignas(16) uint32_t wsum[kSelWaves];
   uint32_t wmin[kSelWaves];
   uint32_t wcnt[kSelWaves];
   int32_t pool[kPoolBlocks];
@@ -231,40 +231,33 @@ CSA2_DEV uint32_t wave_incl_scan(uint32_t x) {
   return x;
 }
 
-// exclusive prefix sum over the workgroup (thread order)
-CSA2_DEV uint32_t block_excl_scan(uint32_t v, SelShared& sh) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t incl = wave_incl_scan(v);
-  if (lane == 63) sh.wsum[wave] = incl;
-  __syncthreads();
-  if (wave == 0) {
-    const uint32_t x = lane < kSelWaves ? sh.wsum[lane] : 0u;
-    const uint32_t xi = wave_incl_scan(x);
-    if (lane < kSelWaves) sh.wsum[lane] = xi - x;
-  }
-  __syncthreads();
-  const uint32_t r = sh.wsum[wave] + incl - v;
-  __syncthreads();
-  return r;
-}
-
-// exclusive prefix sum over the workgroup plus the workgroup total
+// exclusive prefix sum over the workgroup (thread order), plus the total:
+// wave scans, then every thread adds the totals of the lower waves (broadcast
+// LDS reads); the second barrier keeps wsum intact until all have read it
 CSA2_DEV uint32_t block_excl_scan_total(uint32_t v, SelShared& sh, uint32_t& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t incl = wave_incl_scan(v);
   if (lane == 63) sh.wsum[wave] = incl;
   __syncthreads();
-  if (wave == 0) {
-    const uint32_t x = lane < kSelWaves ? sh.wsum[lane] : 0u;
-    const uint32_t xi = wave_incl_scan(x);
-    if (lane < kSelWaves) sh.wsum[lane] = xi - x;
-    if (lane == kSelWaves - 1) sh.bc[3] = xi;
+  uint32_t before = 0u, all = 0u;
+  const u4* w4 = reinterpret_cast<const u4*>(sh.wsum);
+#pragma unroll
+  for (int i = 0; i < kSelWaves / 4; ++i) {
+    const u4 x = w4[i];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      before += 4 * i + c < wave ? x[c] : 0u;
+      all += x[c];
+    }
   }
   __syncthreads();
-  const uint32_t r = sh.wsum[wave] + incl - v;
-  total = sh.bc[3];
-  __syncthreads();
-  return r;
+  total = all;
+  return before + incl - v;
+}
+
+CSA2_DEV uint32_t block_excl_scan(uint32_t v, SelShared& sh) {
+  uint32_t total;
+  return block_excl_scan_total(v, sh, total);
 }
 
 // +1 on counter `bin`.  When every active lane of the wave hits the same bin
@@ -581,6 +574,12 @@ __global__ __launch_bounds__(kSelThreads) void k_select_full(SelectParams p) {
 #pragma unroll
             for (int r = 0; r < kBlock; ++r) ckey[r] = pos0 + r < nv ? p.tkeys[q * p.tk_stride + pos0 + r] : 0u;
           }
+          // with at least 512 blocks, the top 512 hold 512 positions whose
+          // keys equal their block keys (>= thr), so a position with a key
+          // below thr is outranked 512 times: it leaves the candidates
+          const uint32_t kfloor = K1 >= (uint32_t)kTopK ? thr : 1u;
+#pragma unroll
+          for (int r = 0; r < kBlock; ++r) ckey[r] = ckey[r] >= kfloor ? ckey[r] : 0u;
         }
       }
       radix_rest<KPT1>(get, st, sh, &sh.hist[0], tau, need);

@@ -60,6 +60,8 @@ CASES = [  # (B, Qn, T, H_I, D_I, r, wmax)
     (1, 1, 8192, 2, 64, 0, 1),        # all equal, 1,024 blocks: every block a Top-512 candidate
     (1, 1, 8200, 2, 64, 0, 1),        # all equal, 1,025 candidate blocks: the pool is searched
     (2, 1, 12000, 2, 64, 1, 1),       # ties spread over the candidate threshold
+    (1, 2, 4000, 2, 64, 1, 2),        # fewer than 512 blocks, more than 512 positions
+    (2, 1, 2500, 8, 128, 8, 8),       # ... without heavy ties
 ]
 
 
