@@ -75,6 +75,17 @@ CSA2_DEV v8h bf16x8_to_half(u4 w) {
 // ---------------------------------------------------------------- wave helpers
 CSA2_DEV float wave_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
+// x + (x of lane l ^ 16), resp. l ^ 32, with the gfx950 permlane swaps (no LDS
+// traffic); fp32 addition commutes, so both lanes get the same bits.
+CSA2_DEV float sum_swap16(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
+CSA2_DEV float sum_swap32(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
+
 }  // namespace csa2
 
 // ---------------------------------------------------------------- launchers
