@@ -29,8 +29,8 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak (AMD spec)
 # WRITE_SIZE (each scaled by what the counter reads for a plain 1 GiB copy) on
 # the workload and kernel source named here; reported only while both match.
 SCAN_TRAFFIC = {"workload": "decode_group_full_reuse3_b32_t65536",
-                "source_sha256": "b2c67ddc659b7438507e7798b9adc90edbed8ee446a36e2c7be5d25b41290866",
-                "bytes": 268849088 + 9525056}
+                "source_sha256": "82fce35254e1886e46bae805cd39825651b06a0452e2421581fb5b567565930e",
+                "bytes": 268847053 + 9610724}
 
 
 def scan_traffic(w):
@@ -53,11 +53,8 @@ def group_bytes(w) -> dict:
     attn_layer = (nq * (512 * row + w.heads * w.dim * 2 + w.heads * w.dim * 4 + 512 * 4)
                   + w.batch * w.swa_rows * w.dim * 2)
     reindex = nq * (2048 * 4 + 16384 * w.idx_dim + w.idx_heads * (w.idx_dim + 4) + 512 * 4)
-    layers = len(w.layers)
-    if w.layers[0] == "full":
-        total = quant + scan + select + layers * attn_layer
-    else:
-        total = reindex + layers * attn_layer
+    n_full, n_rx = w.layers.count("full"), w.layers.count("reindex")
+    total = n_full * (quant + scan + select) + n_rx * reindex + len(w.layers) * attn_layer
     return dict(scan=scan, select=select, quant=quant, attn_layer=attn_layer, reindex=reindex,
                 total=total)
 
@@ -87,13 +84,23 @@ def cpu_baseline(w, max_queries: int, min_seconds: float = 10.0) -> dict:
     sws = [synth.bf16_bits_to_f32(synth.swa_bf16(w, l)[:n_seq]).astype(np.float64)
            for l in range(len(w.layers))]
     srcs = [synth.kv_source(w, b) for b in range(n_seq)]
+    rx = {l: (synth.index_q(w, l)[:nqs], synth.index_w(w, l)[:nqs])
+          for l, m in enumerate(w.layers) if m == "reindex" and l > 0}
+    if w.layers[0] == "reindex":
+        rx[0] = (iq, iw)
+        iq, iw = synth.index_q(w, 0, pool_source=True)[:nqs], synth.index_w(w, 0, pool_source=True)[:nqs]
+
     def one_pass():
-        oquant.quantize_rows(newr)
+        if w.layers[0] == "full":
+            oquant.quantize_rows(newr)
         for qi in range(nqs):
             b = qi // qn
-            _, pos, _ = oidx.full_query(iq[qi], iw[qi], ik[b], T)
-            codes, scales = oquant.quantize_rows(srcs[b][pos])     # the selected cache rows
-            for l in range(len(w.layers)):
+            pool, pos, _ = oidx.full_query(iq[qi], iw[qi], ik[b], T)
+            for l, m in enumerate(w.layers):
+                if m == "reindex":
+                    pos = oidx.reindex_query(rx[l][0][qi], rx[l][1][qi], ik[b], pool, T)
+                if m in ("full", "reindex"):
+                    codes, scales = oquant.quantize_rows(srcs[b][pos])     # the selected cache rows
                 keys = oattn.query_entries(qi % qn, qn, len(pos), np.arange(len(pos)), codes, scales,
                                            sws[l][b:b + 1], w.window)
                 oattn.attend(qs[l][qi], keys, 1.0 / np.sqrt(w.dim))
@@ -151,25 +158,19 @@ def main() -> int:
     stream = torch.cuda.current_stream()
     nl = len(w.layers)
     full = w.layers[0] == "full"
+    # the step's library calls in order (the Full layer's index call split into
+    # its scan and select so that the scan can be timed on its own)
+    calls = g.calls(stream, split_full=True)
+    roof_stage = "index_scan" if full else "reindex"
+    roof_i = next(i for i, (st, _) in enumerate(calls) if st == roof_stage)
 
     def step(ev=None):
-        # ev: events recorded between the calls (timing only; no sync): ev[0],
-        # ev[1] bracket the scan (or reindex); ev[2], ev[3], when present, the
-        # select and the attention layers
-        if full:
-            g.quantize_new(stream)
-            if ev is not None: ev[0].record(stream)
-            csa2.index_scan(g.iargs, g.iws, stream)
-            if ev is not None: ev[1].record(stream)
-            csa2.index_select(g.iargs, g.pool_out(), g.topk, g.iws, stream)
-        else:
-            if ev is not None: ev[0].record(stream)
-            csa2.index_reindex(g.iargs, g.pool, g.topk, g.iws, stream)
-            if ev is not None: ev[1].record(stream)
-        if ev is not None and len(ev) > 2: ev[2].record(stream)
-        for l in range(nl):
-            csa2.sparse_attn(g.aargs[l], g.aws, stream)
-        if ev is not None and len(ev) > 3: ev[3].record(stream)
+        # ev: an event pair recorded around the first scan (or reindex) call
+        # (timing only; no sync)
+        for i, (_, call) in enumerate(calls):
+            if ev is not None and i == roof_i: ev[0].record(stream)
+            call()
+            if ev is not None and i == roof_i: ev[1].record(stream)
 
     for _ in range(args.warmup):
         step()
@@ -192,21 +193,27 @@ def main() -> int:
     t_wall = time.perf_counter() - t_wall
     ms = start.elapsed_time(stop) / args.steps
     scan_ms = sum(e[0].elapsed_time(e[1]) for e in evs.values()) / len(evs)
-    # per-stage breakdown: a separate pass of K steps after the timed region
-    bev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # per-stage breakdown: a separate pass of K steps after the timed region,
+    # one event after every call
+    bev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
     for k in range(args.steps):
-        step(bev[k])
+        bev[k][0].record(stream)
+        for i, (_, call) in enumerate(calls):
+            call()
+            bev[k][i + 1].record(stream)
     torch.cuda.synchronize()
-    scan_b = sum(e[0].elapsed_time(e[1]) for e in bev) / args.steps
-    sel_ms = sum(e[1].elapsed_time(e[2]) for e in bev) / args.steps
-    attn_ms = sum(e[2].elapsed_time(e[3]) for e in bev) / args.steps
+    stage_ms = {}
+    for k in range(args.steps):
+        for i, (st, _) in enumerate(calls):
+            stage_ms[st] = stage_ms.get(st, 0.0) + bev[k][i].elapsed_time(bev[k][i + 1]) / args.steps
 
     nbytes = group_bytes(w)
     value = w.nq / (ms / 1e3)
     scan_bytes = nbytes["scan"] if full else nbytes["reindex"]
+    group = "group" if nl <= 6 else f"{nl}-layer decoder step"
     achieved = scan_bytes / (scan_ms / 1e3) / 1e9
     out = {
-        "metric": "decode query-tokens/s per CSA2 layer group at 64K ctx + achieved HBM GB/s",
+        "metric": f"decode query-tokens/s per CSA2 layer {group} at 64K ctx + achieved HBM GB/s",
         "value": round(value, 1),
         "unit": "query-tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -219,11 +226,9 @@ def main() -> int:
                    "idx_heads": w.idx_heads, "idx_dim": w.idx_dim, "layers": list(w.layers)},
         "hbm_gbs_group": round(nbytes["total"] / (ms / 1e3) / 1e9, 1),
         "hbm_frac_group": round(nbytes["total"] / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
-        "breakdown_ms": {"pass": "separate, one event pair per stage",
-                         "index_scan" if full else "reindex": round(scan_b, 4),
-                         "index_select" if full else "-": round(sel_ms, 4),
-                         f"attention_x{nl}": round(attn_ms, 4)},
-        "roofline": {"kernel": "k_index_scan" if full else "k_reindex_score+select",
+        "breakdown_ms": dict({"pass": "separate, one event after every call (sums per stage)"},
+                             **{st: round(v, 4) for st, v in stage_ms.items()}),
+        "roofline": {"kernel": "k_index_scan" if full else "k_reindex_score+k_select_reindex",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "bytes_per_launch": scan_bytes, "traffic": scan_traffic(w) if full else None},

@@ -24,12 +24,17 @@ def _dev(a: np.ndarray, device) -> torch.Tensor:
 
 
 class DecodeGroup:
-    """Device state of one synthetic layer group and its step.
+    """Device state of a synthetic sequence of CSA2 layers and its step.
 
-    ``w.layers`` names the group, e.g. ("full", "reuse", "reuse", "reuse") or
-    ("reindex", "reuse", ...).  For a Reindex group the Full layer's pool is
-    produced once at set-up (from the pool-source indexer Q) and is an input
-    of every step, as it would be when the Full layer ran earlier."""
+    ``w.layers`` names the layers, e.g. ("full", "reuse", "reuse", "reuse"),
+    ("reindex", "reuse", ...) or a whole decoder (a Full group followed by
+    Reindex groups).  A Full layer quantises the step's new main-KV rows and
+    runs the Full indexer (pool + Top-K); a Reindex layer rescores the latest
+    pool with its own indexer Q; a Reuse layer attends with the latest Top-K.
+    Each indexing layer writes its own Top-K buffer (``topks[i]``).  When the
+    sequence starts with a Reindex layer, the pool of the Full layer before it
+    is produced once at set-up (from the pool-source indexer Q) and is an
+    input of every step."""
 
     def __init__(self, w: synth.Workload, device: str = "cuda", kv_rows=None):
         self.w = w
@@ -53,19 +58,33 @@ class DecodeGroup:
             self.ik[b].copy_(torch.from_numpy(synth.index_k(w, b)))
         # ---- per-step inputs
         self.new_rows = _dev(synth.new_rows(w), dev)           # [B * new_per_seq, d] fp32
+        nl = len(w.layers)
+        # indexing layers (Full / Reindex) and, per layer, the Top-K it reads
+        self.index_layers = [l for l, m in enumerate(w.layers) if m in ("full", "reindex")]
+        assert self.index_layers and self.index_layers[0] == 0, "the first layer must index"
         self.iq = _dev(synth.index_q(w, 0), dev)
         self.iw = _dev(synth.index_w(w, 0), dev)
-        nl = len(w.layers)
+        self._iqw = {0: (self.iq, self.iw)}
+        for l in self.index_layers[1:]:
+            self._iqw[l] = (_dev(synth.index_q(w, l), dev), _dev(synth.index_w(w, l), dev))
         self.q = [_dev(synth.attn_q_bf16(w, l).view(np.int16), dev) for l in range(nl)]
         self.swa = [_dev(synth.swa_bf16(w, l).view(np.int16), dev) for l in range(nl)]
         # ---- outputs and workspaces
         nq = w.nq
         self.pool = torch.full((nq, B.POOL_BLOCKS), -1, dtype=torch.int32, device=dev)
-        self.topk = torch.full((nq, B.TOPK), -1, dtype=torch.int32, device=dev)
+        self.topks = [torch.full((nq, B.TOPK), -1, dtype=torch.int32, device=dev) for _ in self.index_layers]
+        self.topk = self.topks[0]
         self.out = [torch.empty((nq, w.heads, d), dtype=torch.float32, device=dev) for _ in range(nl)]
-        self.iargs = B.index_args(self.iq, self.iw, self.ik, w.q_per_seq)
+        self.iargs_by_layer = {l: B.index_args(iq, iw, self.ik, w.q_per_seq) for l, (iq, iw) in self._iqw.items()}
+        self.iargs = self.iargs_by_layer[0]
         self.iws = torch.empty(max(256, B.index_workspace_size(self.iargs)), dtype=torch.uint8, device=dev)
-        self.aargs = [B.attn_args(self.q[l], self.codes, self.scales, self.topk, self.swa[l], self.out[l],
+        # Top-K buffer of each layer: the latest indexing layer's
+        self._topk_of = []
+        k = -1
+        for m in w.layers:
+            k += m in ("full", "reindex")
+            self._topk_of.append(self.topks[k])
+        self.aargs = [B.attn_args(self.q[l], self.codes, self.scales, self._topk_of[l], self.swa[l], self.out[l],
                                   w.q_per_seq, T, w.window) for l in range(nl)]
         aws = max(B.attn_workspace_size(a) for a in self.aargs)
         self.aws = torch.empty(max(256, aws), dtype=torch.uint8, device=dev) if aws > 0 else None
@@ -101,13 +120,29 @@ class DecodeGroup:
         """The pool buffer, or None for an encoder group (no Reindex consumes it)."""
         return None if self.w.encoder else self.pool
 
-    # one pass of the whole group
+    def calls(self, stream=None, split_full: bool = False) -> list:
+        """The ordered library calls of one step as (stage, callable) pairs;
+        stages: quantize, index_full (or index_scan + index_select with
+        split_full), reindex, attention."""
+        out = []
+        for l, m in enumerate(self.w.layers):
+            if m == "full":
+                ia, tk = self.iargs_by_layer[l], self._topk_of[l]
+                out.append(("quantize", lambda: self.quantize_new(stream)))
+                if split_full:
+                    out.append(("index_scan", lambda ia=ia: B.index_scan(ia, self.iws, stream)))
+                    out.append(("index_select",
+                                lambda ia=ia, tk=tk: B.index_select(ia, self.pool_out(), tk, self.iws, stream)))
+                else:
+                    out.append(("index_full",
+                                lambda ia=ia, tk=tk: B.index_full(ia, self.pool_out(), tk, self.iws, stream)))
+            elif m == "reindex":
+                ia, tk = self.iargs_by_layer[l], self._topk_of[l]
+                out.append(("reindex", lambda ia=ia, tk=tk: B.index_reindex(ia, self.pool, tk, self.iws, stream)))
+            out.append(("attention", lambda l=l: B.sparse_attn(self.aargs[l], self.aws, stream)))
+        return out
+
+    # one pass of the whole layer sequence
     def step(self, stream=None) -> None:
-        w = self.w
-        if w.layers[0] == "full":
-            self.quantize_new(stream)
-            B.index_full(self.iargs, self.pool_out(), self.topk, self.iws, stream)
-        elif w.layers[0] == "reindex":
-            B.index_reindex(self.iargs, self.pool, self.topk, self.iws, stream)
-        for l in range(len(w.layers)):
-            B.sparse_attn(self.aargs[l], self.aws, stream)
+        for _, call in self.calls(stream):
+            call()

@@ -106,7 +106,15 @@ C5 = Workload("verify_group_full_reuse3_b8_q6_t1m", 5, batch=8, q_per_seq=6, kv_
               layers=("full", "reuse", "reuse", "reuse"),
               note="1M-entry decode with 1 + 5 draft queries per sequence")
 
-WORKLOADS = {w.name: w for w in (C1, C2, C3, C4, C5)}
+# The whole decoder at decode: group 1 (Full + 3 Reuse) followed by four
+# Reindex + 3 Reuse groups, each Reindex layer rescoring the pool of the Full
+# layer of the same step (20 layers).
+C6 = Workload("decoder_step_full_reindex4_b32_t65536", 6, batch=32, q_per_seq=1, kv_len=65536,
+              dim=512, heads=64, window=128, idx_heads=8, idx_dim=128, idx_range=8, w_max=8,
+              layers=("full", "reuse", "reuse", "reuse") + ("reindex", "reuse", "reuse", "reuse") * 4,
+              note="20-layer decoder step: Full group + 4 Reindex groups, batch 32, 64K entries")
+
+WORKLOADS = {w.name: w for w in (C1, C2, C3, C4, C5, C6)}
 
 
 def _rng(w: Workload, tensor: int, layer: int = 0, chunk: int = 0) -> np.random.Generator:

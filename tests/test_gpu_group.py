@@ -28,36 +28,46 @@ def check_group(w, sample=None):
     seqs = sorted({q // w.q_per_seq for q in qs})
     T = w.kv_len
     ik = {b: synth.index_k(w, b) for b in seqs}
-    rtopk = np.full((w.nq, 512), -1, dtype=np.int32)
-    got_pool, got_topk = host(g.pool), host(g.topk)
-    if w.layers[0] == "full":
-        iq, iw = synth.index_q(w), synth.index_w(w)
-        for q in qs:
-            pool, topk, _ = oidx.full_query(iq[q], iw[q], ik[q // w.q_per_seq], T)
-            rtopk[q] = _pad(topk, 512)
-            if not w.encoder:
-                np.testing.assert_array_equal(got_pool[q], _pad(pool, 2048))
-    else:
-        iq0, iw0 = synth.index_q(w, 0, pool_source=True), synth.index_w(w, 0, pool_source=True)
-        iq, iw = synth.index_q(w), synth.index_w(w)
-        for q in qs:
-            pool, _, _ = oidx.full_query(iq0[q], iw0[q], ik[q // w.q_per_seq], T)
+    got_pool = host(g.pool)
+    # the pool every Reindex layer rescores: the Full layer's of this step, or
+    # (for a sequence that starts with a Reindex layer) the earlier Full layer's
+    src = dict(pool_source=True) if w.layers[0] == "reindex" else {}
+    iq0, iw0 = synth.index_q(w, 0, **src), synth.index_w(w, 0, **src)
+    pools, full_topk = {}, {}
+    for q in qs:
+        pool, topk, _ = oidx.full_query(iq0[q], iw0[q], ik[q // w.q_per_seq], T)
+        pools[q], full_topk[q] = pool, topk
+        if not w.encoder:
             np.testing.assert_array_equal(got_pool[q], _pad(pool, 2048))
-            rtopk[q] = _pad(oidx.reindex_query(iq[q], iw[q], ik[q // w.q_per_seq], pool, T), 512)
+    # every indexing layer's Top-K, bit-exact
+    ref_topks = []
+    for k, l in enumerate(g.index_layers):
+        rt = np.full((w.nq, 512), -1, dtype=np.int32)
+        if w.layers[l] == "full":
+            for q in qs:
+                rt[q] = _pad(full_topk[q], 512)
+        else:
+            iq, iw = synth.index_q(w, l), synth.index_w(w, l)
+            for q in qs:
+                rt[q] = _pad(oidx.reindex_query(iq[q], iw[q], ik[q // w.q_per_seq], pools[q], T), 512)
+        np.testing.assert_array_equal(host(g.topks[k])[qs], rt[qs], err_msg=f"Top-K of layer {l}")
+        ref_topks.append(rt)
     del ik
-    np.testing.assert_array_equal(got_topk[qs], rtopk[qs])
-    if w.layers[0] == "full":            # the step's new FP4 rows (Full layers write their KV)
+    has_full = "full" in w.layers
+    if has_full:                         # the step's new FP4 rows (Full layers write their KV)
         n = w.new_per_seq
         for b in (0, w.batch - 1):
             rc, rs = oracle_kv_rows(w, b, np.arange(T - n, T), with_new_rows=True)
             np.testing.assert_array_equal(host(g.codes[b * T + T - n:b * T + T]), rc)
             np.testing.assert_array_equal(host(g.scales[b * T + T - n:b * T + T]), rs)
-    # every layer of the group attends over the same Top-K rows
-    rows = oracle_selected_rows(w, rtopk, qs, with_new_rows=(w.layers[0] == "full"))
-    for l in range(len(w.layers)):
+    # each layer attends over its indexing layer's Top-K rows
+    rows = [oracle_selected_rows(w, rt, qs, with_new_rows=has_full) for rt in ref_topks]
+    k = -1
+    for l, m in enumerate(w.layers):
+        k += m in ("full", "reindex")
         got = host(g.out[l])
-        ref = oracle_attention(w, synth.attn_q_bf16(w, l), synth.swa_bf16(w, l), rtopk,
-                               with_new_rows=(w.layers[0] == "full"), queries=qs, rows=rows)
+        ref = oracle_attention(w, synth.attn_q_bf16(w, l), synth.swa_bf16(w, l), ref_topks[k],
+                               with_new_rows=has_full, queries=qs, rows=rows[k])
         err = rownorm_err(got[qs], ref[qs])
         assert err <= ATTN_TOL, (l, err)
 
@@ -85,3 +95,10 @@ def test_group_verify_b8_q6_t1m():
     entries per sequence; the first and the last sequence are checked."""
     w = synth.C5
     check_group(w, sample=list(range(6)) + list(range(w.nq - 6, w.nq)))
+
+
+def test_decoder_step_full_reindex4_b32_t65536():
+    """The whole 20-layer decoder step: a Full group, then four Reindex groups
+    that rescore the Full layer's pool of the same step; every group's Top-K is
+    checked bit-exact and every layer's output on sampled queries."""
+    check_group(synth.C6, sample=[0, 7, 19, 31])
