@@ -508,11 +508,15 @@ __global__ __launch_bounds__(kSelThreads) void k_select_full(SelectParams p) {
 }
 
 // ============================================================== reindex
-// Score the pool positions of one query: grid (2048 / 256 slots, nq).
+constexpr int kRxSlotsPerWG = 64;
+// Score the pool positions of one query: grid (2048 / 64 slots, nq).  A
+// workgroup takes 64 pool slots (32 16-token tiles, two blocks each); each of
+// its waves loads the block ids of its 8 tiles, then issues all 8 tiles' key
+// gathers before the first MFMA, so 16 KiB per wave are in flight at once.
 template <int DI, int HI>
 __global__ __launch_bounds__(256) void k_reindex_score(ReindexParams p) {
   constexpr int KK = DI / 64;
-  constexpr int kSlotsPerWG = 256;
+  constexpr int TPW = kRxSlotsPerWG / 2 / 4;        // tiles per wave
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int64_t q = blockIdx.y;
@@ -520,6 +524,12 @@ __global__ __launch_bounds__(256) void k_reindex_score(ReindexParams p) {
   int64_t nv = p.nvis ? (int64_t)p.nvis[q] : p.T;
   nv = max((int64_t)0, min(nv, p.T));
   const int64_t nb = (nv + kBlock - 1) / kBlock;
+
+  const int32_t* pool = p.pool + q * kPoolBlocks;
+  const int slot0 = blockIdx.x * kRxSlotsPerWG + 2 * TPW * wave + (n >> 3);   // slot of tile u: slot0 + 2u
+  int32_t blk[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) blk[u] = pool[slot0 + 2 * u];
 
   v4i a[KK];
 #pragma unroll
@@ -533,24 +543,25 @@ __global__ __launch_bounds__(256) void k_reindex_score(ReindexParams p) {
   for (int i = 0; i < 4; ++i) wv[i] = (4 * g + i < HI) ? p.iw[q * HI + 4 * g + i] : 0.0f;
 
   const int8_t* ikb = p.ik + b * p.T * DI;
-  const int32_t* pool = p.pool + q * kPoolBlocks;
-  uint32_t* ck = p.ckeys + q * kPoolPositions;
-  const int slot0 = blockIdx.x * kSlotsPerWG;
-  for (int it = wave; it < kSlotsPerWG / 2; it += 4) {
-    const int slot = slot0 + 2 * it + (n >> 3);
-    const int32_t blk = pool[slot];
-    const int64_t pos = (int64_t)blk * kBlock + (n & 7);
-    const bool ok = blk >= 0 && (int64_t)blk < nb && pos < nv;
-    v4i bf[KK];
+  v4i bf[TPW][KK];
+  bool ok[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int64_t pos = (int64_t)blk[u] * kBlock + (n & 7);
+    ok[u] = blk[u] >= 0 && (int64_t)blk[u] < nb && pos < nv;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       v4i z = {0, 0, 0, 0};
-      if (ok) z = *reinterpret_cast<const v4i*>(ikb + pos * DI + g * 16 + kk * 64);
-      bf[kk] = z;
+      if (ok[u]) z = *reinterpret_cast<const v4i*>(ikb + pos * DI + g * 16 + kk * 64);
+      bf[u][kk] = z;
     }
+  }
+  uint32_t* ck = p.ckeys + q * kPoolPositions;
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
     v4i acc = {0, 0, 0, 0};
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[kk], bf[kk], acc, 0, 0, 0);
+    for (int kk = 0; kk < KK; ++kk) acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[kk], bf[u][kk], acc, 0, 0, 0);
     float val[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) val[i] = wv[i] * (float)max(acc[i], 0);
@@ -562,7 +573,7 @@ __global__ __launch_bounds__(256) void k_reindex_score(ReindexParams p) {
       if constexpr (HI >= 8) tot = sum_swap16(tot);
       if constexpr (HI >= 16) tot = sum_swap32(tot);
     }
-    if (g == 0) ck[slot * kBlock + (n & 7)] = ok ? score_key(tot) : 0u;
+    if (g == 0) ck[(slot0 + 2 * u) * kBlock + (n & 7)] = ok[u] ? score_key(tot) : 0u;
   }
 }
 
@@ -595,7 +606,7 @@ hipError_t launch_select_full(const SelectParams& p, int nq, int64_t max_blocks,
 
 hipError_t launch_reindex(const ReindexParams& p, int nq, int heads, int dim, hipStream_t st) {
   if (nq == 0) return hipSuccess;
-  const dim3 grid(kPoolBlocks / 256, nq);
+  const dim3 grid(kPoolBlocks / kRxSlotsPerWG, nq);
 #define CSA2_RX_CASE(D, H) if (dim == D && heads == H) { hipLaunchKernelGGL((k_reindex_score<D, H>), grid, dim3(256), 0, st, p); } else
   CSA2_RX_CASE(64, 2) CSA2_RX_CASE(64, 4) CSA2_RX_CASE(64, 8) CSA2_RX_CASE(64, 16)
   CSA2_RX_CASE(128, 2) CSA2_RX_CASE(128, 4) CSA2_RX_CASE(128, 8) CSA2_RX_CASE(128, 16)
