@@ -102,6 +102,7 @@ struct SelectParams {
   const uint32_t* bkeys; int64_t bk_stride;
   const int32_t* nvis; int64_t T;
   int32_t* pool; int32_t* topk;
+  int32_t roles;                                         // workgroups per query (set by the launcher)
 };
 struct ReindexParams {
   const int8_t* iq; const float* iw; const int8_t* ik; const int32_t* nvis;

@@ -340,7 +340,12 @@ template <int KPT1>
 __global__ __launch_bounds__(kSelThreads) void k_select_full(SelectParams p) {
   constexpr int KPT2 = kPoolPositions / kSelThreads;   // 16
   __shared__ SelShared sh;
-  const int64_t q = blockIdx.x;
+  // p.roles == 2: two workgroups per query, role 0 selects and writes the
+  // pool, role 1 the Top-512 (from the pruned candidates, or -- when those are
+  // too many -- through its own copy of the pool); p.roles == 1: one
+  // workgroup does both (role 2)
+  const int64_t q = p.roles == 2 ? (int64_t)(blockIdx.x >> 1) : (int64_t)blockIdx.x;
+  const int role = p.roles == 2 ? (int)(blockIdx.x & 1) : 2;
   // the histograms are cleared while the first keys are in flight
   int64_t nv = p.nvis ? (int64_t)p.nvis[q] : p.T;
   nv = max((int64_t)0, min(nv, p.T));
@@ -376,10 +381,10 @@ __global__ __launch_bounds__(kSelThreads) void k_select_full(SelectParams p) {
       // lie in the top 512 blocks, and those have keys >= thr.  When at most
       // one block per thread passes, their ids (ascending) go to sh.cand and
       // their token keys are gathered now, while the pool select finishes.
-      uint32_t mine = 0, ntot;
+      uint32_t mine = 0, ntot = 0xFFFFFFFFu;
 #pragma unroll
       for (int j = 0; j < KPT1; ++j) mine += bkey[j] >= thr ? 1u : 0u;     // thr >= kmin >= 1: key 0 fails
-      uint32_t o = block_excl_scan_total(mine, sh, ntot);
+      uint32_t o = role != 0 ? block_excl_scan_total(mine, sh, ntot) : 0u;
       if (ntot <= (uint32_t)kSelThreads) {
 #pragma unroll
         for (int j = 0; j < KPT1; ++j)
@@ -405,8 +410,12 @@ __global__ __launch_bounds__(kSelThreads) void k_select_full(SelectParams p) {
           for (int r = 0; r < kBlock; ++r) ckey[r] = ckey[r] >= kfloor ? ckey[r] : 0u;
         }
       }
-      radix_rest<KPT1>(get, st, sh, &sh.hist[0], tau, need);
-      compact_topk<KPT1>(get, tau, need, sh, [&](uint32_t o, int j) { sh.pool[o] = (int32_t)(base1 + j); });
+      // the pool: for its output (role 0, or role 2 with an output), or for
+      // the Top-512 select when the candidates were too many
+      if (role == 0 || (role == 2 && p.pool) || ncand < 0) {
+        radix_rest<KPT1>(get, st, sh, &sh.hist[0], tau, need);
+        compact_topk<KPT1>(get, tau, need, sh, [&](uint32_t o, int j) { sh.pool[o] = (int32_t)(base1 + j); });
+      }
     }
   } else {
     // More than 16 blocks per thread: rank super-blocks of 8 blocks by their
@@ -477,10 +486,15 @@ __global__ __launch_bounds__(kSelThreads) void k_select_full(SelectParams p) {
       for (int i = threadIdx.x; i < 3 * kDigitBins / 4; i += kSelThreads) hp[i] = u4{0u, 0u, 0u, 0u};
     }
   }
+  if (role == 1 && ncand >= 0) {              // ---- Top-512 of the candidates only
+    select_positions<kBlock>(ckey, sh, sh.cand, p.topk + q * kTopK);
+    return;
+  }
   for (int i = K1 + threadIdx.x; i < kPoolBlocks; i += kSelThreads) sh.pool[i] = -1;
   __syncthreads();
-  if (p.pool)
+  if (p.pool && role != 1)
     for (int i = threadIdx.x; i < kPoolBlocks; i += kSelThreads) p.pool[q * kPoolBlocks + i] = sh.pool[i];
+  if (role == 0) return;
 
   // ---- step 2: Top-512 positions of the candidate blocks, or of the pool
   if (ncand >= 0) {
@@ -595,12 +609,17 @@ __global__ __launch_bounds__(kSelThreads) void k_select_reindex(ReindexParams p)
 // ============================================================== launchers
 hipError_t launch_select_full(const SelectParams& p, int nq, int64_t max_blocks, hipStream_t st) {
   if (nq == 0) return hipSuccess;
-  if (max_blocks <= 8 * kSelThreads)
-    hipLaunchKernelGGL((k_select_full<8>), dim3(nq), dim3(kSelThreads), 0, st, p);
-  else if (max_blocks <= 128 * kSelThreads)
-    hipLaunchKernelGGL((k_select_full<128>), dim3(nq), dim3(kSelThreads), 0, st, p);
-  else
+  SelectParams pp = p;
+  if (max_blocks <= 8 * kSelThreads) {
+    // with a pool output, the pool and the Top-512 take one workgroup each
+    pp.roles = p.pool ? 2 : 1;
+    hipLaunchKernelGGL((k_select_full<8>), dim3((unsigned)(pp.roles * nq)), dim3(kSelThreads), 0, st, pp);
+  } else if (max_blocks <= 128 * kSelThreads) {
+    pp.roles = 1;
+    hipLaunchKernelGGL((k_select_full<128>), dim3(nq), dim3(kSelThreads), 0, st, pp);
+  } else {
     return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
