@@ -24,7 +24,7 @@ SCALE_GROUP = 16
 EXPORTS = (
     "csa2_status_string", "csa2_version", "csa2_quantize_kv", "csa2_dequantize_kv",
     "csa2_index_workspace_size", "csa2_index_full", "csa2_index_scan", "csa2_index_select",
-    "csa2_index_reindex",
+    "csa2_index_full_append", "csa2_index_select_append", "csa2_index_reindex",
     "csa2_attn_workspace_size", "csa2_sparse_attn",
 )
 
@@ -84,6 +84,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.csa2_index_scan.argtypes = [ctypes.POINTER(IndexArgs), vp, sz, vp]
     lib.csa2_index_select.restype = ctypes.c_int
     lib.csa2_index_select.argtypes = [ctypes.POINTER(IndexArgs), vp, vp, vp, sz, vp]
+    for name in ("csa2_index_full_append", "csa2_index_select_append"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [ctypes.POINTER(IndexArgs), vp, vp, vp, sz, vp, i64, i64, i32, vp, i64, vp, i64, vp]
     lib.csa2_index_reindex.restype = ctypes.c_int
     lib.csa2_index_reindex.argtypes = [ctypes.POINTER(IndexArgs), vp, vp, vp, sz, vp]
     lib.csa2_attn_workspace_size.restype = sz
@@ -157,6 +161,25 @@ def index_scan(args: IndexArgs, ws, stream=None) -> None:
 def index_select(args: IndexArgs, pool, topk, ws, stream=None) -> None:
     _check(load().csa2_index_select(ctypes.byref(args), _ptr(pool), _ptr(topk), _ptr(ws),
                                     ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def _append_args(x, codes, scales):
+    rows, dim = x.shape
+    return (_ptr(x), x.stride(0), rows, dim, _ptr(codes), codes.stride(0), _ptr(scales), scales.stride(0))
+
+
+def index_full_append(args: IndexArgs, pool, topk, ws, x, codes, scales, stream=None) -> None:
+    """index_full plus quantize_kv(x, codes, scales) of the step's new rows."""
+    _check(load().csa2_index_full_append(ctypes.byref(args), _ptr(pool), _ptr(topk), _ptr(ws),
+                                         ws.numel() * ws.element_size() if ws is not None else 0,
+                                         *_append_args(x, codes, scales), _stream(stream)))
+
+
+def index_select_append(args: IndexArgs, pool, topk, ws, x, codes, scales, stream=None) -> None:
+    """index_select plus quantize_kv(x, codes, scales) of the step's new rows."""
+    _check(load().csa2_index_select_append(ctypes.byref(args), _ptr(pool), _ptr(topk), _ptr(ws),
+                                           ws.numel() * ws.element_size() if ws is not None else 0,
+                                           *_append_args(x, codes, scales), _stream(stream)))
 
 
 def index_reindex(args: IndexArgs, pool, topk, ws, stream=None) -> None:

@@ -124,6 +124,47 @@ int check_attn(const csa2_attn_args* a) {
   return CSA2_OK;
 }
 
+int check_quantize(const float* x, int64_t x_stride, int64_t rows, int32_t dim, const uint8_t* codes,
+                   int64_t codes_stride, const uint8_t* scales, int64_t scales_stride) {
+  if (rows < 0 || dim < 32 || dim > 4096 || dim % 32) return CSA2_ERR_SHAPE;
+  if (rows == 0) return CSA2_OK;
+  if (!x || !codes || !scales) return CSA2_ERR_NULL;
+  if (x_stride < dim || codes_stride < dim / 2 || scales_stride < dim / 16) return CSA2_ERR_SHAPE;
+  if (!aligned(x, 16) || x_stride % 4 || !aligned(codes, 8) || codes_stride % 8) return CSA2_ERR_ALIGN;
+  return CSA2_OK;
+}
+
+// arguments of the selection stage (and of csa2_index_full before its scan)
+int check_select(const csa2_index_args* a, const int32_t* pool, const int32_t* topk, const void* ws,
+                 size_t ws_size) {
+  int st = check_index(a);
+  if (st != CSA2_OK) return st;
+  const IndexLayout L = index_layout(a);
+  if (L.nq == 0) return CSA2_OK;
+  if (!topk) return CSA2_ERR_NULL;
+  if (!aligned(a->n_visible, 4) || !aligned(pool, 4) || !aligned(topk, 4)) return CSA2_ERR_ALIGN;
+  if (!ws || ws_size < (size_t)L.total || !aligned(ws, 256)) return CSA2_ERR_WORKSPACE;
+  return CSA2_OK;
+}
+
+// the selection launch, with an optional quantisation job riding along;
+// arguments already checked
+int select_impl(const csa2_index_args* a, int32_t* pool, int32_t* topk, const void* ws, size_t ws_size,
+                const QuantJob& qj, hipStream_t stream) {
+  int st = check_select(a, pool, topk, ws, ws_size);
+  if (st != CSA2_OK) return st;
+  const IndexLayout L = index_layout(a);
+  if (L.nq == 0)
+    return qj.rows > 0 ? hip_status(launch_quantize(qj.x, qj.xs, qj.rows, 16 * qj.groups, qj.codes, qj.cs, qj.scales,
+                                                    qj.ss, stream))
+                       : CSA2_OK;
+  const uint32_t* tkeys = static_cast<const uint32_t*>(ws);
+  const uint32_t* bkeys = tkeys + L.nq * L.tk_stride;
+  SelectParams sel{tkeys, L.tk_stride, bkeys, L.bk_stride, a->n_visible, a->kv_len, pool, topk};
+  sel.qj = qj;
+  return hip_status(launch_select_full(sel, (int)L.nq, (a->kv_len + kBlock - 1) / kBlock, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -144,11 +185,8 @@ int csa2_version(void) { return (1 << 16) | 0; }
 
 int csa2_quantize_kv(const float* x, int64_t x_stride, int64_t rows, int32_t dim, uint8_t* codes,
                      int64_t codes_stride, uint8_t* scales, int64_t scales_stride, hipStream_t stream) {
-  if (rows < 0 || dim < 32 || dim > 4096 || dim % 32) return CSA2_ERR_SHAPE;
-  if (rows == 0) return CSA2_OK;
-  if (!x || !codes || !scales) return CSA2_ERR_NULL;
-  if (x_stride < dim || codes_stride < dim / 2 || scales_stride < dim / 16) return CSA2_ERR_SHAPE;
-  if (!aligned(x, 16) || x_stride % 4 || !aligned(codes, 8) || codes_stride % 8) return CSA2_ERR_ALIGN;
+  const int st = check_quantize(x, x_stride, rows, dim, codes, codes_stride, scales, scales_stride);
+  if (st != CSA2_OK || rows == 0) return st;
   return hip_status(launch_quantize(x, x_stride, rows, dim, codes, codes_stride, scales, scales_stride, stream));
 }
 
@@ -184,27 +222,41 @@ int csa2_index_scan(const csa2_index_args* a, void* ws, size_t ws_size, hipStrea
 
 int csa2_index_select(const csa2_index_args* a, int32_t* pool, int32_t* topk, const void* ws,
                       size_t ws_size, hipStream_t stream) {
-  int st = check_index(a);
-  if (st != CSA2_OK) return st;
-  const IndexLayout L = index_layout(a);
-  if (L.nq == 0) return CSA2_OK;
-  if (!topk) return CSA2_ERR_NULL;
-  if (!aligned(a->n_visible, 4) || !aligned(pool, 4) || !aligned(topk, 4)) return CSA2_ERR_ALIGN;
-  if (!ws || ws_size < (size_t)L.total || !aligned(ws, 256)) return CSA2_ERR_WORKSPACE;
-  const uint32_t* tkeys = static_cast<const uint32_t*>(ws);
-  const uint32_t* bkeys = tkeys + L.nq * L.tk_stride;
-  SelectParams sel{tkeys, L.tk_stride, bkeys, L.bk_stride, a->n_visible, a->kv_len, pool, topk};
-  return hip_status(launch_select_full(sel, (int)L.nq, (a->kv_len + kBlock - 1) / kBlock, stream));
+  return select_impl(a, pool, topk, ws, ws_size, QuantJob{}, stream);
 }
 
 int csa2_index_full(const csa2_index_args* a, int32_t* pool, int32_t* topk, void* ws, size_t ws_size,
                     hipStream_t stream) {
-  int st = check_index(a);
+  int st = check_select(a, pool, topk, ws, ws_size);
   if (st != CSA2_OK) return st;
-  if ((int64_t)a->batch * a->q_per_seq > 0 && !topk) return CSA2_ERR_NULL;
   st = csa2_index_scan(a, ws, ws_size, stream);
   if (st != CSA2_OK) return st;
-  return csa2_index_select(a, pool, topk, ws, ws_size, stream);
+  return select_impl(a, pool, topk, ws, ws_size, QuantJob{}, stream);
+}
+
+int csa2_index_select_append(const csa2_index_args* a, int32_t* pool, int32_t* topk, const void* ws,
+                             size_t ws_size, const float* x, int64_t x_stride, int64_t rows, int32_t dim,
+                             uint8_t* codes, int64_t codes_stride, uint8_t* scales, int64_t scales_stride,
+                             hipStream_t stream) {
+  int st = check_select(a, pool, topk, ws, ws_size);
+  if (st != CSA2_OK) return st;
+  st = check_quantize(x, x_stride, rows, dim, codes, codes_stride, scales, scales_stride);
+  if (st != CSA2_OK) return st;
+  const QuantJob qj{x, x_stride, rows, dim / 16, codes, codes_stride, scales, scales_stride};
+  return select_impl(a, pool, topk, ws, ws_size, qj, stream);
+}
+
+int csa2_index_full_append(const csa2_index_args* a, int32_t* pool, int32_t* topk, void* ws, size_t ws_size,
+                           const float* x, int64_t x_stride, int64_t rows, int32_t dim, uint8_t* codes,
+                           int64_t codes_stride, uint8_t* scales, int64_t scales_stride, hipStream_t stream) {
+  int st = check_select(a, pool, topk, ws, ws_size);
+  if (st != CSA2_OK) return st;
+  st = check_quantize(x, x_stride, rows, dim, codes, codes_stride, scales, scales_stride);
+  if (st != CSA2_OK) return st;
+  st = csa2_index_scan(a, ws, ws_size, stream);
+  if (st != CSA2_OK) return st;
+  const QuantJob qj{x, x_stride, rows, dim / 16, codes, codes_stride, scales, scales_stride};
+  return select_impl(a, pool, topk, ws, ws_size, qj, stream);
 }
 
 int csa2_index_reindex(const csa2_index_args* a, const int32_t* pool, int32_t* topk, void* ws,

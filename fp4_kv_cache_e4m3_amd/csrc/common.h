@@ -97,12 +97,19 @@ struct ScanParams {
   uint32_t* tkeys; int64_t tk_stride;                    // [nq, tk_stride]
   uint32_t* bkeys; int64_t bk_stride;                    // [nq, bk_stride]
 };
+// FP4 quantisation of `rows` main-KV rows of `groups` 16-channel groups
+struct QuantJob {
+  const float* x; int64_t xs, rows; int32_t groups;
+  uint8_t* codes; int64_t cs; uint8_t* scales; int64_t ss;
+};
 struct SelectParams {
   const uint32_t* tkeys; int64_t tk_stride;
   const uint32_t* bkeys; int64_t bk_stride;
   const int32_t* nvis; int64_t T;
   int32_t* pool; int32_t* topk;
   int32_t roles;                                         // workgroups per query (set by the launcher)
+  int32_t sel_wgs;                                       // selection workgroups (set by the launcher)
+  QuantJob qj;                                           // rows == 0: none
 };
 struct ReindexParams {
   const int8_t* iq; const float* iw; const int8_t* ik; const int32_t* nvis;
@@ -122,6 +129,7 @@ struct AttnParams {
 
 hipError_t launch_quantize(const float* x, int64_t xs, int64_t rows, int dim, uint8_t* codes,
                            int64_t cs, uint8_t* scales, int64_t ss, hipStream_t st);
+bool quantize_fits_quad(int64_t rows, int dim);           // small enough for four lanes per group
 hipError_t launch_dequantize(const uint8_t* codes, int64_t cs, const uint8_t* scales, int64_t ss,
                              int64_t rows, int dim, float* out, int64_t os, hipStream_t st);
 hipError_t launch_index_scan(const ScanParams& p, int heads, int dim, hipStream_t st);

@@ -1,0 +1,100 @@
+// Device-side FP4 (E2M1 + E4M3 per 16 channels) quantisation of main-KV rows,
+// shared by the quantise kernels and the fused Full-selection launch.
+// Method and exactness argument: see quant.hip's header (DeepSeek-V4.1-Flash
+// pages, ai-maestro.online, "FP4 KV, Bounded Replay, and other extensions").
+#pragma once
+
+#include "common.h"
+
+namespace csa2 {
+
+// launches of at most this many 16-channel groups use four lanes per group
+constexpr int64_t kQuantQuadMaxGroups = 8192;
+
+// value of non-negative finite E4M3 code c (0..126) as fp32 (exact)
+CSA2_DEV float e4m3_pos(uint32_t c) {
+  const uint32_t e = c >> 3, m = c & 7u;
+  return e == 0 ? (float)m * 0x1p-9f : __builtin_ldexpf((float)(8u + m), (int)e - 10);
+}
+
+// E4M3 code of amax/6: nearest, ties to even, saturating at 448 (0x7E).
+// The code is n = #{c in 0..125 : 6 * mu_c < amax} for the midpoints mu_c
+// between grid values c and c + 1, raised to the even neighbour on a tie.
+// An fp32 estimate y' of amax/6 (relative error ~2^-23, against a grid
+// spacing of at least 1/16) has grid floor ce within one code of the true
+// floor f, and n is f or f + 1; so every c <= ce - 2 counts, every
+// c >= ce + 2 does not, and only mu_{ce-2} .. mu_{ce+1} are compared, each
+// exactly (6 * mu is exact in fp32).
+CSA2_DEV uint32_t scale_code(float amax) {
+  const float yp = amax * (1.0f / 6.0f);
+  int ce;
+  if (!(yp < 448.0f)) ce = 126;
+  else if (yp < 0x1p-6f) ce = (int)(yp * 512.0f);                // subnormal grid, step 2^-9
+  else ce = ((int)((__float_as_uint(yp) >> 23) & 0xFFu) - 120) * 8 + (int)((__float_as_uint(yp) >> 20) & 7u);
+  const int base = ce - 2;
+  int n = base;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int c = base + k;
+    const bool below = c < 0 ? true
+                     : c > 125 ? false
+                               : 3.0f * (e4m3_pos((uint32_t)c) + e4m3_pos((uint32_t)c + 1)) < amax;   // 6 * mu_c, exact
+    n += below ? 1 : 0;
+  }
+  uint32_t c = (uint32_t)n;
+  if (c < 126u) {
+    const float t = 3.0f * (e4m3_pos(c) + e4m3_pos(c + 1));
+    if (t == amax && (c & 1u)) c += 1;                             // tie -> even code
+  }
+  return c;
+}
+
+// E2M1 code of x / s for s > 0: nearest, ties to even, saturating at 6.
+CSA2_DEV uint32_t element_code(float x, float s) {
+  const float a = fabsf(x);
+  const float mids[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
+  uint32_t cnt = 0;
+  bool tie = false;
+#pragma unroll
+  for (int j = 0; j < 7; ++j) {
+    const float t = mids[j] * s;                                   // exact
+    cnt += (t < a) ? 1u : 0u;
+    tie |= (t == a);
+  }
+  const uint32_t mag = cnt + ((tie && (cnt & 1u)) ? 1u : 0u);
+  return mag | ((__float_as_uint(x) >> 28) & 8u);
+}
+
+// One thread per 16-channel group (bulk: every lane's VALU work is its own).
+// Thread gid of a four-lanes-per-group quantisation of `rows` rows of
+// `groups` 16-channel groups (the lanes of a group are four consecutive
+// lanes of one wave; threads past the job return).  Used by the small-launch
+// kernel here and by the extra workgroups of the Full selection launch.
+CSA2_DEV void quantize_quad_thread(const float* __restrict__ x, int64_t xs, int64_t rows, int groups,
+                                   uint8_t* __restrict__ codes, int64_t cs, uint8_t* __restrict__ scales,
+                                   int64_t ss, int64_t gid) {
+  if (gid >= rows * groups * 4) return;            // whole quads: the count is a multiple of 4
+  const int64_t grp = gid >> 2;
+  const int qtr = (int)(gid & 3);
+  const int64_t r = grp / groups;
+  const int g = (int)(grp - r * groups);
+  const float4 f = *reinterpret_cast<const float4*>(x + r * xs + 16 * g + 4 * qtr);
+  const float v[4] = {f.x, f.y, f.z, f.w};
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(amax), 0xB1, 0xF, 0xF, false)));  // xor 1
+  amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(amax), 0x4E, 0xF, 0xF, false)));  // xor 2
+  const uint32_t sc = scale_code(amax);
+  const float s = e4m3_pos(sc);
+  uint32_t bits = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t c = (s == 0.0f) ? ((__float_as_uint(v[i]) >> 28) & 8u) : element_code(v[i], s);
+    bits |= c << (4 * i);
+  }
+  *reinterpret_cast<uint16_t*>(codes + r * cs + 8 * g + 2 * qtr) = (uint16_t)bits;
+  if (qtr == 0) scales[r * ss + g] = (uint8_t)sc;
+}
+
+}  // namespace csa2

@@ -21,7 +21,7 @@
 //    token keys are gathered while the pool select finishes.
 //  * Reindex: the scan's MFMA scoring on gathered pool blocks (2 blocks = one
 //    16-token tile), then the same selection.
-#include "common.h"
+#include "quant_dev.h"
 
 namespace csa2 {
 
@@ -340,6 +340,12 @@ template <int KPT1>
 __global__ __launch_bounds__(kSelThreads) void k_select_full(SelectParams p) {
   constexpr int KPT2 = kPoolPositions / kSelThreads;   // 16
   __shared__ SelShared sh;
+  // workgroups past the selection quantise the step's new main-KV rows
+  if ((int)blockIdx.x >= p.sel_wgs) {
+    quantize_quad_thread(p.qj.x, p.qj.xs, p.qj.rows, p.qj.groups, p.qj.codes, p.qj.cs, p.qj.scales, p.qj.ss,
+                         (int64_t)(blockIdx.x - p.sel_wgs) * kSelThreads + threadIdx.x);
+    return;
+  }
   // p.roles == 2: two workgroups per query, role 0 selects and writes the
   // pool, role 1 the Top-512 (from the pruned candidates, or -- when those are
   // too many -- through its own copy of the pool); p.roles == 1: one
@@ -610,16 +616,30 @@ __global__ __launch_bounds__(kSelThreads) void k_select_reindex(ReindexParams p)
 hipError_t launch_select_full(const SelectParams& p, int nq, int64_t max_blocks, hipStream_t st) {
   if (nq == 0) return hipSuccess;
   SelectParams pp = p;
-  if (max_blocks <= 8 * kSelThreads) {
-    // with a pool output, the pool and the Top-512 take one workgroup each
-    pp.roles = p.pool ? 2 : 1;
-    hipLaunchKernelGGL((k_select_full<8>), dim3((unsigned)(pp.roles * nq)), dim3(kSelThreads), 0, st, pp);
-  } else if (max_blocks <= 128 * kSelThreads) {
-    pp.roles = 1;
-    hipLaunchKernelGGL((k_select_full<128>), dim3(nq), dim3(kSelThreads), 0, st, pp);
-  } else {
-    return hipErrorInvalidValue;
+  // with a pool output, the pool and the Top-512 take one workgroup each (up
+  // to 8,192 blocks); a small quantisation job rides along as extra
+  // workgroups (four lanes per 16-channel group), a larger one is launched
+  // first on its own
+  if (max_blocks > 128 * kSelThreads) return hipErrorInvalidValue;
+  pp.roles = (max_blocks <= 8 * kSelThreads && p.pool) ? 2 : 1;
+  pp.sel_wgs = pp.roles * nq;
+  int extra = 0;
+  if (p.qj.rows > 0) {
+    if (quantize_fits_quad(p.qj.rows, 16 * p.qj.groups)) {
+      extra = (int)((4 * p.qj.rows * p.qj.groups + kSelThreads - 1) / kSelThreads);
+    } else {
+      const hipError_t e = launch_quantize(p.qj.x, p.qj.xs, p.qj.rows, 16 * p.qj.groups, p.qj.codes, p.qj.cs,
+                                           p.qj.scales, p.qj.ss, st);
+      if (e != hipSuccess) return e;
+    }
   }
+  const dim3 grid((unsigned)(pp.sel_wgs + extra));
+  if (max_blocks <= 8 * kSelThreads)
+    hipLaunchKernelGGL((k_select_full<8>), grid, dim3(kSelThreads), 0, st, pp);
+  else if (max_blocks <= 128 * kSelThreads)
+    hipLaunchKernelGGL((k_select_full<128>), grid, dim3(kSelThreads), 0, st, pp);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -126,7 +126,19 @@ class DecodeGroup:
         split_full), reindex, attention."""
         out = []
         for l, m in enumerate(self.w.layers):
-            if m == "full":
+            if m == "full" and len(self._new_calls) == 1:
+                # one strided job: the new rows are quantised by the Full
+                # layer's selection launch itself
+                ia, tk = self.iargs_by_layer[l], self._topk_of[l]
+                x, c, sc = self._new_calls[0]
+                if split_full:
+                    out.append(("index_scan", lambda ia=ia: B.index_scan(ia, self.iws, stream)))
+                    out.append(("index_select", lambda ia=ia, tk=tk: B.index_select_append(
+                        ia, self.pool_out(), tk, self.iws, x, c, sc, stream)))
+                else:
+                    out.append(("index_full", lambda ia=ia, tk=tk: B.index_full_append(
+                        ia, self.pool_out(), tk, self.iws, x, c, sc, stream)))
+            elif m == "full":
                 ia, tk = self.iargs_by_layer[l], self._topk_of[l]
                 out.append(("quantize", lambda: self.quantize_new(stream)))
                 if split_full:

@@ -157,6 +157,32 @@ int csa2_index_select(const csa2_index_args* args, int32_t* pool, int32_t* topk,
                       const void* ws, size_t ws_size, hipStream_t stream);
 
 /*
+ * csa2_index_full_append / csa2_index_select_append -- csa2_index_full
+ * (resp. csa2_index_select) together with csa2_quantize_kv of the step's new
+ * main-KV rows (x, x_stride, rows, dim, codes, codes_stride, scales,
+ * scales_stride: exactly as csa2_quantize_kv).  A Full layer writes its own
+ * entries into the FP4 cache as it indexes (ai-maestro.online, "FP4 KV,
+ * Bounded Replay, and other extensions": quantisation happens where the KV
+ * is written); the rows are independent of the indexer, so a small job
+ * (rows * dim / 16 <= 8,192 groups) runs as extra workgroups of the
+ * selection launch instead of a launch of its own; a larger one is launched
+ * before the selection.  Results are identical to the separate calls.  All
+ * arguments are validated before anything is launched; on error nothing is
+ * written.  The new rows must not be read by anything the call itself reads
+ * (the indexer never reads the main KV).
+ */
+int csa2_index_full_append(const csa2_index_args* args, int32_t* pool, int32_t* topk,
+                           void* ws, size_t ws_size,
+                           const float* x, int64_t x_stride, int64_t rows, int32_t dim,
+                           uint8_t* codes, int64_t codes_stride, uint8_t* scales, int64_t scales_stride,
+                           hipStream_t stream);
+int csa2_index_select_append(const csa2_index_args* args, int32_t* pool, int32_t* topk,
+                             const void* ws, size_t ws_size,
+                             const float* x, int64_t x_stride, int64_t rows, int32_t dim,
+                             uint8_t* codes, int64_t codes_stride, uint8_t* scales, int64_t scales_stride,
+                             hipStream_t stream);
+
+/*
  * csa2_index_reindex -- Reindex layer: rescore only the positions of the last
  * Full layer's pool with this layer's own iq / iw and select the top
  * min(512, #positions) by (score desc, position asc).

@@ -68,6 +68,21 @@ def test_index_rejects(lib):
     assert lib.csa2_index_workspace_size(ctypes.byref(a)) == 0
 
 
+def test_index_append_rejects(lib):
+    """The fused index + new-row quantisation calls validate both parts
+    before launching anything."""
+    import fp4_kv_cache_e4m3_amd as m
+    a = m.IndexArgs(1, 1, 100, 8, 64, 16, 16, 16, None)
+    ws = lib.csa2_index_workspace_size(ctypes.byref(a))
+    for f in (lib.csa2_index_full_append, lib.csa2_index_select_append):
+        assert f(ctypes.byref(a), None, 16, 256, ws, 16, 512, 4, 33, 16, 256, 16, 32, None) == 2    # dim % 32
+        assert f(ctypes.byref(a), None, 16, 256, ws, None, 512, 4, 512, 16, 256, 16, 32, None) == 1  # NULL x
+        assert f(ctypes.byref(a), None, 16, 256, ws, 8, 512, 4, 512, 16, 256, 16, 32, None) == 3     # x misaligned
+        assert f(ctypes.byref(a), None, 16, 256, ws - 1, 16, 512, 4, 512, 16, 256, 16, 32, None) == 4  # workspace
+        bad = m.IndexArgs(1, 1, 100, 3, 64, 16, 16, 16, None)                                       # 3 heads
+        assert f(ctypes.byref(bad), None, 16, 256, ws, 16, 512, 4, 512, 16, 256, 16, 32, None) == 2
+
+
 def test_attn_rejects(lib):
     import fp4_kv_cache_e4m3_amd as m
 

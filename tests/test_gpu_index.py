@@ -165,3 +165,38 @@ def test_index_full_verify_1m_entries():
         rpool, rtopk = oidx.index_full(iq[sl], iw[sl], ik[b:b + 1], w.q_per_seq)
         np.testing.assert_array_equal(pool[sl], rpool)
         np.testing.assert_array_equal(topk[sl], rtopk)
+
+
+@pytest.mark.parametrize("rows,dim,split", [(32, 512, False), (32, 512, True), (300, 512, False), (7, 128, True)],
+                         ids=["32x512", "32x512-split", "300x512-own-launch", "7x128-split"])
+def test_index_append_matches_oracle(rows, dim, split):
+    """csa2_index_full_append / csa2_index_select_append: the Full indexer and
+    the FP4 quantisation of new main-KV rows in one call (small jobs ride in
+    the selection launch, 300 x 512 = 9,600 groups takes its own launch);
+    pool, Top-512, codes and scales bit-exact against the oracle, and rows of
+    the cache outside the job untouched."""
+    from oracle import quant as oquant
+    B, Qn, T = 3, 1, 5003
+    iq, iw, ik = inputs(77, B, Qn, T, 8, 128, 8, 8)
+    x = np.random.default_rng(78).standard_normal((rows, dim), dtype=np.float32)
+    rpool, rtopk = oidx.index_full(iq, iw, ik, Qn)
+    rc, rs = oquant.quantize_rows(x)
+    iq_d, iw_d, ik_d = dev(iq), dev(iw), dev(ik)
+    pool = torch.full((B * Qn, 2048), -7, dtype=torch.int32, device="cuda")
+    topk = torch.full((B * Qn, 512), -7, dtype=torch.int32, device="cuda")
+    # the job writes every other row of a larger cache (strided rows)
+    codes = torch.full((2 * rows, dim // 2), 0xA5, dtype=torch.uint8, device="cuda")
+    scales = torch.full((2 * rows, dim // 16), 0x5A, dtype=torch.uint8, device="cuda")
+    args = csa2.index_args(iq_d, iw_d, ik_d, Qn)
+    ws = torch.empty(max(256, csa2.index_workspace_size(args)), dtype=torch.uint8, device="cuda")
+    if split:
+        csa2.index_scan(args, ws)
+        csa2.index_select_append(args, pool, topk, ws, dev(x), codes[::2], scales[::2])
+    else:
+        csa2.index_full_append(args, pool, topk, ws, dev(x), codes[::2], scales[::2])
+    np.testing.assert_array_equal(host(pool), rpool)
+    np.testing.assert_array_equal(host(topk), rtopk)
+    got_c, got_s = host(codes), host(scales)
+    np.testing.assert_array_equal(got_c[::2], rc)
+    np.testing.assert_array_equal(got_s[::2], rs)
+    assert (got_c[1::2] == 0xA5).all() and (got_s[1::2] == 0x5A).all()
