@@ -122,8 +122,8 @@ def cpu_baseline(w, max_queries: int, min_seconds: float = 10.0) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="decode_group_full_reuse3_b32_t65536")
     ap.add_argument("--cpu-queries", type=int, default=32, help="query tokens in the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")

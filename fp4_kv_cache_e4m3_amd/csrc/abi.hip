@@ -39,7 +39,7 @@ IndexLayout index_layout(const csa2_index_args* a) {
   L.tk_stride = round_up(a->kv_len, 16);
   L.bk_stride = round_up((a->kv_len + kBlock - 1) / kBlock, 16);
   L.full_bytes = L.nq * (L.tk_stride + L.bk_stride) * 4;
-  L.reindex_bytes = L.nq * kPoolPositions * 4;
+  L.reindex_bytes = L.nq * (kPoolPositions + kPoolBlocks) * 4;     // position keys + block keys
   L.total = round_up(L.full_bytes > L.reindex_bytes ? L.full_bytes : L.reindex_bytes, 256);
   return L;
 }
@@ -269,7 +269,8 @@ int csa2_index_reindex(const csa2_index_args* a, const int32_t* pool, int32_t* t
   if (!aligned(a->n_visible, 4) || !aligned(pool, 4)) return CSA2_ERR_ALIGN;
   if (!ws || ws_size < (size_t)L.total || !aligned(ws, 256)) return CSA2_ERR_WORKSPACE;
   ReindexParams rp{a->q, a->w, a->k, a->n_visible, pool, a->q_per_seq, a->kv_len,
-                   static_cast<uint32_t*>(ws), topk};
+                   static_cast<uint32_t*>(ws), topk,
+                   static_cast<uint32_t*>(ws) + L.nq * kPoolPositions};
   return hip_status(launch_reindex(rp, (int)L.nq, a->heads, a->dim, stream));
 }
 

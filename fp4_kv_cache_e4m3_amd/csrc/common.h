@@ -116,6 +116,7 @@ struct ReindexParams {
   const int32_t* pool; int32_t qn; int64_t T;
   uint32_t* ckeys;                                       // [nq, 16384]
   int32_t* topk;
+  uint32_t* bkeys;                                       // [nq, 2048]: max key of each pool block
 };
 struct AttnParams {
   const uint16_t* q; const uint8_t* codes; const uint8_t* scales;

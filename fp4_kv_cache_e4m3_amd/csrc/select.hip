@@ -593,22 +593,75 @@ __global__ __launch_bounds__(256) void k_reindex_score(ReindexParams p) {
       if constexpr (HI >= 8) tot = sum_swap16(tot);
       if constexpr (HI >= 16) tot = sum_swap32(tot);
     }
-    if (g == 0) ck[(slot0 + 2 * u) * kBlock + (n & 7)] = ok[u] ? score_key(tot) : 0u;
+    const uint32_t key = ok[u] ? score_key(tot) : 0u;
+    // the block's maximum: 8 lanes of each half of the 16-lane row
+    uint32_t m = key;
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false));   // xor 1
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, false));   // xor 2
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x141, 0xF, 0xF, false));  // half-row mirror
+    if (g == 0) {
+      ck[(slot0 + 2 * u) * kBlock + (n & 7)] = key;
+      if ((n & 7) == 0) p.bkeys[q * kPoolBlocks + slot0 + 2 * u] = m;
+    }
   }
 }
 
+// Top-512 of the rescored pool.  As in the Full select, the Top-512 positions
+// lie in the top 512 pool blocks (by block maximum, ties to the lower block),
+// so the blocks at or above the first radix digit of the 512th block key are
+// the candidates; with at least 512 non-empty blocks, a position whose key is
+// below that digit's floor is outranked 512 times and leaves too.  When more
+// than 1,024 blocks pass, all 16,384 pool positions are selected from.
 __global__ __launch_bounds__(kSelThreads) void k_select_reindex(ReindexParams p) {
   constexpr int KPT2 = kPoolPositions / kSelThreads;
+  constexpr int BPT = kPoolBlocks / kSelThreads;       // 2 pool slots per thread
   __shared__ SelShared sh;
   const int64_t q = blockIdx.x;
-  // the candidate keys go out first; the histograms are cleared meanwhile
+  // the block keys go out first; the histograms are cleared meanwhile
+  const u2 bv = *reinterpret_cast<const u2*>(p.bkeys + q * kPoolBlocks + BPT * threadIdx.x);
+  const uint32_t bkey[BPT] = {bv[0], bv[1]};
+  hists_clear(sh);
+  for (int i = threadIdx.x; i < kPoolBlocks; i += kSelThreads) sh.pool[i] = p.pool[q * kPoolBlocks + i];
+  __syncthreads();
+  auto get = [&](int j) { return bkey[j]; };
+  uint32_t kmin, kmax, nblk;
+  key_stats<BPT>(get, sh, kmin, kmax, nblk);
+  if (nblk > 0) {
+    uint32_t unused;
+    const uint32_t kx = min(nblk, (uint32_t)kTopK);
+    const RadixState st = radix_first<BPT>(get, kx, kmin, kmax, sh, &sh.hist[0], 0u, unused);
+    const uint32_t thr = kmin + (st.d1 << st.s1);      // floor of the kx-th block key's first digit
+    uint32_t mine = 0, ntot;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) mine += bkey[j] >= thr ? 1u : 0u;
+    uint32_t o = block_excl_scan_total(mine, sh, ntot);
+    if (ntot <= (uint32_t)kSelThreads) {
+#pragma unroll
+      for (int j = 0; j < BPT; ++j)
+        if (bkey[j] >= thr) {
+          sh.cand[o] = BPT * (int)threadIdx.x + j;        // pool slot
+          sh.sbpool[o] = sh.pool[BPT * threadIdx.x + j];  // its block id
+          ++o;
+        }
+      __syncthreads();
+      uint32_t ckey[kBlock] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+      if (threadIdx.x < ntot) {
+        const u4* kp = reinterpret_cast<const u4*>(p.ckeys + q * kPoolPositions + (int64_t)sh.cand[threadIdx.x] * kBlock);
+        const u4 v0 = kp[0], v1 = kp[1];
+        const uint32_t kfloor = nblk >= (uint32_t)kTopK ? thr : 1u;
+        ckey[0] = v0[0]; ckey[1] = v0[1]; ckey[2] = v0[2]; ckey[3] = v0[3];
+        ckey[4] = v1[0]; ckey[5] = v1[1]; ckey[6] = v1[2]; ckey[7] = v1[3];
+#pragma unroll
+        for (int r = 0; r < kBlock; ++r) ckey[r] = ckey[r] >= kfloor ? ckey[r] : 0u;
+      }
+      select_positions<kBlock>(ckey, sh, sh.sbpool, p.topk + q * kTopK);
+      return;
+    }
+  }
   uint32_t key[KPT2];
   const int base = threadIdx.x * KPT2;
 #pragma unroll
   for (int j = 0; j < KPT2; ++j) key[j] = p.ckeys[q * kPoolPositions + base + j];
-  hists_clear(sh);
-  for (int i = threadIdx.x; i < kPoolBlocks; i += kSelThreads) sh.pool[i] = p.pool[q * kPoolBlocks + i];
-  __syncthreads();
   select_positions<KPT2>(key, sh, sh.pool, p.topk + q * kTopK);
 }
 

@@ -140,7 +140,12 @@ def test_index_reindex_batch32_t65536(c2_inputs):
     np.testing.assert_array_equal(run_reindex(iq0, iw0, ik, 1, rpool), rtopk0)
 
 
-@pytest.mark.parametrize("case", CASES[3:7], ids=lambda c: "B{}Q{}T{}H{}D{}".format(*c[:5]))
+# Reindex cases: ragged shapes, heavy ties, all-equal scores (every pool block
+# a candidate: the 16,384-position select), 1,024 candidate blocks exactly
+REINDEX_CASES = CASES[3:7] + [(2, 1, 33000, 8, 64, 0, 1), (1, 1, 8192, 2, 64, 0, 1), (2, 1, 12000, 2, 64, 1, 1)]
+
+
+@pytest.mark.parametrize("case", REINDEX_CASES, ids=lambda c: "B{}Q{}T{}H{}D{}r{}".format(*c[:6]))
 def test_index_reindex_matches_oracle(case):
     B, Qn, T, HI, DI, r, wmax = case
     iq, iw, ik = inputs(hash(case) % 997, B, Qn, T, HI, DI, r, wmax)
