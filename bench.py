@@ -29,8 +29,8 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak (AMD spec)
 # WRITE_SIZE (each scaled by what the counter reads for a plain 1 GiB copy) on
 # the workload and kernel source named here; reported only while both match.
 SCAN_TRAFFIC = {"workload": "decode_group_full_reuse3_b32_t65536",
-                "source_sha256": "82fce35254e1886e46bae805cd39825651b06a0452e2421581fb5b567565930e",
-                "bytes": 268847053 + 9610724}
+                "source_sha256": "553252fd2831abb26431b767fecf7a3b76411e0126791be4828a075cb17ca511",
+                "bytes": 268847234 + 9437842}
 
 
 def scan_traffic(w):

@@ -143,6 +143,11 @@ __global__ __launch_bounds__(256) void k_index_scan(ScanParams p) {
   // lane, hit 16 distinct bank groups per 16 lanes.  All U tiles are issued
   // before the first MFMA.
   constexpr int U = 4;
+  // The keys are read once per step and never again within it: non-temporal
+  // loads (cache policy NT) stream them past the last-level cache, so the
+  // step's other working set (the attention's window rows and gathered FP4
+  // rows, which decode re-reads from one step to the next) stays resident.
+  constexpr int kNonTemporal = 2;
   constexpr int CPR = DI / 16;                 // 16-byte chunks per key row
   constexpr int RPI = 1024 / DI;               // rows per 1 KiB load instruction
   constexpr int NI = 16 * DI / 1024;           // load instructions per 16-row tile
@@ -160,7 +165,7 @@ __global__ __launch_bounds__(256) void k_index_scan(ScanParams p) {
         const int64_t row = t < tend ? t : 0;
         __builtin_amdgcn_global_load_lds(ikb + row * DI + c * 16,
                                          (__attribute__((address_space(3))) void*)(mybuf + u * 16 * DI + i * 1024),
-                                         16, 0, 0);
+                                         16, 0, kNonTemporal);
       }
     }
     // s_waitcnt vmcnt(0) (expcnt, lgkmcnt left at their maximum): the tiles
