@@ -53,14 +53,17 @@ int env_int(const char* name, int dflt) {
 
 // Work split of one attention layer.  A workgroup owns (query, 16 heads, one
 // column half of the output channels, a contiguous range of 16-entry tiles);
-// its NW waves take every NW-th tile.  With few workgroups, 8 waves (two per
-// SIMD) keep the whole tile list in one workgroup; with many, 4.  Splits of
+// its NW waves take every NW-th tile.  When the grid fits one workgroup per
+// CU (<= 256), 8 waves (two per SIMD) keep the whole tile list in one
+// workgroup; otherwise 4-wave workgroups (two per CU) avoid a second wave of
+// 8-wave workgroups (384 workgroups at 48 queries: 121 vs 140 us for four
+// layers).  Splits of
 // the tile list over workgroups are used only when the grid would otherwise
 // leave most CUs idle; their partial states are merged by a second kernel.
 // CSA2_ATTN_WAVES / CSA2_ATTN_SPLITS override the choice (tuning).
 void attn_plan(int64_t nq, int heads, int n_tiles, int& waves, int& splits) {
   const int64_t base = 2 * nq * ((heads + 15) / 16);
-  waves = env_int("CSA2_ATTN_WAVES", base <= 1024 ? 8 : 4);
+  waves = env_int("CSA2_ATTN_WAVES", base <= 256 ? 8 : 4);
   if (waves != 4 && waves != 8) waves = 4;
   int dflt = 1;
   if (base > 0 && base < 128) {            // fewer than half the CUs busy: split
