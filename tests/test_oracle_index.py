@@ -121,3 +121,30 @@ def test_n_visible_limits_positions():
     bpool, btop = brute_full(iq[0], iw[0], ik[0], 1234)
     assert list(topk[0][topk[0] >= 0]) == btop
     assert np.all(topk[1] == -1) and np.all(pool[1] == -1)
+
+
+@pytest.mark.parametrize("seed,T,r", [(0, 40000, 2), (1, 40000, 1), (2, 6000, 0), (3, 4500, 3), (4, 3000, 1)])
+def test_top512_lies_in_top512_blocks(seed, T, r):
+    """The pruning the GPU selection uses, checked on the oracle's scores: the
+    Top-512 positions lie in the top min(512, #blocks) blocks (by block max,
+    ties to the lower block), and when there are at least 512 blocks every
+    selected score is >= the 512th block score, so candidates below it can be
+    dropped.  (T = 3000 and 4500 have fewer than 512 blocks but more than 512
+    positions; r = 0 makes every score equal.)"""
+    rng = np.random.default_rng(300 + seed)
+    iq, iw, ik = _inputs(rng, T, 8, 16, r, 3)
+    _, topk, s = indexer.full_query(iq[0], iw[0], ik[0], T)
+    bs = indexer.block_scores(s, T)
+    nb = len(bs)
+    k = min(512, nb)
+    top_blocks = indexer.top_ids(bs, np.arange(nb), k)
+    assert set((topk // 8).tolist()) <= set(top_blocks.tolist())
+    if nb >= 512:
+        kth = np.sort(bs)[::-1][511]                 # the 512th block score
+        assert s[topk].min() >= kth
+    # the pruned candidate set gives the same Top-512 as the full pool
+    cand = (top_blocks[:, None] * 8 + np.arange(8)[None, :]).reshape(-1)
+    cand = cand[cand < T]
+    if nb >= 512:
+        cand = cand[s[cand] >= np.sort(bs)[::-1][511]]
+    np.testing.assert_array_equal(indexer.top_ids(s[cand], cand, min(512, len(cand))), topk)
