@@ -17,13 +17,16 @@ What it computes, and where the pages say so (DeepSeek-V4.1-Flash pages):
   blocks as the candidate pool, Top-512 positions) and the Reindex layer's
   rescoring of the pool (ai-maestro.online, "Compressed Sparse Attention 2";
   wpnews.pro "What is Compressed Sparse Attention 2 CSA2?").
+* ``swa8``     -- the 8-bit sliding-window cache rows (E4M3 codes, one
+  power-of-two scale per row; kongchang.com "Three Core Innovations": the
+  window keeps 8-bit precision).
 * ``attention`` -- sparse attention over the selected entries merged with the
   layer's 128-token sliding window in one softmax (ai-maestro.online, "Causal
   Encoder-Decoder architecture" for the window, "Compressed Sparse
   Attention 2" for the per-layer Q and SWA).
 
 Each reading of a point the pages leave open is stated next to the code that
-takes it, numbered R1..R25.
+takes it, numbered R1..R28.
 
 Pins (tests/test_oracle_*.py, run with ``-m "not gpu"``): bit-field decoders
 against torch's float8_e4m3fn cast and the E2M1 value fixture; the quantiser
@@ -32,4 +35,4 @@ indexer against pure-Python brute force and the pool invariant; attention
 against closed forms and torch's float64 scaled_dot_product_attention.
 No function here is "parity unpinned".
 """
-from . import formats, quant, indexer, attention  # noqa: F401
+from . import formats, quant, indexer, attention, swa8  # noqa: F401
