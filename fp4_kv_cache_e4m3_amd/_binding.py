@@ -22,7 +22,7 @@ WINDOW = 128
 SCALE_GROUP = 16
 
 EXPORTS = (
-    "csa2_status_string", "csa2_version", "csa2_quantize_kv", "csa2_dequantize_kv",
+    "csa2_status_string", "csa2_version", "csa2_quantize_kv", "csa2_quantize_swa_fp8", "csa2_dequantize_kv",
     "csa2_index_workspace_size", "csa2_index_full", "csa2_index_scan", "csa2_index_select",
     "csa2_index_full_append", "csa2_index_select_append", "csa2_index_reindex",
     "csa2_attn_workspace_size", "csa2_sparse_attn",
@@ -54,6 +54,7 @@ class AttnArgs(ctypes.Structure):
         ("swa_len", ctypes.c_void_p),
         ("sm_scale", ctypes.c_float),
         ("out", ctypes.c_void_p),
+        ("swa_fp8", ctypes.c_int32), ("swa_scale", ctypes.c_void_p),
     ]
 
 
@@ -74,6 +75,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.csa2_version.restype = ctypes.c_int
     lib.csa2_quantize_kv.restype = ctypes.c_int
     lib.csa2_quantize_kv.argtypes = [vp, i64, i64, i32, vp, i64, vp, i64, vp]
+    lib.csa2_quantize_swa_fp8.restype = ctypes.c_int
+    lib.csa2_quantize_swa_fp8.argtypes = [vp, i64, i64, i32, vp, i64, vp, vp]
     lib.csa2_dequantize_kv.restype = ctypes.c_int
     lib.csa2_dequantize_kv.argtypes = [vp, i64, vp, i64, i64, i32, vp, i64, vp]
     lib.csa2_index_workspace_size.restype = sz
@@ -128,6 +131,14 @@ def quantize_kv(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, stre
     rows, dim = x.shape
     _check(load().csa2_quantize_kv(_ptr(x), x.stride(0), rows, dim, _ptr(codes), codes.stride(0),
                                    _ptr(scales), scales.stride(0), _stream(stream)))
+
+
+def quantize_swa_fp8(x: torch.Tensor, out: torch.Tensor, scales: torch.Tensor, stream=None) -> None:
+    """8-bit window rows: bf16 bits x [rows, d] (int16/uint16 storage) -> E4M3
+    codes out [rows, >=d] (uint8) and power-of-two row scales [rows] (fp32)."""
+    rows, dim = x.shape
+    _check(load().csa2_quantize_swa_fp8(_ptr(x), x.stride(0), rows, dim, _ptr(out), out.stride(0), _ptr(scales),
+                                        _stream(stream)))
 
 
 def dequantize_kv(codes: torch.Tensor, scales: torch.Tensor, out: torch.Tensor, stream=None) -> None:
@@ -190,15 +201,17 @@ def index_reindex(args: IndexArgs, pool, topk, ws, stream=None) -> None:
 
 # ------------------------------------------------------------------ attention
 def attn_args(q, codes, scales, topk, swa, out, q_per_seq: int, kv_len: int, window: int = WINDOW,
-              swa_len=None, sm_scale: float = 0.0) -> AttnArgs:
+              swa_len=None, sm_scale: float = 0.0, swa_scale=None) -> AttnArgs:
     """q bf16-as-int16/uint16 [nq, H, d]; codes [B*T, >=d/2]; scales [B*T, >=d/16];
-    topk int32 [nq, k]; swa bf16 [B, window-1+Qn, d]; out fp32 [nq, H, d]."""
+    topk int32 [nq, k]; swa bf16 [B, window-1+Qn, d] -- or, with swa_scale
+    (fp32 [B, window-1+Qn]), E4M3 codes uint8 [B, window-1+Qn, d]; out fp32 [nq, H, d]."""
     nq, heads, dim = q.shape
     return AttnArgs(nq // q_per_seq, q_per_seq, kv_len, heads, dim, _ptr(q),
                     _ptr(codes), codes.stride(0) if codes is not None else dim // 2,
                     _ptr(scales), scales.stride(0) if scales is not None else dim // 16,
                     _ptr(topk), topk.shape[1] if topk is not None else 0,
-                    _ptr(swa), window, _ptr(swa_len), float(sm_scale), _ptr(out))
+                    _ptr(swa), window, _ptr(swa_len), float(sm_scale), _ptr(out),
+                    1 if swa_scale is not None else 0, _ptr(swa_scale))
 
 
 def attn_workspace_size(args: AttnArgs) -> int:

@@ -113,6 +113,9 @@ int check_attn(const csa2_attn_args* a) {
   if (!a->q || !a->out) return CSA2_ERR_NULL;
   if (a->kv_len > 0 && a->topk_k > 0 && (!a->codes || !a->scales || !a->topk)) return CSA2_ERR_NULL;
   if (a->window > 0 && !a->swa) return CSA2_ERR_NULL;
+  if (a->swa_fp8 != 0 && a->swa_fp8 != 1) return CSA2_ERR_SHAPE;
+  if (a->swa_fp8 && a->window > 0 && !a->swa_scale) return CSA2_ERR_NULL;
+  if (a->swa_fp8 && !aligned(a->swa_scale, 4)) return CSA2_ERR_ALIGN;
   if (a->codes_stride < a->dim / 2 || a->scales_stride < a->dim / 16) return CSA2_ERR_SHAPE;
   // one sequence's rows are addressed through 32-bit buffer offsets (24-bit
   // row multiplies)
@@ -191,6 +194,17 @@ int csa2_quantize_kv(const float* x, int64_t x_stride, int64_t rows, int32_t dim
   const int st = check_quantize(x, x_stride, rows, dim, codes, codes_stride, scales, scales_stride);
   if (st != CSA2_OK || rows == 0) return st;
   return hip_status(launch_quantize(x, x_stride, rows, dim, codes, codes_stride, scales, scales_stride, stream));
+}
+
+int csa2_quantize_swa_fp8(const uint16_t* x, int64_t x_stride, int64_t rows, int32_t dim, uint8_t* out,
+                          int64_t out_stride, float* scales, hipStream_t stream) {
+  if (rows < 0 || dim < 8 || dim > 512 || dim % 8) return CSA2_ERR_SHAPE;
+  if (rows == 0) return CSA2_OK;
+  if (!x || !out || !scales) return CSA2_ERR_NULL;
+  if (x_stride < dim || out_stride < dim) return CSA2_ERR_SHAPE;
+  if (!aligned(x, 16) || x_stride % 8 || !aligned(out, 8) || out_stride % 8 || !aligned(scales, 4))
+    return CSA2_ERR_ALIGN;
+  return hip_status(launch_quantize_swa8(x, x_stride, rows, dim, out, out_stride, scales, stream));
 }
 
 int csa2_dequantize_kv(const uint8_t* codes, int64_t codes_stride, const uint8_t* scales,
@@ -305,6 +319,8 @@ int csa2_sparse_attn(const csa2_attn_args* a, void* ws, size_t ws_size, hipStrea
   p.n_sparse_tiles = L.n_sparse_tiles; p.n_tiles = L.n_tiles;
   const float sm = a->sm_scale > 0.0f ? a->sm_scale : 1.0f / std::sqrt((float)a->dim);
   p.qscale = sm * 1.4426950408889634f;
+  p.swa_fp8 = a->swa_fp8;
+  p.swa_scale = a->swa_scale;
   // With no tile at all the kernel still runs: every head ends with an empty
   // softmax and writes zeros (no memset node, so the call stays graph-safe).
   return hip_status(launch_attn(p, (int)L.nq, a->dim, L.waves, stream));

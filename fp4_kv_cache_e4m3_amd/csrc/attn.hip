@@ -128,6 +128,27 @@ struct InterMap {
   static constexpr int off(int j) { return 32 * j; }
 };
 
+// 8-bit window rows ("pairs"): k-steps 2i and 2i+1 of lane g hold the 16
+// consecutive channels 64i + 16g .. +15 of the half, so one 16-byte load
+// covers two k-steps and the 4 lanes of a row read 64 contiguous bytes.
+template <int D>
+struct Fp8Map {
+  static constexpr int LANE = 16;
+  static constexpr int off(int j) { return 64 * (j / 2) + 8 * (j % 2); }
+};
+
+// Eight E4M3 window codes (two dwords, channel order) times the row's
+// power-of-two scale, as fp16: the gfx950 scaled FP8 -> fp16 conversion
+// applies the power of two itself; E4M3 values times 2^k are exact in fp16
+// for k in [-15, 7] (row maxima from about 0.014 to 57,344).
+CSA2_DEV v8h fp8x8_to_half(uint32_t w0, uint32_t w1, float sc) {
+  const v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, sc, false);
+  const v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, sc, true);
+  const v2h c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, sc, false);
+  const v2h d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, sc, true);
+  return v8h{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
 // FP4 data of one entry for this lane (RunsMap): code words w[h][j] of k-step
 // j and the scale words as loaded (D = 512: one word per run; D = 128: one
 // word for both runs, in s[h][0]); index h = 0 is the workgroup's own half.
@@ -274,7 +295,9 @@ CSA2_DEV void attend_tile(const AttnParams& p, KV kvf, ST stage, AfterQK after_q
   wave_lds_sync();
 }
 
-template <int D, int NW>
+// S8: the window rows are 8-bit (E4M3 codes + a power-of-two scale per row)
+// instead of bf16
+template <int D, int NW, bool S8>
 __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
   using G = Geo<D>;
   constexpr int KH = G::KH, NT = G::NT, PITCH = G::PITCH, HALF = G::HALF;
@@ -414,23 +437,39 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
   };
 
   const int swa_first = tile0 + NW * n_fp4;          // the wave's first window tile
-  // ---- window rows (bf16), read through a buffer over this sequence's
-  // window (rows outside it read zeros); w holds one 16-row tile
+  // ---- window rows (bf16, or 8-bit codes with a scale per row), read
+  // through a buffer over this sequence's window (rows outside it read
+  // zeros); w holds one 16-row tile
+  constexpr uint32_t kSwaBytes = S8 ? 1u : 2u;      // per channel
   u4 w[2][KH];
   bool swa_valid = false;
-  const rsrc_t swa_buf = make_rsrc(p.swa + (int64_t)b * p.swa_rows * D, (uint32_t)(p.swa_rows * D * 2));
-  const uint32_t swa_lane = 2u * InterMap<D>::LANE * g;
+  uint32_t swa_sc = 0;                               // S8: the lane's row scale (fp32 bits)
+  uint32_t swa_so = kOob;                            // S8: byte offset of that scale
+  const rsrc_t swa_buf = make_rsrc(reinterpret_cast<const uint8_t*>(p.swa) + (int64_t)b * p.swa_rows * D * kSwaBytes,
+                                   (uint32_t)(p.swa_rows * D * kSwaBytes));
+  const rsrc_t swa_sbuf = make_rsrc(S8 ? p.swa_scale + (int64_t)b * p.swa_rows : nullptr,
+                                    S8 ? (uint32_t)(p.swa_rows * 4) : 0u);
+  const uint32_t swa_lane = S8 ? (uint32_t)(Fp8Map<D>::LANE * g) : 2u * InterMap<D>::LANE * g;
   auto swa_rows = [&](int t) {                      // this lane's row offset of window tile t
     const int wr = (t - p.n_sparse_tiles) * 16 + n;
     const int r = j + wr;
     swa_valid = t < t_end && wr >= 0 && wr < p.window && r >= first_swa && r < p.swa_rows;
-    return (swa_valid ? (uint32_t)r * (2u * D) : kOob) + swa_lane;
+    swa_so = swa_valid ? 4u * (uint32_t)r : kOob;
+    return (swa_valid ? (uint32_t)r * (kSwaBytes * D) : kOob) + swa_lane;
   };
   auto load_swa_half = [&](uint32_t ro, int hh) {
+    if constexpr (S8) {
 #pragma unroll
-    for (int k = 0; k < KH; ++k)
-      w[hh][k] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(swa_buf, ro + 2 * InterMap<D>::off(k),
-                                                                           __builtin_amdgcn_readfirstlane(2 * hb[hh]), 0));
+      for (int i = 0; i < KH / 2; ++i)
+        w[hh][i] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              swa_buf, ro + 64u * i, __builtin_amdgcn_readfirstlane(hb[hh]), 0));
+      if (hh == 0) swa_sc = __builtin_amdgcn_raw_buffer_load_b32(swa_sbuf, swa_so, 0, 0);
+    } else {
+#pragma unroll
+      for (int k = 0; k < KH; ++k)
+        w[hh][k] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(swa_buf, ro + 2 * InterMap<D>::off(k),
+                                                                             __builtin_amdgcn_readfirstlane(2 * hb[hh]), 0));
+    }
   };
   auto load_swa = [&](int t) {
     const uint32_t ro = swa_rows(t);
@@ -489,7 +528,24 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
   // QK runs on the bf16 rows and the bf16 Q as they are; only the own half
   // becomes fp16 (exactly, inside fp16's range) for PV.  Rows outside the
   // window read as zeros and their logits are masked.
-  if (swa_first < t_end) {
+  if constexpr (S8) {
+    // 8-bit rows: decoded to fp16 (exact) with the row's scale and contracted
+    // like the FP4 rows, against the own half of Q reloaded in this map
+    if (swa_first < t_end) {
+      if (n_fp4 == 0) load_swa(swa_first);
+      load_qf(Fp8Map<D>{});
+      _Float16* wrow = my + n * PITCH + Fp8Map<D>::LANE * g;
+      for (int t = swa_first; t < t_end; t += NW) {
+        const bool v = swa_valid;
+        const float sc = __uint_as_float(swa_sc);
+        attend_tile<D, Fp8Map<D>, v8h>(
+            p, [&](int hh, int k) { return fp8x8_to_half(w[hh][k / 2][2 * (k % 2)], w[hh][k / 2][2 * (k % 2) + 1], sc); },
+            [](v8h kv) { return kv; }, [&] { load_swa(t + NW); }, v, qf,
+            reinterpret_cast<const uint16_t*>(qs + n * QPITCH + hb[1] + Fp8Map<D>::LANE * g), wrow, vbase, g, o,
+            m_run, l_run);
+      }
+    }
+  } else if (swa_first < t_end) {
     if (n_fp4 == 0) load_swa(swa_first);
     v8bf qfb[KH];
 #pragma unroll
@@ -604,7 +660,8 @@ hipError_t launch_attn(const AttnParams& p, int nq, int dim, int waves, hipStrea
   const dim3 grid((unsigned)(16 * ngroups), (unsigned)((nq + 7) / 8), (unsigned)p.splits);
 #define CSA2_ATTN_CASE(D, NW)                                                                 \
   if (dim == D && waves == NW) {                                                              \
-    hipLaunchKernelGGL((k_attn<D, NW>), grid, dim3(64 * NW), 0, st, p);                       \
+    if (p.swa_fp8) hipLaunchKernelGGL((k_attn<D, NW, true>), grid, dim3(64 * NW), 0, st, p);  \
+    else hipLaunchKernelGGL((k_attn<D, NW, false>), grid, dim3(64 * NW), 0, st, p);           \
     if (p.splits > 1) hipLaunchKernelGGL(k_attn_combine<D>, dim3(nq * p.heads), dim3(D / 4), 0, st, p); \
     return hipGetLastError();                                                                 \
   }

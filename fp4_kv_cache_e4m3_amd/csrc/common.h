@@ -126,11 +126,15 @@ struct AttnParams {
   int32_t qn, heads, topk_k, window, swa_rows, splits, tiles_per_split, n_sparse_tiles, n_tiles;
   int32_t qn_shift;                                      // log2(qn) when qn is a power of two, else -1
   float qscale;                                          // sm_scale * log2(e)
+  int32_t swa_fp8;                                       // window rows: 0 bf16, 1 E4M3 codes + row scales
+  const float* swa_scale;                                // [B, swa_rows] powers of two (swa_fp8)
 };
 
 hipError_t launch_quantize(const float* x, int64_t xs, int64_t rows, int dim, uint8_t* codes,
                            int64_t cs, uint8_t* scales, int64_t ss, hipStream_t st);
 bool quantize_fits_quad(int64_t rows, int dim);           // small enough for four lanes per group
+hipError_t launch_quantize_swa8(const uint16_t* x, int64_t xs, int64_t rows, int dim, uint8_t* out, int64_t os,
+                                float* scales, hipStream_t st);
 hipError_t launch_dequantize(const uint8_t* codes, int64_t cs, const uint8_t* scales, int64_t ss,
                              int64_t rows, int dim, float* out, int64_t os, hipStream_t st);
 hipError_t launch_index_scan(const ScanParams& p, int heads, int dim, hipStream_t st);

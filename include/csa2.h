@@ -91,6 +91,26 @@ int csa2_quantize_kv(const float* x, int64_t x_stride, int64_t rows, int32_t dim
                      uint8_t* scales, int64_t scales_stride, hipStream_t stream);
 
 /*
+ * csa2_quantize_swa_fp8 -- 8-bit sliding-window rows.
+ * Source: kongchang.com, "Three Core Innovations" (the window keeps 8-bit
+ * precision); the format is not given on the pages.  Each bf16 row r < rows
+ * of dim channels becomes E4M3FN codes with one power-of-two scale:
+ *   scale = 2^k, k the smallest integer with max|x| <= 448 * 2^k (1 for an
+ *   all-zero row);  code_i = E4M3(|x_i| / scale) to nearest, ties to the
+ *   even code, sign bit = sign bit of x_i.
+ * The division is exact and the rounding is decided exactly.
+ *   x       bf16 bits, row r at x + r * x_stride (elements); 16-byte aligned,
+ *           x_stride % 8 == 0.
+ *   dim     % 8 == 0, 8 .. 512.
+ *   out     E4M3 codes, row r at out + r * out_stride (bytes); 8-byte aligned,
+ *           out_stride % 8 == 0, out_stride >= dim.
+ *   scales  fp32 [rows], 4-byte aligned.
+ * csa2_sparse_attn reads such rows as its window when swa_fp8 is set.
+ */
+int csa2_quantize_swa_fp8(const uint16_t* x, int64_t x_stride, int64_t rows, int32_t dim,
+                          uint8_t* out, int64_t out_stride, float* scales, hipStream_t stream);
+
+/*
  * csa2_dequantize_kv -- values of FP4 rows as fp32 (code value x E4M3 scale,
  * exact).  Same row layout and alignment as csa2_quantize_kv; out is fp32
  * [rows, dim] at out + r * out_stride (elements), 16-byte aligned,
@@ -232,6 +252,13 @@ typedef struct {
   const int32_t* swa_len;      /* [B] valid trailing SWA rows, or NULL (= all) */
   float sm_scale;              /* <= 0 selects 1/sqrt(d)                       */
   float* out;                  /* fp32 [nq, H, d]                              */
+  int32_t swa_fp8;             /* 0: swa is bf16 as above.  1: swa holds E4M3
+                                  codes [B, swa_rows, d] (bytes; rows as written
+                                  by csa2_quantize_swa_fp8) and swa_scale their
+                                  row scales; a window value is E4M3(code) *
+                                  scale, exact in fp16 when every row scale is
+                                  in [2^-15, 2^7]                              */
+  const float* swa_scale;      /* fp32 [B, swa_rows] powers of two (swa_fp8)   */
 } csa2_attn_args;
 
 /* Bytes of workspace csa2_sparse_attn needs for these arguments (may be 0). */

@@ -20,7 +20,7 @@ def lib():
 def header_functions():
     text = open(os.path.join(ROOT, "include", "csa2.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(csa2_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(csa2_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol(lib):
@@ -45,6 +45,17 @@ def test_quantize_rejects(lib):
     assert f(16, 512, 4, 512, 16, 100, 16, 32, None) == 2                 # codes stride < d/2
     assert f(8, 512, 4, 512, 16, 256, 16, 32, None) == 3                  # x misaligned
     assert f(None, 512, 0, 512, None, 256, None, 32, None) == 0           # empty: no-op
+
+
+def test_quantize_swa_fp8_rejects(lib):
+    f = lib.csa2_quantize_swa_fp8
+    assert f(16, 512, 4, 12, 16, 512, 16, None) == 2                       # dim % 8
+    assert f(16, 1024, 4, 1024, 16, 1024, 16, None) == 2                   # dim > 512
+    assert f(None, 512, 4, 512, 16, 512, 16, None) == 1                    # NULL x
+    assert f(16, 512, 4, 512, 16, 256, 16, None) == 2                      # out stride < dim
+    assert f(8, 512, 4, 512, 16, 512, 16, None) == 3                       # x misaligned
+    assert f(16, 512, 4, 512, 16, 512, 18, None) == 3                      # scales misaligned
+    assert f(None, 512, 0, 512, None, 512, None, None) == 0                # empty: no-op
 
 
 def test_index_rejects(lib):
