@@ -51,7 +51,7 @@ def group_bytes(w) -> dict:
     select = nq * ((0 if w.encoder else 2048 * 4) + 512 * 4)   # pool (decoder groups) + topk written
     quant = w.batch * w.new_per_seq * (w.dim * 4 + row)
     attn_layer = (nq * (512 * row + w.heads * w.dim * 2 + w.heads * w.dim * 4 + 512 * 4)
-                  + w.batch * w.swa_rows * w.dim * 2)
+                  + w.batch * w.swa_rows * (w.dim + 4 if w.swa8 else w.dim * 2))
     reindex = nq * (2048 * 4 + 16384 * w.idx_dim + w.idx_heads * (w.idx_dim + 4) + 512 * 4)
     n_full, n_rx = w.layers.count("full"), w.layers.count("reindex")
     total = n_full * (quant + scan + select) + n_rx * reindex + len(w.layers) * attn_layer
@@ -83,6 +83,9 @@ def cpu_baseline(w, max_queries: int, min_seconds: float = 10.0) -> dict:
           for l in range(len(w.layers))]
     sws = [synth.bf16_bits_to_f32(synth.swa_bf16(w, l)[:n_seq]).astype(np.float64)
            for l in range(len(w.layers))]
+    if w.swa8:                                          # the window as its 8-bit rows hold it
+        from oracle import swa8 as oswa8
+        sws = [oswa8.swa_values(*oswa8.quantize_swa_rows(s.reshape(-1, w.dim))).reshape(s.shape) for s in sws]
     srcs = [synth.kv_source(w, b) for b in range(n_seq)]
     rx = {l: (synth.index_q(w, l)[:nqs], synth.index_w(w, l)[:nqs])
           for l, m in enumerate(w.layers) if m == "reindex" and l > 0}

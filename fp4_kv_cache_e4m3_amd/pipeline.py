@@ -69,6 +69,14 @@ class DecodeGroup:
             self._iqw[l] = (_dev(synth.index_q(w, l), dev), _dev(synth.index_w(w, l), dev))
         self.q = [_dev(synth.attn_q_bf16(w, l).view(np.int16), dev) for l in range(nl)]
         self.swa = [_dev(synth.swa_bf16(w, l).view(np.int16), dev) for l in range(nl)]
+        # 8-bit window rows: quantised once on the device from the bf16 rows
+        self.swa_scale = [None] * nl
+        if w.swa8:
+            for l in range(nl):
+                codes8 = torch.empty((B_, w.swa_rows, d), dtype=torch.uint8, device=dev)
+                sc8 = torch.empty((B_, w.swa_rows), dtype=torch.float32, device=dev)
+                B.quantize_swa_fp8(self.swa[l].view(B_ * w.swa_rows, d), codes8.view(B_ * w.swa_rows, d), sc8.view(-1))
+                self.swa[l], self.swa_scale[l] = codes8, sc8
         # ---- outputs and workspaces
         nq = w.nq
         self.pool = torch.full((nq, B.POOL_BLOCKS), -1, dtype=torch.int32, device=dev)
@@ -85,7 +93,7 @@ class DecodeGroup:
             k += m in ("full", "reindex")
             self._topk_of.append(self.topks[k])
         self.aargs = [B.attn_args(self.q[l], self.codes, self.scales, self._topk_of[l], self.swa[l], self.out[l],
-                                  w.q_per_seq, T, w.window) for l in range(nl)]
+                                  w.q_per_seq, T, w.window, swa_scale=self.swa_scale[l]) for l in range(nl)]
         aws = max(B.attn_workspace_size(a) for a in self.aargs)
         self.aws = torch.empty(max(256, aws), dtype=torch.uint8, device=dev) if aws > 0 else None
         # a step's new entries land in the last new_per_seq slots of each

@@ -64,6 +64,7 @@ class Workload:
     layers: tuple = ("full",)  # CSA2 layer modes of the group
     ratio: int = 1           # tokens per compressed entry
     encoder: bool = False    # encoder (prefill) group: no Reindex layer consumes the pool
+    swa8: bool = False       # window rows kept as 8-bit codes (quantised from the same bf16 rows)
     note: str = ""
 
     @property
@@ -114,7 +115,11 @@ C6 = Workload("decoder_step_full_reindex4_b32_t65536", 6, batch=32, q_per_seq=1,
               layers=("full", "reuse", "reuse", "reuse") + ("reindex", "reuse", "reuse", "reuse") * 4,
               note="20-layer decoder step: Full group + 4 Reindex groups, batch 32, 64K entries")
 
-WORKLOADS = {w.name: w for w in (C1, C2, C3, C4, C5, C6)}
+# decoder group 1 with the sliding window kept in 8 bits (same seeds as C2)
+C2_SWA8 = C2.replace(name="decode_group_full_reuse3_b32_t65536_swa8", swa8=True,
+                     note="decoder group 1 with 8-bit (E4M3 + row scale) window rows")
+
+WORKLOADS = {w.name: w for w in (C1, C2, C3, C4, C5, C6, C2_SWA8)}
 
 
 def _rng(w: Workload, tensor: int, layer: int = 0, chunk: int = 0) -> np.random.Generator:

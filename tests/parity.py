@@ -12,6 +12,7 @@ from fp4_kv_cache_e4m3_amd import synth
 from oracle import attention as oattn
 from oracle import indexer as oidx
 from oracle import quant as oquant
+from oracle import swa8 as oswa8
 
 ATTN_TOL = 2e-3     # max over (query, head) of max_c |O - O_ref| / max_c |O_ref|
 
@@ -96,6 +97,9 @@ def oracle_attention(w: synth.Workload, q_bits, swa_bits, topk, with_new_rows=Tr
     out = np.zeros((nq, w.heads, w.dim))
     qv = bf16_values(q_bits)
     sv = bf16_values(swa_bits)
+    if w.swa8:                           # the window as its 8-bit rows hold it
+        rc, rs = oswa8.quantize_swa_rows(sv.reshape(-1, w.dim))
+        sv = oswa8.swa_values(rc, rs).reshape(sv.shape)
     if rows is None:
         rows = oracle_selected_rows(w, topk, list(qsel), with_new_rows)
     for qi in qsel:

@@ -97,6 +97,12 @@ def test_group_verify_b8_q6_t1m():
     check_group(w, sample=list(range(6)) + list(range(w.nq - 6, w.nq)))
 
 
+def test_group_full_reuse3_batch32_t65536_swa8():
+    """Decoder group 1 with 8-bit window rows: indices as in the bf16 group,
+    attention against the oracle on the 8-bit rows' values."""
+    check_group(synth.C2_SWA8, sample=range(0, 32, 3))
+
+
 def test_decoder_step_full_reindex4_b32_t65536():
     """The whole 20-layer decoder step: a Full group, then four Reindex groups
     that rescore the Full layer's pool of the same step; every group's Top-K is
