@@ -15,7 +15,12 @@ tensor is drawn from a fixed distribution:
 * indexer q / k: integers uniform in [-r, r] (int8), head weights integers
   uniform in [1, w_max] stored as fp32 -- so every indexer score is an exact
   integer in fp32;
-* attention Q and SWA rows: N(0, 1) rounded to bf16 (round-to-nearest-even).
+* attention Q and SWA rows: N(0, 1) rounded to bf16 (round-to-nearest-even);
+* FP8 indexer (``idx_fp8``): q / k bytes are E4M3FN codes drawn uniformly
+  over the 96 codes of magnitude [0.25, 15] and either sign (a log-uniform
+  spread over six octaves), key scales one per position and query scales one
+  per (query, head), fp32 uniform in [1/32, 1/8), head weights fp32 uniform
+  in [-0.25, 1).
 
 Seeds: ``SeedSequence([0xC5A2, workload_id, tensor_id, layer, chunk])``.
 Large tensors are drawn in fixed-size row chunks so any chunk can be redrawn
@@ -41,6 +46,12 @@ T_SWA = 6         # sliding-window rows, bf16 (per layer)
 T_NEW = 7         # fp32 rows of the tokens appended this step
 T_IQ_POOL = 8     # indexer q of the Full layer that produced a Reindex pool
 T_IW_POOL = 9
+T_IK_SCALE = 10   # fp32 per-position scales of FP8 indexer keys
+T_IQ_SCALE = 11   # fp32 per-(query, head) scales of FP8 indexer queries (per layer)
+T_IQ_SCALE_POOL = 12
+
+# FP8 indexer codes: magnitude codes 0x28..0x57 (E4M3 values 0.25 .. 15), either sign
+_E4M3_LO, _E4M3_N = 0x28, 48
 
 KV_CHUNK_ROWS = 4096   # rows per independently seeded chunk of the KV source / ik
 
@@ -65,6 +76,7 @@ class Workload:
     ratio: int = 1           # tokens per compressed entry
     encoder: bool = False    # encoder (prefill) group: no Reindex layer consumes the pool
     swa8: bool = False       # window rows kept as 8-bit codes (quantised from the same bf16 rows)
+    idx_fp8: bool = False    # indexer q / k as E4M3 codes with fp32 scales instead of integers
     note: str = ""
 
     @property
@@ -119,7 +131,11 @@ C6 = Workload("decoder_step_full_reindex4_b32_t65536", 6, batch=32, q_per_seq=1,
 C2_SWA8 = C2.replace(name="decode_group_full_reuse3_b32_t65536_swa8", swa8=True,
                      note="decoder group 1 with 8-bit (E4M3 + row scale) window rows")
 
-WORKLOADS = {w.name: w for w in (C1, C2, C3, C4, C5, C6, C2_SWA8)}
+# decoder group 1 with a real-valued (E4M3 + fp32 scales) indexer
+C2_IDX8 = C2.replace(name="decode_group_full_reuse3_b32_t65536_idx8", wid=8, idx_fp8=True,
+                     note="decoder group 1 with FP8 indexer keys and queries")
+
+WORKLOADS = {w.name: w for w in (C1, C2, C3, C4, C5, C6, C2_SWA8, C2_IDX8)}
 
 
 def _rng(w: Workload, tensor: int, layer: int = 0, chunk: int = 0) -> np.random.Generator:
@@ -180,15 +196,28 @@ def new_rows(w: Workload, step: int = 0) -> np.ndarray:
     return _rng(w, T_NEW, step).standard_normal((w.batch * w.new_per_seq, w.dim), dtype=np.float32)
 
 
+def _e4m3_codes(g: np.random.Generator, size) -> np.ndarray:
+    v = g.integers(0, 2 * _E4M3_N, size=size, dtype=np.uint8)
+    return np.where(v < _E4M3_N, v + _E4M3_LO, (v - _E4M3_N + _E4M3_LO) | 0x80).astype(np.uint8)
+
+
+def _fp8_scales(g: np.random.Generator, size) -> np.ndarray:
+    return ((g.random(size, dtype=np.float32) + np.float32(1.0)) * np.float32(1.0 / 32)).astype(np.float32)
+
+
 def index_k_rows(w: Workload, b: int, row0: int, nrows: int) -> np.ndarray:
-    """int8 indexer keys of sequence b, rows [row0, row0+nrows), values in [-r, r]."""
-    out = np.empty((nrows, w.idx_dim), dtype=np.int8)
+    """Indexer keys of sequence b, rows [row0, row0+nrows): int8 in [-r, r], or
+    uint8 E4M3 codes for an FP8 indexer."""
+    out = np.empty((nrows, w.idx_dim), dtype=np.uint8 if w.idx_fp8 else np.int8)
     c0 = row0 // KV_CHUNK_ROWS
     c1 = (row0 + nrows - 1) // KV_CHUNK_ROWS if nrows else c0 - 1
     for c in range(c0, c1 + 1):
         rows = min(KV_CHUNK_ROWS, w.kv_len - c * KV_CHUNK_ROWS)
         g = _rng(w, T_IK, 0, b * 100003 + c)
-        chunk = g.integers(-w.idx_range, w.idx_range + 1, size=(rows, w.idx_dim), dtype=np.int8)
+        if w.idx_fp8:
+            chunk = _e4m3_codes(g, (rows, w.idx_dim))
+        else:
+            chunk = g.integers(-w.idx_range, w.idx_range + 1, size=(rows, w.idx_dim), dtype=np.int8)
         lo = max(row0, c * KV_CHUNK_ROWS)
         hi = min(row0 + nrows, c * KV_CHUNK_ROWS + rows)
         out[lo - row0:hi - row0] = chunk[lo - c * KV_CHUNK_ROWS:hi - c * KV_CHUNK_ROWS]
@@ -199,25 +228,47 @@ def index_k(w: Workload, b: int) -> np.ndarray:
     return index_k_rows(w, b, 0, w.kv_len)
 
 
+def index_k_scale(w: Workload, b: int) -> np.ndarray:
+    """[T] fp32 per-position scales of sequence b's FP8 indexer keys."""
+    return _fp8_scales(_rng(w, T_IK_SCALE, 0, b), w.kv_len)
+
+
+def index_k_scale_all(w: Workload) -> np.ndarray:
+    """[B, T] fp32."""
+    return np.stack([index_k_scale(w, b) for b in range(w.batch)])
+
+
 def index_k_all(w: Workload) -> np.ndarray:
-    """[B, T, D_I] int8."""
-    out = np.empty((w.batch, w.kv_len, w.idx_dim), dtype=np.int8)
+    """[B, T, D_I] int8 (uint8 E4M3 codes for an FP8 indexer)."""
+    out = np.empty((w.batch, w.kv_len, w.idx_dim), dtype=np.uint8 if w.idx_fp8 else np.int8)
     with ThreadPoolExecutor(_threads()) as ex:
         list(ex.map(lambda b: out.__setitem__(b, index_k(w, b)), range(w.batch)))
     return out
 
 
 def index_q(w: Workload, layer: int = 0, pool_source: bool = False) -> np.ndarray:
-    """[nq, H_I, D_I] int8 indexer queries of one layer."""
+    """[nq, H_I, D_I] indexer queries of one layer: int8, or uint8 E4M3 codes."""
     t = T_IQ_POOL if pool_source else T_IQ
-    return _rng(w, t, layer).integers(-w.idx_range, w.idx_range + 1,
-                                      size=(w.nq, w.idx_heads, w.idx_dim), dtype=np.int8)
+    g = _rng(w, t, layer)
+    if w.idx_fp8:
+        return _e4m3_codes(g, (w.nq, w.idx_heads, w.idx_dim))
+    return g.integers(-w.idx_range, w.idx_range + 1, size=(w.nq, w.idx_heads, w.idx_dim), dtype=np.int8)
+
+
+def index_q_scale(w: Workload, layer: int = 0, pool_source: bool = False) -> np.ndarray:
+    """[nq, H_I] fp32 scales of the FP8 indexer queries of one layer."""
+    t = T_IQ_SCALE_POOL if pool_source else T_IQ_SCALE
+    return _fp8_scales(_rng(w, t, layer), (w.nq, w.idx_heads))
 
 
 def index_w(w: Workload, layer: int = 0, pool_source: bool = False) -> np.ndarray:
-    """[nq, H_I] fp32 integer-valued head weights in [1, w_max]."""
+    """[nq, H_I] fp32 head weights: integers in [1, w_max], or uniform in
+    [-0.25, 1) for an FP8 indexer."""
     t = T_IW_POOL if pool_source else T_IW
-    return _rng(w, t, layer).integers(1, w.w_max + 1, size=(w.nq, w.idx_heads)).astype(np.float32)
+    g = _rng(w, t, layer)
+    if w.idx_fp8:
+        return (g.random((w.nq, w.idx_heads), dtype=np.float32) * np.float32(1.25) - np.float32(0.25)).astype(np.float32)
+    return g.integers(1, w.w_max + 1, size=(w.nq, w.idx_heads)).astype(np.float32)
 
 
 def attn_q_bf16(w: Workload, layer: int = 0) -> np.ndarray:
