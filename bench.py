@@ -29,15 +29,17 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak (AMD spec)
 # WRITE_SIZE (each scaled by what the counter reads for a plain 1 GiB copy) on
 # the workload and kernel source named here; reported only while both match.
 SCAN_TRAFFIC = {"workload": "decode_group_full_reuse3_b32_t65536",
-                "source_sha256": "553252fd2831abb26431b767fecf7a3b76411e0126791be4828a075cb17ca511",
-                "bytes": 268847234 + 9437842}
+                "source_sha256": "fea1cb9bd8dbdbe457ee78f4c684e9b0054e7a3074d15e8dc9f9b69495aedc6e",   # csrc/index.hip + csrc/common.h
+                "bytes": 268859802 + 9437901}
 
 
 def scan_traffic(w):
     import hashlib
-    src = os.path.join(ROOT, "fp4_kv_cache_e4m3_amd", "csrc", "index.hip")
-    with open(src, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for name in ("index.hip", "common.h"):                  # the scan kernel's sources
+        with open(os.path.join(ROOT, "fp4_kv_cache_e4m3_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    sha = h.hexdigest()
     if w.name == SCAN_TRAFFIC["workload"] and sha == SCAN_TRAFFIC["source_sha256"]:
         return SCAN_TRAFFIC["bytes"]
     return None
@@ -47,12 +49,13 @@ def group_bytes(w) -> dict:
     """Algorithmic bytes of one group step (what the method must move)."""
     nq, T = w.nq, w.kv_len
     row = w.dim // 2 + w.dim // 16                         # FP4 row: codes + scales
-    scan = w.batch * T * w.idx_dim + nq * w.idx_heads * (w.idx_dim + 4)
+    f8 = 4 if w.idx_fp8 else 0                             # fp32 scale per key position / query head
+    scan = w.batch * T * (w.idx_dim + f8) + nq * w.idx_heads * (w.idx_dim + 4 + f8)
     select = nq * ((0 if w.encoder else 2048 * 4) + 512 * 4)   # pool (decoder groups) + topk written
     quant = w.batch * w.new_per_seq * (w.dim * 4 + row)
     attn_layer = (nq * (512 * row + w.heads * w.dim * 2 + w.heads * w.dim * 4 + 512 * 4)
                   + w.batch * w.swa_rows * (w.dim + 4 if w.swa8 else w.dim * 2))
-    reindex = nq * (2048 * 4 + 16384 * w.idx_dim + w.idx_heads * (w.idx_dim + 4) + 512 * 4)
+    reindex = nq * (2048 * 4 + 16384 * (w.idx_dim + f8) + w.idx_heads * (w.idx_dim + 4 + f8) + 512 * 4)
     n_full, n_rx = w.layers.count("full"), w.layers.count("reindex")
     total = n_full * (quant + scan + select) + n_rx * reindex + len(w.layers) * attn_layer
     return dict(scan=scan, select=select, quant=quant, attn_layer=attn_layer, reindex=reindex,
@@ -87,21 +90,40 @@ def cpu_baseline(w, max_queries: int, min_seconds: float = 10.0) -> dict:
         from oracle import swa8 as oswa8
         sws = [oswa8.swa_values(*oswa8.quantize_swa_rows(s.reshape(-1, w.dim))).reshape(s.shape) for s in sws]
     srcs = [synth.kv_source(w, b) for b in range(n_seq)]
-    rx = {l: (synth.index_q(w, l)[:nqs], synth.index_w(w, l)[:nqs])
+    f8 = w.idx_fp8
+    qsc = (lambda l, src=False: synth.index_q_scale(w, l, src)[:nqs]) if f8 else (lambda l, src=False: None)
+    sq = qsc(0)
+    sk = [synth.index_k_scale(w, b) for b in range(n_seq)] if f8 else None
+    rx = {l: (synth.index_q(w, l)[:nqs], synth.index_w(w, l)[:nqs], qsc(l))
           for l, m in enumerate(w.layers) if m == "reindex" and l > 0}
     if w.layers[0] == "reindex":
-        rx[0] = (iq, iw)
+        rx[0] = (iq, iw, sq)
         iq, iw = synth.index_q(w, 0, pool_source=True)[:nqs], synth.index_w(w, 0, pool_source=True)[:nqs]
+        sq = qsc(0, True)
+    if f8:
+        from oracle import indexer_fp8 as o8
+
+        def full_q(qi, b):
+            return o8.full_query(iq[qi], sq[qi], iw[qi], ik[b], sk[b], T)
+
+        def rx_q(l, qi, b, pool):
+            return o8.reindex_query(rx[l][0][qi], rx[l][2][qi], rx[l][1][qi], ik[b], sk[b], pool, T)[0]
+    else:
+        def full_q(qi, b):
+            return oidx.full_query(iq[qi], iw[qi], ik[b], T)
+
+        def rx_q(l, qi, b, pool):
+            return oidx.reindex_query(rx[l][0][qi], rx[l][1][qi], ik[b], pool, T)
 
     def one_pass():
         if w.layers[0] == "full":
             oquant.quantize_rows(newr)
         for qi in range(nqs):
             b = qi // qn
-            pool, pos, _ = oidx.full_query(iq[qi], iw[qi], ik[b], T)
+            pool, pos, _ = full_q(qi, b)
             for l, m in enumerate(w.layers):
                 if m == "reindex":
-                    pos = oidx.reindex_query(rx[l][0][qi], rx[l][1][qi], ik[b], pool, T)
+                    pos = rx_q(l, qi, b, pool)
                 if m in ("full", "reindex"):
                     codes, scales = oquant.quantize_rows(srcs[b][pos])     # the selected cache rows
                 keys = oattn.query_entries(qi % qn, qn, len(pos), np.arange(len(pos)), codes, scales,
@@ -222,11 +244,13 @@ def main() -> int:
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp4e2m1+e4m3/int8/fp16-mfma",
-        "data": "synthetic (seeded numpy; N(0,1) KV/Q/SWA, integer indexer inputs)",
+        "dtype": "fp4e2m1+e4m3/{}/fp16-mfma".format("fp8e4m3" if w.idx_fp8 else "int8"),
+        "data": "synthetic (seeded numpy; N(0,1) KV/Q/SWA, {} indexer inputs)".format(
+            "E4M3 + fp32-scale" if w.idx_fp8 else "integer"),
         "config": {"workload": w.name, "batch": w.batch, "q_per_seq": w.q_per_seq,
                    "kv_len": w.kv_len, "dim": w.dim, "heads": w.heads, "window": w.window,
-                   "idx_heads": w.idx_heads, "idx_dim": w.idx_dim, "layers": list(w.layers)},
+                   "idx_heads": w.idx_heads, "idx_dim": w.idx_dim, "layers": list(w.layers),
+                   "idx_fp8": w.idx_fp8, "swa8": w.swa8},
         "hbm_gbs_group": round(nbytes["total"] / (ms / 1e3) / 1e9, 1),
         "hbm_frac_group": round(nbytes["total"] / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
         "breakdown_ms": dict({"pass": "separate, one event after every call (sums per stage)"},

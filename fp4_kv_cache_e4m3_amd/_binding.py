@@ -39,6 +39,7 @@ class IndexArgs(ctypes.Structure):
         ("heads", ctypes.c_int32), ("dim", ctypes.c_int32),
         ("q", ctypes.c_void_p), ("w", ctypes.c_void_p), ("k", ctypes.c_void_p),
         ("n_visible", ctypes.c_void_p),
+        ("fp8", ctypes.c_int32), ("q_scale", ctypes.c_void_p), ("k_scale", ctypes.c_void_p),
     ]
 
 
@@ -148,11 +149,14 @@ def dequantize_kv(codes: torch.Tensor, scales: torch.Tensor, out: torch.Tensor, 
 
 
 # ------------------------------------------------------------------ indexer
-def index_args(iq, iw, ik, q_per_seq: int, n_visible=None) -> IndexArgs:
-    """iq int8 [nq, H_I, D_I], iw fp32 [nq, H_I], ik int8 [B, T, D_I]."""
+def index_args(iq, iw, ik, q_per_seq: int, n_visible=None, q_scale=None, k_scale=None) -> IndexArgs:
+    """iq [nq, H_I, D_I], iw fp32 [nq, H_I], ik [B, T, D_I]: int8, or E4M3
+    codes (uint8) with q_scale fp32 [nq, H_I] and k_scale fp32 [B, T]."""
     nq, heads, dim = iq.shape
     B, T = ik.shape[0], ik.shape[1]
-    return IndexArgs(B, q_per_seq, T, heads, dim, _ptr(iq), _ptr(iw), _ptr(ik), _ptr(n_visible))
+    fp8 = 1 if (q_scale is not None or k_scale is not None) else 0
+    return IndexArgs(B, q_per_seq, T, heads, dim, _ptr(iq), _ptr(iw), _ptr(ik), _ptr(n_visible),
+                     fp8, _ptr(q_scale), _ptr(k_scale))
 
 
 def index_workspace_size(args: IndexArgs) -> int:

@@ -26,8 +26,19 @@ int check_index(const csa2_index_args* a) {
   if (nq > 0 && (!a->q || !a->w)) return CSA2_ERR_NULL;
   if (nq > 0 && a->kv_len > 0 && !a->k) return CSA2_ERR_NULL;
   if (!aligned(a->q, 16) || !aligned(a->k, 16) || !aligned(a->w, 4)) return CSA2_ERR_ALIGN;
+  if (a->fp8 != 0 && a->fp8 != 1) return CSA2_ERR_SHAPE;
+  if (a->fp8) {
+    if (nq > 0 && !a->q_scale) return CSA2_ERR_NULL;
+    if (nq > 0 && a->kv_len > 0 && !a->k_scale) return CSA2_ERR_NULL;
+    if (!aligned(a->q_scale, 4) || !aligned(a->k_scale, 4)) return CSA2_ERR_ALIGN;
+  }
   return CSA2_OK;
 }
+
+// FP8 scale pointers for the kernels: a NULL key-scale pointer selects the
+// int8 kernels (with an empty cache both give the same, all-empty, result)
+const float* q_scales(const csa2_index_args* a) { return a->fp8 ? a->q_scale : nullptr; }
+const float* k_scales(const csa2_index_args* a) { return a->fp8 ? a->k_scale : nullptr; }
 
 struct IndexLayout {
   int64_t nq, tk_stride, bk_stride, full_bytes, reindex_bytes, total;
@@ -187,7 +198,7 @@ const char* csa2_status_string(int s) {
   }
 }
 
-int csa2_version(void) { return (1 << 16) | 0; }
+int csa2_version(void) { return (1 << 16) | 1; }
 
 int csa2_quantize_kv(const float* x, int64_t x_stride, int64_t rows, int32_t dim, uint8_t* codes,
                      int64_t codes_stride, uint8_t* scales, int64_t scales_stride, hipStream_t stream) {
@@ -232,7 +243,7 @@ int csa2_index_scan(const csa2_index_args* a, void* ws, size_t ws_size, hipStrea
   if (!ws || ws_size < (size_t)L.total || !aligned(ws, 256)) return CSA2_ERR_WORKSPACE;
   uint32_t* tkeys = static_cast<uint32_t*>(ws);
   uint32_t* bkeys = tkeys + L.nq * L.tk_stride;
-  ScanParams sp{a->q, a->w, a->k, a->n_visible, a->batch, a->q_per_seq, a->kv_len, 1024,
+  ScanParams sp{a->q, a->w, a->k, a->n_visible, q_scales(a), k_scales(a), a->batch, a->q_per_seq, a->kv_len, 1024,
                 tkeys, L.tk_stride, bkeys, L.bk_stride};
   return hip_status(launch_index_scan(sp, a->heads, a->dim, stream));
 }
@@ -285,7 +296,7 @@ int csa2_index_reindex(const csa2_index_args* a, const int32_t* pool, int32_t* t
   if (!topk || !pool) return CSA2_ERR_NULL;
   if (!aligned(a->n_visible, 4) || !aligned(pool, 4)) return CSA2_ERR_ALIGN;
   if (!ws || ws_size < (size_t)L.total || !aligned(ws, 256)) return CSA2_ERR_WORKSPACE;
-  ReindexParams rp{a->q, a->w, a->k, a->n_visible, pool, a->q_per_seq, a->kv_len,
+  ReindexParams rp{a->q, a->w, a->k, a->n_visible, q_scales(a), k_scales(a), pool, a->q_per_seq, a->kv_len,
                    static_cast<uint32_t*>(ws), topk,
                    static_cast<uint32_t*>(ws) + L.nq * kPoolPositions};
   return hip_status(launch_reindex(rp, (int)L.nq, a->heads, a->dim, stream));

@@ -86,6 +86,50 @@ CSA2_DEV float sum_swap32(float x) {
   return __uint_as_float(a[0]) + __uint_as_float(a[1]);
 }
 
+// ---------------------------------------------------------------- indexer dots
+// Eight E4M3FN codes (byte i = element i) as eight fp16 values: the gfx950
+// scaled fp8 -> fp16 convert with scale 1.0; every finite E4M3 value is exact
+// in fp16.
+CSA2_DEV v8h e4m3x8_to_half(uint32_t lo, uint32_t hi) {
+  const v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false);
+  const v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true);
+  const v2h c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false);
+  const v2h d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true);
+  const v8h v = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+  return v;
+}
+
+// One 16 x 16 tile of indexer dot products: score row 4g+i (A operand `a`)
+// against token column n (B operand `b`) for lane (n, g), then ReLU.
+// int8 operands: exact int32 dot products.  E4M3FN operands (F8): each
+// 16-byte operand register is decoded to two groups of eight fp16 values
+// (exact) that two fp16 MFMAs contract with fp32 accumulation; both operands
+// are split alike, so every channel still meets its partner.  The products
+// are exact, and the sums stay within the fp32 rounding model.  (The gfx950
+// fp8 MFMA is not used here: its accumulation error, measured on random
+// codes, reaches 2^-11 of the largest product.)
+template <int KK, bool F8>
+CSA2_DEV void index_dots(const v4i (&a)[KK], const v4i (&b)[KK], float (&d)[4]) {
+  if constexpr (F8) {
+    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(e4m3x8_to_half(a[kk][0], a[kk][1]),
+                                                   e4m3x8_to_half(b[kk][0], b[kk][1]), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(e4m3x8_to_half(a[kk][2], a[kk][3]),
+                                                   e4m3x8_to_half(b[kk][2], b[kk][3]), acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d[i] = fmaxf(acc[i], 0.0f);
+  } else {
+    v4i acc = {0, 0, 0, 0};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[kk], b[kk], acc, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d[i] = (float)max(acc[i], 0);
+  }
+}
+
 }  // namespace csa2
 
 // ---------------------------------------------------------------- launchers
@@ -93,6 +137,7 @@ namespace csa2 {
 
 struct ScanParams {
   const int8_t* iq; const float* iw; const int8_t* ik; const int32_t* nvis;
+  const float* iqs; const float* iks;                    // FP8 indexer: [nq, H_I] and [B, T] scales, else NULL
   int32_t batch, qn; int64_t T; int32_t chunk;          // tokens per workgroup
   uint32_t* tkeys; int64_t tk_stride;                    // [nq, tk_stride]
   uint32_t* bkeys; int64_t bk_stride;                    // [nq, bk_stride]
@@ -113,6 +158,7 @@ struct SelectParams {
 };
 struct ReindexParams {
   const int8_t* iq; const float* iw; const int8_t* ik; const int32_t* nvis;
+  const float* iqs; const float* iks;                    // FP8 indexer scales, else NULL
   const int32_t* pool; int32_t qn; int64_t T;
   uint32_t* ckeys;                                       // [nq, 16384]
   int32_t* topk;

@@ -5,7 +5,12 @@
 // Sparse Attention 2": a Full layer scores the whole context with its
 // indexer; its hierarchical indexer keeps a pool of blocks of eight tokens.
 // Score s(q,t) = sum_h w[q,h] * relu(q_h . k_t); block score = max over its
-// visible tokens.  The selection that follows is in select.hip.
+// visible tokens.  The selection that follows is in select.hip.  The pages
+// leave the indexer's precision open: int8 keys and queries (exact integer
+// dot products), or E4M3FN codes with one fp32 scale per key position and
+// per (query, head), scored as sk[t] * sum_h (w[q,h] * sq[q,h]) *
+// relu(E4M3 dot product) (equal to the dequantised score for positive
+// scales).
 //
 // Design (gfx950, wave64): the indexer keys stream once from HBM.  Each wave
 // takes 16-token tiles: an int8 MFMA 16x16x64 contracts the 16 token rows (B
@@ -23,8 +28,8 @@ namespace csa2 {
 // Channel order of the int8 operands: lane group g takes, in k-step kk, the 16
 // channels 16g + 64kk .. +15, so the 4 lanes of a key row read 64 contiguous
 // bytes per load (the contraction only needs both operands to agree).
-// HI: indexer heads (2, 4, 8, 16); DI: indexer dim (64, 128).
-template <int DI, int HI>
+// HI: indexer heads (2, 4, 8, 16); DI: indexer dim (64, 128); F8: E4M3 codes.
+template <int DI, int HI, bool F8>
 __global__ __launch_bounds__(256) void k_index_scan(ScanParams p) {
   constexpr int KK = DI / 64;                 // MFMAs per tile
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -65,7 +70,11 @@ __global__ __launch_bounds__(256) void k_index_scan(ScanParams p) {
     for (int i = 0; i < 4; ++i) {
       const int r2 = 16 * mt + 4 * g + i;
       float w = 0.0f;
-      if (mt < MT && r2 < rows_used) w = p.iw[(int64_t)(b * p.qn + (r0 + r2) / HI) * HI + (r0 + r2) % HI];
+      if (mt < MT && r2 < rows_used) {
+        const int64_t wi = (int64_t)(b * p.qn + (r0 + r2) / HI) * HI + (r0 + r2) % HI;
+        w = p.iw[wi];
+        if constexpr (F8) w *= p.iqs[wi];
+      }
       wv[mt][i] = w;
     }
   }
@@ -77,25 +86,26 @@ __global__ __launch_bounds__(256) void k_index_scan(ScanParams p) {
   }
 
   const int8_t* ikb = p.ik + (int64_t)b * p.T * DI;
+  const float* iksb = F8 ? p.iks + (int64_t)b * p.T : nullptr;
   const int ntile = (int)((tend - t0 + 15) >> 4);
 
-  // score one 16-token tile whose indexer-key fragments are in bf
-  auto process = [&](int it, const v4i (&bf)[KK]) {
+  // score one 16-token tile whose indexer-key fragments are in bf (sk: the
+  // FP8 key scale of this lane's token)
+  auto process = [&](int it, const v4i (&bf)[KK], float sk) {
     const int64_t t = t0 + 16 * it + n;
     const bool tok_ok = t < tend;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       if (mt >= MT) break;
-      v4i acc = {0, 0, 0, 0};
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mt][kk], bf[kk], acc, 0, 0, 0);
       float val[4];
+      index_dots<KK, F8>(a[mt], bf, val);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) val[i] = wv[mt][i] * (float)max(acc[i], 0);
+      for (int i = 0; i < 4; ++i) val[i] *= wv[mt][i];
       if constexpr (HI >= 4) {
         float tot = ((val[0] + val[1]) + val[2]) + val[3];
         if constexpr (HI >= 8) tot = sum_swap16(tot);
         if constexpr (HI >= 16) tot = sum_swap32(tot);
+        if constexpr (F8) tot *= sk;
         const int j = (r0 + 16 * mt + 4 * g) / HI;   // query within the sequence
         const uint32_t key = (tok_ok && t < nvq[mt] && j < p.qn) ? score_key(tot) : 0u;
         // 8-token block max inside each half of the 16-lane row
@@ -112,7 +122,8 @@ __global__ __launch_bounds__(256) void k_index_scan(ScanParams p) {
       } else {  // HI == 2: rows (i0,i1) and (i2,i3) are two queries
 #pragma unroll
         for (int hq = 0; hq < 2; ++hq) {
-          const float tot = val[2 * hq] + val[2 * hq + 1];
+          float tot = val[2 * hq] + val[2 * hq + 1];
+          if constexpr (F8) tot *= sk;
           const int j = (r0 + 16 * mt + 4 * g) / 2 + hq;
           const int nv = (int)min((int64_t)(p.nvis && j < p.qn ? p.nvis[b * p.qn + j] : p.T), p.T);
           const uint32_t key = (tok_ok && t < nv && j < p.qn) ? score_key(tot) : 0u;
@@ -155,6 +166,15 @@ __global__ __launch_bounds__(256) void k_index_scan(ScanParams p) {
   __shared__ __attribute__((aligned(16))) int8_t kbuf[4][U][16 * DI];
   int8_t* const mybuf = &kbuf[wave][0][0];
   for (int64_t base = 16 * (int64_t)blockIdx.x; base < ntile; base += 16 * (int64_t)gridDim.x) {
+    float skv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      skv[u] = 1.0f;
+      if constexpr (F8) {
+        const int64_t t = 16 * (base + 4 * u + wave) + n;
+        if (t < tend) skv[u] = __builtin_nontemporal_load(iksb + t);
+      }
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
 #pragma unroll
@@ -178,7 +198,7 @@ __global__ __launch_bounds__(256) void k_index_scan(ScanParams p) {
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
         bf[kk] = *reinterpret_cast<const v4i*>(mybuf + u * 16 * DI + n * DI + ((g + 4 * kk) ^ ((n / SWD) % CPR)) * 16);
-      if (base + 4 * u + wave < ntile) process((int)(base + 4 * u + wave), bf);
+      if (base + 4 * u + wave < ntile) process((int)(base + 4 * u + wave), bf, skv[u]);
     }
   }
 }
@@ -188,8 +208,11 @@ template <int DI, int HI>
 static void launch_scan_t(const ScanParams& p, hipStream_t st) {
   const int64_t chunks = (p.T + p.chunk - 1) / p.chunk;
   const int64_t groups = ((int64_t)p.qn * HI + 63) / 64;    // 64 score rows per workgroup
-  hipLaunchKernelGGL((k_index_scan<DI, HI>), dim3((unsigned)chunks, (unsigned)p.batch, (unsigned)groups), dim3(256),
-                     0, st, p);
+  const dim3 grid((unsigned)chunks, (unsigned)p.batch, (unsigned)groups);
+  if (p.iks)
+    hipLaunchKernelGGL((k_index_scan<DI, HI, true>), grid, dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL((k_index_scan<DI, HI, false>), grid, dim3(256), 0, st, p);
 }
 
 hipError_t launch_index_scan(const ScanParams& p, int heads, int dim, hipStream_t st) {

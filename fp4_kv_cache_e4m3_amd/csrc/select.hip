@@ -533,7 +533,7 @@ constexpr int kRxSlotsPerWG = 64;
 // workgroup takes 64 pool slots (32 16-token tiles, two blocks each); each of
 // its waves loads the block ids of its 8 tiles, then issues all 8 tiles' key
 // gathers before the first MFMA, so 16 KiB per wave are in flight at once.
-template <int DI, int HI>
+template <int DI, int HI, bool F8>
 __global__ __launch_bounds__(256) void k_reindex_score(ReindexParams p) {
   constexpr int KK = DI / 64;
   constexpr int TPW = kRxSlotsPerWG / 2 / 4;        // tiles per wave
@@ -560,15 +560,21 @@ __global__ __launch_bounds__(256) void k_reindex_score(ReindexParams p) {
   }
   float wv[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) wv[i] = (4 * g + i < HI) ? p.iw[q * HI + 4 * g + i] : 0.0f;
+  for (int i = 0; i < 4; ++i) {
+    wv[i] = (4 * g + i < HI) ? p.iw[q * HI + 4 * g + i] : 0.0f;
+    if constexpr (F8) wv[i] *= (4 * g + i < HI) ? p.iqs[q * HI + 4 * g + i] : 0.0f;
+  }
 
   const int8_t* ikb = p.ik + b * p.T * DI;
   v4i bf[TPW][KK];
   bool ok[TPW];
+  float skv[TPW];
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
     const int64_t pos = (int64_t)blk[u] * kBlock + (n & 7);
     ok[u] = blk[u] >= 0 && (int64_t)blk[u] < nb && pos < nv;
+    skv[u] = 1.0f;
+    if constexpr (F8) skv[u] = ok[u] ? p.iks[b * p.T + pos] : 0.0f;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       v4i z = {0, 0, 0, 0};
@@ -579,12 +585,10 @@ __global__ __launch_bounds__(256) void k_reindex_score(ReindexParams p) {
   uint32_t* ck = p.ckeys + q * kPoolPositions;
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
-    v4i acc = {0, 0, 0, 0};
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[kk], bf[u][kk], acc, 0, 0, 0);
     float val[4];
+    index_dots<KK, F8>(a, bf[u], val);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) val[i] = wv[i] * (float)max(acc[i], 0);
+    for (int i = 0; i < 4; ++i) val[i] *= wv[i];
     float tot;
     if constexpr (HI == 2) {
       tot = val[0] + val[1];
@@ -593,6 +597,7 @@ __global__ __launch_bounds__(256) void k_reindex_score(ReindexParams p) {
       if constexpr (HI >= 8) tot = sum_swap16(tot);
       if constexpr (HI >= 16) tot = sum_swap32(tot);
     }
+    if constexpr (F8) tot *= skv[u];
     const uint32_t key = ok[u] ? score_key(tot) : 0u;
     // the block's maximum: 8 lanes of each half of the 16-lane row
     uint32_t m = key;
@@ -699,7 +704,11 @@ hipError_t launch_select_full(const SelectParams& p, int nq, int64_t max_blocks,
 hipError_t launch_reindex(const ReindexParams& p, int nq, int heads, int dim, hipStream_t st) {
   if (nq == 0) return hipSuccess;
   const dim3 grid(kPoolBlocks / kRxSlotsPerWG, nq);
-#define CSA2_RX_CASE(D, H) if (dim == D && heads == H) { hipLaunchKernelGGL((k_reindex_score<D, H>), grid, dim3(256), 0, st, p); } else
+#define CSA2_RX_CASE(D, H)                                                              \
+  if (dim == D && heads == H) {                                                         \
+    if (p.iks) hipLaunchKernelGGL((k_reindex_score<D, H, true>), grid, dim3(256), 0, st, p); \
+    else hipLaunchKernelGGL((k_reindex_score<D, H, false>), grid, dim3(256), 0, st, p);    \
+  } else
   CSA2_RX_CASE(64, 2) CSA2_RX_CASE(64, 4) CSA2_RX_CASE(64, 8) CSA2_RX_CASE(64, 16)
   CSA2_RX_CASE(128, 2) CSA2_RX_CASE(128, 4) CSA2_RX_CASE(128, 8) CSA2_RX_CASE(128, 16)
   { return hipErrorInvalidValue; }

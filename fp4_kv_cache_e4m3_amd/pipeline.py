@@ -52,21 +52,23 @@ class DecodeGroup:
                 base = b * T + r0
                 B.quantize_kv(src, self.codes[base:base + n], self.scales[base:base + n])
                 del src
-        # ---- indexer keys [B, T, D_I]
-        self.ik = torch.empty((B_, T, w.idx_dim), dtype=torch.int8, device=dev)
+        # ---- indexer keys [B, T, D_I] (int8, or E4M3 codes with [B, T] scales)
+        self.ik = torch.empty((B_, T, w.idx_dim), dtype=torch.uint8 if w.idx_fp8 else torch.int8, device=dev)
         for b in range(B_):
             self.ik[b].copy_(torch.from_numpy(synth.index_k(w, b)))
+        self.ik_scale = _dev(synth.index_k_scale_all(w), dev) if w.idx_fp8 else None
         # ---- per-step inputs
         self.new_rows = _dev(synth.new_rows(w), dev)           # [B * new_per_seq, d] fp32
         nl = len(w.layers)
         # indexing layers (Full / Reindex) and, per layer, the Top-K it reads
         self.index_layers = [l for l, m in enumerate(w.layers) if m in ("full", "reindex")]
         assert self.index_layers and self.index_layers[0] == 0, "the first layer must index"
+        qs = (lambda l, src=False: _dev(synth.index_q_scale(w, l, src), dev)) if w.idx_fp8 else (lambda l, src=False: None)
         self.iq = _dev(synth.index_q(w, 0), dev)
         self.iw = _dev(synth.index_w(w, 0), dev)
-        self._iqw = {0: (self.iq, self.iw)}
+        self._iqw = {0: (self.iq, self.iw, qs(0))}
         for l in self.index_layers[1:]:
-            self._iqw[l] = (_dev(synth.index_q(w, l), dev), _dev(synth.index_w(w, l), dev))
+            self._iqw[l] = (_dev(synth.index_q(w, l), dev), _dev(synth.index_w(w, l), dev), qs(l))
         self.q = [_dev(synth.attn_q_bf16(w, l).view(np.int16), dev) for l in range(nl)]
         self.swa = [_dev(synth.swa_bf16(w, l).view(np.int16), dev) for l in range(nl)]
         # 8-bit window rows: quantised once on the device from the bf16 rows
@@ -83,7 +85,8 @@ class DecodeGroup:
         self.topks = [torch.full((nq, B.TOPK), -1, dtype=torch.int32, device=dev) for _ in self.index_layers]
         self.topk = self.topks[0]
         self.out = [torch.empty((nq, w.heads, d), dtype=torch.float32, device=dev) for _ in range(nl)]
-        self.iargs_by_layer = {l: B.index_args(iq, iw, self.ik, w.q_per_seq) for l, (iq, iw) in self._iqw.items()}
+        self.iargs_by_layer = {l: B.index_args(iq, iw, self.ik, w.q_per_seq, q_scale=sq, k_scale=self.ik_scale)
+                               for l, (iq, iw, sq) in self._iqw.items()}
         self.iargs = self.iargs_by_layer[0]
         self.iws = torch.empty(max(256, B.index_workspace_size(self.iargs)), dtype=torch.uint8, device=dev)
         # Top-K buffer of each layer: the latest indexing layer's
@@ -113,10 +116,11 @@ class DecodeGroup:
         if w.layers[0] == "reindex":
             iq0 = _dev(synth.index_q(w, 0, pool_source=True), dev)
             iw0 = _dev(synth.index_w(w, 0, pool_source=True), dev)
-            pa = B.index_args(iq0, iw0, self.ik, w.q_per_seq)
+            sq0 = qs(0, True)
+            pa = B.index_args(iq0, iw0, self.ik, w.q_per_seq, q_scale=sq0, k_scale=self.ik_scale)
             scratch = torch.empty_like(self.topk)
             B.index_full(pa, self.pool, scratch, self.iws)
-            self._pool_src = (iq0, iw0)
+            self._pool_src = (iq0, iw0, sq0)
         torch.cuda.synchronize()
 
     # the stages of one step (bench.py times them apart)

@@ -131,6 +131,19 @@ int csa2_dequantize_kv(const uint8_t* codes, int64_t codes_stride,
  * sum in fp32 (heads in ascending order).  Scores are exact whenever w is
  * integer-valued and all partial sums stay below 2^24.  Ranking is by
  * (score descending, position ascending): ties go to the lower position.
+ *
+ * Real-valued indexer (fp8 = 1; the pages leave the indexer's precision
+ * open): q and k hold OCP E4M3FN codes, q_scale one fp32 scale per (query,
+ * head) and k_scale one per key position, and
+ *     s(q, t) = sum_h w[q, h] * max(0, q_scale[q, h] * k_scale[b, t] *
+ *                                      sum_c E4M3(q[q, h, c]) * E4M3(k[b, t, c])),
+ * evaluated in fp32 as k_scale[b, t] * sum_h (w[q, h] * q_scale[q, h]) *
+ * max(0, dot), the dot products summing exact products with fp32
+ * accumulation (codes decoded exactly to fp16, fp16 MFMA).  Scales must be
+ * positive and finite; NaN codes (0x7F, 0xFF)
+ * give unspecified rankings.  The result differs from the exact score by at
+ * most (D_I + H_I + 4) * 2^-24 times sum_h |w| q_scale k_scale sum_c |q_c k_c|,
+ * so two positions closer than that may rank in either order.
  */
 typedef struct {
   int32_t batch;             /* B sequences                                   */
@@ -143,6 +156,10 @@ typedef struct {
   const int8_t* k;           /* ik [B, T, D_I] contiguous, 16-byte aligned    */
   const int32_t* n_visible;  /* [nq] in [0, T] or NULL (= T): query q sees
                                 positions [0, n_visible[q])                  */
+  int32_t fp8;               /* 0: int8 q and k.  1: E4M3FN codes + scales   */
+  const float* q_scale;      /* fp8: [nq, H_I] fp32 > 0, 4-byte aligned       */
+  const float* k_scale;      /* fp8: [B, T] fp32 > 0 (row b * T + t), 4-byte
+                                aligned; both NULL when fp8 == 0              */
 } csa2_index_args;
 
 /* Bytes of workspace csa2_index_full / csa2_index_reindex need (0 on bad args). */

@@ -113,3 +113,77 @@ def oracle_attention(w: synth.Workload, q_bits, swa_bits, topk, with_new_rows=Tr
                                    None if swa_len is None else np.asarray(swa_len)[b:b + 1])
         out[qi] = oattn.attend(qv[qi], keys, 1.0 / np.sqrt(w.dim))
     return out
+
+
+# ---------------------------------------------------------------- FP8 indexer
+U32 = 2.0 ** -24
+
+
+def fp8_score_bound(abs_s: np.ndarray, dim: int, heads: int) -> np.ndarray:
+    """Largest |fp32 evaluation - exact score| of an FP8 indexer score whose
+    magnitude sum (oracle.indexer_fp8.abs_scores) is abs_s: D_I products
+    summed (at most D_I - 1 roundings), the weight times query-scale product,
+    the weighted head sum (H_I - 1 roundings), the key-scale product and one
+    rounding of the weighted term each stay within (D_I + H_I + 4) units of
+    2^-24 of the magnitude sum, whatever the summation order."""
+    return (dim + heads + 4) * U32 * np.asarray(abs_s, dtype=np.float64)
+
+
+def keys_to_scores(keys: np.ndarray) -> np.ndarray:
+    """fp32 scores of the library's order-preserving uint32 ranking keys."""
+    k = np.asarray(keys, dtype=np.uint32)
+    bits = np.where(k & np.uint32(0x80000000), k & np.uint32(0x7FFFFFFF), ~k).astype(np.uint32)
+    return bits.view(np.float32).astype(np.float64)
+
+
+def _selection_errors(sel_row, cand, s_of, e_of, k, what):
+    errs = []
+    sel = sel_row[sel_row >= 0].astype(np.int64)
+    if not np.all(sel_row[len(sel):] == -1):
+        errs.append(f"{what}: padding is not trailing -1")
+    if len(sel) != min(k, len(cand)):
+        errs.append(f"{what}: {len(sel)} entries, expected {min(k, len(cand))}")
+    if len(sel) > 1 and np.any(np.diff(sel) <= 0):
+        errs.append(f"{what}: not strictly ascending")
+    if not np.all(np.isin(sel, cand)):
+        errs.append(f"{what}: entries outside the candidates")
+        return errs
+    rest = np.setdiff1d(cand, sel)
+    if len(sel) and len(rest):
+        lo = (s_of(sel) + e_of(sel)).min()
+        hi = (s_of(rest) - e_of(rest)).max()
+        if lo < hi:
+            errs.append(f"{what}: a dropped candidate outranks a selected one beyond the rounding bound "
+                        f"({lo!r} < {hi!r})")
+    return errs
+
+
+def fp8_full_errors(pool_row, topk_row, s: np.ndarray, eps: np.ndarray, n_vis: int):
+    """Problems with a Full layer's pool / Top-512 row given the oracle's exact
+    scores s and bounds eps of positions [0, n_vis): each must be a valid
+    selection for some scores within eps of the exact ones (blocks by their
+    maxima, positions among the pool's), in the library's output format."""
+    nb = (n_vis + 7) // 8
+    sp = np.full(nb * 8, -np.inf)
+    sp[:n_vis] = s[:n_vis]
+    ep = np.zeros(nb * 8)
+    ep[:n_vis] = eps[:n_vis]
+    bmax = sp.reshape(nb, 8).max(axis=1)
+    bep = ep.reshape(nb, 8).max(axis=1)
+    errs = _selection_errors(np.asarray(pool_row), np.arange(nb), lambda i: bmax[i], lambda i: bep[i],
+                             2048, "pool")
+    if errs:
+        return errs
+    blocks = pool_row[pool_row >= 0].astype(np.int64)
+    cand = (blocks[:, None] * 8 + np.arange(8)[None, :]).reshape(-1)
+    cand = cand[cand < n_vis]
+    return _selection_errors(np.asarray(topk_row), cand, lambda i: s[i], lambda i: eps[i], 512, "top-512")
+
+
+def fp8_topk_errors(topk_row, cand: np.ndarray, s_cand: np.ndarray, e_cand: np.ndarray):
+    """Problems with a Reindex Top-512 row over candidate positions cand
+    (ascending) with exact scores s_cand and bounds e_cand."""
+    pos = {int(p): i for i, p in enumerate(cand)}
+    idx = lambda ps: np.array([pos[int(p)] for p in ps], dtype=np.int64)
+    return _selection_errors(np.asarray(topk_row), cand, lambda ps: s_cand[idx(ps)],
+                             lambda ps: e_cand[idx(ps)], 512, "top-512")

@@ -79,6 +79,24 @@ def test_index_rejects(lib):
     assert lib.csa2_index_workspace_size(ctypes.byref(a)) == 0
 
 
+def test_index_fp8_rejects(lib):
+    """FP8 indexer arguments: the flag must be 0 or 1 and both scale arrays
+    present and 4-byte aligned; int8 arguments ignore the scale pointers."""
+    import fp4_kv_cache_e4m3_amd as m
+    a = m.IndexArgs(1, 1, 100, 8, 64, 16, 16, 16, None)
+    ws = lib.csa2_index_workspace_size(ctypes.byref(a))
+    f = lib.csa2_index_full
+    assert f(ctypes.byref(m.IndexArgs(1, 1, 100, 8, 64, 16, 16, 16, None, 2, 16, 16)), None, 16, 256, ws, None) == 2
+    assert f(ctypes.byref(m.IndexArgs(1, 1, 100, 8, 64, 16, 16, 16, None, 1, None, 16)), None, 16, 256, ws, None) == 1
+    assert f(ctypes.byref(m.IndexArgs(1, 1, 100, 8, 64, 16, 16, 16, None, 1, 16, None)), None, 16, 256, ws, None) == 1
+    assert f(ctypes.byref(m.IndexArgs(1, 1, 100, 8, 64, 16, 16, 16, None, 1, 18, 16)), None, 16, 256, ws, None) == 3
+    assert f(ctypes.byref(m.IndexArgs(1, 1, 100, 8, 64, 16, 16, 16, None, 1, 16, 18)), None, 16, 256, ws, None) == 3
+    assert lib.csa2_index_reindex(ctypes.byref(m.IndexArgs(1, 1, 100, 8, 64, 16, 16, 16, None, 1, 16, None)),
+                                  16, 16, 256, ws, None) == 1
+    b = m.IndexArgs(1, 1, 100, 8, 64, 16, 16, 16, None, 1, 16, 16)
+    assert lib.csa2_index_workspace_size(ctypes.byref(b)) == ws
+
+
 def test_index_append_rejects(lib):
     """The fused index + new-row quantisation calls validate both parts
     before launching anything."""
