@@ -19,7 +19,7 @@ tensor is drawn from a fixed distribution:
 * FP8 indexer (``idx_fp8``): q / k bytes are E4M3FN codes drawn uniformly
   over the 96 codes of magnitude [0.25, 15] and either sign (a log-uniform
   spread over six octaves), key scales one per position and query scales one
-  per (query, head), fp32 uniform in [1/32, 1/8), head weights fp32 uniform
+  per (query, head), fp32 uniform in [1/32, 1/16), head weights fp32 uniform
   in [-0.25, 1).
 
 Seeds: ``SeedSequence([0xC5A2, workload_id, tensor_id, layer, chunk])``.
