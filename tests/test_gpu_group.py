@@ -9,7 +9,9 @@ import torch
 
 from fp4_kv_cache_e4m3_amd import DecodeGroup, synth
 from oracle import indexer as oidx
-from tests.parity import ATTN_TOL, host, oracle_attention, oracle_kv_rows, oracle_selected_rows, rownorm_err
+from oracle import indexer_fp8 as o8
+from tests.parity import (ATTN_TOL, fp8_full_errors, fp8_score_bound, host, oracle_attention, oracle_kv_rows,
+                          oracle_selected_rows, rownorm_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -108,3 +110,41 @@ def test_decoder_step_full_reindex4_b32_t65536():
     that rescore the Full layer's pool of the same step; every group's Top-K is
     checked bit-exact and every layer's output on sampled queries."""
     check_group(synth.C6, sample=[0, 7, 19, 31])
+
+
+def test_group_full_reuse3_batch32_t65536_idx8():
+    """Decoder group 1 with a real-valued (E4M3 + fp32 scale) indexer: every
+    query's pool and Top-512 valid within the fp32 rounding bound of the
+    oracle's scores, the step's new FP4 rows bit-exact, and every layer's
+    attention checked on queries whose selection equals the oracle's."""
+    w = synth.C2_IDX8
+    T = w.kv_len
+    g = DecodeGroup(w)
+    g.step()
+    torch.cuda.synchronize()
+    cq, sq, iw = synth.index_q(w), synth.index_q_scale(w), synth.index_w(w)
+    got_pool, got_topk = host(g.pool), host(g.topks[0])
+    ref_topk = np.full((w.nq, 512), -1, dtype=np.int32)
+    exact = []
+    for q in range(w.nq):
+        ck, sk = synth.index_k(w, q), synth.index_k_scale(w, q)
+        pool, topk, s = o8.full_query(cq[q], sq[q], iw[q], ck, sk, T)
+        eps = fp8_score_bound(o8.abs_scores(cq[q], sq[q], iw[q], ck, sk), w.idx_dim, w.idx_heads)
+        problems = fp8_full_errors(got_pool[q], got_topk[q], s, eps, T)
+        assert problems == [], f"query {q}: {problems}"
+        ref_topk[q] = _pad(topk, 512)
+        if np.array_equal(got_pool[q], _pad(pool, 2048)) and np.array_equal(got_topk[q], ref_topk[q]):
+            exact.append(q)
+    assert len(exact) >= 24, f"only {len(exact)} of 32 queries equal the oracle's selection"
+    n = w.new_per_seq
+    for b in (0, w.batch - 1):
+        rc, rs = oracle_kv_rows(w, b, np.arange(T - n, T), with_new_rows=True)
+        np.testing.assert_array_equal(host(g.codes[b * T + T - n:b * T + T]), rc)
+        np.testing.assert_array_equal(host(g.scales[b * T + T - n:b * T + T]), rs)
+    qs = exact[::3]
+    rows = oracle_selected_rows(w, ref_topk, qs, with_new_rows=True)
+    for l in range(len(w.layers)):
+        ref = oracle_attention(w, synth.attn_q_bf16(w, l), synth.swa_bf16(w, l), ref_topk,
+                               with_new_rows=True, queries=qs, rows=rows)
+        err = rownorm_err(host(g.out[l])[qs], ref[qs])
+        assert err <= ATTN_TOL, (l, err)
