@@ -22,7 +22,8 @@ WINDOW = 128
 SCALE_GROUP = 16
 
 EXPORTS = (
-    "csa2_status_string", "csa2_version", "csa2_quantize_kv", "csa2_quantize_swa_fp8", "csa2_dequantize_kv",
+    "csa2_status_string", "csa2_version", "csa2_quantize_kv", "csa2_quantize_kv_paged", "csa2_quantize_swa_fp8",
+    "csa2_dequantize_kv",
     "csa2_index_workspace_size", "csa2_index_full", "csa2_index_scan", "csa2_index_select",
     "csa2_index_full_append", "csa2_index_select_append", "csa2_index_reindex",
     "csa2_attn_workspace_size", "csa2_sparse_attn",
@@ -56,6 +57,8 @@ class AttnArgs(ctypes.Structure):
         ("sm_scale", ctypes.c_float),
         ("out", ctypes.c_void_p),
         ("swa_fp8", ctypes.c_int32), ("swa_scale", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p), ("max_pages", ctypes.c_int32), ("page_size", ctypes.c_int32),
+        ("cache_rows", ctypes.c_int64), ("swa_start", ctypes.c_void_p),
     ]
 
 
@@ -76,6 +79,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.csa2_version.restype = ctypes.c_int
     lib.csa2_quantize_kv.restype = ctypes.c_int
     lib.csa2_quantize_kv.argtypes = [vp, i64, i64, i32, vp, i64, vp, i64, vp]
+    lib.csa2_quantize_kv_paged.restype = ctypes.c_int
+    lib.csa2_quantize_kv_paged.argtypes = [vp, i64, i64, i32, vp, vp, vp, i32, i32, i32, vp, i64, vp, i64, i64, vp]
     lib.csa2_quantize_swa_fp8.restype = ctypes.c_int
     lib.csa2_quantize_swa_fp8.argtypes = [vp, i64, i64, i32, vp, i64, vp, vp]
     lib.csa2_dequantize_kv.restype = ctypes.c_int
@@ -132,6 +137,18 @@ def quantize_kv(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, stre
     rows, dim = x.shape
     _check(load().csa2_quantize_kv(_ptr(x), x.stride(0), rows, dim, _ptr(codes), codes.stride(0),
                                    _ptr(scales), scales.stride(0), _stream(stream)))
+
+
+def quantize_kv_paged(x: torch.Tensor, row_seq: torch.Tensor, row_pos: torch.Tensor, block_table: torch.Tensor,
+                      page_size: int, codes: torch.Tensor, scales: torch.Tensor, stream=None) -> None:
+    """FP4-quantise fp32 rows x [rows, d] into a paged cache: row r to position
+    row_pos[r] of sequence row_seq[r] through block_table int32 [B, max_pages];
+    codes [cache_rows, >=d/2] / scales [cache_rows, >=d/16]."""
+    rows, dim = x.shape
+    B, max_pages = block_table.shape
+    _check(load().csa2_quantize_kv_paged(_ptr(x), x.stride(0), rows, dim, _ptr(row_seq), _ptr(row_pos),
+                                         _ptr(block_table), B, max_pages, page_size, _ptr(codes), codes.stride(0),
+                                         _ptr(scales), scales.stride(0), codes.shape[0], _stream(stream)))
 
 
 def quantize_swa_fp8(x: torch.Tensor, out: torch.Tensor, scales: torch.Tensor, stream=None) -> None:
@@ -205,17 +222,23 @@ def index_reindex(args: IndexArgs, pool, topk, ws, stream=None) -> None:
 
 # ------------------------------------------------------------------ attention
 def attn_args(q, codes, scales, topk, swa, out, q_per_seq: int, kv_len: int, window: int = WINDOW,
-              swa_len=None, sm_scale: float = 0.0, swa_scale=None) -> AttnArgs:
+              swa_len=None, sm_scale: float = 0.0, swa_scale=None, block_table=None, page_size: int = 0,
+              swa_start=None) -> AttnArgs:
     """q bf16-as-int16/uint16 [nq, H, d]; codes [B*T, >=d/2]; scales [B*T, >=d/16];
     topk int32 [nq, k]; swa bf16 [B, window-1+Qn, d] -- or, with swa_scale
-    (fp32 [B, window-1+Qn]), E4M3 codes uint8 [B, window-1+Qn, d]; out fp32 [nq, H, d]."""
+    (fp32 [B, window-1+Qn]), E4M3 codes uint8 [B, window-1+Qn, d]; out fp32 [nq, H, d].
+    Paged cache: block_table int32 [B, max_pages] and page_size, codes / scales
+    then hold every physical row.  swa_start int32 [B]: window ring slots."""
     nq, heads, dim = q.shape
+    paged = block_table is not None
     return AttnArgs(nq // q_per_seq, q_per_seq, kv_len, heads, dim, _ptr(q),
                     _ptr(codes), codes.stride(0) if codes is not None else dim // 2,
                     _ptr(scales), scales.stride(0) if scales is not None else dim // 16,
                     _ptr(topk), topk.shape[1] if topk is not None else 0,
                     _ptr(swa), window, _ptr(swa_len), float(sm_scale), _ptr(out),
-                    1 if swa_scale is not None else 0, _ptr(swa_scale))
+                    1 if swa_scale is not None else 0, _ptr(swa_scale),
+                    _ptr(block_table), block_table.shape[1] if paged else 0, page_size if paged else 0,
+                    codes.shape[0] if paged and codes is not None else 0, _ptr(swa_start))
 
 
 def attn_workspace_size(args: AttnArgs) -> int:

@@ -138,6 +138,16 @@ int check_attn(const csa2_attn_args* a) {
   if (!aligned(a->q, 16) || !aligned(a->codes, 16) || !aligned(a->scales, 8) || !aligned(a->swa, 16) ||
       !aligned(a->out, 16) || !aligned(a->topk, 4) || (a->codes_stride % 16) || (a->scales_stride % 8))
     return CSA2_ERR_ALIGN;
+  if (a->block_table) {                              // paged cache: the whole cache is one buffer
+    const int ps = a->page_size;
+    if (ps < 1 || ps > 65536 || (ps & (ps - 1))) return CSA2_ERR_SHAPE;
+    if (a->max_pages < 1 || (int64_t)a->max_pages * ps < a->kv_len) return CSA2_ERR_SHAPE;
+    if (a->cache_rows < 0 || a->cache_rows >= (1 << 24) || a->cache_rows * a->codes_stride > kBufMax ||
+        a->cache_rows * a->scales_stride > kBufMax)
+      return CSA2_ERR_SHAPE;
+    if (!aligned(a->block_table, 4)) return CSA2_ERR_ALIGN;
+  }
+  if (!aligned(a->swa_start, 4)) return CSA2_ERR_ALIGN;
   return CSA2_OK;
 }
 
@@ -205,6 +215,24 @@ int csa2_quantize_kv(const float* x, int64_t x_stride, int64_t rows, int32_t dim
   const int st = check_quantize(x, x_stride, rows, dim, codes, codes_stride, scales, scales_stride);
   if (st != CSA2_OK || rows == 0) return st;
   return hip_status(launch_quantize(x, x_stride, rows, dim, codes, codes_stride, scales, scales_stride, stream));
+}
+
+int csa2_quantize_kv_paged(const float* x, int64_t x_stride, int64_t rows, int32_t dim, const int32_t* row_seq,
+                           const int32_t* row_pos, const int32_t* block_table, int32_t batch, int32_t max_pages,
+                           int32_t page_size, uint8_t* codes, int64_t codes_stride, uint8_t* scales,
+                           int64_t scales_stride, int64_t cache_rows, hipStream_t stream) {
+  int st = check_quantize(x, x_stride, rows, dim, codes, codes_stride, scales, scales_stride);
+  if (st != CSA2_OK) return st;
+  if (page_size < 1 || page_size > 65536 || (page_size & (page_size - 1)) || max_pages < 1 || batch < 1 ||
+      cache_rows < 0 || rows * (dim / 16) > ((int64_t)1 << 28))
+    return CSA2_ERR_SHAPE;
+  if (rows == 0) return CSA2_OK;
+  if (!row_seq || !row_pos || !block_table) return CSA2_ERR_NULL;
+  if (!aligned(row_seq, 4) || !aligned(row_pos, 4) || !aligned(block_table, 4)) return CSA2_ERR_ALIGN;
+  PagedRows d{row_seq, row_pos, block_table, batch, max_pages, 0, cache_rows};
+  while ((1 << d.shift) < page_size) ++d.shift;
+  return hip_status(launch_quantize_paged(x, x_stride, rows, dim, d, codes, codes_stride, scales, scales_stride,
+                                          stream));
 }
 
 int csa2_quantize_swa_fp8(const uint16_t* x, int64_t x_stride, int64_t rows, int32_t dim, uint8_t* out,
@@ -332,6 +360,14 @@ int csa2_sparse_attn(const csa2_attn_args* a, void* ws, size_t ws_size, hipStrea
   p.qscale = sm * 1.4426950408889634f;
   p.swa_fp8 = a->swa_fp8;
   p.swa_scale = a->swa_scale;
+  p.block_table = a->block_table;
+  if (a->block_table) {
+    p.max_pages = a->max_pages;
+    p.page_shift = 0;
+    while ((1 << p.page_shift) < a->page_size) ++p.page_shift;
+    p.cache_rows = a->cache_rows;
+  }
+  p.swa_start = a->swa_start;
   // With no tile at all the kernel still runs: every head ends with an empty
   // softmax and writes zeros (no memset node, so the call stays graph-safe).
   return hip_status(launch_attn(p, (int)L.nq, a->dim, L.waves, stream));

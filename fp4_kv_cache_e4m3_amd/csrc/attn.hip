@@ -297,7 +297,7 @@ CSA2_DEV void attend_tile(const AttnParams& p, KV kvf, ST stage, AfterQK after_q
 
 // S8: the window rows are 8-bit (E4M3 codes + a power-of-two scale per row)
 // instead of bf16
-template <int D, int NW, bool S8>
+template <int D, int NW, bool S8, bool PG>
 __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
   using G = Geo<D>;
   constexpr int KH = G::KH, NT = G::NT, PITCH = G::PITCH, HALF = G::HALF;
@@ -353,9 +353,26 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
     const int slot_i = (tile0 + NW * i) * 16 + n;
     pos0[i] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(tk_buf, i < n_fp4 && slot_i < p.topk_k ? 4u * (uint32_t)slot_i : kOob, 0, 0);
   }
+  // Paged cache (PG): a Top-K position t of sequence b is row
+  // block_table[b][t >> page_shift] * page_size + (t & (page_size - 1)) of the
+  // whole cache; positions outside [0, T), negative page ids and rows past the
+  // cache become -1 (empty).  Positions are translated where they are staged.
+  const rsrc_t bt_buf = make_rsrc(PG ? p.block_table + (int64_t)b * p.max_pages : nullptr,
+                                  PG ? (uint32_t)p.max_pages * 4u : 0u);
+  auto to_row = [&](int32_t pos) -> int32_t {
+    if constexpr (!PG) {
+      return pos;
+    } else {
+      const bool ok = pos >= 0 && (int64_t)pos < p.T;
+      const int32_t page = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(
+          bt_buf, ok ? 4u * (uint32_t)(pos >> p.page_shift) : kOob, 0, 0);
+      const int64_t row = ((int64_t)page << p.page_shift) + (pos & ((1 << p.page_shift) - 1));
+      return ok && page >= 0 && row < p.cache_rows ? (int32_t)row : -1;
+    }
+  };
   auto first_position = [&](int i) {
     const int slot_i = (tile0 + NW * i) * 16 + n;
-    return i < n_fp4 && slot_i < p.topk_k ? pos0[i] : -1;
+    return i < n_fp4 && slot_i < p.topk_k ? to_row(pos0[i]) : -1;
   };
   constexpr int SPT = (kMaxTopK + 64 * NW - 1) / (64 * NW);
   int32_t sraw[SPT];
@@ -384,8 +401,10 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
   // ---- FP4 rows: the first two gathers go out as soon as their positions
   // are known
   Fp4Src src;
-  src.codes = make_rsrc(p.codes + b * p.T * p.codes_stride, (uint32_t)(p.T * p.codes_stride));
-  src.scales = make_rsrc(p.scales + b * p.T * p.scales_stride, (uint32_t)(p.T * p.scales_stride));
+  // the sequence's rows, or (PG) the whole cache
+  const int64_t row0 = PG ? 0 : b * p.T, nrows = PG ? p.cache_rows : p.T;
+  src.codes = make_rsrc(p.codes + row0 * p.codes_stride, (uint32_t)(nrows * p.codes_stride));
+  src.scales = make_rsrc(p.scales + row0 * p.scales_stride, (uint32_t)(nrows * p.scales_stride));
   src.cstride = (uint32_t)p.codes_stride;
   src.sstride = (uint32_t)p.scales_stride;
   src.oob = kOob;
@@ -400,7 +419,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
     const uint32_t b1 = KH == 8 ? b0 + 1u : 0x0Cu;               // 0x0C selects a zero byte
     src.psel[r] = b0 | (0x0Cu << 8) | (b1 << 16) | (0x0Cu << 24);
   }
-  const uint32_t T32 = (uint32_t)p.T;
+  const uint32_t T32 = (uint32_t)nrows;
   Fp4Raw<D> raw[2];
   bool vld[2];
   vld[0] = load_fp4<D>(src, first_position(0), T32, raw[0]);
@@ -418,7 +437,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
 #pragma unroll
   for (int i = 0; i < SPT; ++i) {
     const int sl = (int)threadIdx.x + 64 * NW * i;
-    if (sl < n_slots) spos[sl] = slot0 + sl < p.topk_k ? sraw[i] : -1;
+    if (sl < n_slots) spos[sl] = slot0 + sl < p.topk_k ? to_row(sraw[i]) : -1;
   }
   __syncthreads();
 
@@ -450,12 +469,16 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
   const rsrc_t swa_sbuf = make_rsrc(S8 ? p.swa_scale + (int64_t)b * p.swa_rows : nullptr,
                                     S8 ? (uint32_t)(p.swa_rows * 4) : 0u);
   const uint32_t swa_lane = S8 ? (uint32_t)(Fp8Map<D>::LANE * g) : 2u * InterMap<D>::LANE * g;
+  // ring buffer: window row r of the sequence sits in slot (r + start) mod rows
+  int swa_st = p.swa_start ? p.swa_start[b] : 0;
+  swa_st = swa_st >= 0 && swa_st < p.swa_rows ? swa_st : 0;
   auto swa_rows = [&](int t) {                      // this lane's row offset of window tile t
     const int wr = (t - p.n_sparse_tiles) * 16 + n;
     const int r = j + wr;
     swa_valid = t < t_end && wr >= 0 && wr < p.window && r >= first_swa && r < p.swa_rows;
-    swa_so = swa_valid ? 4u * (uint32_t)r : kOob;
-    return (swa_valid ? (uint32_t)r * (kSwaBytes * D) : kOob) + swa_lane;
+    const int rs = r + swa_st >= p.swa_rows ? r + swa_st - p.swa_rows : r + swa_st;
+    swa_so = swa_valid ? 4u * (uint32_t)rs : kOob;
+    return (swa_valid ? (uint32_t)rs * (kSwaBytes * D) : kOob) + swa_lane;
   };
   auto load_swa_half = [&](uint32_t ro, int hh) {
     if constexpr (S8) {
@@ -660,8 +683,13 @@ hipError_t launch_attn(const AttnParams& p, int nq, int dim, int waves, hipStrea
   const dim3 grid((unsigned)(16 * ngroups), (unsigned)((nq + 7) / 8), (unsigned)p.splits);
 #define CSA2_ATTN_CASE(D, NW)                                                                 \
   if (dim == D && waves == NW) {                                                              \
-    if (p.swa_fp8) hipLaunchKernelGGL((k_attn<D, NW, true>), grid, dim3(64 * NW), 0, st, p);  \
-    else hipLaunchKernelGGL((k_attn<D, NW, false>), grid, dim3(64 * NW), 0, st, p);           \
+    if (p.block_table) {                                                                      \
+      if (p.swa_fp8) hipLaunchKernelGGL((k_attn<D, NW, true, true>), grid, dim3(64 * NW), 0, st, p); \
+      else hipLaunchKernelGGL((k_attn<D, NW, false, true>), grid, dim3(64 * NW), 0, st, p);        \
+    } else {                                                                                  \
+      if (p.swa_fp8) hipLaunchKernelGGL((k_attn<D, NW, true, false>), grid, dim3(64 * NW), 0, st, p); \
+      else hipLaunchKernelGGL((k_attn<D, NW, false, false>), grid, dim3(64 * NW), 0, st, p);        \
+    }                                                                                         \
     if (p.splits > 1) hipLaunchKernelGGL(k_attn_combine<D>, dim3(nq * p.heads), dim3(D / 4), 0, st, p); \
     return hipGetLastError();                                                                 \
   }

@@ -174,10 +174,21 @@ struct AttnParams {
   float qscale;                                          // sm_scale * log2(e)
   int32_t swa_fp8;                                       // window rows: 0 bf16, 1 E4M3 codes + row scales
   const float* swa_scale;                                // [B, swa_rows] powers of two (swa_fp8)
+  const int32_t* block_table;                            // paged cache [B, max_pages], or NULL
+  int32_t max_pages, page_shift;
+  int64_t cache_rows;                                    // physical rows of a paged cache
+  const int32_t* swa_start;                              // ring slot of window row 0 per sequence, or NULL
 };
 
 hipError_t launch_quantize(const float* x, int64_t xs, int64_t rows, int dim, uint8_t* codes,
                            int64_t cs, uint8_t* scales, int64_t ss, hipStream_t st);
+// destination of new rows in a paged cache
+struct PagedRows {
+  const int32_t* seq; const int32_t* pos; const int32_t* bt;
+  int32_t batch, max_pages, shift; int64_t cache_rows;
+};
+hipError_t launch_quantize_paged(const float* x, int64_t xs, int64_t rows, int dim, const PagedRows& d,
+                                 uint8_t* codes, int64_t cs, uint8_t* scales, int64_t ss, hipStream_t st);
 bool quantize_fits_quad(int64_t rows, int dim);           // small enough for four lanes per group
 hipError_t launch_quantize_swa8(const uint16_t* x, int64_t xs, int64_t rows, int dim, uint8_t* out, int64_t os,
                                 float* scales, hipStream_t st);

@@ -62,6 +62,32 @@ __global__ __launch_bounds__(256) void k_quantize_quad(const float* __restrict__
   quantize_quad_thread(x, xs, rows, groups, codes, cs, scales, ss, (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
 }
 
+// New rows into a paged cache: row r goes to position pos[r] of sequence
+// seq[r], i.e. cache row block_table[seq][pos / P] * P + pos % P.  Rows whose
+// sequence, position or page is out of range are skipped.
+__global__ __launch_bounds__(256) void k_quantize_paged(const float* __restrict__ x, int64_t xs, int64_t rows,
+                                                   int groups, uint8_t* __restrict__ codes, int64_t cs,
+                                                   uint8_t* __restrict__ scales, int64_t ss, PagedRows d) {
+  quantize_quad_thread_to(x, xs, rows, groups, codes, cs, scales, ss, (int64_t)blockIdx.x * blockDim.x + threadIdx.x,
+                          [&](int64_t r) -> int64_t {
+                            const int32_t sq = d.seq[r], t = d.pos[r];
+                            if (sq < 0 || sq >= d.batch || t < 0 || (t >> d.shift) >= d.max_pages) return -1;
+                            const int32_t page = d.bt[(int64_t)sq * d.max_pages + (t >> d.shift)];
+                            const int64_t row = ((int64_t)page << d.shift) + (t & ((1 << d.shift) - 1));
+                            return page >= 0 && row < d.cache_rows ? row : -1;
+                          });
+}
+
+hipError_t launch_quantize_paged(const float* x, int64_t xs, int64_t rows, int dim, const PagedRows& d,
+                                 uint8_t* codes, int64_t cs, uint8_t* scales, int64_t ss, hipStream_t st) {
+  const int groups = dim / 16;
+  const int64_t n = rows * groups;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_quantize_paged, dim3((unsigned)((4 * n + 255) / 256)), dim3(256), 0, st, x, xs, rows, groups,
+                     codes, cs, scales, ss, d);
+  return hipGetLastError();
+}
+
 __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ codes, int64_t cs,
                                                     const uint8_t* __restrict__ scales, int64_t ss,
                                                     int64_t rows, int groups, float* __restrict__ out,

@@ -70,14 +70,19 @@ CSA2_DEV uint32_t element_code(float x, float s) {
 // `groups` 16-channel groups (the lanes of a group are four consecutive
 // lanes of one wave; threads past the job return).  Used by the small-launch
 // kernel here and by the extra workgroups of the Full selection launch.
-CSA2_DEV void quantize_quad_thread(const float* __restrict__ x, int64_t xs, int64_t rows, int groups,
-                                   uint8_t* __restrict__ codes, int64_t cs, uint8_t* __restrict__ scales,
-                                   int64_t ss, int64_t gid) {
+// dst(r): the cache row that source row r is written to (-1: none); the four
+// lanes of a group share r, so they take the same branch.
+template <class Dst>
+CSA2_DEV void quantize_quad_thread_to(const float* __restrict__ x, int64_t xs, int64_t rows, int groups,
+                                      uint8_t* __restrict__ codes, int64_t cs, uint8_t* __restrict__ scales,
+                                      int64_t ss, int64_t gid, Dst dst) {
   if (gid >= rows * groups * 4) return;            // whole quads: the count is a multiple of 4
   const int64_t grp = gid >> 2;
   const int qtr = (int)(gid & 3);
   const int64_t r = grp / groups;
   const int g = (int)(grp - r * groups);
+  const int64_t dr = dst(r);
+  if (dr < 0) return;
   const float4 f = *reinterpret_cast<const float4*>(x + r * xs + 16 * g + 4 * qtr);
   const float v[4] = {f.x, f.y, f.z, f.w};
   float amax = 0.0f;
@@ -93,8 +98,14 @@ CSA2_DEV void quantize_quad_thread(const float* __restrict__ x, int64_t xs, int6
     const uint32_t c = (s == 0.0f) ? ((__float_as_uint(v[i]) >> 28) & 8u) : element_code(v[i], s);
     bits |= c << (4 * i);
   }
-  *reinterpret_cast<uint16_t*>(codes + r * cs + 8 * g + 2 * qtr) = (uint16_t)bits;
-  if (qtr == 0) scales[r * ss + g] = (uint8_t)sc;
+  *reinterpret_cast<uint16_t*>(codes + dr * cs + 8 * g + 2 * qtr) = (uint16_t)bits;
+  if (qtr == 0) scales[dr * ss + g] = (uint8_t)sc;
+}
+
+CSA2_DEV void quantize_quad_thread(const float* __restrict__ x, int64_t xs, int64_t rows, int groups,
+                                   uint8_t* __restrict__ codes, int64_t cs, uint8_t* __restrict__ scales,
+                                   int64_t ss, int64_t gid) {
+  quantize_quad_thread_to(x, xs, rows, groups, codes, cs, scales, ss, gid, [](int64_t r) { return r; });
 }
 
 }  // namespace csa2

@@ -91,6 +91,29 @@ int csa2_quantize_kv(const float* x, int64_t x_stride, int64_t rows, int32_t dim
                      uint8_t* scales, int64_t scales_stride, hipStream_t stream);
 
 /*
+ * csa2_quantize_kv_paged -- csa2_quantize_kv of new rows into a paged cache.
+ * The quantisation happens where the row is written, as for the contiguous
+ * cache (wpnews.pro TL;DR: the FP4 cache needs no separate quantisation
+ * pass); only the destination differs.  Row r of x (the token at position
+ * row_pos[r] of sequence row_seq[r]) is written to cache row
+ *     block_table[row_seq[r] * max_pages + row_pos[r] / page_size] * page_size
+ *         + row_pos[r] % page_size
+ * of codes / scales (same row format as csa2_quantize_kv).  Rows whose
+ * sequence is outside [0, batch), whose position is negative or past
+ * max_pages * page_size, whose page id is negative or whose cache row is at
+ * or past cache_rows are skipped.  Destination rows must be distinct.
+ *   row_seq, row_pos  int32 [rows] device arrays, 4-byte aligned.
+ *   block_table       int32 [batch, max_pages], 4-byte aligned.
+ *   page_size         power of two, 1 .. 65536.
+ *   rows * dim / 16 <= 2^28.
+ */
+int csa2_quantize_kv_paged(const float* x, int64_t x_stride, int64_t rows, int32_t dim,
+                           const int32_t* row_seq, const int32_t* row_pos,
+                           const int32_t* block_table, int32_t batch, int32_t max_pages, int32_t page_size,
+                           uint8_t* codes, int64_t codes_stride, uint8_t* scales, int64_t scales_stride,
+                           int64_t cache_rows, hipStream_t stream);
+
+/*
  * csa2_quantize_swa_fp8 -- 8-bit sliding-window rows.
  * Source: kongchang.com, "Three Core Innovations" (the window keeps 8-bit
  * precision); the format is not given on the pages.  Each bf16 row r < rows
@@ -276,6 +299,24 @@ typedef struct {
                                   scale, exact in fp16 when every row scale is
                                   in [2^-15, 2^7]                              */
   const float* swa_scale;      /* fp32 [B, swa_rows] powers of two (swa_fp8)   */
+  /* Paged FP4 cache (block_table != NULL): codes / scales hold cache_rows
+     physical rows in pages of page_size rows; position t of sequence b is
+     row block_table[b * max_pages + t / page_size] * page_size
+         + t % page_size.
+     A negative page id, or a row at or past cache_rows, leaves that Top-K
+     entry empty.  The same stride and alignment rules apply; a row may be
+     shared by several sequences.  NULL: the contiguous [B, T] layout above. */
+  const int32_t* block_table;  /* [B, max_pages] int32, 4-byte aligned        */
+  int32_t max_pages;           /* >= ceil(T / page_size)                       */
+  int32_t page_size;           /* power of two, 1 .. 65536                     */
+  int64_t cache_rows;          /* < 2^24; cache_rows * codes_stride and
+                                  cache_rows * scales_stride < 4 GiB - 8 KiB   */
+  /* Window ring buffer: NULL, or [B] int32 start slots.  Window row r of
+     sequence b (the r of the window description above) is stored in slot
+     (swa_start[b] + r) mod swa_rows of that sequence's swa (and swa_scale)
+     rows, so a decode step overwrites one slot instead of shifting the
+     window.  Starts outside [0, swa_rows) count as 0.  */
+  const int32_t* swa_start;
 } csa2_attn_args;
 
 /* Bytes of workspace csa2_sparse_attn needs for these arguments (may be 0). */

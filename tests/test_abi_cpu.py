@@ -112,6 +112,41 @@ def test_index_append_rejects(lib):
         assert f(ctypes.byref(bad), None, 16, 256, ws, 16, 512, 4, 512, 16, 256, 16, 32, None) == 2
 
 
+def test_paged_rejects(lib):
+    """Paged-cache and window-ring arguments are validated before any launch:
+    page size a power of two in 1 .. 65536, enough pages for T, the cache
+    within 2^24 rows and 4 GiB, 4-byte alignment; no compute runs (no GPU)."""
+    import fp4_kv_cache_e4m3_amd as m
+
+    def args(**kw):
+        base = dict(batch=2, q_per_seq=1, kv_len=64, heads=16, dim=512, q=256, codes=256,
+                    codes_stride=256, scales=256, scales_stride=32, topk=256, topk_k=512, swa=256,
+                    window=128, swa_len=None, sm_scale=0.0, out=256, block_table=256, max_pages=4,
+                    page_size=16, cache_rows=1024)
+        base.update(kw)
+        return m.AttnArgs(**base)
+
+    sa = lib.csa2_attn_workspace_size
+    assert sa(ctypes.byref(args())) > 0
+    assert sa(ctypes.byref(args(page_size=24))) == 0            # not a power of two
+    assert sa(ctypes.byref(args(page_size=0))) == 0
+    assert sa(ctypes.byref(args(page_size=1 << 17))) == 0
+    assert sa(ctypes.byref(args(max_pages=3))) == 0              # 3 x 16 < T = 64
+    assert sa(ctypes.byref(args(cache_rows=1 << 24))) == 0
+    assert sa(ctypes.byref(args(cache_rows=-1))) == 0
+    assert lib.csa2_sparse_attn(ctypes.byref(args(block_table=258)), None, 0, None) == 3
+    assert lib.csa2_sparse_attn(ctypes.byref(args(swa_start=258)), None, 0, None) == 3
+    q = lib.csa2_quantize_kv_paged
+    #        x    xs   rows dim  seq  pos  bt   B  maxp ps  codes cs   scales ss rows_c stream
+    assert q(16, 512, 4, 512, 16, 16, 16, 2, 4, 24, 16, 256, 16, 32, 64, None) == 2     # page size
+    assert q(16, 512, 4, 512, 16, 16, 16, 0, 4, 16, 16, 256, 16, 32, 64, None) == 2     # batch
+    assert q(16, 512, 4, 512, None, 16, 16, 2, 4, 16, 16, 256, 16, 32, 64, None) == 1   # no row_seq
+    assert q(16, 512, 4, 512, 16, 16, None, 2, 4, 16, 16, 256, 16, 32, 64, None) == 1   # no table
+    assert q(16, 512, 4, 512, 18, 16, 16, 2, 4, 16, 16, 256, 16, 32, 64, None) == 3     # misaligned
+    assert q(16, 512, 4, 33, 16, 16, 16, 2, 4, 16, 16, 256, 16, 32, 64, None) == 2      # dim % 32
+    assert q(None, 512, 0, 512, None, None, None, 2, 4, 16, None, 256, None, 32, 64, None) == 0   # empty
+
+
 def test_attn_rejects(lib):
     import fp4_kv_cache_e4m3_amd as m
 
