@@ -53,7 +53,8 @@ def group_bytes(w) -> dict:
     scan = w.batch * T * (w.idx_dim + f8) + nq * w.idx_heads * (w.idx_dim + 4 + f8)
     select = nq * ((0 if w.encoder else 2048 * 4) + 512 * 4)   # pool (decoder groups) + topk written
     quant = w.batch * w.new_per_seq * (w.dim * 4 + row)
-    attn_layer = (nq * (512 * row + w.heads * w.dim * 2 + w.heads * w.dim * 4 + 512 * 4)
+    bt = 512 * 4 if w.page_size else 0                     # paged: one block-table entry per Top-K entry
+    attn_layer = (nq * (512 * row + w.heads * w.dim * 2 + w.heads * w.dim * 4 + 512 * 4 + bt)
                   + w.batch * w.swa_rows * (w.dim + 4 if w.swa8 else w.dim * 2))
     reindex = nq * (2048 * 4 + 16384 * (w.idx_dim + f8) + w.idx_heads * (w.idx_dim + 4 + f8) + 512 * 4)
     n_full, n_rx = w.layers.count("full"), w.layers.count("reindex")
@@ -250,7 +251,7 @@ def main() -> int:
         "config": {"workload": w.name, "batch": w.batch, "q_per_seq": w.q_per_seq,
                    "kv_len": w.kv_len, "dim": w.dim, "heads": w.heads, "window": w.window,
                    "idx_heads": w.idx_heads, "idx_dim": w.idx_dim, "layers": list(w.layers),
-                   "idx_fp8": w.idx_fp8, "swa8": w.swa8},
+                   "idx_fp8": w.idx_fp8, "swa8": w.swa8, "page_size": w.page_size, "swa_ring": w.swa_ring},
         "hbm_gbs_group": round(nbytes["total"] / (ms / 1e3) / 1e9, 1),
         "hbm_frac_group": round(nbytes["total"] / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
         "breakdown_ms": dict({"pass": "separate, one event after every call (sums per stage)"},

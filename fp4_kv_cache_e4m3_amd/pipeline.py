@@ -41,16 +41,28 @@ class DecodeGroup:
         self.device = device
         dev = device
         B_, T, d = w.batch, w.kv_len, w.dim
-        # ---- FP4 main KV cache: quantised on the device from seeded fp32 rows
-        self.codes = torch.empty((B_ * T, d // 2), dtype=torch.uint8, device=dev)
-        self.scales = torch.empty((B_ * T, d // 16), dtype=torch.uint8, device=dev)
+        # ---- FP4 main KV cache: quantised on the device from seeded fp32 rows,
+        # contiguous [B * T] rows or (paged) pages named by a block table
+        P = w.page_size
+        self.block_table_host = synth.block_table(w) if P else None
+        self.block_table = _dev(self.block_table_host, dev) if P else None
+        n_rows = synth.page_count(w)[1] * P if P else B_ * T
+        self.codes = torch.empty((n_rows, d // 2), dtype=torch.uint8, device=dev)
+        self.scales = torch.empty((n_rows, d // 16), dtype=torch.uint8, device=dev)
         chunk = 65536
         for b in range(B_):
             for r0 in range(0, T, chunk):
                 n = min(chunk, T - r0)
                 src = _dev(synth.kv_source_rows(w, b, r0, n), dev)
-                base = b * T + r0
-                B.quantize_kv(src, self.codes[base:base + n], self.scales[base:base + n])
+                if P:
+                    seq = torch.full((n,), b, dtype=torch.int32, device=dev)
+                    pos = torch.arange(r0, r0 + n, dtype=torch.int32, device=dev)
+                    B.quantize_kv_paged(src, seq, pos, self.block_table, P, self.codes, self.scales)
+                    torch.cuda.synchronize()
+                    del seq, pos
+                else:
+                    base = b * T + r0
+                    B.quantize_kv(src, self.codes[base:base + n], self.scales[base:base + n])
                 del src
         # ---- indexer keys [B, T, D_I] (int8, or E4M3 codes with [B, T] scales)
         self.ik = torch.empty((B_, T, w.idx_dim), dtype=torch.uint8 if w.idx_fp8 else torch.int8, device=dev)
@@ -70,7 +82,17 @@ class DecodeGroup:
         for l in self.index_layers[1:]:
             self._iqw[l] = (_dev(synth.index_q(w, l), dev), _dev(synth.index_w(w, l), dev), qs(l))
         self.q = [_dev(synth.attn_q_bf16(w, l).view(np.int16), dev) for l in range(nl)]
-        self.swa = [_dev(synth.swa_bf16(w, l).view(np.int16), dev) for l in range(nl)]
+        # windows: linear [B, W - 1 + Qn] rows, or a ring whose row r of
+        # sequence b sits in slot (start[b] + r) mod rows
+        self.swa_start = [None] * nl
+        self.swa = []
+        for l in range(nl):
+            rows = synth.swa_bf16(w, l)
+            if w.swa_ring:
+                st = synth.swa_ring_start(w, l)
+                rows = np.stack([np.roll(rows[b], int(st[b]), axis=0) for b in range(B_)])
+                self.swa_start[l] = _dev(st, dev)
+            self.swa.append(_dev(np.ascontiguousarray(rows).view(np.int16), dev))
         # 8-bit window rows: quantised once on the device from the bf16 rows
         self.swa_scale = [None] * nl
         if w.swa8:
@@ -96,7 +118,9 @@ class DecodeGroup:
             k += m in ("full", "reindex")
             self._topk_of.append(self.topks[k])
         self.aargs = [B.attn_args(self.q[l], self.codes, self.scales, self._topk_of[l], self.swa[l], self.out[l],
-                                  w.q_per_seq, T, w.window, swa_scale=self.swa_scale[l]) for l in range(nl)]
+                                  w.q_per_seq, T, w.window, swa_scale=self.swa_scale[l],
+                                  block_table=self.block_table, page_size=P, swa_start=self.swa_start[l])
+                      for l in range(nl)]
         aws = max(B.attn_workspace_size(a) for a in self.aargs)
         self.aws = torch.empty(max(256, aws), dtype=torch.uint8, device=dev) if aws > 0 else None
         # a step's new entries land in the last new_per_seq slots of each
@@ -104,7 +128,12 @@ class DecodeGroup:
         # sequence or per slot index, whichever is fewer
         n = w.new_per_seq
         self._new_calls = []
-        if n == 1:
+        self._new_paged = None
+        if P:                                   # one call: rows through the block table
+            self._new_paged = (self.new_rows,
+                               _dev(np.repeat(np.arange(B_, dtype=np.int32), n), dev),
+                               _dev(np.tile(np.arange(T - n, T, dtype=np.int32), B_), dev))
+        elif n == 1:
             self._new_calls.append((self.new_rows, self.codes[T - 1::T], self.scales[T - 1::T]))
         elif B_ <= n:
             for b in range(B_):
@@ -125,8 +154,19 @@ class DecodeGroup:
 
     # the stages of one step (bench.py times them apart)
     def quantize_new(self, stream=None) -> None:
+        if self._new_paged is not None:
+            x, seq, pos = self._new_paged
+            B.quantize_kv_paged(x, seq, pos, self.block_table, self.w.page_size, self.codes, self.scales, stream)
         for x, c, s in self._new_calls:
             B.quantize_kv(x, c, s, stream)
+
+    def cache_rows(self, b: int, positions) -> np.ndarray:
+        """Rows of codes / scales holding sequence b's positions."""
+        positions = np.asarray(positions, dtype=np.int64)
+        if not self.w.page_size:
+            return b * self.w.kv_len + positions
+        P = self.w.page_size
+        return self.block_table_host[b, positions // P].astype(np.int64) * P + positions % P
 
     def pool_out(self):
         """The pool buffer, or None for an encoder group (no Reindex consumes it)."""

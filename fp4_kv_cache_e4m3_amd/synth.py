@@ -49,6 +49,8 @@ T_IW_POOL = 9
 T_IK_SCALE = 10   # fp32 per-position scales of FP8 indexer keys
 T_IQ_SCALE = 11   # fp32 per-(query, head) scales of FP8 indexer queries (per layer)
 T_IQ_SCALE_POOL = 12
+T_PAGES = 13      # page order of a paged cache
+T_RING = 14       # window ring start slots
 
 # FP8 indexer codes: magnitude codes 0x28..0x57 (E4M3 values 0.25 .. 15), either sign
 _E4M3_LO, _E4M3_N = 0x28, 48
@@ -77,6 +79,8 @@ class Workload:
     encoder: bool = False    # encoder (prefill) group: no Reindex layer consumes the pool
     swa8: bool = False       # window rows kept as 8-bit codes (quantised from the same bf16 rows)
     idx_fp8: bool = False    # indexer q / k as E4M3 codes with fp32 scales instead of integers
+    page_size: int = 0       # > 0: the FP4 cache is paged (pages of this many rows, shuffled)
+    swa_ring: bool = False   # window rows held in a ring buffer with a per-sequence start slot
     note: str = ""
 
     @property
@@ -135,7 +139,12 @@ C2_SWA8 = C2.replace(name="decode_group_full_reuse3_b32_t65536_swa8", swa8=True,
 C2_IDX8 = C2.replace(name="decode_group_full_reuse3_b32_t65536_idx8", wid=8, idx_fp8=True,
                      note="decoder group 1 with FP8 indexer keys and queries")
 
-WORKLOADS = {w.name: w for w in (C1, C2, C3, C4, C5, C6, C2_SWA8, C2_IDX8)}
+# decoder group 1 over a paged FP4 cache (256-row pages in shuffled order)
+# and ring-buffer windows
+C2_PAGED = C2.replace(name="decode_group_full_reuse3_b32_t65536_paged", wid=9, page_size=256, swa_ring=True,
+                      note="decoder group 1 over a paged FP4 cache and ring-buffer windows")
+
+WORKLOADS = {w.name: w for w in (C1, C2, C3, C4, C5, C6, C2_SWA8, C2_IDX8, C2_PAGED)}
 
 
 def _rng(w: Workload, tensor: int, layer: int = 0, chunk: int = 0) -> np.random.Generator:
@@ -269,6 +278,24 @@ def index_w(w: Workload, layer: int = 0, pool_source: bool = False) -> np.ndarra
     if w.idx_fp8:
         return (g.random((w.nq, w.idx_heads), dtype=np.float32) * np.float32(1.25) - np.float32(0.25)).astype(np.float32)
     return g.integers(1, w.w_max + 1, size=(w.nq, w.idx_heads)).astype(np.float32)
+
+
+def page_count(w: Workload) -> tuple:
+    """(pages per sequence, physical pages) of a paged cache: one sequence's
+    worth of spare pages that no block-table entry names."""
+    per_seq = (w.kv_len + w.page_size - 1) // w.page_size
+    return per_seq, (w.batch + 1) * per_seq
+
+
+def block_table(w: Workload) -> np.ndarray:
+    """[B, pages per sequence] int32: distinct physical pages in random order."""
+    per_seq, n_phys = page_count(w)
+    return _rng(w, T_PAGES).permutation(n_phys)[: w.batch * per_seq].astype(np.int32).reshape(w.batch, per_seq)
+
+
+def swa_ring_start(w: Workload, layer: int = 0) -> np.ndarray:
+    """[B] int32 ring slot of each sequence's first window row."""
+    return _rng(w, T_RING, layer).integers(0, w.swa_rows, size=w.batch).astype(np.int32)
 
 
 def attn_q_bf16(w: Workload, layer: int = 0) -> np.ndarray:
