@@ -102,6 +102,8 @@ CASES = [  # (B, Qn, T, H_I, D_I, kind)
     (1, 3, 33000, 4, 128, "synth"),
     (1, 2, 100003, 8, 128, "synth"),    # more than 8,192 blocks
     (2, 1, 2500, 2, 64, "all"),         # fewer than 512 blocks
+    (1, 16, 9000, 8, 128, "synth"),     # 128 score rows: two scan workgroups per key chunk
+    (2, 9, 12000, 16, 64, "all"),       # 144 score rows: three, the last partial
 ]
 
 
