@@ -54,8 +54,9 @@ def group_bytes(w) -> dict:
     select = nq * ((0 if w.encoder else 2048 * 4) + 512 * 4)   # pool (decoder groups) + topk written
     quant = w.batch * w.new_per_seq * (w.dim * 4 + row)
     bt = 512 * 4 if w.page_size else 0                     # paged: one block-table entry per Top-K entry
+    swa_new = nq * (w.dim * 2 + w.dim + 4) if w.swa8 else 0  # 8-bit windows: the step's new rows quantised
     attn_layer = (nq * (512 * row + w.heads * w.dim * 2 + w.heads * w.dim * 4 + 512 * 4 + bt)
-                  + w.batch * w.swa_rows * (w.dim + 4 if w.swa8 else w.dim * 2))
+                  + w.batch * w.swa_rows * (w.dim + 4 if w.swa8 else w.dim * 2) + swa_new)
     reindex = nq * (2048 * 4 + 16384 * (w.idx_dim + f8) + w.idx_heads * (w.idx_dim + 4 + f8) + 512 * 4)
     n_full, n_rx = w.layers.count("full"), w.layers.count("reindex")
     total = n_full * (quant + scan + select) + n_rx * reindex + len(w.layers) * attn_layer
@@ -87,9 +88,12 @@ def cpu_baseline(w, max_queries: int, min_seconds: float = 10.0) -> dict:
           for l in range(len(w.layers))]
     sws = [synth.bf16_bits_to_f32(synth.swa_bf16(w, l)[:n_seq]).astype(np.float64)
            for l in range(len(w.layers))]
+    new_sw = None
     if w.swa8:                                          # the window as its 8-bit rows hold it
         from oracle import swa8 as oswa8
         sws = [oswa8.swa_values(*oswa8.quantize_swa_rows(s.reshape(-1, w.dim))).reshape(s.shape) for s in sws]
+        new_sw = [synth.bf16_bits_to_f32(synth.new_swa_rows(w, l)[:n_seq * qn]).astype(np.float64)
+                  for l in range(len(w.layers))]
     srcs = [synth.kv_source(w, b) for b in range(n_seq)]
     f8 = w.idx_fp8
     qsc = (lambda l, src=False: synth.index_q_scale(w, l, src)[:nqs]) if f8 else (lambda l, src=False: None)
@@ -119,6 +123,10 @@ def cpu_baseline(w, max_queries: int, min_seconds: float = 10.0) -> dict:
     def one_pass():
         if w.layers[0] == "full":
             oquant.quantize_rows(newr)
+        if new_sw is not None:                          # the step's new 8-bit window rows
+            for l in range(len(w.layers)):
+                v = oswa8.swa_values(*oswa8.quantize_swa_rows(new_sw[l]))
+                sws[l][:, w.swa_rows - qn:] = v.reshape(n_seq, qn, w.dim)
         for qi in range(nqs):
             b = qi // qn
             pool, pos, _ = full_q(qi, b)

@@ -82,7 +82,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.csa2_quantize_kv_paged.restype = ctypes.c_int
     lib.csa2_quantize_kv_paged.argtypes = [vp, i64, i64, i32, vp, vp, vp, i32, i32, i32, vp, i64, vp, i64, i64, vp]
     lib.csa2_quantize_swa_fp8.restype = ctypes.c_int
-    lib.csa2_quantize_swa_fp8.argtypes = [vp, i64, i64, i32, vp, i64, vp, vp]
+    lib.csa2_quantize_swa_fp8.argtypes = [vp, i64, i64, i32, vp, i64, vp, i64, vp]
     lib.csa2_dequantize_kv.restype = ctypes.c_int
     lib.csa2_dequantize_kv.argtypes = [vp, i64, vp, i64, i64, i32, vp, i64, vp]
     lib.csa2_index_workspace_size.restype = sz
@@ -153,10 +153,11 @@ def quantize_kv_paged(x: torch.Tensor, row_seq: torch.Tensor, row_pos: torch.Ten
 
 def quantize_swa_fp8(x: torch.Tensor, out: torch.Tensor, scales: torch.Tensor, stream=None) -> None:
     """8-bit window rows: bf16 bits x [rows, d] (int16/uint16 storage) -> E4M3
-    codes out [rows, >=d] (uint8) and power-of-two row scales [rows] (fp32)."""
+    codes out [rows, >=d] (uint8) and power-of-two row scales [rows] (fp32,
+    any row stride)."""
     rows, dim = x.shape
     _check(load().csa2_quantize_swa_fp8(_ptr(x), x.stride(0), rows, dim, _ptr(out), out.stride(0), _ptr(scales),
-                                        _stream(stream)))
+                                        scales.stride(0), _stream(stream)))
 
 
 def dequantize_kv(codes: torch.Tensor, scales: torch.Tensor, out: torch.Tensor, stream=None) -> None:

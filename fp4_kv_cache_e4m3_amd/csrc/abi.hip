@@ -236,14 +236,14 @@ int csa2_quantize_kv_paged(const float* x, int64_t x_stride, int64_t rows, int32
 }
 
 int csa2_quantize_swa_fp8(const uint16_t* x, int64_t x_stride, int64_t rows, int32_t dim, uint8_t* out,
-                          int64_t out_stride, float* scales, hipStream_t stream) {
+                          int64_t out_stride, float* scales, int64_t scales_stride, hipStream_t stream) {
   if (rows < 0 || dim < 8 || dim > 512 || dim % 8) return CSA2_ERR_SHAPE;
   if (rows == 0) return CSA2_OK;
   if (!x || !out || !scales) return CSA2_ERR_NULL;
-  if (x_stride < dim || out_stride < dim) return CSA2_ERR_SHAPE;
+  if (x_stride < dim || out_stride < dim || scales_stride < 1) return CSA2_ERR_SHAPE;
   if (!aligned(x, 16) || x_stride % 8 || !aligned(out, 8) || out_stride % 8 || !aligned(scales, 4))
     return CSA2_ERR_ALIGN;
-  return hip_status(launch_quantize_swa8(x, x_stride, rows, dim, out, out_stride, scales, stream));
+  return hip_status(launch_quantize_swa8(x, x_stride, rows, dim, out, out_stride, scales, scales_stride, stream));
 }
 
 int csa2_dequantize_kv(const uint8_t* codes, int64_t codes_stride, const uint8_t* scales,

@@ -191,7 +191,7 @@ hipError_t launch_quantize_paged(const float* x, int64_t xs, int64_t rows, int d
                                  uint8_t* codes, int64_t cs, uint8_t* scales, int64_t ss, hipStream_t st);
 bool quantize_fits_quad(int64_t rows, int dim);           // small enough for four lanes per group
 hipError_t launch_quantize_swa8(const uint16_t* x, int64_t xs, int64_t rows, int dim, uint8_t* out, int64_t os,
-                                float* scales, hipStream_t st);
+                                float* scales, int64_t ss, hipStream_t st);
 hipError_t launch_dequantize(const uint8_t* codes, int64_t cs, const uint8_t* scales, int64_t ss,
                              int64_t rows, int dim, float* out, int64_t os, hipStream_t st);
 hipError_t launch_index_scan(const ScanParams& p, int heads, int dim, hipStream_t st);

@@ -141,7 +141,7 @@ CSA2_DEV uint32_t e4m3_rne_code(float y) {          // 0 <= y <= 448
 
 __global__ __launch_bounds__(256) void k_quantize_swa8(const uint16_t* __restrict__ x, int64_t xs, int64_t rows,
                                                        int dim, uint8_t* __restrict__ out, int64_t os,
-                                                       float* __restrict__ scales) {
+                                                       float* __restrict__ scales, int64_t ss) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;                         // whole waves
@@ -171,14 +171,14 @@ __global__ __launch_bounds__(256) void k_quantize_swa8(const uint16_t* __restric
     word[i / 4] |= c << (8 * (i % 4));
   }
   if (act) *reinterpret_cast<u2*>(out + row * os + 8 * lane) = u2{word[0], word[1]};
-  if (lane == 0) scales[row] = __builtin_ldexpf(1.0f, k);
+  if (lane == 0) scales[row * ss] = __builtin_ldexpf(1.0f, k);
 }
 
 hipError_t launch_quantize_swa8(const uint16_t* x, int64_t xs, int64_t rows, int dim, uint8_t* out, int64_t os,
-                                float* scales, hipStream_t st) {
+                                float* scales, int64_t ss, hipStream_t st) {
   if (rows == 0) return hipSuccess;
   hipLaunchKernelGGL(k_quantize_swa8, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, x, xs, rows, dim, out, os,
-                     scales);
+                     scales, ss);
   return hipGetLastError();
 }
 

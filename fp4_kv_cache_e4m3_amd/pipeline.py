@@ -93,14 +93,22 @@ class DecodeGroup:
                 rows = np.stack([np.roll(rows[b], int(st[b]), axis=0) for b in range(B_)])
                 self.swa_start[l] = _dev(st, dev)
             self.swa.append(_dev(np.ascontiguousarray(rows).view(np.int16), dev))
-        # 8-bit window rows: quantised once on the device from the bf16 rows
+        # 8-bit window rows: the older rows quantised once on the device from
+        # the bf16 rows; each step quantises its query tokens' new rows into
+        # the newest slots (rows swa_rows - Qn .. swa_rows - 1)
         self.swa_scale = [None] * nl
+        self._swa_new = [[] for _ in range(nl)]
+        assert not (w.swa8 and w.swa_ring), "8-bit rings are not set up here"
         if w.swa8:
             for l in range(nl):
                 codes8 = torch.empty((B_, w.swa_rows, d), dtype=torch.uint8, device=dev)
                 sc8 = torch.empty((B_, w.swa_rows), dtype=torch.float32, device=dev)
                 B.quantize_swa_fp8(self.swa[l].view(B_ * w.swa_rows, d), codes8.view(B_ * w.swa_rows, d), sc8.view(-1))
                 self.swa[l], self.swa_scale[l] = codes8, sc8
+                nb = _dev(synth.new_swa_rows(w, l).view(np.int16), dev).view(B_, w.q_per_seq, d)
+                for i in range(w.q_per_seq):          # one strided call per query slot
+                    r = w.swa_rows - w.q_per_seq + i
+                    self._swa_new[l].append((nb[:, i, :], codes8[:, r, :], sc8[:, r]))
         # ---- outputs and workspaces
         nq = w.nq
         self.pool = torch.full((nq, B.POOL_BLOCKS), -1, dtype=torch.int32, device=dev)
@@ -160,6 +168,11 @@ class DecodeGroup:
         for x, c, s in self._new_calls:
             B.quantize_kv(x, c, s, stream)
 
+    def quantize_window(self, l: int, stream=None) -> None:
+        """8-bit windows: the step's new window rows of layer l into their slots."""
+        for x, c, s in self._swa_new[l]:
+            B.quantize_swa_fp8(x, c, s, stream)
+
     def cache_rows(self, b: int, positions) -> np.ndarray:
         """Rows of codes / scales holding sequence b's positions."""
         positions = np.asarray(positions, dtype=np.int64)
@@ -203,6 +216,8 @@ class DecodeGroup:
             elif m == "reindex":
                 ia, tk = self.iargs_by_layer[l], self._topk_of[l]
                 out.append(("reindex", lambda ia=ia, tk=tk: B.index_reindex(ia, self.pool, tk, self.iws, stream)))
+            if self._swa_new[l]:
+                out.append(("quantize_window", lambda l=l: self.quantize_window(l, stream)))
             out.append(("attention", lambda l=l: B.sparse_attn(self.aargs[l], self.aws, stream)))
         return out
 

@@ -51,6 +51,7 @@ T_IQ_SCALE = 11   # fp32 per-(query, head) scales of FP8 indexer queries (per la
 T_IQ_SCALE_POOL = 12
 T_PAGES = 13      # page order of a paged cache
 T_RING = 14       # window ring start slots
+T_NEW_SWA = 15    # bf16 window rows of the tokens appended this step (per layer)
 
 # FP8 indexer codes: magnitude codes 0x28..0x57 (E4M3 values 0.25 .. 15), either sign
 _E4M3_LO, _E4M3_N = 0x28, 48
@@ -278,6 +279,13 @@ def index_w(w: Workload, layer: int = 0, pool_source: bool = False) -> np.ndarra
     if w.idx_fp8:
         return (g.random((w.nq, w.idx_heads), dtype=np.float32) * np.float32(1.25) - np.float32(0.25)).astype(np.float32)
     return g.integers(1, w.w_max + 1, size=(w.nq, w.idx_heads)).astype(np.float32)
+
+
+def new_swa_rows(w: Workload, layer: int = 0) -> np.ndarray:
+    """[B * Qn, d] bf16 bit patterns of N(0,1) window rows of the step's query
+    tokens (one per query, the newest rows of the window)."""
+    x = _rng(w, T_NEW_SWA, layer).standard_normal((w.nq, w.dim), dtype=np.float32)
+    return f32_to_bf16_bits(x)
 
 
 def page_count(w: Workload) -> tuple:

@@ -127,11 +127,14 @@ int csa2_quantize_kv_paged(const float* x, int64_t x_stride, int64_t rows, int32
  *   dim     % 8 == 0, 8 .. 512.
  *   out     E4M3 codes, row r at out + r * out_stride (bytes); 8-byte aligned,
  *           out_stride % 8 == 0, out_stride >= dim.
- *   scales  fp32 [rows], 4-byte aligned.
+ *   scales  fp32, row r's scale at scales[r * scales_stride]; 4-byte aligned,
+ *           scales_stride >= 1 (strided rows let a decode step write its new
+ *           row straight into the newest slot of every sequence's window).
  * csa2_sparse_attn reads such rows as its window when swa_fp8 is set.
  */
 int csa2_quantize_swa_fp8(const uint16_t* x, int64_t x_stride, int64_t rows, int32_t dim,
-                          uint8_t* out, int64_t out_stride, float* scales, hipStream_t stream);
+                          uint8_t* out, int64_t out_stride, float* scales, int64_t scales_stride,
+                          hipStream_t stream);
 
 /*
  * csa2_dequantize_kv -- values of FP4 rows as fp32 (code value x E4M3 scale,

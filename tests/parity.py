@@ -88,6 +88,16 @@ def oracle_selected_rows(w: synth.Workload, topk, queries, with_new_rows=True) -
     return out
 
 
+def window_bits(w: synth.Workload, layer: int) -> np.ndarray:
+    """bf16 window rows of a layer as a step leaves them: with 8-bit windows
+    the step writes its query tokens' new rows into the newest slots."""
+    bits = synth.swa_bf16(w, layer)
+    if w.swa8:
+        nb = synth.new_swa_rows(w, layer).reshape(w.batch, w.q_per_seq, w.dim)
+        bits[:, w.swa_rows - w.q_per_seq:] = nb
+    return bits
+
+
 def oracle_attention(w: synth.Workload, q_bits, swa_bits, topk, with_new_rows=True, queries=None,
                      swa_len=None, rows=None):
     """Oracle output of one layer for the given Top-K (oracle's own), [nq, H, d].

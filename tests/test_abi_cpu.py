@@ -49,13 +49,14 @@ def test_quantize_rejects(lib):
 
 def test_quantize_swa_fp8_rejects(lib):
     f = lib.csa2_quantize_swa_fp8
-    assert f(16, 512, 4, 12, 16, 512, 16, None) == 2                       # dim % 8
-    assert f(16, 1024, 4, 1024, 16, 1024, 16, None) == 2                   # dim > 512
-    assert f(None, 512, 4, 512, 16, 512, 16, None) == 1                    # NULL x
-    assert f(16, 512, 4, 512, 16, 256, 16, None) == 2                      # out stride < dim
-    assert f(8, 512, 4, 512, 16, 512, 16, None) == 3                       # x misaligned
-    assert f(16, 512, 4, 512, 16, 512, 18, None) == 3                      # scales misaligned
-    assert f(None, 512, 0, 512, None, 512, None, None) == 0                # empty: no-op
+    assert f(16, 512, 4, 12, 16, 512, 16, 1, None) == 2                    # dim % 8
+    assert f(16, 1024, 4, 1024, 16, 1024, 16, 1, None) == 2                # dim > 512
+    assert f(None, 512, 4, 512, 16, 512, 16, 1, None) == 1                 # NULL x
+    assert f(16, 512, 4, 512, 16, 256, 16, 1, None) == 2                   # out stride < dim
+    assert f(16, 512, 4, 512, 16, 512, 16, 0, None) == 2                   # scale stride < 1
+    assert f(8, 512, 4, 512, 16, 512, 16, 1, None) == 3                    # x misaligned
+    assert f(16, 512, 4, 512, 16, 512, 18, 1, None) == 3                   # scales misaligned
+    assert f(None, 512, 0, 512, None, 512, None, 1, None) == 0             # empty: no-op
 
 
 def test_index_rejects(lib):

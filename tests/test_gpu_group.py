@@ -11,7 +11,7 @@ from fp4_kv_cache_e4m3_amd import DecodeGroup, synth
 from oracle import indexer as oidx
 from oracle import indexer_fp8 as o8
 from tests.parity import (ATTN_TOL, fp8_full_errors, fp8_score_bound, host, oracle_attention, oracle_kv_rows,
-                          oracle_selected_rows, rownorm_err)
+                          oracle_selected_rows, rownorm_err, window_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -69,7 +69,7 @@ def check_group(w, sample=None):
     for l, m in enumerate(w.layers):
         k += m in ("full", "reindex")
         got = host(g.out[l])
-        ref = oracle_attention(w, synth.attn_q_bf16(w, l), synth.swa_bf16(w, l), ref_topks[k],
+        ref = oracle_attention(w, synth.attn_q_bf16(w, l), window_bits(w, l), ref_topks[k],
                                with_new_rows=has_full, queries=qs, rows=rows[k])
         err = rownorm_err(got[qs], ref[qs])
         assert err <= ATTN_TOL, (l, err)

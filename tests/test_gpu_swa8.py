@@ -9,6 +9,7 @@ import fp4_kv_cache_e4m3_amd as csa2
 from oracle import attention as oattn
 from oracle import swa8
 from tests.parity import ATTN_TOL, bf16_values, dev, host, rownorm_err
+from fp4_kv_cache_e4m3_amd import synth
 from tests.test_gpu_attn import CASES, make_case
 
 pytestmark = pytest.mark.gpu
@@ -101,3 +102,20 @@ def test_attn_with_8bit_partial_window():
     got, ref = run_case(case, swa_len=[129, 5, 0], kill=[1, 4, 5])
     assert np.all(got[4:6] == 0.0)
     assert rownorm_err(got, ref) <= ATTN_TOL
+
+
+def test_quantize_into_newest_window_slots():
+    """A decode step's new rows go straight into slot R-1 of every sequence's
+    window (rows strided by R * d bytes, scales by R): bit-exact against the
+    oracle, every other slot untouched."""
+    B, R, d = 5, 128, 512
+    rng = np.random.default_rng(77)
+    bits = synth.f32_to_bf16_bits((rng.standard_normal((B, d)) * 3).astype(np.float32))
+    codes = torch.full((B, R, d), 0xA5, dtype=torch.uint8, device="cuda")
+    sc = torch.full((B, R), float("nan"), dtype=torch.float32, device="cuda")
+    csa2.quantize_swa_fp8(dev(bits.view(np.int16)), codes[:, R - 1, :], sc[:, R - 1])
+    got_c, got_s = host(codes), host(sc)
+    rc, rs = swa8.quantize_swa_rows(bf16_values(bits))
+    np.testing.assert_array_equal(got_c[:, R - 1], rc)
+    np.testing.assert_array_equal(got_s[:, R - 1], rs.astype(np.float32))
+    assert np.all(got_c[:, :R - 1] == 0xA5) and np.all(np.isnan(got_s[:, :R - 1]))
