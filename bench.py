@@ -27,10 +27,10 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak (AMD spec)
 
 # HBM bytes per k_index_scan launch measured with rocprofv3 FETCH_SIZE and
 # WRITE_SIZE (each scaled by what the counter reads for a plain 1 GiB copy) on
-# the workload and kernel source named here; reported only while both match.
-SCAN_TRAFFIC = {"workload": "decode_group_full_reuse3_b32_t65536",
-                "source_sha256": "fea1cb9bd8dbdbe457ee78f4c684e9b0054e7a3074d15e8dc9f9b69495aedc6e",   # csrc/index.hip + csrc/common.h
-                "bytes": 268859802 + 9437901}
+# the workloads and kernel sources named here; reported only while they match.
+SCAN_TRAFFIC = {"source_sha256": "55d1bb418e37ce6c3549156d2e0aafe865edb24d6b4df566ff9ed0a51df5418a",   # csrc/index.hip + csrc/common.h
+                "bytes": {"decode_group_full_reuse3_b32_t65536": 268862259 + 9438003,
+                          "decode_group_full_reuse3_b32_t65536_idx8": 278879642 + 9437901}}
 
 
 def scan_traffic(w):
@@ -40,8 +40,8 @@ def scan_traffic(w):
         with open(os.path.join(ROOT, "fp4_kv_cache_e4m3_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     sha = h.hexdigest()
-    if w.name == SCAN_TRAFFIC["workload"] and sha == SCAN_TRAFFIC["source_sha256"]:
-        return SCAN_TRAFFIC["bytes"]
+    if sha == SCAN_TRAFFIC["source_sha256"]:
+        return SCAN_TRAFFIC["bytes"].get(w.name)
     return None
 
 

@@ -14,14 +14,14 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 constexpr int64_t kMaxKvLen = 1 << 20;           // 131,072 blocks per query in the pool select
-constexpr int64_t kMaxScoreRows = 64 * 65535;    // Qn * H_I: 64 score rows per scan workgroup
+constexpr int64_t kMaxScoreRows = 64 * 65535;    // Qn * H_I: 64 score rows per scan workgroup (32 with fp8)
 
 int check_index(const csa2_index_args* a) {
   if (!a) return CSA2_ERR_NULL;
   if (a->batch < 0 || a->q_per_seq < 1 || a->kv_len < 0 || a->kv_len > kMaxKvLen) return CSA2_ERR_SHAPE;
   if (!(a->heads == 2 || a->heads == 4 || a->heads == 8 || a->heads == 16)) return CSA2_ERR_SHAPE;
   if (!(a->dim == 64 || a->dim == 128)) return CSA2_ERR_SHAPE;
-  if ((int64_t)a->q_per_seq * a->heads > kMaxScoreRows) return CSA2_ERR_SHAPE;
+  if ((int64_t)a->q_per_seq * a->heads > (a->fp8 == 1 ? kMaxScoreRows / 2 : kMaxScoreRows)) return CSA2_ERR_SHAPE;
   const int64_t nq = (int64_t)a->batch * a->q_per_seq;
   if (nq > 0 && (!a->q || !a->w)) return CSA2_ERR_NULL;
   if (nq > 0 && a->kv_len > 0 && !a->k) return CSA2_ERR_NULL;

@@ -15,9 +15,9 @@
 // Design (gfx950, wave64): the indexer keys stream once from HBM.  Each wave
 // takes 16-token tiles: an int8 MFMA 16x16x64 contracts the 16 token rows (B
 // operand, one token per lane column) with up to 64 score rows (A operand: 64
-// of the sequence's Qn * H_I query-head rows; more rows take more workgroups,
-// so prefill chunks reuse the keys from L2), so the dot products are exact
-// int32.  ReLU, head weights and the head sum run on the 4 accumulator rows a
+// of the sequence's Qn * H_I query-head rows, 32 for E4M3 operands; more rows
+// take more workgroups, so prefill chunks reuse the keys from L2), so the dot
+// products are exact int32.  ReLU, head weights and the head sum run on the 4 accumulator rows a
 // lane holds plus cross-lane adds; the 8-token block maximum is three DPP max
 // steps inside each 16-lane row.  Token keys and block keys (order-preserving
 // uint32 of the fp32 score) go to the workspace.
@@ -32,13 +32,16 @@ namespace csa2 {
 template <int DI, int HI, bool F8>
 __global__ __launch_bounds__(256) void k_index_scan(ScanParams p) {
   constexpr int KK = DI / 64;                 // MFMAs per tile
+  // M tiles (16 score rows each) per workgroup: 4, or 2 for E4M3 operands,
+  // whose fp16 decodes the compiler keeps for the whole loop
+  constexpr int MTX = F8 ? 2 : 4;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int b = blockIdx.y;
   // score rows (query j, head h) -> row j*HI + h; this workgroup takes rows
-  // [r0, r0 + rows_used) of its sequence, at most 64 (4 M tiles)
-  const int r0 = 64 * (int)blockIdx.z;
-  const int rows_used = min(64, p.qn * HI - r0);
+  // [r0, r0 + rows_used) of its sequence, at most 16 * MTX
+  const int r0 = 16 * MTX * (int)blockIdx.z;
+  const int rows_used = min(16 * MTX, p.qn * HI - r0);
   const int MT = (rows_used + 15) >> 4;
   const int j_lo = r0 / HI, j_hi = (r0 + rows_used - 1) / HI;
 
@@ -52,10 +55,10 @@ __global__ __launch_bounds__(256) void k_index_scan(ScanParams p) {
   const int64_t t0 = 0, tend = vmax;
 
   // A operands (score rows) and weights of the 4 output rows each lane holds
-  v4i a[4][KK];
-  float wv[4][4];
+  v4i a[MTX][KK];
+  float wv[MTX][4];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+  for (int mt = 0; mt < MTX; ++mt) {
     const int r = 16 * mt + n;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
@@ -78,9 +81,9 @@ __global__ __launch_bounds__(256) void k_index_scan(ScanParams p) {
       wv[mt][i] = w;
     }
   }
-  int nvq[4];   // visibility of the queries whose rows this lane's group holds (HI >= 4 case)
+  int nvq[MTX];   // visibility of the queries whose rows this lane's group holds (HI >= 4 case)
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+  for (int mt = 0; mt < MTX; ++mt) {
     const int j = (r0 + 16 * mt + 4 * g) / HI;
     nvq[mt] = (int)min((int64_t)(p.nvis && j < p.qn ? p.nvis[b * p.qn + j] : p.T), p.T);
   }
@@ -95,7 +98,7 @@ __global__ __launch_bounds__(256) void k_index_scan(ScanParams p) {
     const int64_t t = t0 + 16 * it + n;
     const bool tok_ok = t < tend;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
+    for (int mt = 0; mt < MTX; ++mt) {
       if (mt >= MT) break;
       float val[4];
       index_dots<KK, F8>(a[mt], bf, val);
@@ -207,7 +210,8 @@ __global__ __launch_bounds__(256) void k_index_scan(ScanParams p) {
 template <int DI, int HI>
 static void launch_scan_t(const ScanParams& p, hipStream_t st) {
   const int64_t chunks = (p.T + p.chunk - 1) / p.chunk;
-  const int64_t groups = ((int64_t)p.qn * HI + 63) / 64;    // 64 score rows per workgroup
+  const int rows = p.iks ? 32 : 64;                          // score rows per workgroup
+  const int64_t groups = ((int64_t)p.qn * HI + rows - 1) / rows;
   const dim3 grid((unsigned)chunks, (unsigned)p.batch, (unsigned)groups);
   if (p.iks)
     hipLaunchKernelGGL((k_index_scan<DI, HI, true>), grid, dim3(256), 0, st, p);

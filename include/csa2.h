@@ -202,7 +202,8 @@ size_t csa2_index_workspace_size(const csa2_index_args* args);
  *          (may be NULL when no Reindex layer will consume it).
  *   topk   out [nq, 512] int32 positions, ascending, padded with -1.
  *   ws     workspace of csa2_index_workspace_size(args) bytes, 256-B aligned.
- * Supports Qn * H_I <= 4,194,240 (prefill chunks included).
+ * Supports Qn * H_I <= 4,194,240 (prefill chunks included; 2,097,120 with
+ * fp8).
  */
 int csa2_index_full(const csa2_index_args* args, int32_t* pool, int32_t* topk,
                     void* ws, size_t ws_size, hipStream_t stream);

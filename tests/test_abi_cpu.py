@@ -96,6 +96,10 @@ def test_index_fp8_rejects(lib):
                                   16, 16, 256, ws, None) == 1
     b = m.IndexArgs(1, 1, 100, 8, 64, 16, 16, 16, None, 1, 16, 16)
     assert lib.csa2_index_workspace_size(ctypes.byref(b)) == ws
+    # 32 score rows per scan workgroup with fp8: Qn * H_I <= 32 * 65535
+    assert lib.csa2_index_workspace_size(ctypes.byref(m.IndexArgs(1, 131070, 100, 16, 64, 16, 16, 16, None, 1, 16, 16))) > 0
+    assert lib.csa2_index_workspace_size(ctypes.byref(m.IndexArgs(1, 131071, 100, 16, 64, 16, 16, 16, None, 1, 16, 16))) == 0
+    assert lib.csa2_index_workspace_size(ctypes.byref(m.IndexArgs(1, 131071, 100, 16, 64, 16, 16, 16, None))) > 0
 
 
 def test_index_append_rejects(lib):
