@@ -28,13 +28,13 @@ namespace csa2 {
 // Channel order of the int8 operands: lane group g takes, in k-step kk, the 16
 // channels 16g + 64kk .. +15, so the 4 lanes of a key row read 64 contiguous
 // bytes per load (the contraction only needs both operands to agree).
-// HI: indexer heads (2, 4, 8, 16); DI: indexer dim (64, 128); F8: E4M3 codes.
-template <int DI, int HI, bool F8>
+// HI: indexer heads (2, 4, 8, 16); DI: indexer dim (64, 128); F8: E4M3 codes;
+// MTX: M tiles (16 score rows each) per workgroup.  Fewer M tiles hold fewer
+// query operands in registers (more waves per SIMD); more M tiles read each
+// key tile for more score rows.
+template <int DI, int HI, bool F8, int MTX>
 __global__ __launch_bounds__(256) void k_index_scan(ScanParams p) {
   constexpr int KK = DI / 64;                 // MFMAs per tile
-  // M tiles (16 score rows each) per workgroup: 4, or 2 for E4M3 operands,
-  // whose fp16 decodes the compiler keeps for the whole loop
-  constexpr int MTX = F8 ? 2 : 4;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int b = blockIdx.y;
@@ -210,13 +210,19 @@ __global__ __launch_bounds__(256) void k_index_scan(ScanParams p) {
 template <int DI, int HI>
 static void launch_scan_t(const ScanParams& p, hipStream_t st) {
   const int64_t chunks = (p.T + p.chunk - 1) / p.chunk;
-  const int rows = p.iks ? 32 : 64;                          // score rows per workgroup
+  // two M tiles for E4M3 operands (whose fp16 decodes the compiler keeps for
+  // the whole loop) and for sequences of at most 32 score rows (decode: 84
+  // instead of 118 VGPRs, 5 waves per SIMD); four otherwise
+  const bool two = p.iks || (int64_t)p.qn * HI <= 32;
+  const int rows = two ? 32 : 64;                            // score rows per workgroup
   const int64_t groups = ((int64_t)p.qn * HI + rows - 1) / rows;
   const dim3 grid((unsigned)chunks, (unsigned)p.batch, (unsigned)groups);
   if (p.iks)
-    hipLaunchKernelGGL((k_index_scan<DI, HI, true>), grid, dim3(256), 0, st, p);
+    hipLaunchKernelGGL((k_index_scan<DI, HI, true, 2>), grid, dim3(256), 0, st, p);
+  else if (two)
+    hipLaunchKernelGGL((k_index_scan<DI, HI, false, 2>), grid, dim3(256), 0, st, p);
   else
-    hipLaunchKernelGGL((k_index_scan<DI, HI, false>), grid, dim3(256), 0, st, p);
+    hipLaunchKernelGGL((k_index_scan<DI, HI, false, 4>), grid, dim3(256), 0, st, p);
 }
 
 hipError_t launch_index_scan(const ScanParams& p, int heads, int dim, hipStream_t st) {
