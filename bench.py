@@ -28,9 +28,9 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak (AMD spec)
 # HBM bytes per k_index_scan launch measured with rocprofv3 FETCH_SIZE and
 # WRITE_SIZE (each scaled by what the counter reads for a plain 1 GiB copy) on
 # the workloads and kernel sources named here; reported only while they match.
-SCAN_TRAFFIC = {"source_sha256": "55d1bb418e37ce6c3549156d2e0aafe865edb24d6b4df566ff9ed0a51df5418a",   # csrc/index.hip + csrc/common.h
-                "bytes": {"decode_group_full_reuse3_b32_t65536": 268862259 + 9438003,
-                          "decode_group_full_reuse3_b32_t65536_idx8": 278879642 + 9437901}}
+SCAN_TRAFFIC = {"source_sha256": "f3f1c76d7cdaf1731b2db303ac5fa51ab31f934b079dfdd6b9b3d422d6ba8fa9",   # csrc/index.hip + csrc/common.h
+                "bytes": {"decode_group_full_reuse3_b32_t65536": 268807782 + 9437798,
+                          "decode_group_full_reuse3_b32_t65536_idx8": 278917120 + 9437901}}
 
 
 def scan_traffic(w):

@@ -31,8 +31,9 @@ namespace csa2 {
 // HI: indexer heads (2, 4, 8, 16); DI: indexer dim (64, 128); F8: E4M3 codes;
 // MTX: M tiles (16 score rows each) per workgroup.  Fewer M tiles hold fewer
 // query operands in registers (more waves per SIMD); more M tiles read each
-// key tile for more score rows.
-template <int DI, int HI, bool F8, int MTX>
+// key tile for more score rows.  NT: the keys are read by one workgroup per
+// key tile (non-temporal loads).
+template <int DI, int HI, bool F8, int MTX, bool NT>
 __global__ __launch_bounds__(256) void k_index_scan(ScanParams p) {
   constexpr int KK = DI / 64;                 // MFMAs per tile
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -157,11 +158,14 @@ __global__ __launch_bounds__(256) void k_index_scan(ScanParams p) {
   // lane, hit 16 distinct bank groups per 16 lanes.  All U tiles are issued
   // before the first MFMA.
   constexpr int U = 4;
-  // The keys are read once per step and never again within it: non-temporal
-  // loads (cache policy NT) stream them past the last-level cache, so the
-  // step's other working set (the attention's window rows and gathered FP4
-  // rows, which decode re-reads from one step to the next) stays resident.
-  constexpr int kNonTemporal = 2;
+  // With one score-row group per sequence (decode, verify) the keys are read
+  // once per step and never again within it: non-temporal loads (cache
+  // policy NT) stream them past the last-level cache, so the step's other
+  // working set (the attention's window rows and gathered FP4 rows, which
+  // decode re-reads from one step to the next) stays resident.  With several
+  // groups (prefill) every group reads each key tile, and the later reads
+  // should hit the cache: normal policy.
+  constexpr int kNonTemporal = NT ? 2 : 0;
   constexpr int CPR = DI / 16;                 // 16-byte chunks per key row
   constexpr int RPI = 1024 / DI;               // rows per 1 KiB load instruction
   constexpr int NI = 16 * DI / 1024;           // load instructions per 16-row tile
@@ -175,7 +179,7 @@ __global__ __launch_bounds__(256) void k_index_scan(ScanParams p) {
       skv[u] = 1.0f;
       if constexpr (F8) {
         const int64_t t = 16 * (base + 4 * u + wave) + n;
-        if (t < tend) skv[u] = __builtin_nontemporal_load(iksb + t);
+        if (t < tend) skv[u] = NT ? __builtin_nontemporal_load(iksb + t) : iksb[t];
       }
     }
 #pragma unroll
@@ -217,12 +221,16 @@ static void launch_scan_t(const ScanParams& p, hipStream_t st) {
   const int rows = two ? 32 : 64;                            // score rows per workgroup
   const int64_t groups = ((int64_t)p.qn * HI + rows - 1) / rows;
   const dim3 grid((unsigned)chunks, (unsigned)p.batch, (unsigned)groups);
-  if (p.iks)
-    hipLaunchKernelGGL((k_index_scan<DI, HI, true, 2>), grid, dim3(256), 0, st, p);
-  else if (two)
-    hipLaunchKernelGGL((k_index_scan<DI, HI, false, 2>), grid, dim3(256), 0, st, p);
-  else
-    hipLaunchKernelGGL((k_index_scan<DI, HI, false, 4>), grid, dim3(256), 0, st, p);
+  const bool once = groups == 1;                             // each key tile read by one workgroup
+  if (p.iks) {
+    if (once) hipLaunchKernelGGL((k_index_scan<DI, HI, true, 2, true>), grid, dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((k_index_scan<DI, HI, true, 2, false>), grid, dim3(256), 0, st, p);
+  } else if (two) {                                          // groups == 1
+    hipLaunchKernelGGL((k_index_scan<DI, HI, false, 2, true>), grid, dim3(256), 0, st, p);
+  } else {
+    if (once) hipLaunchKernelGGL((k_index_scan<DI, HI, false, 4, true>), grid, dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((k_index_scan<DI, HI, false, 4, false>), grid, dim3(256), 0, st, p);
+  }
 }
 
 hipError_t launch_index_scan(const ScanParams& p, int heads, int dim, hipStream_t st) {
