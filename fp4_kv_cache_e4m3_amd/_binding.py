@@ -25,7 +25,8 @@ EXPORTS = (
     "csa2_status_string", "csa2_version", "csa2_quantize_kv", "csa2_quantize_kv_paged", "csa2_quantize_swa_fp8",
     "csa2_dequantize_kv",
     "csa2_index_workspace_size", "csa2_index_full", "csa2_index_scan", "csa2_index_select",
-    "csa2_index_full_append", "csa2_index_select_append", "csa2_index_reindex",
+    "csa2_index_full_append", "csa2_index_select_append", "csa2_index_full_append_paged",
+    "csa2_index_select_append_paged", "csa2_index_reindex",
     "csa2_attn_workspace_size", "csa2_sparse_attn",
 )
 
@@ -81,6 +82,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.csa2_quantize_kv.argtypes = [vp, i64, i64, i32, vp, i64, vp, i64, vp]
     lib.csa2_quantize_kv_paged.restype = ctypes.c_int
     lib.csa2_quantize_kv_paged.argtypes = [vp, i64, i64, i32, vp, vp, vp, i32, i32, i32, vp, i64, vp, i64, i64, vp]
+    for name in ("csa2_index_full_append_paged", "csa2_index_select_append_paged"):
+        getattr(lib, name).restype = ctypes.c_int
+        getattr(lib, name).argtypes = [ctypes.POINTER(IndexArgs), vp, vp, vp, sz, vp, i64, i64, i32, vp, vp, vp,
+                                       i32, i32, i32, vp, i64, vp, i64, i64, vp]
     lib.csa2_quantize_swa_fp8.restype = ctypes.c_int
     lib.csa2_quantize_swa_fp8.argtypes = [vp, i64, i64, i32, vp, i64, vp, i64, vp]
     lib.csa2_dequantize_kv.restype = ctypes.c_int
@@ -206,6 +211,28 @@ def index_full_append(args: IndexArgs, pool, topk, ws, x, codes, scales, stream=
     _check(load().csa2_index_full_append(ctypes.byref(args), _ptr(pool), _ptr(topk), _ptr(ws),
                                          ws.numel() * ws.element_size() if ws is not None else 0,
                                          *_append_args(x, codes, scales), _stream(stream)))
+
+
+def _paged_append_args(x, row_seq, row_pos, block_table, page_size, codes, scales):
+    B, max_pages = block_table.shape
+    return (_ptr(x), x.stride(0), x.shape[0], x.shape[1], _ptr(row_seq), _ptr(row_pos), _ptr(block_table), B,
+            max_pages, page_size, _ptr(codes), codes.stride(0), _ptr(scales), scales.stride(0), codes.shape[0])
+
+
+def index_full_append_paged(args: IndexArgs, pool, topk, ws, x, row_seq, row_pos, block_table, page_size: int,
+                            codes, scales, stream=None) -> None:
+    """index_full plus quantize_kv_paged of the step's new rows."""
+    _check(load().csa2_index_full_append_paged(
+        ctypes.byref(args), _ptr(pool), _ptr(topk), _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0,
+        *_paged_append_args(x, row_seq, row_pos, block_table, page_size, codes, scales), _stream(stream)))
+
+
+def index_select_append_paged(args: IndexArgs, pool, topk, ws, x, row_seq, row_pos, block_table, page_size: int,
+                              codes, scales, stream=None) -> None:
+    """index_select plus quantize_kv_paged of the step's new rows."""
+    _check(load().csa2_index_select_append_paged(
+        ctypes.byref(args), _ptr(pool), _ptr(topk), _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0,
+        *_paged_append_args(x, row_seq, row_pos, block_table, page_size, codes, scales), _stream(stream)))
 
 
 def index_select_append(args: IndexArgs, pool, topk, ws, x, codes, scales, stream=None) -> None:

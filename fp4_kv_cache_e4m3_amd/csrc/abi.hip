@@ -217,10 +217,11 @@ int csa2_quantize_kv(const float* x, int64_t x_stride, int64_t rows, int32_t dim
   return hip_status(launch_quantize(x, x_stride, rows, dim, codes, codes_stride, scales, scales_stride, stream));
 }
 
-int csa2_quantize_kv_paged(const float* x, int64_t x_stride, int64_t rows, int32_t dim, const int32_t* row_seq,
-                           const int32_t* row_pos, const int32_t* block_table, int32_t batch, int32_t max_pages,
-                           int32_t page_size, uint8_t* codes, int64_t codes_stride, uint8_t* scales,
-                           int64_t scales_stride, int64_t cache_rows, hipStream_t stream) {
+// arguments of new rows written through a block table; fills d on success
+int check_paged_rows(const float* x, int64_t x_stride, int64_t rows, int32_t dim, const int32_t* row_seq,
+                     const int32_t* row_pos, const int32_t* block_table, int32_t batch, int32_t max_pages,
+                     int32_t page_size, const uint8_t* codes, int64_t codes_stride, const uint8_t* scales,
+                     int64_t scales_stride, int64_t cache_rows, PagedRows& d) {
   int st = check_quantize(x, x_stride, rows, dim, codes, codes_stride, scales, scales_stride);
   if (st != CSA2_OK) return st;
   if (page_size < 1 || page_size > 65536 || (page_size & (page_size - 1)) || max_pages < 1 || batch < 1 ||
@@ -229,10 +230,54 @@ int csa2_quantize_kv_paged(const float* x, int64_t x_stride, int64_t rows, int32
   if (rows == 0) return CSA2_OK;
   if (!row_seq || !row_pos || !block_table) return CSA2_ERR_NULL;
   if (!aligned(row_seq, 4) || !aligned(row_pos, 4) || !aligned(block_table, 4)) return CSA2_ERR_ALIGN;
-  PagedRows d{row_seq, row_pos, block_table, batch, max_pages, 0, cache_rows};
+  d = PagedRows{row_seq, row_pos, block_table, batch, max_pages, 0, cache_rows};
   while ((1 << d.shift) < page_size) ++d.shift;
+  return CSA2_OK;
+}
+
+int csa2_quantize_kv_paged(const float* x, int64_t x_stride, int64_t rows, int32_t dim, const int32_t* row_seq,
+                           const int32_t* row_pos, const int32_t* block_table, int32_t batch, int32_t max_pages,
+                           int32_t page_size, uint8_t* codes, int64_t codes_stride, uint8_t* scales,
+                           int64_t scales_stride, int64_t cache_rows, hipStream_t stream) {
+  PagedRows d{};
+  const int st = check_paged_rows(x, x_stride, rows, dim, row_seq, row_pos, block_table, batch, max_pages, page_size,
+                                  codes, codes_stride, scales, scales_stride, cache_rows, d);
+  if (st != CSA2_OK || rows == 0) return st;
   return hip_status(launch_quantize_paged(x, x_stride, rows, dim, d, codes, codes_stride, scales, scales_stride,
                                           stream));
+}
+
+int csa2_index_select_append_paged(const csa2_index_args* a, int32_t* pool, int32_t* topk, const void* ws,
+                                   size_t ws_size, const float* x, int64_t x_stride, int64_t rows, int32_t dim,
+                                   const int32_t* row_seq, const int32_t* row_pos, const int32_t* block_table,
+                                   int32_t batch, int32_t max_pages, int32_t page_size, uint8_t* codes,
+                                   int64_t codes_stride, uint8_t* scales, int64_t scales_stride, int64_t cache_rows,
+                                   hipStream_t stream) {
+  int st = check_select(a, pool, topk, ws, ws_size);
+  if (st != CSA2_OK) return st;
+  PagedRows d{};
+  st = check_paged_rows(x, x_stride, rows, dim, row_seq, row_pos, block_table, batch, max_pages, page_size, codes,
+                        codes_stride, scales, scales_stride, cache_rows, d);
+  if (st != CSA2_OK) return st;
+  const QuantJob qj{x, x_stride, rows, dim / 16, codes, codes_stride, scales, scales_stride, d};
+  return select_impl(a, pool, topk, ws, ws_size, qj, stream);
+}
+
+int csa2_index_full_append_paged(const csa2_index_args* a, int32_t* pool, int32_t* topk, void* ws, size_t ws_size,
+                                 const float* x, int64_t x_stride, int64_t rows, int32_t dim, const int32_t* row_seq,
+                                 const int32_t* row_pos, const int32_t* block_table, int32_t batch,
+                                 int32_t max_pages, int32_t page_size, uint8_t* codes, int64_t codes_stride,
+                                 uint8_t* scales, int64_t scales_stride, int64_t cache_rows, hipStream_t stream) {
+  int st = check_select(a, pool, topk, ws, ws_size);
+  if (st != CSA2_OK) return st;
+  PagedRows d{};
+  st = check_paged_rows(x, x_stride, rows, dim, row_seq, row_pos, block_table, batch, max_pages, page_size, codes,
+                        codes_stride, scales, scales_stride, cache_rows, d);
+  if (st != CSA2_OK) return st;
+  st = csa2_index_scan(a, ws, ws_size, stream);
+  if (st != CSA2_OK) return st;
+  const QuantJob qj{x, x_stride, rows, dim / 16, codes, codes_stride, scales, scales_stride, d};
+  return select_impl(a, pool, topk, ws, ws_size, qj, stream);
 }
 
 int csa2_quantize_swa_fp8(const uint16_t* x, int64_t x_stride, int64_t rows, int32_t dim, uint8_t* out,

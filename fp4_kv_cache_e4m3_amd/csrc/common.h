@@ -143,9 +143,15 @@ struct ScanParams {
   uint32_t* bkeys; int64_t bk_stride;                    // [nq, bk_stride]
 };
 // FP4 quantisation of `rows` main-KV rows of `groups` 16-channel groups
+// destination of new rows in a paged cache
+struct PagedRows {
+  const int32_t* seq; const int32_t* pos; const int32_t* bt;   // bt == NULL: contiguous rows
+  int32_t batch, max_pages, shift; int64_t cache_rows;
+};
 struct QuantJob {
   const float* x; int64_t xs, rows; int32_t groups;
   uint8_t* codes; int64_t cs; uint8_t* scales; int64_t ss;
+  PagedRows pg;                                          // pg.bt != NULL: rows go through a block table
 };
 struct SelectParams {
   const uint32_t* tkeys; int64_t tk_stride;
@@ -182,11 +188,6 @@ struct AttnParams {
 
 hipError_t launch_quantize(const float* x, int64_t xs, int64_t rows, int dim, uint8_t* codes,
                            int64_t cs, uint8_t* scales, int64_t ss, hipStream_t st);
-// destination of new rows in a paged cache
-struct PagedRows {
-  const int32_t* seq; const int32_t* pos; const int32_t* bt;
-  int32_t batch, max_pages, shift; int64_t cache_rows;
-};
 hipError_t launch_quantize_paged(const float* x, int64_t xs, int64_t rows, int dim, const PagedRows& d,
                                  uint8_t* codes, int64_t cs, uint8_t* scales, int64_t ss, hipStream_t st);
 bool quantize_fits_quad(int64_t rows, int dim);           // small enough for four lanes per group

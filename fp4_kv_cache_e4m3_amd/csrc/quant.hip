@@ -69,13 +69,7 @@ __global__ __launch_bounds__(256) void k_quantize_paged(const float* __restrict_
                                                    int groups, uint8_t* __restrict__ codes, int64_t cs,
                                                    uint8_t* __restrict__ scales, int64_t ss, PagedRows d) {
   quantize_quad_thread_to(x, xs, rows, groups, codes, cs, scales, ss, (int64_t)blockIdx.x * blockDim.x + threadIdx.x,
-                          [&](int64_t r) -> int64_t {
-                            const int32_t sq = d.seq[r], t = d.pos[r];
-                            if (sq < 0 || sq >= d.batch || t < 0 || (t >> d.shift) >= d.max_pages) return -1;
-                            const int32_t page = d.bt[(int64_t)sq * d.max_pages + (t >> d.shift)];
-                            const int64_t row = ((int64_t)page << d.shift) + (t & ((1 << d.shift) - 1));
-                            return page >= 0 && row < d.cache_rows ? row : -1;
-                          });
+                          [&](int64_t r) { return paged_row(d, r); });
 }
 
 hipError_t launch_quantize_paged(const float* x, int64_t xs, int64_t rows, int dim, const PagedRows& d,

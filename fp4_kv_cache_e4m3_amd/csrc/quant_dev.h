@@ -108,4 +108,24 @@ CSA2_DEV void quantize_quad_thread(const float* __restrict__ x, int64_t xs, int6
   quantize_quad_thread_to(x, xs, rows, groups, codes, cs, scales, ss, gid, [](int64_t r) { return r; });
 }
 
+// Cache row of new row r in a paged cache: position pos[r] of sequence
+// seq[r] is row block_table[seq][pos / P] * P + pos % P; -1 when the
+// sequence, the position or the page is out of range.
+CSA2_DEV int64_t paged_row(const PagedRows& d, int64_t r) {
+  const int32_t sq = d.seq[r], t = d.pos[r];
+  if (sq < 0 || sq >= d.batch || t < 0 || (t >> d.shift) >= d.max_pages) return -1;
+  const int32_t page = d.bt[(int64_t)sq * d.max_pages + (t >> d.shift)];
+  const int64_t row = ((int64_t)page << d.shift) + (t & ((1 << d.shift) - 1));
+  return page >= 0 && row < d.cache_rows ? row : -1;
+}
+
+// one thread of the four-lane quantiser for a job (contiguous or paged rows)
+CSA2_DEV void quantize_job_thread(const QuantJob& q, int64_t gid) {
+  if (q.pg.bt)
+    quantize_quad_thread_to(q.x, q.xs, q.rows, q.groups, q.codes, q.cs, q.scales, q.ss, gid,
+                            [&](int64_t r) { return paged_row(q.pg, r); });
+  else
+    quantize_quad_thread(q.x, q.xs, q.rows, q.groups, q.codes, q.cs, q.scales, q.ss, gid);
+}
+
 }  // namespace csa2

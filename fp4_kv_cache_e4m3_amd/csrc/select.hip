@@ -342,8 +342,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_full(SelectParams p) {
   __shared__ SelShared sh;
   // workgroups past the selection quantise the step's new main-KV rows
   if ((int)blockIdx.x >= p.sel_wgs) {
-    quantize_quad_thread(p.qj.x, p.qj.xs, p.qj.rows, p.qj.groups, p.qj.codes, p.qj.cs, p.qj.scales, p.qj.ss,
-                         (int64_t)(blockIdx.x - p.sel_wgs) * kSelThreads + threadIdx.x);
+    quantize_job_thread(p.qj, (int64_t)(blockIdx.x - p.sel_wgs) * kSelThreads + threadIdx.x);
     return;
   }
   // p.roles == 2: two workgroups per query, role 0 selects and writes the
@@ -686,8 +685,11 @@ hipError_t launch_select_full(const SelectParams& p, int nq, int64_t max_blocks,
     if (quantize_fits_quad(p.qj.rows, 16 * p.qj.groups)) {
       extra = (int)((4 * p.qj.rows * p.qj.groups + kSelThreads - 1) / kSelThreads);
     } else {
-      const hipError_t e = launch_quantize(p.qj.x, p.qj.xs, p.qj.rows, 16 * p.qj.groups, p.qj.codes, p.qj.cs,
-                                           p.qj.scales, p.qj.ss, st);
+      const hipError_t e = p.qj.pg.bt
+          ? launch_quantize_paged(p.qj.x, p.qj.xs, p.qj.rows, 16 * p.qj.groups, p.qj.pg, p.qj.codes, p.qj.cs,
+                                  p.qj.scales, p.qj.ss, st)
+          : launch_quantize(p.qj.x, p.qj.xs, p.qj.rows, 16 * p.qj.groups, p.qj.codes, p.qj.cs, p.qj.scales,
+                            p.qj.ss, st);
       if (e != hipSuccess) return e;
     }
   }

@@ -191,7 +191,20 @@ class DecodeGroup:
         split_full), reindex, attention."""
         out = []
         for l, m in enumerate(self.w.layers):
-            if m == "full" and len(self._new_calls) == 1:
+            if m == "full" and self._new_paged is not None:
+                # paged cache: the new rows go through the block table, as
+                # extra workgroups of the selection launch
+                ia, tk = self.iargs_by_layer[l], self._topk_of[l]
+                x, seq, pos = self._new_paged
+                pg = (x, seq, pos, self.block_table, self.w.page_size, self.codes, self.scales)
+                if split_full:
+                    out.append(("index_scan", lambda ia=ia: B.index_scan(ia, self.iws, stream)))
+                    out.append(("index_select", lambda ia=ia, tk=tk, pg=pg: B.index_select_append_paged(
+                        ia, self.pool_out(), tk, self.iws, *pg, stream)))
+                else:
+                    out.append(("index_full", lambda ia=ia, tk=tk, pg=pg: B.index_full_append_paged(
+                        ia, self.pool_out(), tk, self.iws, *pg, stream)))
+            elif m == "full" and len(self._new_calls) == 1:
                 # one strided job: the new rows are quantised by the Full
                 # layer's selection launch itself
                 ia, tk = self.iargs_by_layer[l], self._topk_of[l]

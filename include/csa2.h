@@ -247,6 +247,28 @@ int csa2_index_select_append(const csa2_index_args* args, int32_t* pool, int32_t
                              hipStream_t stream);
 
 /*
+ * csa2_index_full_append_paged / csa2_index_select_append_paged --
+ * csa2_index_full_append / csa2_index_select_append with the new rows
+ * written into a paged cache as csa2_quantize_kv_paged writes them (same
+ * arguments, same skipping rules), as extra workgroups of the selection
+ * launch.  Everything is validated before anything is launched.
+ */
+int csa2_index_full_append_paged(const csa2_index_args* args, int32_t* pool, int32_t* topk,
+                                 void* ws, size_t ws_size,
+                                 const float* x, int64_t x_stride, int64_t rows, int32_t dim,
+                                 const int32_t* row_seq, const int32_t* row_pos,
+                                 const int32_t* block_table, int32_t batch, int32_t max_pages, int32_t page_size,
+                                 uint8_t* codes, int64_t codes_stride, uint8_t* scales, int64_t scales_stride,
+                                 int64_t cache_rows, hipStream_t stream);
+int csa2_index_select_append_paged(const csa2_index_args* args, int32_t* pool, int32_t* topk,
+                                   const void* ws, size_t ws_size,
+                                   const float* x, int64_t x_stride, int64_t rows, int32_t dim,
+                                   const int32_t* row_seq, const int32_t* row_pos,
+                                   const int32_t* block_table, int32_t batch, int32_t max_pages, int32_t page_size,
+                                   uint8_t* codes, int64_t codes_stride, uint8_t* scales, int64_t scales_stride,
+                                   int64_t cache_rows, hipStream_t stream);
+
+/*
  * csa2_index_reindex -- Reindex layer: rescore only the positions of the last
  * Full layer's pool with this layer's own iq / iw and select the top
  * min(512, #positions) by (score desc, position asc).

@@ -150,6 +150,16 @@ def test_paged_rejects(lib):
     assert q(16, 512, 4, 512, 18, 16, 16, 2, 4, 16, 16, 256, 16, 32, 64, None) == 3     # misaligned
     assert q(16, 512, 4, 33, 16, 16, 16, 2, 4, 16, 16, 256, 16, 32, 64, None) == 2      # dim % 32
     assert q(None, 512, 0, 512, None, None, None, 2, 4, 16, None, 256, None, 32, 64, None) == 0   # empty
+    # the fused index + paged new-row calls validate both parts first
+    ia = m.IndexArgs(1, 1, 100, 8, 64, 16, 16, 16, None)
+    ws = lib.csa2_index_workspace_size(ctypes.byref(ia))
+    for f in (lib.csa2_index_full_append_paged, lib.csa2_index_select_append_paged):
+        ok = (16, 512, 4, 512, 16, 16, 16, 2, 4, 16, 16, 256, 16, 32, 64)
+        assert f(ctypes.byref(ia), None, 16, 256, ws, *ok[:9], 24, *ok[10:], None) == 2           # page size
+        assert f(ctypes.byref(ia), None, 16, 256, ws, *ok[:6], None, *ok[7:], None) == 1          # no table
+        assert f(ctypes.byref(ia), None, 16, 256, ws - 1, *ok, None) == 4                         # workspace
+        bad = m.IndexArgs(1, 1, 100, 3, 64, 16, 16, 16, None)                                      # 3 heads
+        assert f(ctypes.byref(bad), None, 16, 256, ws, *ok, None) == 2
 
 
 def test_attn_rejects(lib):

@@ -155,3 +155,45 @@ def test_quantize_kv_paged_matches_oracle():
         written[row] = True
     assert written.sum() == 6
     assert np.all(got_c[~written] == 0xA5) and np.all(got_s[~written] == 0xA5)
+
+
+@pytest.mark.parametrize("rows,split", [(32, False), (32, True), (600, False)])
+def test_index_append_paged_equals_separate_calls(rows, split):
+    """csa2_index_full_append_paged (and the split select form) give the same
+    pool, Top-512 and paged cache rows as csa2_index_full followed by
+    csa2_quantize_kv_paged; 600 rows x 32 groups exceed the extra-workgroup
+    job and take a launch of their own."""
+    rng = np.random.default_rng(rows + split)
+    B, T, d, P, HI, DI = 4, 5000, 512, 64, 8, 128
+    iq = rng.integers(-8, 9, size=(B, HI, DI), dtype=np.int8)
+    iw = rng.integers(1, 9, size=(B, HI)).astype(np.float32)
+    ik = rng.integers(-8, 9, size=(B, T, DI), dtype=np.int8)
+    bt, _, n_rows = page_layout(rng, B, T, P)
+    x = rng.standard_normal((rows, d)).astype(np.float32)
+    seq = rng.integers(0, B, size=rows).astype(np.int32)
+    pos = rng.permutation(T)[:rows].astype(np.int32)              # distinct positions -> distinct rows
+    d_in = [dev(a) for a in (iq, iw, ik, x, seq, pos, bt)]
+    args = csa2.index_args(d_in[0], d_in[1], d_in[2], 1)
+    ws = torch.empty(max(256, csa2.index_workspace_size(args)), dtype=torch.uint8, device="cuda")
+    outs = []
+    for fused in (True, False):
+        pool = torch.full((B, 2048), -7, dtype=torch.int32, device="cuda")
+        topk = torch.full((B, 512), -7, dtype=torch.int32, device="cuda")
+        codes = torch.full((n_rows, d // 2), 0xA5, dtype=torch.uint8, device="cuda")
+        scales = torch.full((n_rows, d // 16), 0xA5, dtype=torch.uint8, device="cuda")
+        pg = (d_in[3], d_in[4], d_in[5], d_in[6], P, codes, scales)
+        if fused and split:
+            csa2.index_scan(args, ws)
+            csa2.index_select_append_paged(args, pool, topk, ws, *pg)
+        elif fused:
+            csa2.index_full_append_paged(args, pool, topk, ws, *pg)
+        else:
+            csa2.index_full(args, pool, topk, ws)
+            csa2.quantize_kv_paged(d_in[3], d_in[4], d_in[5], d_in[6], P, codes, scales)
+        outs.append([host(pool), host(topk), host(codes), host(scales)])
+    for a, b in zip(*outs):
+        np.testing.assert_array_equal(a, b)
+    rc, rs = oquant.quantize_rows(x)
+    dst = bt[seq, pos // P].astype(np.int64) * P + pos % P
+    np.testing.assert_array_equal(outs[0][2][dst], rc)
+    np.testing.assert_array_equal(outs[0][3][dst], rs)
