@@ -86,6 +86,26 @@ def test_attn_paged_equals_contiguous(case):
     assert rownorm_err(got, want) <= ATTN_TOL
 
 
+@pytest.mark.parametrize("P", [16, 256])
+def test_attn_paged_with_8bit_window_ring(P):
+    """All options together: paged FP4 cache, 8-bit window rows, window ring;
+    bit-identical to the contiguous cache with a linear 8-bit window."""
+    B, Qn, T, d, H, W, k = 3, 2, 3000, 512, 64, 128, 512
+    codes, scales, q, swa, topk = make_case(P + 3, B, Qn, T, d, H, W, k)
+    R = swa.shape[1]
+    c8, s8 = oswa8.quantize_swa_rows(bf16_values(swa).reshape(-1, d))
+    c8, s8 = c8.reshape(B, R, d), s8.reshape(B, R).astype(np.float32)
+    start = np.array([3, 0, R - 2], np.int32)
+    ring = np.stack([np.roll(c8[b], start[b], axis=0) for b in range(B)])
+    rsc = np.stack([np.roll(s8[b], start[b]) for b in range(B)])
+    rng = np.random.default_rng(P)
+    bt, rows, n_rows = page_layout(rng, B, T, P)
+    pc, ps = paged_copy(codes, scales, rows, n_rows)
+    ref = run_attn(q, codes, scales, topk, c8, Qn, T, W, swa_scale=s8)
+    got = run_attn(q, pc, ps, topk, ring, Qn, T, W, block_table=bt, page_size=P, swa_scale=rsc, swa_start=start)
+    np.testing.assert_array_equal(got, ref)
+
+
 def test_attn_paged_shared_and_missing_pages():
     """Two sequences share their first pages (a common prefix); a page id of
     -1 or past the cache leaves its positions out, as -1 Top-K slots do."""
