@@ -28,9 +28,9 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak (AMD spec)
 # HBM bytes per k_index_scan launch measured with rocprofv3 FETCH_SIZE and
 # WRITE_SIZE (each scaled by what the counter reads for a plain 1 GiB copy) on
 # the workloads and kernel sources named here; reported only while they match.
-SCAN_TRAFFIC = {"source_sha256": "58494a46bd526fbfbbb7e363fc1fde144f8a2d87424397abb8a35b6f49565d59",   # csrc/index.hip + csrc/common.h
-                "bytes": {"decode_group_full_reuse3_b32_t65536": 268807987 + 9438106,
-                          "decode_group_full_reuse3_b32_t65536_idx8": 278906266 + 9437901}}
+SCAN_TRAFFIC = {"source_sha256": "1214327788d67b3031e6015cbab68259b978a7f18b83b279fe30910123cbdeb8",   # csrc/index.hip + csrc/common.h
+                "bytes": {"decode_group_full_reuse3_b32_t65536": 268807424 + 9437230,
+                          "decode_group_full_reuse3_b32_t65536_idx8": 278938423 + 9438107}}
 
 
 def scan_traffic(w):

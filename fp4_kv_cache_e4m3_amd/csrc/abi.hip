@@ -316,7 +316,7 @@ int csa2_index_scan(const csa2_index_args* a, void* ws, size_t ws_size, hipStrea
   if (!ws || ws_size < (size_t)L.total || !aligned(ws, 256)) return CSA2_ERR_WORKSPACE;
   uint32_t* tkeys = static_cast<uint32_t*>(ws);
   uint32_t* bkeys = tkeys + L.nq * L.tk_stride;
-  ScanParams sp{a->q, a->w, a->k, a->n_visible, q_scales(a), k_scales(a), a->batch, a->q_per_seq, a->kv_len, 1024,
+  ScanParams sp{a->q, a->w, a->k, a->n_visible, q_scales(a), k_scales(a), a->batch, a->q_per_seq, a->kv_len,
                 tkeys, L.tk_stride, bkeys, L.bk_stride};
   return hip_status(launch_index_scan(sp, a->heads, a->dim, stream));
 }

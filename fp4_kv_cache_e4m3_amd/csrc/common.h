@@ -138,7 +138,7 @@ namespace csa2 {
 struct ScanParams {
   const int8_t* iq; const float* iw; const int8_t* ik; const int32_t* nvis;
   const float* iqs; const float* iks;                    // FP8 indexer: [nq, H_I] and [B, T] scales, else NULL
-  int32_t batch, qn; int64_t T; int32_t chunk;          // tokens per workgroup
+  int32_t batch, qn; int64_t T;
   uint32_t* tkeys; int64_t tk_stride;                    // [nq, tk_stride]
   uint32_t* bkeys; int64_t bk_stride;                    // [nq, bk_stride]
 };

@@ -213,13 +213,19 @@ __global__ __launch_bounds__(256) void k_index_scan(ScanParams p) {
 // ============================================================== launcher
 template <int DI, int HI>
 static void launch_scan_t(const ScanParams& p, hipStream_t st) {
-  const int64_t chunks = (p.T + p.chunk - 1) / p.chunk;
   // two M tiles for E4M3 operands (whose fp16 decodes the compiler keeps for
   // the whole loop) and for sequences of at most 32 score rows (decode: 84
   // instead of 118 VGPRs, 5 waves per SIMD); four otherwise
   const bool two = p.iks || (int64_t)p.qn * HI <= 32;
   const int rows = two ? 32 : 64;                            // score rows per workgroup
   const int64_t groups = ((int64_t)p.qn * HI + rows - 1) / rows;
+  // Tokens per workgroup.  The int8 decode scan: 256, one round of 16 tiles
+  // (batch-32, 64K-entry decode group: step 122 us against 123 / 124.5 /
+  // 126 us with 512 / 1024 / 128).  Every other instantiation: 1024, where
+  // 256 was slower (E4M3 decode scan 53.2 vs 49.2 us, prefill 0.88 vs
+  // 0.64 ms, 1M-entry verify 268 vs 260 us).
+  const int64_t chunk = (!p.iks && two) ? 256 : 1024;
+  const int64_t chunks = (p.T + chunk - 1) / chunk;
   const dim3 grid((unsigned)chunks, (unsigned)p.batch, (unsigned)groups);
   const bool once = groups == 1;                             // each key tile read by one workgroup
   if (p.iks) {
