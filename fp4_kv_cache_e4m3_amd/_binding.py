@@ -174,7 +174,9 @@ def dequantize_kv(codes: torch.Tensor, scales: torch.Tensor, out: torch.Tensor, 
 # ------------------------------------------------------------------ indexer
 def index_args(iq, iw, ik, q_per_seq: int, n_visible=None, q_scale=None, k_scale=None) -> IndexArgs:
     """iq [nq, H_I, D_I], iw fp32 [nq, H_I], ik [B, T, D_I]: int8, or E4M3
-    codes (uint8) with q_scale fp32 [nq, H_I] and k_scale fp32 [B, T]."""
+    codes (uint8) with q_scale fp32 [nq, H_I] and k_scale fp32 [B, T].
+    The struct holds raw device pointers: the tensors must stay alive until
+    the calls that use it are enqueued."""
     nq, heads, dim = iq.shape
     B, T = ik.shape[0], ik.shape[1]
     fp8 = 1 if (q_scale is not None or k_scale is not None) else 0
@@ -256,7 +258,9 @@ def attn_args(q, codes, scales, topk, swa, out, q_per_seq: int, kv_len: int, win
     topk int32 [nq, k]; swa bf16 [B, window-1+Qn, d] -- or, with swa_scale
     (fp32 [B, window-1+Qn]), E4M3 codes uint8 [B, window-1+Qn, d]; out fp32 [nq, H, d].
     Paged cache: block_table int32 [B, max_pages] and page_size, codes / scales
-    then hold every physical row.  swa_start int32 [B]: window ring slots."""
+    then hold every physical row.  swa_start int32 [B]: window ring slots.
+    The struct holds raw device pointers: the tensors must stay alive until
+    the calls that use it are enqueued."""
     nq, heads, dim = q.shape
     paged = block_table is not None
     return AttnArgs(nq // q_per_seq, q_per_seq, kv_len, heads, dim, _ptr(q),

@@ -79,7 +79,10 @@ def run_case(case, swa_len=None, kill=None):
     sc_d = dev(s8.reshape(swa.shape[:2]).astype(np.float32)) if W > 0 else None
     sl_d = dev(np.asarray(swa_len, np.int32)) if swa_len is not None else None
     out = torch.full((nq, H, d), float("nan"), dtype=torch.float32, device="cuda")
-    args = csa2.attn_args(q_d, dev(codes), dev(scales), t_d, sw_d, out, Qn, T, W, sl_d,
+    # the argument struct holds raw pointers: keep every device buffer alive
+    # until the call (a temporary's block could be handed to the workspace)
+    c_d, s_d = dev(codes), dev(scales)
+    args = csa2.attn_args(q_d, c_d, s_d, t_d, sw_d, out, Qn, T, W, sl_d,
                           swa_scale=sc_d if W > 0 else None)
     n = csa2.attn_workspace_size(args)
     ws = torch.empty(max(n, 256), dtype=torch.uint8, device="cuda") if n else None
