@@ -45,6 +45,13 @@
 // softmax uses exp2.
 #include "common.h"
 
+#ifndef CSA2_ATTN_QREG
+#define CSA2_ATTN_QREG 0
+#endif
+#ifndef CSA2_ATTN_WPF
+#define CSA2_ATTN_WPF 1
+#endif
+
 namespace csa2 {
 
 CSA2_DEV void wave_lds_sync() {
@@ -107,20 +114,34 @@ struct Geo {
   static constexpr int PITCH = HALF + 8;   // LDS row pitch of a half-tile, in halves
 };
 
-// Lane -> channel maps of a half (a lane holds 8 channels per 32-channel
-// k-step j; lanes g = 0..3 of an entry share the k-step).  The QK contraction
-// does not care about the channel order as long as K and Q use the same map,
-// so each data type gets the map that coalesces its loads:
-//  * FP4 codes ("runs"): lane g holds two runs of CPL/2 channels, at
-//    g*CPL/2 and HALF/2 + g*CPL/2; the 4 lanes of an entry read one contiguous
-//    stretch of code bytes per load.
-//  * bf16 window rows ("interleaved"): k-step j, lane g holds channels
-//    32j + 8g .. +7; the 4 lanes of an entry read 64 contiguous bytes per load.
-// off(j) + LANE * g is the channel within the half.
+// Column halves.  Each workgroup owns one half of the output channels.  The
+// halves interleave in blocks: the D channels form 4 blocks of BLK = D/4, and
+// half ch holds the second half of every block if ch = 1, the first if ch = 0.
+// A half's channels are numbered o = 0 .. D/2-1 ("half index"); gch(o, ch) is
+// the channel of half index o.  This way lane g of an FP4 entry owns block g
+// outright -- both its halves, BLK/2 contiguous code bytes and BLK/16
+// contiguous scale bytes -- so a tile's gather is one wide load per 16 code
+// bytes and a single load for the scales.
 template <int D>
-struct RunsMap {
-  static constexpr int LANE = Geo<D>::CPL / 2;
-  static constexpr int off(int j) { return (j / (Geo<D>::KH / 2)) * (Geo<D>::HALF / 2) + 8 * (j % (Geo<D>::KH / 2)); }
+struct Halves {
+  static constexpr int BLK = D / 4;
+  static constexpr int SUB = BLK / 2;                 // channels of a half in one block
+  static constexpr int gch(int o, int ch) { return BLK * (o / SUB) + SUB * ch + (o % SUB); }
+};
+
+// Lane -> half-index maps (a lane holds 8 channels per 32-channel k-step j;
+// lanes g = 0..3 of an entry share the k-step).  The QK contraction does not
+// care about the channel order as long as K and Q use the same map, so each
+// data type gets the map that suits its loads; off(j) + LANE * g is the half
+// index of the lane's first channel of k-step j.
+//  * FP4 codes ("blocks"): lane g holds half indices SUB*g .. SUB*g + SUB - 1,
+//    i.e. its own block.
+//  * bf16 window rows ("interleaved"): k-step j, lane g holds half indices
+//    32j + 8g .. +7; the 4 lanes of a row read contiguous bytes.
+template <int D>
+struct BlockMap {
+  static constexpr int LANE = Halves<D>::SUB;
+  static constexpr int off(int j) { return 8 * j; }
 };
 template <int D>
 struct InterMap {
@@ -129,8 +150,8 @@ struct InterMap {
 };
 
 // 8-bit window rows ("pairs"): k-steps 2i and 2i+1 of lane g hold the 16
-// consecutive channels 64i + 16g .. +15 of the half, so one 16-byte load
-// covers two k-steps and the 4 lanes of a row read 64 contiguous bytes.
+// consecutive half indices 64i + 16g .. +15, so one 16-byte load covers two
+// k-steps.
 template <int D>
 struct Fp8Map {
   static constexpr int LANE = 16;
@@ -149,15 +170,16 @@ CSA2_DEV v8h fp8x8_to_half(uint32_t w0, uint32_t w1, float sc) {
   return v8h{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-// FP4 data of one entry for this lane (RunsMap): code words w[h][j] of k-step
-// j and the scale words as loaded (D = 512: one word per run; D = 128: one
-// word for both runs, in s[h][0]); index h = 0 is the workgroup's own half.
-// The scale bytes are picked out where they are used, so issuing a gather
-// never waits for its own data.
+// FP4 data of one entry for this lane (BlockMap): code words w[h][j] of
+// k-step j of half h (h = 0: the workgroup's own half) and the scale bytes of
+// the lane's block as loaded (D = 512: s[0] = groups 8g .. 8g+3, s[1] =
+// groups 8g+4 .. 8g+7; D = 128: one word holding groups 2g, 2g+1).  The
+// scale bytes are picked out where they are used, so issuing a gather never
+// waits for its own data.
 template <int D>
 struct Fp4Raw {
   uint32_t w[2][Geo<D>::KH];
-  uint32_t s[2][2];
+  uint32_t s[2];
 };
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -173,9 +195,8 @@ CSA2_DEV rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 struct Fp4Src {
   rsrc_t codes, scales;
   uint32_t cstride, sstride, oob;
-  int hcb[2], hsb[2];          // code / scale byte offset of each half (0 = own)
-  uint32_t lcb, lsb;           // per-lane code offset, scale word offset
-  uint32_t psel[2];            // per run: v_perm selector of its scale bytes in the scale word
+  int hcb[2];                  // code byte offset of each half within the lane's block (0 = own)
+  uint32_t lcb, lsb;           // per-lane code / scale byte offset (the lane's block)
 };
 
 template <int D>
@@ -189,25 +210,30 @@ CSA2_DEV bool load_fp4(const Fp4Src& src, int32_t pos, uint32_t T, Fp4Raw<D>& r)
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
+    if constexpr (G::KH == 8) {
+      // a half of the lane's block: 32 code bytes, two 16-byte loads
 #pragma unroll
-    for (int run = 0; run < 2; ++run) {
-      if constexpr (G::KH == 8) {
+      for (int i = 0; i < 2; ++i) {
         const u4 c = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                src.codes, rc + src.lcb + run * (G::HALF / 4), src.hcb[h], 0));
-        r.w[h][4 * run + 0] = c[0]; r.w[h][4 * run + 1] = c[1];
-        r.w[h][4 * run + 2] = c[2]; r.w[h][4 * run + 3] = c[3];
-        __builtin_amdgcn_sched_barrier(0);
-        r.s[h][run] = __builtin_amdgcn_raw_buffer_load_b32(src.scales, rs + src.lsb + run * 8, src.hsb[h], 0);
-        __builtin_amdgcn_sched_barrier(0);
-      } else {
-        static_assert(G::KH == 2, "D must be 128 or 512");
-        r.w[h][run] = __builtin_amdgcn_raw_buffer_load_b32(src.codes, rc + src.lcb + run * (G::HALF / 4), src.hcb[h], 0);
-        __builtin_amdgcn_sched_barrier(0);
-        if (run == 0) r.s[h][0] = __builtin_amdgcn_raw_buffer_load_b32(src.scales, rs, src.hsb[h], 0);
+                                                src.codes, rc + src.lcb + 16 * i, src.hcb[h], 0));
+        r.w[h][4 * i + 0] = c[0]; r.w[h][4 * i + 1] = c[1];
+        r.w[h][4 * i + 2] = c[2]; r.w[h][4 * i + 3] = c[3];
         __builtin_amdgcn_sched_barrier(0);
       }
+    } else {
+      static_assert(G::KH == 2, "D must be 128 or 512");
+      const u2 c = __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(src.codes, rc + src.lcb, src.hcb[h], 0));
+      r.w[h][0] = c[0]; r.w[h][1] = c[1];
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
+  if constexpr (G::KH == 8) {
+    const u2 s = __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(src.scales, rs + src.lsb, 0, 0));
+    r.s[0] = s[0]; r.s[1] = s[1];
+  } else {
+    r.s[0] = __builtin_amdgcn_raw_buffer_load_b32(src.scales, rs + src.lsb, 0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
   return valid;
 }
 
@@ -220,15 +246,15 @@ CSA2_DEV v4f mfma_qk(v8bf a, v8bf b, v4f c) { return __builtin_amdgcn_mfma_f32_1
 // One 16-entry tile: logits, online-softmax update, O += P V for the own half.
 // kvf(h, j) gives this lane's 8 channels of k-step j of half h under channel
 // map M as a QK operand of type V8 (fp16 for FP4 rows, the raw bf16 for window
-// rows); the matching Q channels are qf[j] (own half, registers) and
-// qo + M::off(j) (other half, LDS: read per k-step, which keeps the register
-// budget of two waves per SIMD).  stage(kv) turns an own-half operand into the
+// rows); qop(h, j) gives the matching Q channels (the own half from
+// registers, the other half from registers or LDS).  stage(kv) turns an
+// own-half operand into the
 // fp16 V values staged at wrow (this lane's LDS row plus M::LANE * g) for PV;
 // after_qk() runs once the raw tile data has been consumed.
-template <int D, typename M, typename V8, typename KV, typename ST, typename AfterQK>
-CSA2_DEV void attend_tile(const AttnParams& p, KV kvf, ST stage, AfterQK after_qk, bool valid,
-                          const V8 (&qf)[Geo<D>::KH], const uint16_t* qo, _Float16* wrow, const _Float16* vbase, int g,
-                          v4f (&o)[Geo<D>::NT], float& m_run, float& l_run) {
+template <int D, typename M, typename V8, typename KV, typename QO, typename ST, typename AfterQK>
+CSA2_DEV void attend_tile(const AttnParams& p, KV kvf, QO qop, ST stage, AfterQK after_qk, bool valid,
+                          _Float16* wrow, const _Float16* vbase, int g, v4f (&o)[Geo<D>::NT], float& m_run,
+                          float& l_run) {
   constexpr int KH = Geo<D>::KH, NT = Geo<D>::NT;
   // one accumulation chain per half (the two halves interleave); the half sums
   // are added last
@@ -238,7 +264,7 @@ CSA2_DEV void attend_tile(const AttnParams& p, KV kvf, ST stage, AfterQK after_q
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const V8 kv = kvf(h, j);
-      const V8 qv = h == 0 ? qf[j] : *reinterpret_cast<const V8*>(qo + M::off(j));
+      const V8 qv = qop(h, j);
       part[h] = mfma_qk(kv, qv, part[h]);
       if (h == 0) *reinterpret_cast<v8h*>(wrow + M::off(j)) = stage(kv);
     }
@@ -300,6 +326,8 @@ CSA2_DEV void attend_tile(const AttnParams& p, KV kvf, ST stage, AfterQK after_q
 template <int D, int NW, bool S8, bool PG>
 __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
   using G = Geo<D>;
+  constexpr bool QREG = CSA2_ATTN_QREG;             // both halves of Q in registers for the FP4 tiles
+  constexpr bool WPF = CSA2_ATTN_WPF;               // window tile prefetched during the last FP4 pair
   constexpr int KH = G::KH, NT = G::NT, PITCH = G::PITCH, HALF = G::HALF;
   constexpr int TILE_HALVES = 16 * PITCH;
   constexpr int QPITCH = D + 8;
@@ -333,7 +361,10 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
   const int t_end = min(p.n_tiles, (split + 1) * p.tiles_per_split);
   const int sp_end = min(t_end, p.n_sparse_tiles);
   const int tile0 = split * p.tiles_per_split + wave;
-  const int hb[2] = {c0 * HALF, (1 - c0) * HALF};                // first channel of each half (0 = own)
+  using HV = Halves<D>;
+  const int ch[2] = {c0, 1 - c0};                                // column half of each operand half (0 = own)
+  // channel of half index o of half ch (SUB is a power of two)
+  auto gch = [](int o, int chh) { return HV::BLK * (o / HV::SUB) + HV::SUB * chh + (o % HV::SUB); };
 
   // Every load below is issued unconditionally (slots, rows and heads that do
   // not exist read zeros through out-of-range buffer offsets), so the compiler
@@ -408,17 +439,15 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
   src.cstride = (uint32_t)p.codes_stride;
   src.sstride = (uint32_t)p.scales_stride;
   src.oob = kOob;
-  src.hcb[0] = hb[0] / 2; src.hcb[1] = hb[1] / 2;
-  src.hsb[0] = hb[0] / 16; src.hsb[1] = hb[1] / 16;
-  src.lcb = (uint32_t)(g * RunsMap<D>::LANE / 2);
-  src.lsb = KH == 8 ? 4u * (uint32_t)(g >> 1) : 0u;
-  // D = 512: a run's two scales are bytes 2(g&1), 2(g&1)+1 of its word;
-  // D = 128: run r's scale is byte (g>>1) + 2r of the shared word
-  for (int r = 0; r < 2; ++r) {
-    const uint32_t b0 = KH == 8 ? 2u * (uint32_t)(g & 1) : (uint32_t)(g >> 1) + 2u * r;
-    const uint32_t b1 = KH == 8 ? b0 + 1u : 0x0Cu;               // 0x0C selects a zero byte
-    src.psel[r] = b0 | (0x0Cu << 8) | (b1 << 16) | (0x0Cu << 24);
-  }
+  // lane g's block: code bytes BLK/2 * g .. (two halves of SUB/2 bytes each),
+  // scale bytes BLK/16 * g .. (D = 512: eight bytes; D = 128: the two bytes
+  // 2g, 2g+1, read with the word that holds them)
+  src.hcb[0] = HV::SUB / 2 * ch[0]; src.hcb[1] = HV::SUB / 2 * ch[1];
+  src.lcb = (uint32_t)(HV::BLK / 2 * g);
+  src.lsb = KH == 8 ? 8u * (uint32_t)g : 4u * (uint32_t)(g >> 1);
+  // D = 128: the scale of half h is byte 2(g & 1) + ch[h] of the word
+  uint32_t psel128[2];
+  for (int h = 0; h < 2; ++h) psel128[h] = (uint32_t)(2 * (g & 1) + ch[h]) | (0x0Cu << 8) | (0x0Cu << 16) | (0x0Cu << 24);
   const uint32_t T32 = (uint32_t)nrows;
   Fp4Raw<D> raw[2];
   bool vld[2];
@@ -452,7 +481,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
   auto load_qf = [&](auto map) {
     using M = decltype(map);
 #pragma unroll
-    for (int k = 0; k < KH; ++k) qf[k] = *reinterpret_cast<const v8h*>(qs + n * QPITCH + hb[0] + M::off(k) + M::LANE * g);
+    for (int k = 0; k < KH; ++k) qf[k] = *reinterpret_cast<const v8h*>(qs + n * QPITCH + gch(M::off(k) + M::LANE * g, ch[0]));
   };
 
   const int swa_first = tile0 + NW * n_fp4;          // the wave's first window tile
@@ -468,7 +497,9 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
                                    (uint32_t)(p.swa_rows * D * kSwaBytes));
   const rsrc_t swa_sbuf = make_rsrc(S8 ? p.swa_scale + (int64_t)b * p.swa_rows : nullptr,
                                     S8 ? (uint32_t)(p.swa_rows * 4) : 0u);
-  const uint32_t swa_lane = S8 ? (uint32_t)(Fp8Map<D>::LANE * g) : 2u * InterMap<D>::LANE * g;
+  // byte offset of the lane's first channel within a row (half 0 of block 0;
+  // the k-step and the half are added where loaded)
+  const uint32_t swa_lane = S8 ? (uint32_t)gch(Fp8Map<D>::LANE * g, 0) : 2u * (uint32_t)gch(InterMap<D>::LANE * g, 0);
   // ring buffer: window row r of the sequence sits in slot (r + start) mod rows
   int swa_st = p.swa_start ? p.swa_start[b] : 0;
   swa_st = swa_st >= 0 && swa_st < p.swa_rows ? swa_st : 0;
@@ -485,13 +516,15 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
 #pragma unroll
       for (int i = 0; i < KH / 2; ++i)
         w[hh][i] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(
-                                              swa_buf, ro + 64u * i, __builtin_amdgcn_readfirstlane(hb[hh]), 0));
+                                              swa_buf, ro + (uint32_t)gch(64 * i, 0),
+                                              __builtin_amdgcn_readfirstlane(HV::SUB * ch[hh]), 0));
       if (hh == 0) swa_sc = __builtin_amdgcn_raw_buffer_load_b32(swa_sbuf, swa_so, 0, 0);
     } else {
 #pragma unroll
       for (int k = 0; k < KH; ++k)
-        w[hh][k] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(swa_buf, ro + 2 * InterMap<D>::off(k),
-                                                                             __builtin_amdgcn_readfirstlane(2 * hb[hh]), 0));
+        w[hh][k] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              swa_buf, ro + 2u * (uint32_t)gch(InterMap<D>::off(k), 0),
+                                              __builtin_amdgcn_readfirstlane(2 * HV::SUB * ch[hh]), 0));
     }
   };
   auto load_swa = [&](int t) {
@@ -509,40 +542,65 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
   // wait counts stay exact.  The last pair loads the two halves of the wave's
   // first window tile in place of gathers (the same number of loads).
   if (n_fp4 > 0) {
-    load_qf(RunsMap<D>{});
-    _Float16* wrow = my + n * PITCH + RunsMap<D>::LANE * g;
+    load_qf(BlockMap<D>{});
+    v8h qo[KH];
+#pragma unroll
+    for (int k = 0; k < KH; ++k)
+      if constexpr (QREG)
+        qo[k] = *reinterpret_cast<const v8h*>(qs + n * QPITCH + gch(BlockMap<D>::off(k) + BlockMap<D>::LANE * g, ch[1]));
+    // the other half's Q of k-step k: BlockMap keeps the k-steps of a lane in
+    // one block, so they are consecutive
+    const _Float16* qol = qs + n * QPITCH + gch(BlockMap<D>::LANE * g, ch[1]);
+    _Float16* wrow = my + n * PITCH + BlockMap<D>::LANE * g;
     auto fp4_tile = [&](int u, auto after) {
       Fp4Raw<D>& cur = raw[u];
       // an empty slot read zero codes and scales: finite zeros in V; its
       // logits are masked
-      v2h sc[2][2];                // per half and run: its scales times 2^-8
+      // per half: its scales times 2^-8 (D = 512: four groups of 16 channels
+      // per half, k-step k in group k / 2; D = 128: one group per half)
+      v2h sc[2][2];
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int run = 0; run < 2; ++run)
-          sc[hh][run] = e4m3_pair_s8(KH == 8 ? cur.s[hh][run] : cur.s[hh][0], src.psel[run]);
+      for (int hh = 0; hh < 2; ++hh) {
+        if constexpr (KH == 8) {
+          const uint32_t sw = ch[hh] ? cur.s[1] : cur.s[0];
+          sc[hh][0] = e4m3_pair_s8(sw, 0x0C010C00u);
+          sc[hh][1] = e4m3_pair_s8(sw, 0x0C030C02u);
+        } else {
+          sc[hh][0] = sc[hh][1] = e4m3_pair_s8(cur.s[0], psel128[hh]);
+        }
+      }
       const bool v = vld[u];
-      attend_tile<D, RunsMap<D>, v8h>(
+      attend_tile<D, BlockMap<D>, v8h>(
           p,
           [&](int hh, int k) {
-            constexpr int HK = KH / 2;
-            return fp4x8_to_half_s8(cur.w[hh][k], sc[hh][k / HK][(k % HK) / 2]);
+            return fp4x8_to_half_s8(cur.w[hh][k], KH == 8 ? sc[hh][k >> 2][(k >> 1) & 1] : sc[hh][0][0]);
           },
-          [](v8h kv) { return kv; }, after, v, qf,
-          reinterpret_cast<const uint16_t*>(qs + n * QPITCH + hb[1] + RunsMap<D>::LANE * g), wrow, vbase, g, o, m_run,
-          l_run);
+          [&](int hh, int k) {
+            if constexpr (QREG) return hh == 0 ? qf[k] : qo[k];
+            else return hh == 0 ? qf[k] : *reinterpret_cast<const v8h*>(qol + BlockMap<D>::off(k));
+          },
+          [](v8h kv) { return kv; }, after, v, wrow, vbase, g, o, m_run, l_run);
     };
-    int i0 = 0;
-    for (; i0 + 2 < n_fp4; i0 += 2) {
+    if constexpr (WPF) {
+      int i0 = 0;
+      for (; i0 + 2 < n_fp4; i0 += 2) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) fp4_tile(u, [&]() { vld[u] = load_fp4<D>(src, position(i0 + u + 2), T32, raw[u]); });
+        for (int u = 0; u < 2; ++u) fp4_tile(u, [&]() { vld[u] = load_fp4<D>(src, position(i0 + u + 2), T32, raw[u]); });
+      }
+      fp4_tile(0, [&]() {
+        swa_ro = swa_rows(swa_first);
+        load_swa_half(swa_ro, 0);
+      });
+      fp4_tile(1, [&]() { load_swa_half(swa_ro, 1); });
+    } else {
+      for (int i0 = 0; i0 < n_fp4; i0 += 2) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) fp4_tile(u, [&]() { vld[u] = load_fp4<D>(src, position(i0 + u + 2), T32, raw[u]); });
+      }
     }
-    fp4_tile(0, [&]() {
-      swa_ro = swa_rows(swa_first);
-      load_swa_half(swa_ro, 0);
-    });
-    fp4_tile(1, [&]() { load_swa_half(swa_ro, 1); });
   }
+  if (!WPF || n_fp4 == 0)
+    if (swa_first < t_end) load_swa(swa_first);
 
   // ---- sliding-window tiles (bf16 rows, interleaved channel map); the
   // first one was loaded during the last FP4 pair (or is loaded here when the
@@ -555,7 +613,6 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
     // 8-bit rows: decoded to fp16 (exact) with the row's scale and contracted
     // like the FP4 rows, against the own half of Q reloaded in this map
     if (swa_first < t_end) {
-      if (n_fp4 == 0) load_swa(swa_first);
       load_qf(Fp8Map<D>{});
       _Float16* wrow = my + n * PITCH + Fp8Map<D>::LANE * g;
       for (int t = swa_first; t < t_end; t += NW) {
@@ -563,25 +620,29 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
         const float sc = __uint_as_float(swa_sc);
         attend_tile<D, Fp8Map<D>, v8h>(
             p, [&](int hh, int k) { return fp8x8_to_half(w[hh][k / 2][2 * (k % 2)], w[hh][k / 2][2 * (k % 2) + 1], sc); },
-            [](v8h kv) { return kv; }, [&] { load_swa(t + NW); }, v, qf,
-            reinterpret_cast<const uint16_t*>(qs + n * QPITCH + hb[1] + Fp8Map<D>::LANE * g), wrow, vbase, g, o,
-            m_run, l_run);
+            [&](int hh, int k) {
+              return hh == 0 ? qf[k]
+                             : *reinterpret_cast<const v8h*>(qs + n * QPITCH + gch(Fp8Map<D>::off(k) + Fp8Map<D>::LANE * g, ch[1]));
+            },
+            [](v8h kv) { return kv; }, [&] { if (t + NW < t_end) load_swa(t + NW); }, v, wrow, vbase, g, o, m_run, l_run);
       }
     }
   } else if (swa_first < t_end) {
-    if (n_fp4 == 0) load_swa(swa_first);
     v8bf qfb[KH];
 #pragma unroll
     for (int k = 0; k < KH; ++k)
-      qfb[k] = *reinterpret_cast<const v8bf*>(qsb + n * QPITCH + hb[0] + InterMap<D>::off(k) + InterMap<D>::LANE * g);
+      qfb[k] = *reinterpret_cast<const v8bf*>(qsb + n * QPITCH + gch(InterMap<D>::off(k) + InterMap<D>::LANE * g, ch[0]));
     _Float16* wrow = my + n * PITCH + InterMap<D>::LANE * g;
     for (int t = swa_first; t < t_end; t += NW) {
       const bool v = swa_valid;
       attend_tile<D, InterMap<D>, v8bf>(
           p, [&](int hh, int k) { return __builtin_bit_cast(v8bf, w[hh][k]); },
-          [](v8bf kv) { return bf16x8_to_half(__builtin_bit_cast(u4, kv)); }, [&] { load_swa(t + NW); }, v, qfb,
-          reinterpret_cast<const uint16_t*>(qsb + n * QPITCH + hb[1] + InterMap<D>::LANE * g), wrow, vbase, g, o,
-          m_run, l_run);
+          [&](int hh, int k) {
+            return hh == 0 ? qfb[k]
+                           : *reinterpret_cast<const v8bf*>(qsb + n * QPITCH + gch(InterMap<D>::off(k) + InterMap<D>::LANE * g, ch[1]));
+          },
+          [](v8bf kv) { return bf16x8_to_half(__builtin_bit_cast(u4, kv)); }, [&] { if (t + NW < t_end) load_swa(t + NW); }, v, wrow,
+          vbase, g, o, m_run, l_run);
     }
   }
 
@@ -633,7 +694,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
     v4f sum = fb[t * 64 + lane];
 #pragma unroll
     for (int w = 1; w < NW; ++w) sum += fb[(w * NT + t) * 64 + lane];
-    const int chg = c0 * HALF + 16 * t + n;
+    const int chg = gch(16 * t + n, c0);
     if (p.splits == 1) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
