@@ -45,13 +45,6 @@
 // softmax uses exp2.
 #include "common.h"
 
-#ifndef CSA2_ATTN_QREG
-#define CSA2_ATTN_QREG 0
-#endif
-#ifndef CSA2_ATTN_WPF
-#define CSA2_ATTN_WPF 1
-#endif
-
 namespace csa2 {
 
 CSA2_DEV void wave_lds_sync() {
@@ -326,8 +319,6 @@ CSA2_DEV void attend_tile(const AttnParams& p, KV kvf, QO qop, ST stage, AfterQK
 template <int D, int NW, bool S8, bool PG>
 __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
   using G = Geo<D>;
-  constexpr bool QREG = CSA2_ATTN_QREG;             // both halves of Q in registers for the FP4 tiles
-  constexpr bool WPF = CSA2_ATTN_WPF;               // window tile prefetched during the last FP4 pair
   constexpr int KH = G::KH, NT = G::NT, PITCH = G::PITCH, HALF = G::HALF;
   constexpr int TILE_HALVES = 16 * PITCH;
   constexpr int QPITCH = D + 8;
@@ -543,11 +534,6 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
   // first window tile in place of gathers (the same number of loads).
   if (n_fp4 > 0) {
     load_qf(BlockMap<D>{});
-    v8h qo[KH];
-#pragma unroll
-    for (int k = 0; k < KH; ++k)
-      if constexpr (QREG)
-        qo[k] = *reinterpret_cast<const v8h*>(qs + n * QPITCH + gch(BlockMap<D>::off(k) + BlockMap<D>::LANE * g, ch[1]));
     // the other half's Q of k-step k: BlockMap keeps the k-steps of a lane in
     // one block, so they are consecutive
     const _Float16* qol = qs + n * QPITCH + gch(BlockMap<D>::LANE * g, ch[1]);
@@ -575,32 +561,21 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
           [&](int hh, int k) {
             return fp4x8_to_half_s8(cur.w[hh][k], KH == 8 ? sc[hh][k >> 2][(k >> 1) & 1] : sc[hh][0][0]);
           },
-          [&](int hh, int k) {
-            if constexpr (QREG) return hh == 0 ? qf[k] : qo[k];
-            else return hh == 0 ? qf[k] : *reinterpret_cast<const v8h*>(qol + BlockMap<D>::off(k));
-          },
+          [&](int hh, int k) { return hh == 0 ? qf[k] : *reinterpret_cast<const v8h*>(qol + BlockMap<D>::off(k)); },
           [](v8h kv) { return kv; }, after, v, wrow, vbase, g, o, m_run, l_run);
     };
-    if constexpr (WPF) {
-      int i0 = 0;
-      for (; i0 + 2 < n_fp4; i0 += 2) {
+    int i0 = 0;
+    for (; i0 + 2 < n_fp4; i0 += 2) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) fp4_tile(u, [&]() { vld[u] = load_fp4<D>(src, position(i0 + u + 2), T32, raw[u]); });
-      }
-      fp4_tile(0, [&]() {
-        swa_ro = swa_rows(swa_first);
-        load_swa_half(swa_ro, 0);
-      });
-      fp4_tile(1, [&]() { load_swa_half(swa_ro, 1); });
-    } else {
-      for (int i0 = 0; i0 < n_fp4; i0 += 2) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) fp4_tile(u, [&]() { vld[u] = load_fp4<D>(src, position(i0 + u + 2), T32, raw[u]); });
-      }
+      for (int u = 0; u < 2; ++u) fp4_tile(u, [&]() { vld[u] = load_fp4<D>(src, position(i0 + u + 2), T32, raw[u]); });
     }
+    fp4_tile(0, [&]() {
+      swa_ro = swa_rows(swa_first);
+      load_swa_half(swa_ro, 0);
+    });
+    fp4_tile(1, [&]() { load_swa_half(swa_ro, 1); });
   }
-  if (!WPF || n_fp4 == 0)
-    if (swa_first < t_end) load_swa(swa_first);
+  if (n_fp4 == 0 && swa_first < t_end) load_swa(swa_first);
 
   // ---- sliding-window tiles (bf16 rows, interleaved channel map); the
   // first one was loaded during the last FP4 pair (or is loaded here when the
