@@ -60,6 +60,7 @@ class AttnArgs(ctypes.Structure):
         ("swa_fp8", ctypes.c_int32), ("swa_scale", ctypes.c_void_p),
         ("block_table", ctypes.c_void_p), ("max_pages", ctypes.c_int32), ("page_size", ctypes.c_int32),
         ("cache_rows", ctypes.c_int64), ("swa_start", ctypes.c_void_p),
+        ("waves", ctypes.c_int32), ("splits", ctypes.c_int32),
     ]
 
 
@@ -175,13 +176,15 @@ def dequantize_kv(codes: torch.Tensor, scales: torch.Tensor, out: torch.Tensor, 
 def index_args(iq, iw, ik, q_per_seq: int, n_visible=None, q_scale=None, k_scale=None) -> IndexArgs:
     """iq [nq, H_I, D_I], iw fp32 [nq, H_I], ik [B, T, D_I]: int8, or E4M3
     codes (uint8) with q_scale fp32 [nq, H_I] and k_scale fp32 [B, T].
-    The struct holds raw device pointers: the tensors must stay alive until
-    the calls that use it are enqueued."""
+    The struct holds raw device pointers; it also keeps references to the
+    tensors they point into, so they live at least as long as the struct."""
     nq, heads, dim = iq.shape
     B, T = ik.shape[0], ik.shape[1]
     fp8 = 1 if (q_scale is not None or k_scale is not None) else 0
-    return IndexArgs(B, q_per_seq, T, heads, dim, _ptr(iq), _ptr(iw), _ptr(ik), _ptr(n_visible),
+    args = IndexArgs(B, q_per_seq, T, heads, dim, _ptr(iq), _ptr(iw), _ptr(ik), _ptr(n_visible),
                      fp8, _ptr(q_scale), _ptr(k_scale))
+    args._keep = (iq, iw, ik, n_visible, q_scale, k_scale)   # the tensors its pointers name
+    return args
 
 
 def index_workspace_size(args: IndexArgs) -> int:
@@ -253,24 +256,28 @@ def index_reindex(args: IndexArgs, pool, topk, ws, stream=None) -> None:
 # ------------------------------------------------------------------ attention
 def attn_args(q, codes, scales, topk, swa, out, q_per_seq: int, kv_len: int, window: int = WINDOW,
               swa_len=None, sm_scale: float = 0.0, swa_scale=None, block_table=None, page_size: int = 0,
-              swa_start=None) -> AttnArgs:
+              swa_start=None, waves: int = 0, splits: int = 0) -> AttnArgs:
     """q bf16-as-int16/uint16 [nq, H, d]; codes [B*T, >=d/2]; scales [B*T, >=d/16];
     topk int32 [nq, k]; swa bf16 [B, window-1+Qn, d] -- or, with swa_scale
     (fp32 [B, window-1+Qn]), E4M3 codes uint8 [B, window-1+Qn, d]; out fp32 [nq, H, d].
     Paged cache: block_table int32 [B, max_pages] and page_size, codes / scales
     then hold every physical row.  swa_start int32 [B]: window ring slots.
-    The struct holds raw device pointers: the tensors must stay alive until
-    the calls that use it are enqueued."""
+    waves / splits: the work split (0 = the library's choice).
+    The struct holds raw device pointers; it also keeps references to the
+    tensors they point into, so they live at least as long as the struct."""
     nq, heads, dim = q.shape
     paged = block_table is not None
-    return AttnArgs(nq // q_per_seq, q_per_seq, kv_len, heads, dim, _ptr(q),
+    args = AttnArgs(nq // q_per_seq, q_per_seq, kv_len, heads, dim, _ptr(q),
                     _ptr(codes), codes.stride(0) if codes is not None else dim // 2,
                     _ptr(scales), scales.stride(0) if scales is not None else dim // 16,
                     _ptr(topk), topk.shape[1] if topk is not None else 0,
                     _ptr(swa), window, _ptr(swa_len), float(sm_scale), _ptr(out),
                     1 if swa_scale is not None else 0, _ptr(swa_scale),
                     _ptr(block_table), block_table.shape[1] if paged else 0, page_size if paged else 0,
-                    codes.shape[0] if paged and codes is not None else 0, _ptr(swa_start))
+                    codes.shape[0] if paged and codes is not None else 0, _ptr(swa_start),
+                    int(waves), int(splits))
+    args._keep = (q, codes, scales, topk, swa, out, swa_len, swa_scale, block_table, swa_start)
+    return args
 
 
 def attn_workspace_size(args: AttnArgs) -> int:

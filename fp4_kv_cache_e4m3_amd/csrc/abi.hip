@@ -1,7 +1,6 @@
 // C ABI of the CSA2 library: host-side validation, workspace sizing and
 // dispatch to the gfx950 kernels.  Declarations and contracts: include/csa2.h.
 #include <cmath>
-#include <cstdlib>
 
 #include "../../include/csa2.h"
 #include "common.h"
@@ -57,33 +56,26 @@ IndexLayout index_layout(const csa2_index_args* a) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_ERR_HIP; }
 
-int env_int(const char* name, int dflt) {
-  const char* e = std::getenv(name);
-  return e ? std::atoi(e) : dflt;
-}
-
 // Work split of one attention layer.  A workgroup owns (query, 16 heads, one
 // column half of the output channels, a contiguous range of 16-entry tiles);
 // its NW waves take every NW-th tile.  When the grid fits one workgroup per
 // CU (<= 256), 8 waves (two per SIMD) keep the whole tile list in one
 // workgroup; otherwise 4-wave workgroups (two per CU) avoid a second wave of
 // 8-wave workgroups (384 workgroups at 48 queries: 121 vs 140 us for four
-// layers).  Splits of
-// the tile list over workgroups are used only when the grid would otherwise
-// leave most CUs idle; their partial states are merged by a second kernel.
-// CSA2_ATTN_WAVES / CSA2_ATTN_SPLITS override the choice (tuning).
-void attn_plan(int64_t nq, int heads, int n_tiles, int& waves, int& splits) {
+// layers).  Splits of the tile list over workgroups are used only when the
+// grid would otherwise leave most CUs idle; their partial states are merged
+// by a second kernel.  The caller may fix either choice (csa2_attn_args
+// waves / splits; 0 = this choice).
+void attn_plan(int64_t nq, int heads, int n_tiles, int want_waves, int want_splits, int& waves, int& splits) {
   const int64_t base = 2 * nq * ((heads + 15) / 16);
-  waves = env_int("CSA2_ATTN_WAVES", base <= 256 ? 8 : 4);
-  if (waves != 4 && waves != 8) waves = 4;
+  waves = want_waves > 0 ? want_waves : (base <= 256 ? 8 : 4);
   int dflt = 1;
   if (base > 0 && base < 128) {            // fewer than half the CUs busy: split
     dflt = (int)((256 + base - 1) / base);
     const int cap = n_tiles / (2 * waves) > 1 ? n_tiles / (2 * waves) : 1;
     if (dflt > cap) dflt = cap;
   }
-  int s = env_int("CSA2_ATTN_SPLITS", dflt);
-  if (s < 1) s = 1;
+  int s = want_splits > 0 ? want_splits : dflt;
   if (n_tiles == 0) s = 1;
   if (s > n_tiles && n_tiles > 0) s = n_tiles;
   const int tps = n_tiles > 0 ? (n_tiles + s - 1) / s : 1;
@@ -102,7 +94,7 @@ AttnLayout attn_layout(const csa2_attn_args* a) {
   L.n_sparse_tiles = a->kv_len > 0 ? (a->topk_k + 15) / 16 : 0;
   L.swa_rows = a->window > 0 ? a->window - 1 + a->q_per_seq : 0;
   L.n_tiles = L.n_sparse_tiles + (a->window + 15) / 16;
-  attn_plan(L.nq, a->heads, L.n_tiles, L.waves, L.splits);
+  attn_plan(L.nq, a->heads, L.n_tiles, a->waves, a->splits, L.waves, L.splits);
   L.tps = L.n_tiles > 0 ? (L.n_tiles + L.splits - 1) / L.splits : 1;
   L.ws_bytes = 0;
   if (L.splits > 1) {
@@ -116,6 +108,7 @@ int check_attn(const csa2_attn_args* a) {
   if (!a) return CSA2_ERR_NULL;
   if (a->batch < 0 || a->q_per_seq < 1 || a->kv_len < 0 || a->kv_len > (int64_t)1 << 31) return CSA2_ERR_SHAPE;
   if (a->heads < 1 || a->heads > 128) return CSA2_ERR_SHAPE;
+  if (!(a->waves == 0 || a->waves == 4 || a->waves == 8) || a->splits < 0 || a->splits > 256) return CSA2_ERR_SHAPE;
   if (!(a->dim == 128 || a->dim == 512)) return CSA2_ERR_SHAPE;
   if (a->topk_k < 0 || a->topk_k > kMaxTopK || a->window < 0 || a->window > 1024) return CSA2_ERR_SHAPE;
   const int64_t nq = (int64_t)a->batch * a->q_per_seq;

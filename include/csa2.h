@@ -303,7 +303,8 @@ typedef struct {
   int64_t kv_len;              /* T rows per sequence in the FP4 cache, < 2^24;
                                   T * codes_stride and T * scales_stride must
                                   stay below 4 GiB - 8 KiB                      */
-  int32_t heads;               /* H: 8 or a multiple of 16, <= 128             */
+  int32_t heads;               /* H: 1 .. 128 (a workgroup takes 16 heads; a
+                                  last partial group reads zero Q rows)        */
   int32_t dim;                 /* d: 128 or 512                                */
   const uint16_t* q;           /* bf16 [nq, H, d], 16-byte aligned             */
   const uint8_t* codes;        /* FP4 codes, row b*T+t at codes + row*codes_stride;
@@ -343,6 +344,15 @@ typedef struct {
      rows, so a decode step overwrites one slot instead of shifting the
      window.  Starts outside [0, swa_rows) count as 0.  */
   const int32_t* swa_start;
+  /* Work split (0 = the library's choice for the shape).  waves: 4 or 8
+     waves per workgroup, each taking every waves-th 16-entry tile of its
+     query; splits >= 1: the tile list is cut into that many contiguous
+     ranges, one workgroup each, whose partial softmax states a second kernel
+     merges (needs csa2_attn_workspace_size bytes of workspace).  Both change
+     the fp32 summation order, so outputs may differ in the last bits between
+     choices; each choice is deterministic.  Other values: CSA2_ERR_SHAPE.   */
+  int32_t waves;
+  int32_t splits;
 } csa2_attn_args;
 
 /* Bytes of workspace csa2_sparse_attn needs for these arguments (may be 0). */

@@ -184,3 +184,47 @@ def test_attn_rejects(lib):
     assert need > 0                                   # 2 queries x 4 head groups -> split
     assert sa(ctypes.byref(a), None, 0, None) == 4
     assert sa(ctypes.byref(a), 256, need - 1, None) == 4
+    # the caller's work split: waves 4 or 8, splits >= 0 (0 = the library's choice)
+    assert sa(ctypes.byref(args(waves=5)), None, 0, None) == 2
+    assert sa(ctypes.byref(args(splits=-1)), None, 0, None) == 2
+    assert lib.csa2_attn_workspace_size(ctypes.byref(args(waves=8, splits=1))) == 0
+    assert lib.csa2_attn_workspace_size(ctypes.byref(args(waves=4, splits=3))) > 0
+
+
+def test_argument_structs_keep_their_tensors_alive():
+    """index_args / attn_args hold raw pointers; the structs also hold the
+    tensors, so a caller dropping its own references cannot free memory that
+    a later call reads (the caching allocator would hand it out again)."""
+    import gc
+    import weakref
+
+    import torch
+
+    import fp4_kv_cache_e4m3_amd as m
+
+    iq = torch.zeros((2, 8, 128), dtype=torch.int8)
+    iw, ik = torch.ones((2, 8)), torch.zeros((2, 64, 128), dtype=torch.int8)
+    refs = [weakref.ref(t) for t in (iq, iw, ik)]
+    ia = m.index_args(iq, iw, ik, 1)
+    del iq, iw, ik
+    gc.collect()
+    assert all(r() is not None for r in refs)
+    assert ia.q == ia._keep[0].data_ptr()
+    del ia
+    gc.collect()
+    assert all(r() is None for r in refs)
+
+    q = torch.zeros((2, 16, 128), dtype=torch.int16)
+    codes, scales = torch.zeros((128, 64), dtype=torch.uint8), torch.zeros((128, 8), dtype=torch.uint8)
+    topk, swa = torch.zeros((2, 64), dtype=torch.int32), torch.zeros((2, 127, 128), dtype=torch.int16)
+    out = torch.zeros((2, 16, 128))
+    ts = (q, codes, scales, topk, swa, out)
+    refs = [weakref.ref(t) for t in ts]
+    aa = m.attn_args(*ts, 1, 64, 128, waves=4, splits=2)
+    del ts, q, codes, scales, topk, swa, out
+    gc.collect()
+    assert all(r() is not None for r in refs)
+    assert (aa.waves, aa.splits) == (4, 2)
+    del aa
+    gc.collect()
+    assert all(r() is None for r in refs)

@@ -17,7 +17,7 @@ from tests.parity import ATTN_TOL, bf16_values, dev, host, oracle_attention, row
 pytestmark = pytest.mark.gpu
 
 
-def gpu_attn(q_bits, codes, scales, topk, swa_bits, qn, T, window, swa_len=None, sm_scale=0.0):
+def gpu_attn(q_bits, codes, scales, topk, swa_bits, qn, T, window, swa_len=None, sm_scale=0.0, waves=0, splits=0):
     nq, H, d = q_bits.shape
     q_d = dev(q_bits.view(np.int16))
     c_d, s_d = dev(codes), dev(scales)
@@ -25,7 +25,7 @@ def gpu_attn(q_bits, codes, scales, topk, swa_bits, qn, T, window, swa_len=None,
     sw_d = dev(swa_bits.view(np.int16)) if window > 0 else None
     sl_d = dev(np.asarray(swa_len, np.int32)) if swa_len is not None else None
     out = torch.full((nq, H, d), float("nan"), dtype=torch.float32, device="cuda")
-    args = csa2.attn_args(q_d, c_d, s_d, t_d, sw_d, out, qn, T, window, sl_d, sm_scale)
+    args = csa2.attn_args(q_d, c_d, s_d, t_d, sw_d, out, qn, T, window, sl_d, sm_scale, waves=waves, splits=splits)
     if t_d is None:
         args.topk_k = 0
     n = csa2.attn_workspace_size(args)
@@ -152,3 +152,56 @@ def test_attn_batch32_t65536_layer():
     ref = oracle_attention(w, q, swa, topk, with_new_rows=False)
     err = rownorm_err(got, ref)
     assert err <= ATTN_TOL, err
+
+
+@pytest.mark.parametrize("waves", [4, 8])
+@pytest.mark.parametrize("splits", [1, 2, 3, 4, 40])
+def test_attn_work_split_sweep(waves, splits):
+    """Every work split the caller may choose (waves per workgroup x splits of
+    the tile list, the latter merged by the second kernel; 40 splits = one
+    16-entry tile each) stays within 2e-3
+    of the oracle at the decode layer's shape (512 Top-K + 128-row window, 64
+    heads, d = 512), and each split is bit-identical from run to run."""
+    B, Qn, T, d, H, W, k = 8, 1, 8000, 512, 64, 128, 512
+    codes, scales, q, swa, topk = make_case(31, B, Qn, T, d, H, W, k, fill=1.0)
+    a = gpu_attn(q, codes, scales, topk, swa, Qn, T, W, waves=waves, splits=splits)
+    b = gpu_attn(q, codes, scales, topk, swa, Qn, T, W, waves=waves, splits=splits)
+    assert np.array_equal(a, b)
+    ref = oracle_out(q, codes, scales, topk, swa, Qn, T, W)
+    err = rownorm_err(a, ref)
+    assert err <= ATTN_TOL, err
+
+
+def test_attn_large_q_magnitudes():
+    """|Q| up to about 4e4 (inside the documented fp16 range of the QK^T
+    operands): Q is scaled by 2^13 and the FP4 rows and window by 2^-13, so
+    the logits keep their N(0,1) spread and the softmax stays well
+    conditioned."""
+    B, Qn, T, d, H, W, k = 2, 1, 3000, 512, 64, 128, 512
+    rng = np.random.default_rng(41)
+    x = (rng.standard_normal((B * T, d)) * 2.0 ** -13).astype(np.float32)
+    codes, scales = oquant.quantize_rows(x)
+    q = synth.f32_to_bf16_bits((rng.standard_normal((B * Qn, H, d)) * 2.0 ** 13).astype(np.float32))
+    swa = synth.f32_to_bf16_bits((rng.standard_normal((B, W - 1 + Qn, d)) * 2.0 ** -13).astype(np.float32))
+    assert np.abs(bf16_values(q)).max() > 2.0 ** 15
+    topk = np.stack([np.sort(rng.choice(T, size=k, replace=False)) for _ in range(B * Qn)]).astype(np.int32)
+    got = gpu_attn(q, codes, scales, topk, swa, Qn, T, W)
+    ref = oracle_out(q, codes, scales, topk, swa, Qn, T, W)
+    assert np.all(np.isfinite(got))
+    assert rownorm_err(got, ref) <= ATTN_TOL
+
+
+def test_attn_large_window_values_and_tiny_q():
+    """Window values up to about 4e4 (they are V in fp16 for PV) against a Q
+    scaled by 2^-13, whose smaller elements fall below fp16's normal range
+    (the documented 2^-25 absolute conversion loss)."""
+    B, Qn, T, d, H, W, k = 2, 2, 3000, 512, 32, 128, 512
+    codes, scales, q, swa, topk = make_case(43, B, Qn, T, d, H, W, k, fill=1.0)
+    q = synth.f32_to_bf16_bits((bf16_values(q) * 2.0 ** -13).astype(np.float32))
+    swa = synth.f32_to_bf16_bits((bf16_values(swa) * 2.0 ** 13).astype(np.float32))
+    assert np.abs(bf16_values(swa)).max() > 2.0 ** 15
+    assert (np.abs(bf16_values(q)) < 2.0 ** -14).mean() > 0.2
+    got = gpu_attn(q, codes, scales, topk, swa, Qn, T, W)
+    ref = oracle_out(q, codes, scales, topk, swa, Qn, T, W)
+    assert np.all(np.isfinite(got))
+    assert rownorm_err(got, ref) <= ATTN_TOL

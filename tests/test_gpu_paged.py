@@ -8,18 +8,28 @@
   shared pages, -1 pages) gives bit-identical outputs to the same call over
   the contiguous cache, and matches the oracle within 2e-3.
 * A window held as a ring (rows rotated by a per-sequence start slot) gives
-  bit-identical outputs to the linear window, for bf16 and 8-bit rows."""
+  bit-identical outputs to the linear window, for bf16 and 8-bit rows.
+Every attention case is also checked against the oracle within 2e-3."""
 import numpy as np
 import pytest
 import torch
 
 import fp4_kv_cache_e4m3_amd as csa2
+from oracle import attention as oattn
 from oracle import quant as oquant
 from oracle import swa8 as oswa8
 from tests.parity import ATTN_TOL, bf16_values, dev, host, rownorm_err
 from tests.test_gpu_attn import make_case, oracle_out
 
 pytestmark = pytest.mark.gpu
+
+
+def oracle_out_8bit(q, codes, scales, topk, c8, s8, qn, T, W):
+    """Oracle attention over a linear 8-bit window: E4M3 codes [B, R, d] with
+    row scales [B, R], decoded by the oracle's own 8-bit window format."""
+    d = c8.shape[-1]
+    vals = oswa8.swa_values(c8.reshape(-1, d), s8.reshape(-1)).reshape(c8.shape)
+    return oattn.sparse_attn(bf16_values(q), codes, scales, topk, vals, qn, T, window=W)
 
 
 def page_layout(rng, B, T, P, spare=7):
@@ -104,6 +114,8 @@ def test_attn_paged_with_8bit_window_ring(P):
     ref = run_attn(q, codes, scales, topk, c8, Qn, T, W, swa_scale=s8)
     got = run_attn(q, pc, ps, topk, ring, Qn, T, W, block_table=bt, page_size=P, swa_scale=rsc, swa_start=start)
     np.testing.assert_array_equal(got, ref)
+    want = oracle_out_8bit(q, codes, scales, topk, c8, s8, Qn, T, W)
+    assert rownorm_err(got, want) <= ATTN_TOL
 
 
 def test_attn_paged_shared_and_missing_pages():
@@ -126,6 +138,9 @@ def test_attn_paged_shared_and_missing_pages():
     ref = run_attn(q, codes, scales, ref_topk, swa, Qn, T, W)
     got = run_attn(q, pc, ps, topk, swa, Qn, T, W, block_table=bt, page_size=P)
     np.testing.assert_array_equal(got, ref)
+    # the oracle over the contiguous rows, with the missing pages' positions out
+    want = oracle_out(q, codes, scales, ref_topk, swa, Qn, T, W)
+    assert rownorm_err(got, want) <= ATTN_TOL
 
 
 @pytest.mark.parametrize("swa8", [False, True])
@@ -147,6 +162,11 @@ def test_attn_window_ring_equals_linear(swa8):
     ref = run_attn(q, codes, scales, topk, swa, Qn, T, W, swa_scale=sc)
     got = run_attn(q, codes, scales, topk, ring, Qn, T, W, swa_scale=rsc, swa_start=start)
     np.testing.assert_array_equal(got, ref)
+    if swa8:
+        want = oracle_out_8bit(q, codes, scales, topk, swa, sc, Qn, T, W)
+    else:
+        want = oracle_out(q, codes, scales, topk, swa, Qn, T, W)
+    assert rownorm_err(got, want) <= ATTN_TOL
 
 
 def test_quantize_kv_paged_matches_oracle():
