@@ -9,8 +9,15 @@ whole group over one batch; inputs are synthetic, seeded, and resident in HBM
 before timing starts.
 
 Prints one JSON line: query-tokens/s, achieved HBM GB/s of the group, the
-roofline of the dominant kernel (the indexer scan) from HIP events recorded
-around it inside the timed region, and the FP64 oracle timed on the host.
+roofline of the dominant kernel (the indexer scan) and of the attention
+kernel from HIP events recorded around them inside the timed region, and the
+FP64 oracle timed on the host.
+
+Timing: every timed step starts with a cold last-level cache -- a 512 MiB
+device write (twice the MI355X's 256 MB Infinity Cache) runs between steps,
+outside the step's own event pair -- and the line reports the median step
+(with p10 / p90); back-to-back steps, which find the previous step's rows and
+windows still cached, are reported beside it as "warm".
 """
 from __future__ import annotations
 
@@ -64,14 +71,23 @@ def group_bytes(w) -> dict:
                 total=total)
 
 
-def cpu_baseline(w, max_queries: int, min_seconds: float = 10.0) -> dict:
+def host_cores() -> int:
+    """Cores this process may run on (the affinity mask), else the count."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(w, max_queries: int, min_seconds: float = 10.0, threads: int | None = None) -> dict:
     """The FP64 oracle on the first max_queries query tokens of the same
     workload (one full group step each: new-entry quantisation of their
     sequences, Full index over all T positions, every layer's attention),
     repeated until at least min_seconds of wall time have been timed.
-    Input generation is not timed."""
+    Input generation is not timed.  threads: the BLAS thread-pool size to run
+    with (None: the pool as numpy set it up)."""
     import numpy as np
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     from fp4_kv_cache_e4m3_amd import synth
     from oracle import attention as oattn
@@ -139,16 +155,17 @@ def cpu_baseline(w, max_queries: int, min_seconds: float = 10.0) -> dict:
                                            sws[l][b:b + 1], w.window)
                 oattn.attend(qs[l][qi], keys, 1.0 / np.sqrt(w.dim))
 
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        one_pass()
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds:
-            break
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": reps * nqs / dt, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
+    with threadpool_limits(limits=threads):
+        used = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        reps = 0
+        t0 = time.perf_counter()
+        while True:
+            one_pass()
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_seconds:
+                break
+    return {"value": reps * nqs / dt, "unit": "query-tokens/s", "cores": used, "kind": "oracle",
             "sample": f"first {nqs} of {w.nq} query tokens ({n_seq} of {w.batch} sequences), full group "
                       f"step ({'+'.join(w.layers)}), T={T}, repeated {reps}x; {dt:.2f} s wall"}
 
@@ -198,37 +215,60 @@ def main() -> int:
     roof_stage = "index_scan" if full else "reindex"
     roof_i = next(i for i, (st, _) in enumerate(calls) if st == roof_stage)
 
-    def step(ev=None):
-        # ev: an event pair recorded around the first scan (or reindex) call
-        # (timing only; no sync)
+    attn_i = next(i for i, (st, _) in enumerate(calls) if st == "attention")
+
+    def step(ev=None, at=None):
+        # ev / at: event pairs recorded around the first scan (or reindex) call
+        # and the first attention call (timing only; no sync)
         for i, (_, call) in enumerate(calls):
             if ev is not None and i == roof_i: ev[0].record(stream)
+            if at is not None and i == attn_i: at[0].record(stream)
             call()
             if ev is not None and i == roof_i: ev[1].record(stream)
+            if at is not None and i == attn_i: at[1].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # timed region: K steps; only the scan (the roofline kernel) is bracketed
-    # by events, on every 5th step, since every event on the stream costs
-    # about 2.5 us
-    sampled = [k for k in range(args.steps) if k % 5 == 0]
-    evs = {k: [torch.cuda.Event(enable_timing=True) for _ in range(2)] for k in sampled}
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
+    def pair():
+        return [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    # timed region: K cold steps.  Before each, a 512 MiB write evicts the
+    # last-level cache (outside the step's event pair); the scan and the
+    # first attention call are bracketed by their own events on alternate
+    # sampled steps (every event on the stream costs a few microseconds)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    step_ev = [pair() for _ in range(args.steps)]
+    scan_ev = {k: pair() for k in range(args.steps) if k % 5 == 0}
+    attn_ev = {k: pair() for k in range(args.steps) if k % 5 == 2}
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
-    start.record(stream)
     for k in range(args.steps):
-        step(evs.get(k))
-    stop.record(stream)
+        flush.fill_(k & 0xFF)
+        step_ev[k][0].record(stream)
+        step(scan_ev.get(k), attn_ev.get(k))
+        step_ev[k][1].record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
-    ms = start.elapsed_time(stop) / args.steps
-    scan_ms = sum(e[0].elapsed_time(e[1]) for e in evs.values()) / len(evs)
-    # per-stage breakdown: a separate pass of K steps after the timed region,
-    # one event after every call
+    step_ms = sorted(e[0].elapsed_time(e[1]) for e in step_ev)
+    pct = lambda f: step_ms[min(len(step_ms) - 1, int(round(f * (len(step_ms) - 1))))]
+    ms = pct(0.5)
+    scan_ms = sorted(e[0].elapsed_time(e[1]) for e in scan_ev.values())[len(scan_ev) // 2]
+    attn_ms = sorted(e[0].elapsed_time(e[1]) for e in attn_ev.values())[len(attn_ev) // 2]
+
+    # warm: K steps back to back between two events
+    start, stop = pair()
+    torch.cuda.synchronize()
+    start.record(stream)
+    for k in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    warm_ms = start.elapsed_time(stop) / args.steps
+
+    # per-stage breakdown: a separate warm pass of K steps, one event after
+    # every call
     bev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
     for k in range(args.steps):
         bev[k][0].record(stream)
@@ -246,6 +286,7 @@ def main() -> int:
     scan_bytes = nbytes["scan"] if full else nbytes["reindex"]
     group = "group" if nl <= 6 else f"{nl}-layer decoder step"
     achieved = scan_bytes / (scan_ms / 1e3) / 1e9
+    attn_achieved = nbytes["attn_layer"] / (attn_ms / 1e3) / 1e9
     out = {
         "metric": f"decode query-tokens/s per CSA2 layer {group} at 64K ctx + achieved HBM GB/s",
         "value": round(value, 1),
@@ -260,6 +301,12 @@ def main() -> int:
                    "kv_len": w.kv_len, "dim": w.dim, "heads": w.heads, "window": w.window,
                    "idx_heads": w.idx_heads, "idx_dim": w.idx_dim, "layers": list(w.layers),
                    "idx_fp8": w.idx_fp8, "swa8": w.swa8, "page_size": w.page_size, "swa_ring": w.swa_ring},
+        "timing": "cold last-level cache (512 MiB write between steps, outside the events); "
+                  "median of the per-step event times",
+        "ms_per_step_p10": round(pct(0.1), 4), "ms_per_step_p90": round(pct(0.9), 4),
+        "warm": {"ms_per_step": round(warm_ms, 4), "value": round(w.nq / (warm_ms / 1e3), 1),
+                 "hbm_frac_group": round(nbytes["total"] / (warm_ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+                 "timing": "steps back to back between two events"},
         "hbm_gbs_group": round(nbytes["total"] / (ms / 1e3) / 1e9, 1),
         "hbm_frac_group": round(nbytes["total"] / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
         "breakdown_ms": dict({"pass": "separate, one event after every call (sums per stage)"},
@@ -268,10 +315,18 @@ def main() -> int:
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "bytes_per_launch": scan_bytes, "traffic": scan_traffic(w) if full else None},
+        "roofline_attn": {"kernel": "k_attn", "bound": "hbm", "achieved": round(attn_achieved, 1),
+                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(attn_achieved / PEAK_HBM_GBS, 4),
+                          "bytes_per_launch": nbytes["attn_layer"], "ms": round(attn_ms, 4)},
         "wall_s_timed": round(t_wall, 3),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_queries)
+        cb = cpu_baseline(w, args.cpu_queries)
+        one = cpu_baseline(w, args.cpu_queries, threads=1)
+        cb["host_cores"] = host_cores()
+        cb["value_1thread"] = one["value"]
+        cb["sample_1thread"] = one["sample"]
+        out["cpu_baseline"] = cb
     print(json.dumps(out), flush=True)
     return 0
 
