@@ -27,7 +27,7 @@ EXPORTS = (
     "csa2_index_workspace_size", "csa2_index_full", "csa2_index_scan", "csa2_index_select",
     "csa2_index_full_append", "csa2_index_select_append", "csa2_index_full_append_paged",
     "csa2_index_select_append_paged", "csa2_index_reindex",
-    "csa2_attn_workspace_size", "csa2_sparse_attn",
+    "csa2_attn_workspace_size", "csa2_sparse_attn", "csa2_index_full_noalloc",
 )
 
 
@@ -95,6 +95,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.csa2_index_workspace_size.argtypes = [ctypes.POINTER(IndexArgs)]
     lib.csa2_index_full.restype = ctypes.c_int
     lib.csa2_index_full.argtypes = [ctypes.POINTER(IndexArgs), vp, vp, vp, sz, vp]
+    lib.csa2_index_full_noalloc.restype = ctypes.c_int
+    lib.csa2_index_full_noalloc.argtypes = [ctypes.POINTER(IndexArgs), vp, vp, vp]
     lib.csa2_index_scan.restype = ctypes.c_int
     lib.csa2_index_scan.argtypes = [ctypes.POINTER(IndexArgs), vp, sz, vp]
     lib.csa2_index_select.restype = ctypes.c_int
@@ -194,6 +196,12 @@ def index_workspace_size(args: IndexArgs) -> int:
 def index_full(args: IndexArgs, pool, topk, ws, stream=None) -> None:
     _check(load().csa2_index_full(ctypes.byref(args), _ptr(pool), _ptr(topk), _ptr(ws),
                                   ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream)))
+
+
+def index_full_noalloc(args: IndexArgs, pool, topk, stream=None) -> None:
+    """index_full on the library's fixed per-GPU scratch (no workspace, no
+    allocation; calls on one GPU must not overlap)."""
+    _check(load().csa2_index_full_noalloc(ctypes.byref(args), _ptr(pool), _ptr(topk), _stream(stream)))
 
 
 def index_scan(args: IndexArgs, ws, stream=None) -> None:

@@ -1,9 +1,16 @@
 // C ABI of the CSA2 library: host-side validation, workspace sizing and
 // dispatch to the gfx950 kernels.  Declarations and contracts: include/csa2.h.
 #include <cmath>
+#include <mutex>
 
 #include "../../include/csa2.h"
 #include "common.h"
+
+// Scratch of csa2_index_full_noalloc: one array per GPU, loaded with the
+// library's code object.  Host code never passes this name to a kernel (on
+// the host it is only a stand-in); it uses the device address looked up once
+// per device below.
+__device__ __align__(256) unsigned char scratch[CSA2_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -55,6 +62,24 @@ IndexLayout index_layout(const csa2_index_args* a) {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_ERR_HIP; }
+
+// Device address of the current GPU's scratch array, looked up on the first
+// call on each device (thread-safe) and kept for the life of the process.
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return CSA2_ERR_HIP;
+  std::call_once(g_scratch_once[dev], [dev] {
+    g_scratch_err[dev] = hipGetSymbolAddress(&g_scratch_ptr[dev], HIP_SYMBOL(scratch));
+  });
+  if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev]) return CSA2_ERR_HIP;
+  *out = g_scratch_ptr[dev];
+  return CSA2_OK;
+}
 
 // Work split of one attention layer.  A workgroup owns (query, 16 heads, one
 // column half of the output channels, a contiguous range of 16-entry tiles);
@@ -197,6 +222,8 @@ const char* csa2_status_string(int s) {
     case CSA2_ERR_ALIGN: return "CSA2_ERR_ALIGN: pointer or stride misaligned";
     case CSA2_ERR_WORKSPACE: return "CSA2_ERR_WORKSPACE: workspace missing or too small";
     case CSA2_ERR_HIP: return "CSA2_ERR_HIP: the HIP runtime reported an error";
+    case CSA2_ERR_SCRATCH:
+      return "CSA2_ERR_SCRATCH: the problem needs more than the 64 MiB scratch of csa2_index_full_noalloc";
     default: return "unknown csa2 status";
   }
 }
@@ -326,6 +353,18 @@ int csa2_index_full(const csa2_index_args* a, int32_t* pool, int32_t* topk, void
   st = csa2_index_scan(a, ws, ws_size, stream);
   if (st != CSA2_OK) return st;
   return select_impl(a, pool, topk, ws, ws_size, QuantJob{}, stream);
+}
+
+int csa2_index_full_noalloc(const csa2_index_args* a, int32_t* pool, int32_t* topk, hipStream_t stream) {
+  int st = check_index(a);
+  if (st != CSA2_OK) return st;
+  const IndexLayout L = index_layout(a);
+  if ((size_t)L.total > CSA2_NOALLOC_SCRATCH_BYTES) return CSA2_ERR_SCRATCH;
+  if (L.nq == 0) return CSA2_OK;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != CSA2_OK) return st;
+  return csa2_index_full(a, pool, topk, ws, CSA2_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int csa2_index_select_append(const csa2_index_args* a, int32_t* pool, int32_t* topk, const void* ws,

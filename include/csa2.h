@@ -52,7 +52,9 @@ typedef enum {
   CSA2_ERR_SHAPE = 2,      /* unsupported or inconsistent size               */
   CSA2_ERR_ALIGN = 3,      /* pointer or stride not aligned as documented    */
   CSA2_ERR_WORKSPACE = 4,  /* workspace NULL or smaller than the query says  */
-  CSA2_ERR_HIP = 5         /* the HIP runtime reported a launch error        */
+  CSA2_ERR_HIP = 5,        /* the HIP runtime reported a launch error        */
+  CSA2_ERR_SCRATCH = 6     /* csa2_index_full_noalloc: the problem needs more
+                              than its fixed scratch (CSA2_NOALLOC_SCRATCH_BYTES) */
 } csa2_status;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -207,6 +209,22 @@ size_t csa2_index_workspace_size(const csa2_index_args* args);
  */
 int csa2_index_full(const csa2_index_args* args, int32_t* pool, int32_t* topk,
                     void* ws, size_t ws_size, hipStream_t stream);
+
+/*
+ * csa2_index_full_noalloc -- csa2_index_full for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  It takes no workspace; the scan's score
+ * and block keys go to a fixed scratch array of CSA2_NOALLOC_SCRATCH_BYTES
+ * that the library holds on each GPU it runs on until the process ends
+ * (its address is looked up once per device on the first call there).  The
+ * call allocates nothing.  Sizes whose csa2_index_workspace_size exceeds the
+ * scratch return CSA2_ERR_SCRATCH before any launch.  Every call on one GPU
+ * shares that GPU's scratch: calls that may overlap on one GPU (different
+ * streams, or host threads) race and must be serialised by the caller.
+ * Results are those of csa2_index_full, bit for bit.
+ */
+#define CSA2_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int csa2_index_full_noalloc(const csa2_index_args* args, int32_t* pool, int32_t* topk, hipStream_t stream);
 
 /*
  * The two stages of csa2_index_full, for callers that schedule them apart
