@@ -8,10 +8,9 @@ path.
 
 What it computes, and where the pages say so (DeepSeek-V4.1-Flash pages):
 
-* ``formats``  -- FP4 E2M1 and E4M3 decoders from their bit fields (the
-  formats named in ai-maestro.online "FP4 KV, Bounded Replay, and other
-  extensions": E2M1 values with one E4M3 scale per 16 channels, NVFP4 without
-  the global scale).
+* ``formats``  -- FP4 E2M1 and E4M3 decoders from their bit fields (the two
+  formats ai-maestro.online names in "FP4 KV, Bounded Replay, and other
+  extensions" for the main cache and its per-16-channel multipliers).
 * ``quant``    -- the per-16-channel quantiser (same section).
 * ``indexer``  -- Full-layer indexer (block max over 8-token blocks, top-2,048
   blocks as the candidate pool, Top-512 positions) and the Reindex layer's
@@ -20,8 +19,8 @@ What it computes, and where the pages say so (DeepSeek-V4.1-Flash pages):
 * ``indexer_fp8`` -- the same indexer over real-valued E4M3 keys and queries
   with fp32 scales (the pages leave the indexer's precision open).
 * ``swa8``     -- the 8-bit sliding-window cache rows (E4M3 codes, one
-  power-of-two scale per row; kongchang.com "Three Core Innovations": the
-  window keeps 8-bit precision).
+  power-of-two scale per row; kongchang.com "Three Core Innovations" gives
+  the window cache an 8-bit format).
 * ``attention`` -- sparse attention over the selected entries merged with the
   layer's 128-token sliding window in one softmax (ai-maestro.online, "Causal
   Encoder-Decoder architecture" for the window, "Compressed Sparse

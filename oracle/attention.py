@@ -2,12 +2,13 @@
 
 Test infrastructure only (see the package docstring).
 
-Pages: every layer keeps its own main Q and its own sliding-window KV cache
-(ai-maestro.online, "Compressed Sparse Attention 2"); sliding-window
-attention runs in every layer with a 128-token window (same page, "Causal
-Encoder-Decoder architecture"); Full/Reindex layers attend over fresh Top-512
-indices, Reuse layers over the latest ones; the main KV is stored as FP4
-(E2M1 with one E4M3 scale per 16 channels).
+What the pages fix: each layer attends with a query and a local-window
+cache of its own (ai-maestro.online, "Compressed Sparse Attention 2"); the
+local window covers the latest 128 tokens (same page, "Causal
+Encoder-Decoder architecture"); the sparse entries are the Top-512 list the
+layer's mode supplies (Full and Reindex layers make a new one, Reuse layers
+take the most recent); main-cache entries are E2M1 values with an E4M3
+multiplier per 16 channels.
 
 Readings taken for what the pages leave open:
 

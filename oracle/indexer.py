@@ -2,16 +2,16 @@
 
 Test infrastructure only (see the package docstring).
 
-Pages (ai-maestro.online, "Compressed Sparse Attention 2"): a Full layer
-projects the indexer K and selects fresh Top-512 indices; a Reindex layer
-reuses the main KV and indexer K of the last Full layer but rescores them
-with its own indexer Q; a Reuse layer reuses the latest Top-K and skips the
-indexer.  The Hierarchical Sparse Indexer lets the Full layer build a
-candidate pool of up to 16,384 positions, 2,048 blocks of eight tokens, and
-later Reindex layers score only that bounded set.  (Same scheme:
-wpnews.pro "What is Compressed Sparse Attention 2 CSA2?"; kongchang.com
-"Three Core Innovations", where "16,000 blocks" is a garble of 16,384
-positions.)
+What the pages fix (ai-maestro.online, "Compressed Sparse Attention 2"):
+three per-layer modes.  A Full layer computes indexer keys of its own and
+picks a new Top-512; a Reindex layer keeps the preceding Full layer's caches
+and candidate set but scores them with a query of its own; a Reuse layer does
+no indexing and takes the most recent Top-512.  The Full layer's
+hierarchical indexer keeps the 2,048 best 8-token blocks (16,384 positions)
+as the candidate set, so a Reindex layer's cost does not grow with the
+context.  (The same scheme: wpnews.pro "What is Compressed Sparse Attention 2
+CSA2?"; kongchang.com "Three Core Innovations", whose "16,000 blocks" is read
+as a garble of 16,384 positions.)
 
 Readings taken for what the pages leave open:
 

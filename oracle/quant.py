@@ -2,11 +2,11 @@
 
 Test infrastructure only (see the package docstring).
 
-Pages: the main key-value cache quantises to E2M1 with one E4M3 scale per 16
-channels, NVFP4 without its global scale (ai-maestro.online, "FP4 KV, Bounded
+What the pages fix: each main-cache entry is stored as 4-bit E2M1 values,
+every run of 16 channels sharing one 8-bit E4M3 multiplier -- the NVFP4
+layout without its tensor-wide factor (ai-maestro.online, "FP4 KV, Bounded
 Replay, and other extensions"; wpnews.pro, "What is Compressed Sparse
-Attention 2 CSA2?": one E4M3 scaling factor per 16 channels; cutthecrap,
-"Architectural Breakthroughs": one scale for every 16 values).
+Attention 2 CSA2?"; cutthecrap, "Architectural Breakthroughs").
 
 The pages give no formula; the readings taken for what they leave open:
 
