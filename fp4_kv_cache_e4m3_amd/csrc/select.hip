@@ -316,12 +316,16 @@ CSA2_DEV void compact_topk(Get get, uint32_t tau, uint32_t need, SelShared& sh, 
 
 // Candidate step shared by Full and Reindex: candidate c = 8*slot + r refers
 // to position 8*pool[slot] + r; keys[c] is its score key (0 = not a candidate).
+// known_k2 > 0: the caller knows K2 = min(512, #nonzero keys), a lower bound
+// kmin of the nonzero keys and an upper bound kmax of all keys, and the
+// statistics pass is skipped (the radix digits then span [kmin, kmax]).
 template <int KPT2>
 CSA2_DEV void select_positions(const uint32_t (&key)[KPT2], SelShared& sh, const int32_t* pool_slots,
-                               int32_t* topk_out) {
+                               int32_t* topk_out, uint32_t known_k2 = 0u, uint32_t known_kmin = 0u,
+                               uint32_t known_kmax = 0u) {
   auto get = [&](int j) { return key[j]; };
-  uint32_t kmin, kmax, nvalid;
-  key_stats<KPT2>(get, sh, kmin, kmax, nvalid);
+  uint32_t kmin = known_kmin, kmax = known_kmax, nvalid = known_k2;
+  if (known_k2 == 0u) key_stats<KPT2>(get, sh, kmin, kmax, nvalid);
   const uint32_t K2 = min(nvalid, (uint32_t)kTopK);
   if (K2 > 0) {
     uint32_t tau, need;
@@ -362,6 +366,9 @@ __global__ __launch_bounds__(kSelThreads) void k_select_full(SelectParams p) {
   const uint32_t* bk = p.bkeys + q * p.bk_stride;
   int ncand = -1;                       // >= 0: Top-512 candidates are sh.cand[0..ncand), keys in ckey
   uint32_t ckey[kBlock] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+  // for the candidates' select: how many positions it takes, a floor of the
+  // candidate keys and the largest key (the best block's maximum)
+  uint32_t c_k2 = 0u, c_kmin = 0u, c_kmax = 0u;
   if constexpr (KPT1 <= 16) {
     uint32_t bkey[KPT1];
     if (base1 + KPT1 <= nb) {                 // whole run visible: 16-byte loads
@@ -414,6 +421,13 @@ __global__ __launch_bounds__(kSelThreads) void k_select_full(SelectParams p) {
 #pragma unroll
           for (int r = 0; r < kBlock; ++r) ckey[r] = ckey[r] >= kfloor ? ckey[r] : 0u;
         }
+        // With >= 512 blocks at least 512 candidate keys reach the floor (the
+        // top 512 blocks' maxima); with fewer, every block is a candidate and
+        // every visible position has a nonzero key.  The best block's maximum
+        // is the largest key of all.
+        c_k2 = K1 >= (uint32_t)kTopK ? (uint32_t)kTopK : (uint32_t)min(nv, (int64_t)kTopK);
+        c_kmin = K1 >= (uint32_t)kTopK ? thr : 1u;
+        c_kmax = kmax;
       }
       // the pool: for its output (role 0, or role 2 with an output), or for
       // the Top-512 select when the candidates were too many
@@ -492,7 +506,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_full(SelectParams p) {
     }
   }
   if (role == 1 && ncand >= 0) {              // ---- Top-512 of the candidates only
-    select_positions<kBlock>(ckey, sh, sh.cand, p.topk + q * kTopK);
+    select_positions<kBlock>(ckey, sh, sh.cand, p.topk + q * kTopK, c_k2, c_kmin, c_kmax);
     return;
   }
   for (int i = K1 + threadIdx.x; i < kPoolBlocks; i += kSelThreads) sh.pool[i] = -1;
@@ -503,7 +517,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_full(SelectParams p) {
 
   // ---- step 2: Top-512 positions of the candidate blocks, or of the pool
   if (ncand >= 0) {
-    select_positions<kBlock>(ckey, sh, sh.cand, p.topk + q * kTopK);
+    select_positions<kBlock>(ckey, sh, sh.cand, p.topk + q * kTopK, c_k2, c_kmin, c_kmax);
     return;
   }
   uint32_t key[KPT2];
