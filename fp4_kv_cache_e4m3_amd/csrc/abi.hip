@@ -46,18 +46,43 @@ int check_index(const csa2_index_args* a) {
 const float* q_scales(const csa2_index_args* a) { return a->fp8 ? a->q_scale : nullptr; }
 const float* k_scales(const csa2_index_args* a) { return a->fp8 ? a->k_scale : nullptr; }
 
+// Contexts of at least 2^19 entries take the long path of the Full index:
+// the scan writes only the 8-token block maxima, the select forms the pool,
+// and the Top-512 comes from rescoring the pool's positions with the layer's
+// own indexer query (the Reindex kernels).  That equals the Full layer's
+// Top-512 position for position (the pool holds the global Top-512, and the
+// rescored keys are the scan's, computed in the same order).  It trades the
+// scan's token-key writes (4 B per query and position) for gathers of the
+// pool's key rows (2,048 x 8 x D_I bytes per query): cheaper from 2^19
+// entries on at D_I = 128.
+constexpr int64_t kLongKvLen = 1 << 19;
+
 struct IndexLayout {
   int64_t nq, tk_stride, bk_stride, full_bytes, reindex_bytes, total;
+  bool long_path;
+  int64_t bk_off, pool_off;          // bytes: block keys; the pool (long path, when the caller passes none)
 };
 
 IndexLayout index_layout(const csa2_index_args* a) {
   IndexLayout L{};
   L.nq = (int64_t)a->batch * a->q_per_seq;
+  L.long_path = a->kv_len >= kLongKvLen;
   L.tk_stride = round_up(a->kv_len, 16);
   L.bk_stride = round_up((a->kv_len + kBlock - 1) / kBlock, 16);
-  L.full_bytes = L.nq * (L.tk_stride + L.bk_stride) * 4;
   L.reindex_bytes = L.nq * (kPoolPositions + kPoolBlocks) * 4;     // position keys + block keys
-  L.total = round_up(L.full_bytes > L.reindex_bytes ? L.full_bytes : L.reindex_bytes, 256);
+  if (!L.long_path) {
+    L.full_bytes = L.nq * (L.tk_stride + L.bk_stride) * 4;
+    L.bk_off = L.nq * L.tk_stride * 4;
+    L.total = round_up(L.full_bytes > L.reindex_bytes ? L.full_bytes : L.reindex_bytes, 256);
+    L.pool_off = -1;
+  } else {
+    // block keys at the front (the Reindex keys reuse that space once the
+    // pool is formed), then room for a pool
+    L.full_bytes = L.nq * L.bk_stride * 4;
+    L.bk_off = 0;
+    L.pool_off = round_up(L.full_bytes > L.reindex_bytes ? L.full_bytes : L.reindex_bytes, 256);
+    L.total = round_up(L.pool_off + L.nq * kPoolBlocks * 4, 256);
+  }
   return L;
 }
 
@@ -203,11 +228,24 @@ int select_impl(const csa2_index_args* a, int32_t* pool, int32_t* topk, const vo
     return qj.rows > 0 ? hip_status(launch_quantize(qj.x, qj.xs, qj.rows, 16 * qj.groups, qj.codes, qj.cs, qj.scales,
                                                     qj.ss, stream))
                        : CSA2_OK;
-  const uint32_t* tkeys = static_cast<const uint32_t*>(ws);
-  const uint32_t* bkeys = tkeys + L.nq * L.tk_stride;
-  SelectParams sel{tkeys, L.tk_stride, bkeys, L.bk_stride, a->n_visible, a->kv_len, pool, topk};
+  const uint32_t* tkeys = L.long_path ? nullptr : static_cast<const uint32_t*>(ws);
+  const uint32_t* bkeys = reinterpret_cast<const uint32_t*>(static_cast<const char*>(ws) + L.bk_off);
+  if (!L.long_path) {
+    SelectParams sel{tkeys, L.tk_stride, bkeys, L.bk_stride, a->n_visible, a->kv_len, pool, topk};
+    sel.qj = qj;
+    return hip_status(launch_select_full(sel, (int)L.nq, (a->kv_len + kBlock - 1) / kBlock, stream));
+  }
+  // long path: the pool (into the workspace when the caller takes none), then
+  // the Top-512 of its positions rescored with this layer's own query
+  int32_t* pl = pool ? pool : reinterpret_cast<int32_t*>(static_cast<char*>(const_cast<void*>(ws)) + L.pool_off);
+  SelectParams sel{nullptr, L.tk_stride, bkeys, L.bk_stride, a->n_visible, a->kv_len, pl, nullptr};
   sel.qj = qj;
-  return hip_status(launch_select_full(sel, (int)L.nq, (a->kv_len + kBlock - 1) / kBlock, stream));
+  hipError_t e = launch_select_full(sel, (int)L.nq, (a->kv_len + kBlock - 1) / kBlock, stream);
+  if (e != hipSuccess) return CSA2_ERR_HIP;
+  uint32_t* rk = static_cast<uint32_t*>(const_cast<void*>(ws));
+  ReindexParams rp{a->q, a->w, a->k, a->n_visible, q_scales(a), k_scales(a), pl, a->q_per_seq, a->kv_len,
+                   rk, topk, rk + L.nq * kPoolPositions};
+  return hip_status(launch_reindex(rp, (int)L.nq, a->heads, a->dim, stream));
 }
 
 }  // namespace
@@ -334,8 +372,8 @@ int csa2_index_scan(const csa2_index_args* a, void* ws, size_t ws_size, hipStrea
   if (L.nq == 0) return CSA2_OK;
   if (!aligned(a->n_visible, 4)) return CSA2_ERR_ALIGN;
   if (!ws || ws_size < (size_t)L.total || !aligned(ws, 256)) return CSA2_ERR_WORKSPACE;
-  uint32_t* tkeys = static_cast<uint32_t*>(ws);
-  uint32_t* bkeys = tkeys + L.nq * L.tk_stride;
+  uint32_t* tkeys = L.long_path ? nullptr : static_cast<uint32_t*>(ws);
+  uint32_t* bkeys = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + L.bk_off);
   ScanParams sp{a->q, a->w, a->k, a->n_visible, q_scales(a), k_scales(a), a->batch, a->q_per_seq, a->kv_len,
                 tkeys, L.tk_stride, bkeys, L.bk_stride};
   return hip_status(launch_index_scan(sp, a->heads, a->dim, stream));

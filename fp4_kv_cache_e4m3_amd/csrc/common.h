@@ -139,7 +139,7 @@ struct ScanParams {
   const int8_t* iq; const float* iw; const int8_t* ik; const int32_t* nvis;
   const float* iqs; const float* iks;                    // FP8 indexer: [nq, H_I] and [B, T] scales, else NULL
   int32_t batch, qn; int64_t T;
-  uint32_t* tkeys; int64_t tk_stride;                    // [nq, tk_stride]
+  uint32_t* tkeys; int64_t tk_stride;                    // [nq, tk_stride], or NULL: block maxima only
   uint32_t* bkeys; int64_t bk_stride;                    // [nq, bk_stride]
 };
 // FP4 quantisation of `rows` main-KV rows of `groups` 16-channel groups
@@ -157,7 +157,7 @@ struct SelectParams {
   const uint32_t* tkeys; int64_t tk_stride;
   const uint32_t* bkeys; int64_t bk_stride;
   const int32_t* nvis; int64_t T;
-  int32_t* pool; int32_t* topk;
+  int32_t* pool; int32_t* topk;                          // topk NULL: the pool only (> 8,192 blocks)
   int32_t roles;                                         // workgroups per query (set by the launcher)
   int32_t sel_wgs;                                       // selection workgroups (set by the launcher)
   QuantJob qj;                                           // rows == 0: none

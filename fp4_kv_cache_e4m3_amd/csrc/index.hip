@@ -120,7 +120,7 @@ __global__ __launch_bounds__(256) void k_index_scan(ScanParams p) {
         const bool writer = (HI == 4) || (HI == 8 && (g & 1) == 0) || (HI == 16 && g == 0);
         if (writer && j < p.qn && tok_ok) {
           const int64_t q = (int64_t)b * p.qn + j;
-          p.tkeys[q * p.tk_stride + t] = key;
+          if (p.tkeys) p.tkeys[q * p.tk_stride + t] = key;      // NULL: block maxima only
           if ((n & 7) == 0) p.bkeys[q * p.bk_stride + (t >> 3)] = m;
         }
       } else {  // HI == 2: rows (i0,i1) and (i2,i3) are two queries
@@ -137,7 +137,7 @@ __global__ __launch_bounds__(256) void k_index_scan(ScanParams p) {
           m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x141, 0xF, 0xF, false));
           if (j < p.qn && tok_ok) {
             const int64_t q = (int64_t)b * p.qn + j;
-            p.tkeys[q * p.tk_stride + t] = key;
+            if (p.tkeys) p.tkeys[q * p.tk_stride + t] = key;
             if ((n & 7) == 0) p.bkeys[q * p.bk_stride + (t >> 3)] = m;
           }
         }

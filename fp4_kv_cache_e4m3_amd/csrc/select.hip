@@ -436,7 +436,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_full(SelectParams p) {
         compact_topk<KPT1>(get, tau, need, sh, [&](uint32_t o, int j) { sh.pool[o] = (int32_t)(base1 + j); });
       }
     }
-  } else {
+  } else if (K1 > 0) {                       // (no visible block: the pool stays empty)
     // More than 16 blocks per thread: rank super-blocks of 8 blocks by their
     // maximum first.  The top 2,048 blocks lie in the top 2,048 super-blocks
     // (ranked by (max desc, id asc)): every super-block ranked above a chosen
@@ -513,7 +513,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_full(SelectParams p) {
   __syncthreads();
   if (p.pool && role != 1)
     for (int i = threadIdx.x; i < kPoolBlocks; i += kSelThreads) p.pool[q * kPoolBlocks + i] = sh.pool[i];
-  if (role == 0) return;
+  if (role == 0 || !p.topk) return;
 
   // ---- step 2: Top-512 positions of the candidate blocks, or of the pool
   if (ncand >= 0) {
@@ -692,6 +692,8 @@ hipError_t launch_select_full(const SelectParams& p, int nq, int64_t max_blocks,
   // workgroups (four lanes per 16-channel group), a larger one is launched
   // first on its own
   if (max_blocks > 128 * kSelThreads) return hipErrorInvalidValue;
+  // the pool alone (no Top-512) is selected only for the super-block path
+  if (!p.topk && (max_blocks <= 8 * kSelThreads || !p.pool)) return hipErrorInvalidValue;
   pp.roles = (max_blocks <= 8 * kSelThreads && p.pool) ? 2 : 1;
   pp.sel_wgs = pp.roles * nq;
   int extra = 0;

@@ -157,6 +157,40 @@ def test_index_reindex_matches_oracle(case):
     np.testing.assert_array_equal(topk, oidx.index_reindex(iq2, iw2, ik, Qn, rpool, nv))
 
 
+# From 2^19 positions on, the scan writes only block maxima and the Top-512 is
+# taken from the pool rescored with the layer's own query.
+LONG_CASES = [  # (B, Qn, T, H_I, D_I, r, wmax)
+    (1, 2, 1 << 19, 8, 64, 1, 2),           # at the threshold, heavy ties
+    (1, 1, (1 << 19) + 3, 2, 64, 0, 1),     # all scores equal, ragged tail
+    (2, 3, 600001, 8, 128, 8, 8),
+    (1, 2, 700000, 16, 64, 2, 2),
+    (1, 2, 530000, 4, 128, 1, 1),
+]
+
+
+@pytest.mark.parametrize("case", LONG_CASES, ids=lambda c: "B{}Q{}T{}H{}D{}".format(*c[:5]))
+def test_index_full_long_matches_oracle(case):
+    B, Qn, T, HI, DI, r, wmax = case
+    iq, iw, ik = inputs(hash(case) % 1000, B, Qn, T, HI, DI, r, wmax)
+    pool, topk = run_full(iq, iw, ik, Qn)
+    rpool, rtopk = oidx.index_full(iq, iw, ik, Qn)
+    np.testing.assert_array_equal(pool, rpool)
+    np.testing.assert_array_equal(topk, rtopk)
+    _, topk2 = run_full(iq, iw, ik, Qn, with_pool=False)      # the pool then lives in the workspace
+    np.testing.assert_array_equal(topk2, rtopk)
+
+
+def test_index_full_long_n_visible_ragged():
+    B, Qn, T = 1, 8, (1 << 19) + 5
+    iq, iw, ik = inputs(13, B, Qn, T, 8, 128, 3, 5)
+    nv = np.array([T, 0, 1, 9, 513, 65537, 300001, T - 1], dtype=np.int32)
+    pool, topk = run_full(iq, iw, ik, Qn, nv)
+    rpool, rtopk = oidx.index_full(iq, iw, ik, Qn, nv)
+    np.testing.assert_array_equal(pool, rpool)
+    np.testing.assert_array_equal(topk, rtopk)
+    assert np.all(pool[1] == -1) and np.all(topk[1] == -1)
+
+
 def test_index_full_verify_1m_entries():
     """1,048,576 entries per sequence, 1 + 5 draft queries per sequence: the
     131,072-block pool select that streams its block keys from memory.  The

@@ -36,9 +36,10 @@ def both(seed, B, Qn, T):
 
 
 def test_noalloc_equals_workspace_call_twice():
-    # first call: 16 sequences x 40,000 positions (2.8 MiB of keys per
-    # sequence row set), second: a smaller and ragged one over the same scratch
-    for seed, (B, Qn, T) in [(1, (16, 1, 40000)), (2, (3, 2, 5003))]:
+    # first call: 2 queries over 2^19 positions (block maxima only), then 16
+    # sequences x 40,000 positions (token keys), then a smaller and ragged one,
+    # all over the same scratch
+    for seed, (B, Qn, T) in [(4, (1, 2, 1 << 19)), (1, (16, 1, 40000)), (2, (3, 2, 5003))]:
         pool, topk, rpool, rtopk = both(seed, B, Qn, T)
         np.testing.assert_array_equal(pool, rpool)
         np.testing.assert_array_equal(topk, rtopk)
@@ -47,8 +48,9 @@ def test_noalloc_equals_workspace_call_twice():
 
 def test_noalloc_rejects_sizes_past_the_scratch():
     iq, iw, ik = index_inputs(3, 1, 1, 16)
-    # 64 query rows over 2^20 positions need 64 x (2^20 + 2^17) x 4 B > 64 MiB
-    big = csa2.IndexArgs(64, 1, 1 << 20, 8, 128, iq.data_ptr(), iw.data_ptr(), ik.data_ptr(), None)
+    # 256 query rows over 2^20 positions need 256 x 2^17 x 4 B of block keys
+    # and 256 x 2,048 x 4 B of pool: more than 64 MiB
+    big = csa2.IndexArgs(256, 1, 1 << 20, 8, 128, iq.data_ptr(), iw.data_ptr(), ik.data_ptr(), None)
     assert csa2.index_workspace_size(big) > (64 << 20)
     st = csa2.load().csa2_index_full_noalloc(big, None, 16, None)
     assert st == 6
