@@ -137,10 +137,24 @@ class DecodeGroup:
         n = w.new_per_seq
         self._new_calls = []
         self._new_paged = None
+        # several new rows in each of several sequences of a contiguous
+        # cache: the cache is a paged one whose block table maps page i of
+        # sequence b to page b * (T / P) + i (P the largest power of two
+        # <= 65,536 dividing T), so the rows go out in one job of the
+        # selection launch
+        P_id = min(T & -T, 65536)
         if P:                                   # one call: rows through the block table
             self._new_paged = (self.new_rows,
                                _dev(np.repeat(np.arange(B_, dtype=np.int32), n), dev),
-                               _dev(np.tile(np.arange(T - n, T, dtype=np.int32), B_), dev))
+                               _dev(np.tile(np.arange(T - n, T, dtype=np.int32), B_), dev),
+                               self.block_table, P)
+        elif n > 1 and B_ > 1 and P_id >= 64:
+            pages = T // P_id
+            table = (np.arange(B_, dtype=np.int32)[:, None] * pages + np.arange(pages, dtype=np.int32)[None, :])
+            self._new_paged = (self.new_rows,
+                               _dev(np.repeat(np.arange(B_, dtype=np.int32), n), dev),
+                               _dev(np.tile(np.arange(T - n, T, dtype=np.int32), B_), dev),
+                               _dev(table, dev), P_id)
         elif n == 1:
             self._new_calls.append((self.new_rows, self.codes[T - 1::T], self.scales[T - 1::T]))
         elif B_ <= n:
@@ -163,8 +177,8 @@ class DecodeGroup:
     # the stages of one step (bench.py times them apart)
     def quantize_new(self, stream=None) -> None:
         if self._new_paged is not None:
-            x, seq, pos = self._new_paged
-            B.quantize_kv_paged(x, seq, pos, self.block_table, self.w.page_size, self.codes, self.scales, stream)
+            x, seq, pos, bt, page = self._new_paged
+            B.quantize_kv_paged(x, seq, pos, bt, page, self.codes, self.scales, stream)
         for x, c, s in self._new_calls:
             B.quantize_kv(x, c, s, stream)
 
@@ -192,11 +206,12 @@ class DecodeGroup:
         out = []
         for l, m in enumerate(self.w.layers):
             if m == "full" and self._new_paged is not None:
-                # paged cache: the new rows go through the block table, as
-                # extra workgroups of the selection launch
+                # the new rows go through a block table (the cache's own, or
+                # the identity table of a contiguous cache), as extra
+                # workgroups of the selection launch
                 ia, tk = self.iargs_by_layer[l], self._topk_of[l]
-                x, seq, pos = self._new_paged
-                pg = (x, seq, pos, self.block_table, self.w.page_size, self.codes, self.scales)
+                x, seq, pos, bt, page = self._new_paged
+                pg = (x, seq, pos, bt, page, self.codes, self.scales)
                 if split_full:
                     out.append(("index_scan", lambda ia=ia: B.index_scan(ia, self.iws, stream)))
                     out.append(("index_select", lambda ia=ia, tk=tk, pg=pg: B.index_select_append_paged(
