@@ -132,9 +132,13 @@ void attn_plan(int64_t nq, int heads, int n_tiles, int want_waves, int want_spli
   splits = n_tiles > 0 ? (n_tiles + tps - 1) / tps : 1;
 }
 
+// the one-workgroup-per-query kernel pays off from two workgroups per CU on
+constexpr int64_t kWideMinWorkgroups = 512;
+
 struct AttnLayout {
   int64_t nq;
   int n_sparse_tiles, n_tiles, splits, tps, swa_rows, waves;
+  bool wide;
   int64_t ws_bytes;
 };
 
@@ -144,6 +148,15 @@ AttnLayout attn_layout(const csa2_attn_args* a) {
   L.n_sparse_tiles = a->kv_len > 0 ? (a->topk_k + 15) / 16 : 0;
   L.swa_rows = a->window > 0 ? a->window - 1 + a->q_per_seq : 0;
   L.n_tiles = L.n_sparse_tiles + (a->window + 15) / 16;
+  const bool wide_ok = a->dim == 512 && a->swa_fp8 == 0 && a->waves == 0 && a->splits == 0;
+  L.wide = a->kernel == 2 || (a->kernel == 0 && wide_ok && L.nq * ((a->heads + 63) / 64) >= kWideMinWorkgroups);
+  if (L.wide) {
+    L.waves = 4;
+    L.splits = 1;
+    L.tps = L.n_tiles > 0 ? L.n_tiles : 1;
+    L.ws_bytes = 0;
+    return L;
+  }
   attn_plan(L.nq, a->heads, L.n_tiles, a->waves, a->splits, L.waves, L.splits);
   L.tps = L.n_tiles > 0 ? (L.n_tiles + L.splits - 1) / L.splits : 1;
   L.ws_bytes = 0;
@@ -159,6 +172,8 @@ int check_attn(const csa2_attn_args* a) {
   if (a->batch < 0 || a->q_per_seq < 1 || a->kv_len < 0 || a->kv_len > (int64_t)1 << 31) return CSA2_ERR_SHAPE;
   if (a->heads < 1 || a->heads > 128) return CSA2_ERR_SHAPE;
   if (!(a->waves == 0 || a->waves == 4 || a->waves == 8) || a->splits < 0 || a->splits > 256) return CSA2_ERR_SHAPE;
+  if (a->kernel < 0 || a->kernel > 2) return CSA2_ERR_SHAPE;
+  if (a->kernel == 2 && (a->dim != 512 || a->swa_fp8 != 0 || a->waves != 0 || a->splits != 0)) return CSA2_ERR_SHAPE;
   if (!(a->dim == 128 || a->dim == 512)) return CSA2_ERR_SHAPE;
   if (a->topk_k < 0 || a->topk_k > kMaxTopK || a->window < 0 || a->window > 1024) return CSA2_ERR_SHAPE;
   const int64_t nq = (int64_t)a->batch * a->q_per_seq;
@@ -485,6 +500,7 @@ int csa2_sparse_attn(const csa2_attn_args* a, void* ws, size_t ws_size, hipStrea
   p.swa_start = a->swa_start;
   // With no tile at all the kernel still runs: every head ends with an empty
   // softmax and writes zeros (no memset node, so the call stays graph-safe).
+  if (L.wide) return hip_status(launch_attn_wide(p, (int)L.nq, stream));
   return hip_status(launch_attn(p, (int)L.nq, a->dim, L.waves, stream));
 }
 

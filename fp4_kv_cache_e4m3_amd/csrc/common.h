@@ -199,5 +199,6 @@ hipError_t launch_index_scan(const ScanParams& p, int heads, int dim, hipStream_
 hipError_t launch_select_full(const SelectParams& p, int nq, int64_t max_blocks, hipStream_t st);
 hipError_t launch_reindex(const ReindexParams& p, int nq, int heads, int dim, hipStream_t st);
 hipError_t launch_attn(const AttnParams& p, int nq, int dim, int waves, hipStream_t st);
+hipError_t launch_attn_wide(const AttnParams& p, int nq, hipStream_t st);   // dim 512, bf16 window
 
 }  // namespace csa2

@@ -196,6 +196,17 @@ def test_attn_rejects(lib):
     assert sa(ctypes.byref(args(splits=-1)), None, 0, None) == 2
     assert lib.csa2_attn_workspace_size(ctypes.byref(args(waves=8, splits=1))) == 0
     assert lib.csa2_attn_workspace_size(ctypes.byref(args(waves=4, splits=3))) > 0
+    # kernel: 0 the library's choice, 1 head groups, 2 one workgroup per query
+    # (dim 512, bf16 window, no explicit waves / splits; never a workspace)
+    assert sa(ctypes.byref(args(kernel=3)), None, 0, None) == 2
+    assert sa(ctypes.byref(args(kernel=-1)), None, 0, None) == 2
+    assert sa(ctypes.byref(args(kernel=2, dim=128, codes_stride=64, scales_stride=8)), None, 0, None) == 2
+    assert sa(ctypes.byref(args(kernel=2, waves=4)), None, 0, None) == 2
+    assert sa(ctypes.byref(args(kernel=2, splits=2)), None, 0, None) == 2
+    assert sa(ctypes.byref(args(kernel=2, swa_fp8=1, swa_scale=256)), None, 0, None) == 2
+    assert lib.csa2_attn_workspace_size(ctypes.byref(args(kernel=2))) == 0
+    # the library's choice for a prefill chunk (4,096 queries): no workspace
+    assert lib.csa2_attn_workspace_size(ctypes.byref(args(batch=1, q_per_seq=4096))) == 0
 
 
 def test_argument_structs_keep_their_tensors_alive():

@@ -17,7 +17,8 @@ from tests.parity import ATTN_TOL, bf16_values, dev, host, oracle_attention, row
 pytestmark = pytest.mark.gpu
 
 
-def gpu_attn(q_bits, codes, scales, topk, swa_bits, qn, T, window, swa_len=None, sm_scale=0.0, waves=0, splits=0):
+def gpu_attn(q_bits, codes, scales, topk, swa_bits, qn, T, window, swa_len=None, sm_scale=0.0, waves=0, splits=0,
+             kernel=0):
     nq, H, d = q_bits.shape
     q_d = dev(q_bits.view(np.int16))
     c_d, s_d = dev(codes), dev(scales)
@@ -25,7 +26,8 @@ def gpu_attn(q_bits, codes, scales, topk, swa_bits, qn, T, window, swa_len=None,
     sw_d = dev(swa_bits.view(np.int16)) if window > 0 else None
     sl_d = dev(np.asarray(swa_len, np.int32)) if swa_len is not None else None
     out = torch.full((nq, H, d), float("nan"), dtype=torch.float32, device="cuda")
-    args = csa2.attn_args(q_d, c_d, s_d, t_d, sw_d, out, qn, T, window, sl_d, sm_scale, waves=waves, splits=splits)
+    args = csa2.attn_args(q_d, c_d, s_d, t_d, sw_d, out, qn, T, window, sl_d, sm_scale, waves=waves, splits=splits,
+                          kernel=kernel)
     if t_d is None:
         args.topk_k = 0
     n = csa2.attn_workspace_size(args)

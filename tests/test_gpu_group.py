@@ -89,8 +89,12 @@ def test_group_reindex_reuse3_batch32_t65536():
 
 def test_group_prefill_q4096_t65536():
     """Encoder group: 4,096 query tokens over 65,536 entries, Full + 5 Reuse,
-    2,048 new entries quantised; sampled queries across the chunk."""
-    check_group(synth.C4, sample=[0, 1, 127, 128, 1000, 2047, 3333, 4095])
+    2,048 new entries quantised.  64 sampled queries: both ends of the chunk
+    (8 each) and 48 spread over it, together covering every residue mod 8
+    (the workgroup-to-XCD placement of the attention kernel)."""
+    sample = list(range(8)) + list(range(4088, 4096)) + [97 + 83 * k for k in range(48)]
+    assert len(set(sample)) == 64 and {q % 8 for q in sample} == set(range(8))
+    check_group(synth.C4, sample=sample)
 
 
 def test_group_verify_b8_q6_t1m():

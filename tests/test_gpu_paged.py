@@ -55,7 +55,8 @@ def paged_copy(codes, scales, rows, n_rows, fill=0x5A):
     return pc, ps
 
 
-def run_attn(q, codes, scales, topk, swa, qn, T, W, block_table=None, page_size=0, swa_scale=None, swa_start=None):
+def run_attn(q, codes, scales, topk, swa, qn, T, W, block_table=None, page_size=0, swa_scale=None, swa_start=None,
+             kernel=0):
     nq, H, d = q.shape
     keep = [dev(q.view(np.int16)), dev(codes), dev(scales), dev(topk.astype(np.int32)),
             dev(swa.view(np.int16) if swa_scale is None else swa)]
@@ -64,7 +65,7 @@ def run_attn(q, codes, scales, topk, swa, qn, T, W, block_table=None, page_size=
     sc_d = dev(swa_scale.astype(np.float32)) if swa_scale is not None else None
     st_d = dev(np.asarray(swa_start, np.int32)) if swa_start is not None else None
     args = csa2.attn_args(keep[0], keep[1], keep[2], keep[3], keep[4], out, qn, T, W, swa_scale=sc_d,
-                          block_table=bt_d, page_size=page_size, swa_start=st_d)
+                          block_table=bt_d, page_size=page_size, swa_start=st_d, kernel=kernel)
     n = csa2.attn_workspace_size(args)
     ws = torch.empty(max(n, 256), dtype=torch.uint8, device="cuda") if n else None
     csa2.sparse_attn(args, ws)
