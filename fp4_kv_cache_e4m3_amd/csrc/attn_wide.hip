@@ -10,23 +10,24 @@
 // Design.  With thousands of queries the work is a dense contraction per
 // query (64 heads x 640 entries x 512 channels, twice), so this kernel is
 // laid out for the matrix cores: one workgroup per (query, group of 64
-// heads), four waves, 32-entry tiles.  Wave w = (hh, dh): head half hh (32
-// heads), channel half dh (256 channels).
-//  * QK^T: wave (hh, dh) contracts its channel half for its 32 heads
-//    (MFMA 16x16x32, entries as A rows, heads as B columns; Q is read from
-//    LDS, lane-contiguous, once per k-step).  Each wave decodes only its own channel half of the tile's
-//    FP4 rows, so a row is decoded twice per workgroup (once per head half),
-//    not once per head group.  The two channel halves' partial logits meet
-//    through LDS and are added in a fixed order, so both waves of a head half
-//    hold bit-identical logits and run the same online softmax.
-//  * PV: wave (hh, dh) owns output channel quarter 2 dh + hh for all 64
-//    heads (O in 128 accumulator registers).  That quarter lies inside the
-//    channel half the wave decoded, so it stages its own fp16 values in LDS
-//    and reads them back transposed (ds_read_b64_tr_b16) as the B operand;
-//    the probabilities of its own head half are already in the A-operand
-//    layout of MFMA 16x16x32, those of the other half come through LDS (with
-//    their rescale factors).
-//  * Per tile: two barriers (partial logits, probabilities).
+// heads), eight waves (two per SIMD), 32-entry tiles.  Wave w = (hh, dq):
+// head half hh (32 heads), channel quarter dq (128 channels).
+//  * QK^T: wave (hh, dq) contracts its channel quarter for its 32 heads
+//    (MFMA 16x16x32, entries as A rows, heads as B columns, Q in registers).
+//    It decodes only that quarter of the tile's FP4 rows, so a row is
+//    decoded twice per query (once per head half).
+//  * The four quarters' partial logits meet in LDS: wave (hh, dq) adds the
+//    four partials (in quarter order) of one 16 x 16 block, entries of
+//    subtile dq / 2 and heads of tile dq % 2, and runs the online softmax
+//    on it; the two waves holding a head's two entry halves exchange their
+//    tile maxima, so both move the reference max together.  Every logit is
+//    computed and exponentiated once.
+//  * PV: wave (hh, dq) owns output channels 128 dq + 64 hh .. + 63 for all
+//    64 heads.  Those lie in its own channel quarter, so it stages its own
+//    fp16 values in LDS and reads them back transposed (ds_read_b64_tr_b16)
+//    as the B operand; the probabilities of all four head tiles come from
+//    LDS in the A-operand layout of MFMA 16x16x32.
+//  * Per tile: three barriers (partial logits, tile maxima, probabilities).
 // Precision as in attn.hip: FP4 values and bf16 Q are exact in fp16 (Q and
 // window rows inside fp16's range); window logits run on bf16 MFMA with the
 // bf16 Q; probabilities are fp16, normalised by the sum of the rounded values.
@@ -37,21 +38,22 @@ namespace csa2 {
 namespace {
 constexpr int kWD = 512;                // head dim
 constexpr int kWTE = 32;                // entries per tile
-constexpr int kWKH = 8;                 // 32-channel k-steps per channel half
-constexpr int kWVP = 128 + 8;           // halves per staged V row (one channel quarter)
+constexpr int kWKQ = 4;                 // 32-channel k-steps per channel quarter
+constexpr int kWVP = 64 + 8;            // halves per staged V row (one channel eighth)
 constexpr uint32_t kWOob = 0xFFFFF000u; // offset past every buffer
+constexpr int kWDepth = 1;              // FP4 tiles in flight per wave
 
-// FP4 data of two 16-entry subtiles for one lane: 64 channels (32 code bytes)
-// and their four E4M3 scales per entry
+// FP4 data of two 16-entry subtiles for one lane: 32 channels (16 code bytes)
+// and the scale word holding their two E4M3 scales, per entry
 struct WRaw {
-  uint32_t c[2][kWKH];
+  uint32_t c[2][kWKQ];
   uint32_t s[2];
   bool v[2];                            // the entry exists
 };
 
-// window rows (bf16) of two 16-entry subtiles: 64 channels per entry
+// window rows (bf16) of two 16-entry subtiles: 32 channels per entry
 struct WRawW {
-  u4 w[2][kWKH];
+  u4 w[2][kWKQ];
 };
 
 CSA2_DEV v8bf half8_to_bf16(v8h x) {
@@ -63,20 +65,23 @@ CSA2_DEV v8bf half8_to_bf16(v8h x) {
 }  // namespace
 
 template <bool PG>
-__global__ __launch_bounds__(256, 1) void k_attn_wide(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) _Float16 vst[4][kWTE * kWVP];   // staged V per wave
-  __shared__ __attribute__((aligned(16))) v4f xs[4][4 * 64];              // partial logits per wave
-  __shared__ __attribute__((aligned(16))) v8h pbuf[2][2 * 64];            // probabilities per head half
-  __shared__ float alph[2][32];                                           // rescale factors per head half
-  __shared__ float lsum[2][32];                                           // softmax sums per head half
-  __shared__ int32_t rflag[2];
+__global__ __launch_bounds__(512, 1) void k_attn_wide(AttnParams p) {
+  __shared__ __attribute__((aligned(16))) v4f xs[8][4 * 64];              // partial logits per wave
+  __shared__ __attribute__((aligned(16))) _Float16 vst[8][kWTE * kWVP];   // staged V per wave
+  __shared__ __attribute__((aligned(16))) v4h pg[2][2][2][64];            // probabilities [hh][et][ht][lane]
+  __shared__ float tmx[8][16];                                            // tile max per wave and head
+  __shared__ float alph[64];                                              // rescale factor per head
+  __shared__ int32_t rflag[4];                                            // per head tile: some head rescaled
+  __shared__ float lsum[8][16];                                           // softmax sums per wave and head
   __shared__ int32_t spos[kMaxTopK];                                      // rows of the Top-K slots, -1 empty
-  __shared__ __attribute__((aligned(16))) u4 qlds[4][2 * kWKH * 64];      // each wave's Q operands
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
-  const int hh = wave & 1, dh = wave >> 1, cq = 2 * dh + hh;
-  const bool stager = (g >> 1) == hh;     // this lane's 64 channels lie in the wave's output quarter
+  const int hh = wave >> 2, dq = wave & 3;
+  const int et_o = dq >> 1, ht_o = dq & 1;          // the logit block this wave reduces
+  const int partner = (hh << 2) | (dq ^ 2);         // the other entry half of the same heads
+  const bool stager = (g >> 1) == hh;               // this lane's channels lie in the wave's output eighth
+  const int cb = 128 * dq + 64 * hh;                // first output channel of the wave
 
   // workgroup -> (query, head group): consecutive queries on one XCD (the
   // dispatcher deals workgroup ids round-robin to the 8 XCDs), so a query's
@@ -91,21 +96,17 @@ __global__ __launch_bounds__(256, 1) void k_attn_wide(AttnParams p) {
   const int j = q - b * p.qn;
   const int h0 = 64 * grp;
 
-  // ---- Q: this wave's 32 heads x 256 channels as the QK^T B operand; lane
-  // (n, g) holds, in k-step kk, channels 256 dh + 64 g + 8 kk .. + 7 of head
-  // 32 hh + 16 ht + n (the k order inside an MFMA only has to match the K
-  // rows').  Kept in LDS (fp16; bf16 for the window tiles), one 16-byte
-  // operand per lane and (ht, kk), wave-private, read back lane-contiguous.
-  // The loads go out first; they are converted once the first gathers are out.
+  // ---- Q: lane (n, g) holds, in k-step kk, channels 128 dq + 32 g + 8 kk ..
+  // + 7 of head 32 hh + 16 ht + n (the k order inside an MFMA only has to
+  // match the K rows')
   const rsrc_t q_buf = make_rsrc(p.q + ((int64_t)q * p.heads + h0) * kWD, (uint32_t)(min(64, p.heads - h0) * kWD * 2));
-  u4* const myq = &qlds[wave][0];
-  u4 qraw[2 * kWKH];
+  u4 qraw[2][kWKQ];
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht)
 #pragma unroll
-    for (int kk = 0; kk < kWKH; ++kk) {
-      const uint32_t off = 2u * (uint32_t)((32 * hh + 16 * ht + n) * kWD + 256 * dh + 64 * g + 8 * kk);
-      qraw[ht * kWKH + kk] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(q_buf, off, 0, 0));
+    for (int kk = 0; kk < kWKQ; ++kk) {
+      const uint32_t off = 2u * (uint32_t)((32 * hh + 16 * ht + n) * kWD + 128 * dq + 32 * g + 8 * kk);
+      qraw[ht][kk] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(q_buf, off, 0, 0));
     }
 
   // ---- Top-K slot s -> cache row (paged: through the block table), -1 empty
@@ -127,37 +128,40 @@ __global__ __launch_bounds__(256, 1) void k_attn_wide(AttnParams p) {
     return row;
   };
 
-  // ---- FP4 rows of tile i: lane (n, g) loads, for entry 32 i + 16 et + n,
-  // code bytes 128 dh + 32 g .. + 31 and scale bytes 16 dh + 4 g .. + 3
+  // ---- FP4 rows: lane (n, g) loads, for entry 32 i + 16 et + n, code bytes
+  // 64 dq + 16 g .. + 15 and the aligned scale word holding scale bytes
+  // 8 dq + 2 g, + 1
   const rsrc_t codes = make_rsrc(p.codes + row0 * p.codes_stride, (uint32_t)(nrows * p.codes_stride));
   const rsrc_t scales = make_rsrc(p.scales + row0 * p.scales_stride, (uint32_t)(nrows * p.scales_stride));
-  const uint32_t lcb = (uint32_t)(128 * dh + 32 * g), lsb = (uint32_t)(16 * dh + 4 * g);
+  const uint32_t lcb = (uint32_t)(64 * dq + 16 * g), lsb = (uint32_t)(8 * dq + 4 * (g >> 1));
+  const uint32_t ssel = (uint32_t)(2 * (g & 1)) | (0x0Cu << 8) | ((uint32_t)(2 * (g & 1) + 1) << 16) | (0x0Cu << 24);
   auto load_rows = [&](const int32_t (&row)[2], WRaw& r) {
 #pragma unroll
     for (int et = 0; et < 2; ++et) {
       const uint32_t rc = row[et] >= 0 ? __umul24((uint32_t)row[et], (uint32_t)p.codes_stride) : kWOob;
       const uint32_t rs = row[et] >= 0 ? __umul24((uint32_t)row[et], (uint32_t)p.scales_stride) : kWOob;
-      const u4 c0 = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(codes, rc + lcb, 0, 0));
-      const u4 c1 = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(codes, rc + lcb + 16, 0, 0));
-      r.c[et][0] = c0[0]; r.c[et][1] = c0[1]; r.c[et][2] = c0[2]; r.c[et][3] = c0[3];
-      r.c[et][4] = c1[0]; r.c[et][5] = c1[1]; r.c[et][6] = c1[2]; r.c[et][7] = c1[3];
+      const u4 c = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(codes, rc + lcb, 0, 0));
+      r.c[et][0] = c[0]; r.c[et][1] = c[1]; r.c[et][2] = c[2]; r.c[et][3] = c[3];
       r.s[et] = __builtin_amdgcn_raw_buffer_load_b32(scales, rs + lsb, 0, 0);
       r.v[et] = row[et] >= 0;
     }
   };
-  // the first two tiles' rows straight from the Top-K row, so their gathers
-  // go out before anything waits; the other slots' rows go to LDS
-  WRaw raw[2];
+  // the first tiles' rows straight from the Top-K row, so their gathers go
+  // out before anything waits; the other slots' rows go to LDS
+  WRaw raw[kWDepth];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < kWDepth; ++i) {
     int32_t row[2];
 #pragma unroll
     for (int et = 0; et < 2; ++et) row[et] = i < nft ? slot_row(kWTE * i + 16 * et + n) : -1;
     load_rows(row, raw[i]);
   }
-  for (int s = 2 * kWTE + threadIdx.x; s < nft * kWTE; s += 256) spos[s] = slot_row(s);
+  for (int s = kWDepth * kWTE + threadIdx.x; s < nft * kWTE; s += 512) spos[s] = slot_row(s);
+  v8h qf[2][kWKQ];
 #pragma unroll
-  for (int f = 0; f < 2 * kWKH; ++f) myq[f * 64 + lane] = __builtin_bit_cast(u4, bf16x8_to_half(qraw[f]));
+  for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+    for (int kk = 0; kk < kWKQ; ++kk) qf[ht][kk] = bf16x8_to_half(qraw[ht][kk]);
   __syncthreads();                                  // spos
   auto load_fp4 = [&](int i, WRaw& r) {
     int32_t row[2];
@@ -167,8 +171,8 @@ __global__ __launch_bounds__(256, 1) void k_attn_wide(AttnParams p) {
   };
 
   // ---- window rows of window tile i: entry e = 32 i + 16 et + n is window
-  // row j + e (ring slot (j + e + start) mod rows); lane (n, g) loads its 64
-  // channels 256 dh + 64 g .. (128 bytes)
+  // row j + e (ring slot (j + e + start) mod rows); lane (n, g) loads its 32
+  // channels 128 dq + 32 g .. (64 bytes)
   const int first_swa = p.swa_len ? p.swa_rows - p.swa_len[b] : 0;
   int swa_st = p.swa_start ? p.swa_start[b] : 0;
   swa_st = swa_st >= 0 && swa_st < p.swa_rows ? swa_st : 0;
@@ -187,137 +191,99 @@ __global__ __launch_bounds__(256, 1) void k_attn_wide(AttnParams p) {
       const int rs = rr + swa_st >= p.swa_rows ? rr + swa_st - p.swa_rows : rr + swa_st;
       const uint32_t ro = swa_valid(i, et) ? (uint32_t)rs * (uint32_t)(2 * kWD) : kWOob;
 #pragma unroll
-      for (int kk = 0; kk < kWKH; ++kk)
+      for (int kk = 0; kk < kWKQ; ++kk)
         r.w[et][kk] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                 swa_buf, ro + 2u * (uint32_t)(256 * dh + 64 * g + 8 * kk), 0, 0));
+                                                 swa_buf, ro + 2u * (uint32_t)(128 * dq + 32 * g + 8 * kk), 0, 0));
     }
   };
 
-  // O rows of the wave's own head half (oo) and of the other one (ox):
-  // oo[ht][t] holds heads 32 hh + 16 ht + 4 g + i, ox those of half hh ^ 1,
-  // channel 128 cq + 16 t + n (static indices only: the arrays stay in
-  // registers)
-  v4f oo[2][8], ox[2][8];
+  // O: o[a][t] holds heads 16 a + 4 g + i (a = 2 hh' + ht'), channel
+  // cb + 16 t + n
+  v4f o[4][4];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      oo[a][t] = v4f{0.f, 0.f, 0.f, 0.f};
-      ox[a][t] = v4f{0.f, 0.f, 0.f, 0.f};
-    }
-  float m_run[2] = {-__builtin_inff(), -__builtin_inff()};
-  float l_run[2] = {0.0f, 0.0f};
+    for (int t = 0; t < 4; ++t) o[a][t] = v4f{0.f, 0.f, 0.f, 0.f};
+  float m_run = -__builtin_inff(), l_run = 0.0f;   // head 32 hh + 16 ht_o + n over entry half et_o
 
   _Float16* const my = &vst[wave][0];
-  // V staging: lane (n, g) (stager) writes entry 16 et + n, quarter channels
-  // 64 (g & 1) + 8 kk; transposing read: lane (n, g) gets entries
-  // 16 et + 4 g .. + 3 of quarter channel 16 t + n
-  _Float16* const vrow = my + n * kWVP + 64 * (g & 1);
+  // V staging: lane (n, g) (stager) writes entry 16 et + n, channels
+  // 32 (g & 1) + 8 kk of the wave's eighth; transposing read: lane (n, g)
+  // gets entries 16 et + 4 g .. + 3 of eighth channel 16 t + n
+  _Float16* const vrow = my + n * kWVP + 32 * (g & 1);
   const _Float16* const vb = my + (4 * g + (n >> 2)) * kWVP + 4 * (n & 3);
 
   // the rest of a tile once the wave's partial logits acc[et][ht] (entries
-  // 16 et + 4 g + i, head 32 hh + 16 ht + n, channel half dh) are in
+  // 16 et + 4 g + i, head 32 hh + 16 ht + n, channel quarter dq) are in
   auto finish_tile = [&](v4f (&acc)[2][2], uint32_t vmask) {
 #pragma unroll
     for (int et = 0; et < 2; ++et)
 #pragma unroll
       for (int ht = 0; ht < 2; ++ht) xs[wave][(2 * et + ht) * 64 + lane] = acc[et][ht];
     __syncthreads();
-    // logits: channel half 0 + channel half 1, in that order in both waves
-    float s[2][2][4];
+    // logits of block (et_o, ht_o): the four quarters, added in quarter order
+    v4f sfull = xs[hh << 2][dq * 64 + lane];
 #pragma unroll
-    for (int et = 0; et < 2; ++et)
+    for (int d = 1; d < 4; ++d) sfull += xs[(hh << 2) | d][dq * 64 + lane];
+    float s[4];
 #pragma unroll
-      for (int ht = 0; ht < 2; ++ht) {
-        const v4f other = xs[wave ^ 2][(2 * et + ht) * 64 + lane];
-        const v4f full = dh == 0 ? acc[et][ht] + other : other + acc[et][ht];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bool v = (vmask >> (16 * et + 4 * g + i)) & 1u;
-          s[et][ht][i] = v ? full[i] * p.qscale : -__builtin_inff();
-        }
-      }
-    // online softmax per head (lane n, head half ht); the reference max moves
-    // only when a tile's max exceeds it by more than 2^8 (probabilities stay
-    // <= 256, fine for fp16)
-    v8h pr[2];
-    float alpha[2];
-    bool resc = false;
-#pragma unroll
-    for (int ht = 0; ht < 2; ++ht) {
-      float tmax = -__builtin_inff();
-#pragma unroll
-      for (int et = 0; et < 2; ++et)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, s[et][ht][i]);
-      tmax = max_over_quarters(tmax);
-      const bool grow = tmax > m_run[ht] + 8.0f;
-      const bool rs = grow && m_run[ht] != -__builtin_inff();
-      alpha[ht] = rs ? __builtin_amdgcn_exp2f(m_run[ht] - tmax) : 1.0f;
-      resc |= rs;
-      if (grow) m_run[ht] = tmax;
-      const float mref = m_run[ht] == -__builtin_inff() ? 0.0f : m_run[ht];
-#pragma unroll
-      for (int et = 0; et < 2; ++et)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pr[ht][4 * et + i] = (_Float16)__builtin_amdgcn_exp2f(s[et][ht][i] - mref);
-      const v2h one2 = {(_Float16)1.0f, (_Float16)1.0f};
-      float ps = 0.0f;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) ps = __builtin_amdgcn_fdot2(v2h{pr[ht][2 * k], pr[ht][2 * k + 1]}, one2, ps, false);
-      l_run[ht] = l_run[ht] * alpha[ht] + ps;
+    for (int i = 0; i < 4; ++i) {
+      const bool v = (vmask >> (16 * et_o + 4 * g + i)) & 1u;
+      s[i] = v ? sfull[i] * p.qscale : -__builtin_inff();
     }
-    const bool any_resc = __any(resc);
-    if (dh == 0) {
+    float hmax = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    hmax = max_over_quarters(hmax);
+    if (g == 0) tmx[wave][n] = hmax;
+    __syncthreads();
+    // online softmax of head n: both entry halves move the reference max
+    // together (it moves only when the tile max exceeds it by more than 2^8,
+    // so probabilities stay <= 256, fine for fp16)
+    const float tmax = et_o == 0 ? fmaxf(hmax, tmx[partner][n]) : fmaxf(tmx[partner][n], hmax);
+    const bool grow = tmax > m_run + 8.0f;
+    const bool rs = grow && m_run != -__builtin_inff();
+    const float alpha = rs ? __builtin_amdgcn_exp2f(m_run - tmax) : 1.0f;
+    if (grow) m_run = tmax;
+    const float mref = m_run == -__builtin_inff() ? 0.0f : m_run;
+    v4h pr;
 #pragma unroll
-      for (int ht = 0; ht < 2; ++ht) {
-        pbuf[hh][ht * 64 + lane] = pr[ht];
-        if (g == 0) alph[hh][16 * ht + n] = alpha[ht];
-      }
-      if (lane == 0) rflag[hh] = any_resc ? 1 : 0;
+    for (int i = 0; i < 4; ++i) pr[i] = (_Float16)__builtin_amdgcn_exp2f(s[i] - mref);
+    const v2h one2 = {(_Float16)1.0f, (_Float16)1.0f};
+    const float ps = __builtin_amdgcn_fdot2(v2h{pr[2], pr[3]}, one2, __builtin_amdgcn_fdot2(v2h{pr[0], pr[1]}, one2, 0.0f, false), false);
+    l_run = l_run * alpha + ps;
+    pg[hh][et_o][ht_o][lane] = pr;
+    if (et_o == 0) {
+      const bool any_rs = __any(rs);
+      if (g == 0) alph[32 * hh + 16 * ht_o + n] = alpha;
+      if (lane == 0) rflag[2 * hh + ht_o] = any_rs ? 1 : 0;
     }
     __syncthreads();
-    v8h po[2];
-#pragma unroll
-    for (int ht = 0; ht < 2; ++ht) po[ht] = pbuf[hh ^ 1][ht * 64 + lane];
-    // rescale O rows (heads 16 a + 4 g + i) of either half that moved its max
-    if (any_resc) {
-#pragma unroll
-      for (int ht = 0; ht < 2; ++ht) {
-        float ai[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha[ht], 4 * g + i, 64);
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) oo[ht][t][i] *= ai[i];
-      }
-    }
-    if (rflag[hh ^ 1]) {
-#pragma unroll
-      for (int ht = 0; ht < 2; ++ht) {
-        float ai[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ai[i] = alph[hh ^ 1][16 * ht + 4 * g + i];
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) ox[ht][t][i] *= ai[i];
-      }
-    }
+    // rescale the O rows of every head tile that moved its max, then
     // O += P V over the 32 entries: k slot s of lane group g is entry
-    // 4 g + s (s < 4) or 16 + 4 g + s - 4, in P (from the logits' layout) and
-    // in V (two transposing reads)
+    // 4 g + s (s < 4) or 16 + 4 g + s - 4, in P and in V (two transposing
+    // reads)
+    v8h pa[4];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
+    for (int a = 0; a < 4; ++a) {
+      const v4h p0 = pg[a >> 1][0][a & 1][lane];
+      const v4h p1 = pg[a >> 1][1][a & 1][lane];
+      pa[a] = v8h{p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+      if (rflag[a]) {
+        float ai[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ai[i] = alph[16 * a + 4 * g + i];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[a][t][i] *= ai[i];
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
       const v4h v0 = lds_read_tr16(vb + 16 * t);
       const v4h v1 = lds_read_tr16(vb + 16 * kWVP + 16 * t);
       const v8h vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
 #pragma unroll
-      for (int ht = 0; ht < 2; ++ht) {
-        oo[ht][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pr[ht], vv, oo[ht][t], 0, 0, 0);
-        ox[ht][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(po[ht], vv, ox[ht][t], 0, 0, 0);
-      }
+      for (int a = 0; a < 4; ++a) o[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[a], vv, o[a][t], 0, 0, 0);
     }
   };
 
@@ -325,37 +291,30 @@ __global__ __launch_bounds__(256, 1) void k_attn_wide(AttnParams p) {
     return (uint32_t)(__ballot(v0) & 0xFFFFu) | ((uint32_t)(__ballot(v1) & 0xFFFFu) << 16);
   };
 
-  // ---- FP4 tiles: two in flight; tile i + 2 is loaded into tile i's
-  // registers as soon as tile i's logits are done with them
+  // ---- FP4 tiles: kWDepth in flight; tile i + kWDepth is loaded into tile
+  // i's registers as soon as tile i's logits are done with them
   if (nft > 0) {
-    for (int i0 = 0; i0 < nft; i0 += 2) {
+    for (int i0 = 0; i0 < nft; i0 += kWDepth) {
 #pragma unroll
-      for (int uu = 0; uu < 2; ++uu) {
+      for (int uu = 0; uu < kWDepth; ++uu) {
         const int i = i0 + uu;
         if (i >= nft) break;
         const uint32_t vmask = tile_mask(raw[uu].v[0], raw[uu].v[1]);
         v4f acc[2][2] = {{v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}},
                          {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}}};
-        v2h sa[2], sb[2];
+        v2h sc[2];
 #pragma unroll
-        for (int et = 0; et < 2; ++et) {
-          sa[et] = e4m3_pair_s8(raw[uu].s[et], 0x0C010C00u);
-          sb[et] = e4m3_pair_s8(raw[uu].s[et], 0x0C030C02u);
-        }
+        for (int et = 0; et < 2; ++et) sc[et] = e4m3_pair_s8(raw[uu].s[et], ssel);
 #pragma unroll
-        for (int kk = 0; kk < kWKH; ++kk) {
-          const v8h q0 = __builtin_bit_cast(v8h, myq[kk * 64 + lane]);
-          const v8h q1 = __builtin_bit_cast(v8h, myq[(kWKH + kk) * 64 + lane]);
+        for (int kk = 0; kk < kWKQ; ++kk)
 #pragma unroll
           for (int et = 0; et < 2; ++et) {
-            const _Float16 s8 = kk < 4 ? sa[et][kk >> 1] : sb[et][(kk >> 1) - 2];
-            const v8h kf = fp4x8_to_half_s8(raw[uu].c[et][kk], s8);
-            acc[et][0] = mfma_qk(kf, q0, acc[et][0]);
-            acc[et][1] = mfma_qk(kf, q1, acc[et][1]);
+            const v8h kf = fp4x8_to_half_s8(raw[uu].c[et][kk], sc[et][kk >> 1]);
+            acc[et][0] = mfma_qk(kf, qf[0][kk], acc[et][0]);
+            acc[et][1] = mfma_qk(kf, qf[1][kk], acc[et][1]);
             if (stager) *reinterpret_cast<v8h*>(vrow + 16 * et * kWVP + 8 * kk) = kf;
           }
-        }
-        if (i + 2 < nft) load_fp4(i + 2, raw[uu]);
+        if (i + kWDepth < nft) load_fp4(i + kWDepth, raw[uu]);
         finish_tile(acc, vmask);
       }
     }
@@ -363,11 +322,13 @@ __global__ __launch_bounds__(256, 1) void k_attn_wide(AttnParams p) {
 
   // ---- window tiles: bf16 logits against the bf16 Q (converted back from
   // the fp16 copy, exact for values that came from bf16); the next tile's
-  // rows are loaded as soon as this tile's logits are done
+  // rows go out as soon as this tile's logits are done with its registers
   if (nwt > 0) {
+    v8bf qb[2][kWKQ];
 #pragma unroll
-    for (int f = 0; f < 2 * kWKH; ++f)
-      myq[f * 64 + lane] = __builtin_bit_cast(u4, half8_to_bf16(__builtin_bit_cast(v8h, myq[f * 64 + lane])));
+    for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+      for (int kk = 0; kk < kWKQ; ++kk) qb[ht][kk] = half8_to_bf16(qf[ht][kk]);
     WRawW wr;
     load_swa(0, wr);
     for (int i = 0; i < nwt; ++i) {
@@ -375,59 +336,49 @@ __global__ __launch_bounds__(256, 1) void k_attn_wide(AttnParams p) {
       v4f acc[2][2] = {{v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}},
                        {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}}};
 #pragma unroll
-      for (int kk = 0; kk < kWKH; ++kk) {
-        const v8bf q0 = __builtin_bit_cast(v8bf, myq[kk * 64 + lane]);
-        const v8bf q1 = __builtin_bit_cast(v8bf, myq[(kWKH + kk) * 64 + lane]);
+      for (int kk = 0; kk < kWKQ; ++kk)
 #pragma unroll
         for (int et = 0; et < 2; ++et) {
           const v8bf kb = __builtin_bit_cast(v8bf, wr.w[et][kk]);
-          acc[et][0] = mfma_qk(kb, q0, acc[et][0]);
-          acc[et][1] = mfma_qk(kb, q1, acc[et][1]);
+          acc[et][0] = mfma_qk(kb, qb[0][kk], acc[et][0]);
+          acc[et][1] = mfma_qk(kb, qb[1][kk], acc[et][1]);
           if (stager) *reinterpret_cast<v8h*>(vrow + 16 * et * kWVP + 8 * kk) = bf16x8_to_half(wr.w[et][kk]);
         }
-      }
       if (i + 1 < nwt) load_swa(i + 1, wr);
       finish_tile(acc, vmask);
     }
   }
 
-  // ---- normalise: the sums of every head of both halves
-  float lt[2];
-#pragma unroll
-  for (int ht = 0; ht < 2; ++ht) {
-    float l = l_run[ht] + __shfl_xor(l_run[ht], 16, 64);
-    lt[ht] = l + __shfl_xor(l, 32, 64);
-  }
-  if (dh == 0 && g == 0) {
-    lsum[hh][n] = lt[0];
-    lsum[hh][16 + n] = lt[1];
+  // ---- normalise: each head's sum over its two entry halves (in order)
+  {
+    float l = l_run + __shfl_xor(l_run, 16, 64);
+    l = l + __shfl_xor(l, 32, 64);
+    if (g == 0) lsum[wave][n] = l;
   }
   __syncthreads();
-  auto store_half = [&](const v4f (&oh)[2][8], int half) {
 #pragma unroll
-    for (int ht = 0; ht < 2; ++ht)
+  for (int a = 0; a < 4; ++a) {
+    const int w0 = ((a >> 1) << 2) | (a & 1);       // et 0 owner of head tile a; et 1 owner is w0 + 2
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int hl = 32 * half + 16 * ht + 4 * g + i;  // head within the group
-        const float l = lsum[half][16 * ht + 4 * g + i];
-        const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-        if (h0 + hl < p.heads) {
-          float* const orow = p.out + ((int64_t)q * p.heads + h0 + hl) * kWD + 128 * cq + n;
+    for (int i = 0; i < 4; ++i) {
+      const int hl = 16 * a + 4 * g + i;            // head within the group
+      const float l = lsum[w0][4 * g + i] + lsum[w0 + 2][4 * g + i];
+      const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+      if (h0 + hl < p.heads) {
+        float* const orow = p.out + ((int64_t)q * p.heads + h0 + hl) * kWD + cb + n;
 #pragma unroll
-          for (int t = 0; t < 8; ++t) orow[16 * t] = oh[ht][t][i] * inv;
-        }
+        for (int t = 0; t < 4; ++t) orow[16 * t] = o[a][t][i] * inv;
       }
-  };
-  store_half(oo, hh);
-  store_half(ox, hh ^ 1);
+    }
+  }
 }
 
 hipError_t launch_attn_wide(const AttnParams& p, int nq, hipStream_t st) {
   if (nq == 0) return hipSuccess;
   const int64_t total = (int64_t)nq * ((p.heads + 63) / 64);
   const dim3 grid((unsigned)(8 * ((total + 7) / 8)));
-  if (p.block_table) hipLaunchKernelGGL(k_attn_wide<true>, grid, dim3(256), 0, st, p);
-  else hipLaunchKernelGGL(k_attn_wide<false>, grid, dim3(256), 0, st, p);
+  if (p.block_table) hipLaunchKernelGGL(k_attn_wide<true>, grid, dim3(512), 0, st, p);
+  else hipLaunchKernelGGL(k_attn_wide<false>, grid, dim3(512), 0, st, p);
   return hipGetLastError();
 }
 
