@@ -9,9 +9,10 @@ whole group over one batch; inputs are synthetic, seeded, and resident in HBM
 before timing starts.
 
 Prints one JSON line: query-tokens/s, achieved HBM GB/s of the group, the
-roofline of the dominant kernel (the indexer scan) and of the attention
-kernel from HIP events recorded around them inside the timed region, and the
-FP64 oracle timed on the host.
+roofline of the dominant kernel (the indexer scan; for a prefill chunk the
+attention against the fp16 MFMA peak, with the scan against the int8 peak
+beside it) and of the attention kernel, from HIP events recorded around them
+inside the timed region, and the FP64 oracle timed on the host.
 
 Timing: every timed step starts with a cold last-level cache -- a 512 MiB
 device write (twice the MI355X's 256 MB Infinity Cache) runs between steps,
@@ -31,6 +32,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak (AMD spec)
+PEAK_F16_TFLOPS = 2500.0       # MI355X dense fp16 / bf16 MFMA peak (AMD spec)
+PEAK_I8_TOPS = 5000.0          # MI355X dense int8 MFMA peak (AMD spec)
 
 # HBM bytes per k_index_scan launch measured with rocprofv3 FETCH_SIZE and
 # WRITE_SIZE (each scaled by what the counter reads for a plain 1 GiB copy) on
@@ -287,6 +290,13 @@ def main() -> int:
     group = "group" if nl <= 6 else f"{nl}-layer decoder step"
     achieved = scan_bytes / (scan_ms / 1e3) / 1e9
     attn_achieved = nbytes["attn_layer"] / (attn_ms / 1e3) / 1e9
+    # the library runs the one-workgroup-per-query kernel for many query tokens
+    wide = w.dim == 512 and not w.swa8 and w.nq * ((w.heads + 63) // 64) >= 512
+    attn_kernel = "k_attn_wide" if wide else "k_attn"
+    # matrix work of one attention layer: QK^T and PV over the Top-512 and window entries
+    attn_tflop = 4.0 * w.nq * w.heads * (512 + w.window) * w.dim / 1e12
+    # integer work of the indexer scan: every score row against every position
+    scan_tops = 2.0 * w.nq * w.idx_heads * w.kv_len * w.idx_dim / 1e12
     out = {
         "metric": f"decode query-tokens/s per CSA2 layer {group} at 64K ctx + achieved HBM GB/s",
         "value": round(value, 1),
@@ -315,11 +325,22 @@ def main() -> int:
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "bytes_per_launch": scan_bytes, "traffic": scan_traffic(w) if full else None},
-        "roofline_attn": {"kernel": "k_attn", "bound": "hbm", "achieved": round(attn_achieved, 1),
+        "roofline_attn": {"kernel": attn_kernel, "bound": "hbm", "achieved": round(attn_achieved, 1),
                           "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(attn_achieved / PEAK_HBM_GBS, 4),
                           "bytes_per_launch": nbytes["attn_layer"], "ms": round(attn_ms, 4)},
         "wall_s_timed": round(t_wall, 3),
     }
+    if w.encoder:
+        # a prefill chunk is matrix work: the attention (the step's dominant
+        # kernel) against the fp16 MFMA peak, the scan against the int8 one
+        a_tf = attn_tflop / (attn_ms / 1e3)
+        out["roofline"] = {"kernel": attn_kernel, "bound": "mfma", "achieved": round(a_tf, 1),
+                           "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s", "frac": round(a_tf / PEAK_F16_TFLOPS, 4),
+                           "flop_per_launch": attn_tflop * 1e12, "ms": round(attn_ms, 4), "traffic": None}
+        s_tops = scan_tops / (scan_ms / 1e3)
+        out["roofline_scan"] = {"kernel": "k_index_scan", "bound": "mfma", "achieved": round(s_tops, 1),
+                                "peak": PEAK_I8_TOPS, "unit": "TOP/s", "frac": round(s_tops / PEAK_I8_TOPS, 4),
+                                "ops_per_launch": scan_tops * 1e12, "ms": round(scan_ms, 4)}
     if not args.no_cpu_baseline:
         cb = cpu_baseline(w, args.cpu_queries)
         one = cpu_baseline(w, args.cpu_queries, threads=1)
