@@ -27,7 +27,7 @@ EXPORTS = (
     "csa2_index_workspace_size", "csa2_index_full", "csa2_index_scan", "csa2_index_select",
     "csa2_index_full_append", "csa2_index_select_append", "csa2_index_full_append_paged",
     "csa2_index_select_append_paged", "csa2_index_reindex",
-    "csa2_attn_workspace_size", "csa2_sparse_attn", "csa2_index_full_noalloc",
+    "csa2_attn_workspace_size", "csa2_sparse_attn", "csa2_index_full_noalloc", "csa2_check_index",
 )
 
 
@@ -111,6 +111,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.csa2_attn_workspace_size.argtypes = [ctypes.POINTER(AttnArgs)]
     lib.csa2_sparse_attn.restype = ctypes.c_int
     lib.csa2_sparse_attn.argtypes = [ctypes.POINTER(AttnArgs), vp, sz, vp]
+    lib.csa2_check_index.restype = ctypes.c_int
+    lib.csa2_check_index.argtypes = [ctypes.POINTER(IndexArgs), vp, vp, i32, vp, vp]
     _lib = lib
     return lib
 
@@ -253,6 +255,13 @@ def index_select_append(args: IndexArgs, pool, topk, ws, x, codes, scales, strea
     _check(load().csa2_index_select_append(ctypes.byref(args), _ptr(pool), _ptr(topk), _ptr(ws),
                                            ws.numel() * ws.element_size() if ws is not None else 0,
                                            *_append_args(x, codes, scales), _stream(stream)))
+
+
+def check_index(args: IndexArgs, pool, topk, mode: int, bad, stream=None) -> None:
+    """Device-side check of index rows (mode 0 Full outputs, 1 Reindex
+    outputs against the given pool, 2 a Reindex input pool): the number of
+    failing rows is added to bad (a device uint32 / int32 scalar tensor)."""
+    _check(load().csa2_check_index(ctypes.byref(args), _ptr(pool), _ptr(topk), int(mode), _ptr(bad), _stream(stream)))
 
 
 def index_reindex(args: IndexArgs, pool, topk, ws, stream=None) -> None:

@@ -1,16 +1,21 @@
 // C ABI of the CSA2 library: host-side validation, workspace sizing and
 // dispatch to the gfx950 kernels.  Declarations and contracts: include/csa2.h.
 #include <cmath>
+#include <cstdlib>
 #include <mutex>
 
 #include "../../include/csa2.h"
 #include "common.h"
+#include "check.h"
 
 // Scratch of csa2_index_full_noalloc: one array per GPU, loaded with the
 // library's code object.  Host code never passes this name to a kernel (on
 // the host it is only a stand-in); it uses the device address looked up once
 // per device below.
 __device__ __align__(256) unsigned char scratch[CSA2_NOALLOC_SCRATCH_BYTES];
+
+// Debug mode's failure counter (one per GPU; same rule for host code).
+__device__ __align__(256) uint32_t debug_bad[64];
 
 namespace {
 
@@ -104,6 +109,45 @@ int scratch_address(void** out) {
   if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev]) return CSA2_ERR_HIP;
   *out = g_scratch_ptr[dev];
   return CSA2_OK;
+}
+
+// ---- debug mode: CSA2_DEBUG=1 when the library is loaded (read once, here)
+const bool g_debug = [] {
+  const char* v = std::getenv("CSA2_DEBUG");
+  return v != nullptr && v[0] == '1' && v[1] == 0;
+}();
+std::once_flag g_debug_once[kMaxDevices];
+uint32_t* g_debug_ptr[kMaxDevices];
+hipError_t g_debug_err[kMaxDevices];
+
+// index-row check into `bad` (arguments already validated)
+hipError_t check_rows(const csa2_index_args* a, const int32_t* pool, const int32_t* topk, int mode, uint32_t* bad,
+                      hipStream_t stream) {
+  CheckParams cp{pool, topk, a->n_visible, a->kv_len, mode, bad};
+  return launch_check_index(cp, a->batch * a->q_per_seq, stream);
+}
+
+// Debug mode after (or, mode 2, before) an index call that returned `st`:
+// check the rows on the device, wait for the stream, report failures.
+int debug_check(int st, const csa2_index_args* a, const int32_t* pool, const int32_t* topk, int mode,
+                hipStream_t stream) {
+  if (!g_debug || st != CSA2_OK || (int64_t)a->batch * a->q_per_seq == 0) return st;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return CSA2_ERR_HIP;
+  std::call_once(g_debug_once[dev], [dev] {
+    void* ptr = nullptr;
+    g_debug_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(debug_bad));
+    g_debug_ptr[dev] = static_cast<uint32_t*>(ptr);
+  });
+  if (g_debug_err[dev] != hipSuccess || !g_debug_ptr[dev]) return CSA2_ERR_HIP;
+  uint32_t* bad = g_debug_ptr[dev];
+  uint32_t host = 0;
+  if (hipMemsetAsync(bad, 0, sizeof(uint32_t), stream) != hipSuccess) return CSA2_ERR_HIP;
+  if (check_rows(a, pool, topk, mode, bad, stream) != hipSuccess) return CSA2_ERR_HIP;
+  if (hipMemcpyAsync(&host, bad, sizeof(uint32_t), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return CSA2_ERR_HIP;
+  return host ? CSA2_ERR_DEBUG : CSA2_OK;
 }
 
 // Work split of one attention layer.  A workgroup owns (query, 16 heads, one
@@ -277,6 +321,8 @@ const char* csa2_status_string(int s) {
     case CSA2_ERR_HIP: return "CSA2_ERR_HIP: the HIP runtime reported an error";
     case CSA2_ERR_SCRATCH:
       return "CSA2_ERR_SCRATCH: the problem needs more than the 64 MiB scratch of csa2_index_full_noalloc";
+    case CSA2_ERR_DEBUG:
+      return "CSA2_ERR_DEBUG: a pool or Top-K row failed the device-side check (CSA2_DEBUG=1)";
     default: return "unknown csa2 status";
   }
 }
@@ -333,7 +379,7 @@ int csa2_index_select_append_paged(const csa2_index_args* a, int32_t* pool, int3
                         codes_stride, scales, scales_stride, cache_rows, d);
   if (st != CSA2_OK) return st;
   const QuantJob qj{x, x_stride, rows, dim / 16, codes, codes_stride, scales, scales_stride, d};
-  return select_impl(a, pool, topk, ws, ws_size, qj, stream);
+  return debug_check(select_impl(a, pool, topk, ws, ws_size, qj, stream), a, pool, topk, 0, stream);
 }
 
 int csa2_index_full_append_paged(const csa2_index_args* a, int32_t* pool, int32_t* topk, void* ws, size_t ws_size,
@@ -350,7 +396,7 @@ int csa2_index_full_append_paged(const csa2_index_args* a, int32_t* pool, int32_
   st = csa2_index_scan(a, ws, ws_size, stream);
   if (st != CSA2_OK) return st;
   const QuantJob qj{x, x_stride, rows, dim / 16, codes, codes_stride, scales, scales_stride, d};
-  return select_impl(a, pool, topk, ws, ws_size, qj, stream);
+  return debug_check(select_impl(a, pool, topk, ws, ws_size, qj, stream), a, pool, topk, 0, stream);
 }
 
 int csa2_quantize_swa_fp8(const uint16_t* x, int64_t x_stride, int64_t rows, int32_t dim, uint8_t* out,
@@ -396,7 +442,7 @@ int csa2_index_scan(const csa2_index_args* a, void* ws, size_t ws_size, hipStrea
 
 int csa2_index_select(const csa2_index_args* a, int32_t* pool, int32_t* topk, const void* ws,
                       size_t ws_size, hipStream_t stream) {
-  return select_impl(a, pool, topk, ws, ws_size, QuantJob{}, stream);
+  return debug_check(select_impl(a, pool, topk, ws, ws_size, QuantJob{}, stream), a, pool, topk, 0, stream);
 }
 
 int csa2_index_full(const csa2_index_args* a, int32_t* pool, int32_t* topk, void* ws, size_t ws_size,
@@ -405,7 +451,7 @@ int csa2_index_full(const csa2_index_args* a, int32_t* pool, int32_t* topk, void
   if (st != CSA2_OK) return st;
   st = csa2_index_scan(a, ws, ws_size, stream);
   if (st != CSA2_OK) return st;
-  return select_impl(a, pool, topk, ws, ws_size, QuantJob{}, stream);
+  return debug_check(select_impl(a, pool, topk, ws, ws_size, QuantJob{}, stream), a, pool, topk, 0, stream);
 }
 
 int csa2_index_full_noalloc(const csa2_index_args* a, int32_t* pool, int32_t* topk, hipStream_t stream) {
@@ -429,7 +475,7 @@ int csa2_index_select_append(const csa2_index_args* a, int32_t* pool, int32_t* t
   st = check_quantize(x, x_stride, rows, dim, codes, codes_stride, scales, scales_stride);
   if (st != CSA2_OK) return st;
   const QuantJob qj{x, x_stride, rows, dim / 16, codes, codes_stride, scales, scales_stride};
-  return select_impl(a, pool, topk, ws, ws_size, qj, stream);
+  return debug_check(select_impl(a, pool, topk, ws, ws_size, qj, stream), a, pool, topk, 0, stream);
 }
 
 int csa2_index_full_append(const csa2_index_args* a, int32_t* pool, int32_t* topk, void* ws, size_t ws_size,
@@ -442,7 +488,7 @@ int csa2_index_full_append(const csa2_index_args* a, int32_t* pool, int32_t* top
   st = csa2_index_scan(a, ws, ws_size, stream);
   if (st != CSA2_OK) return st;
   const QuantJob qj{x, x_stride, rows, dim / 16, codes, codes_stride, scales, scales_stride};
-  return select_impl(a, pool, topk, ws, ws_size, qj, stream);
+  return debug_check(select_impl(a, pool, topk, ws, ws_size, qj, stream), a, pool, topk, 0, stream);
 }
 
 int csa2_index_reindex(const csa2_index_args* a, const int32_t* pool, int32_t* topk, void* ws,
@@ -454,10 +500,23 @@ int csa2_index_reindex(const csa2_index_args* a, const int32_t* pool, int32_t* t
   if (!topk || !pool) return CSA2_ERR_NULL;
   if (!aligned(a->n_visible, 4) || !aligned(pool, 4)) return CSA2_ERR_ALIGN;
   if (!ws || ws_size < (size_t)L.total || !aligned(ws, 256)) return CSA2_ERR_WORKSPACE;
+  st = debug_check(CSA2_OK, a, pool, nullptr, 2, stream);   // debug mode: the pool's shape first
+  if (st != CSA2_OK) return st;
   ReindexParams rp{a->q, a->w, a->k, a->n_visible, q_scales(a), k_scales(a), pool, a->q_per_seq, a->kv_len,
                    static_cast<uint32_t*>(ws), topk,
                    static_cast<uint32_t*>(ws) + L.nq * kPoolPositions};
-  return hip_status(launch_reindex(rp, (int)L.nq, a->heads, a->dim, stream));
+  return debug_check(hip_status(launch_reindex(rp, (int)L.nq, a->heads, a->dim, stream)), a, pool, topk, 1, stream);
+}
+
+int csa2_check_index(const csa2_index_args* a, const int32_t* pool, const int32_t* topk, int32_t mode, uint32_t* bad,
+                     hipStream_t stream) {
+  int st = check_index(a);
+  if (st != CSA2_OK) return st;
+  if (mode < 0 || mode > 2) return CSA2_ERR_SHAPE;
+  if ((int64_t)a->batch * a->q_per_seq == 0) return CSA2_OK;
+  if (!bad || (mode != 2 && !topk) || (mode != 0 && !pool)) return CSA2_ERR_NULL;
+  if (!aligned(bad, 4) || !aligned(pool, 4) || !aligned(topk, 4) || !aligned(a->n_visible, 4)) return CSA2_ERR_ALIGN;
+  return hip_status(check_rows(a, pool, mode == 2 ? nullptr : topk, (int)mode, bad, stream));
 }
 
 size_t csa2_attn_workspace_size(const csa2_attn_args* a) {

@@ -28,6 +28,13 @@
  *   - Reuse layers have no entry point: they pass the latest Top-K buffer to
  *     csa2_sparse_attn (ai-maestro.online, "Compressed Sparse Attention 2":
  *     Reuse skips the indexer entirely).
+ *   - Debug mode: with CSA2_DEBUG=1 in the environment when the library is
+ *     loaded (read once, at load), every index call checks its pool and
+ *     Top-K rows on the device after its launches (csa2_check_index, mode 0
+ *     or 1), csa2_index_reindex first checks the shape of the pool it is
+ *     given (mode 2), and the call then synchronises its stream and returns
+ *     CSA2_ERR_DEBUG when a row fails.  Debug mode breaks the
+ *     no-synchronisation rule above and is off by default.
  */
 #ifndef CSA2_H_
 #define CSA2_H_
@@ -53,8 +60,10 @@ typedef enum {
   CSA2_ERR_ALIGN = 3,      /* pointer or stride not aligned as documented    */
   CSA2_ERR_WORKSPACE = 4,  /* workspace NULL or smaller than the query says  */
   CSA2_ERR_HIP = 5,        /* the HIP runtime reported a launch error        */
-  CSA2_ERR_SCRATCH = 6     /* csa2_index_full_noalloc: the problem needs more
+  CSA2_ERR_SCRATCH = 6,    /* csa2_index_full_noalloc: the problem needs more
                               than its fixed scratch (CSA2_NOALLOC_SCRATCH_BYTES) */
+  CSA2_ERR_DEBUG = 7       /* debug mode (CSA2_DEBUG=1): a pool or Top-K row
+                              failed the device-side check (csa2_check_index) */
 } csa2_status;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -297,6 +306,35 @@ int csa2_index_select_append_paged(const csa2_index_args* args, int32_t* pool, i
  */
 int csa2_index_reindex(const csa2_index_args* args, const int32_t* pool, int32_t* topk,
                        void* ws, size_t ws_size, hipStream_t stream);
+
+/*
+ * csa2_check_index -- device-side check of index rows against the contract
+ * the calls above follow (ai-maestro.online, "Compressed Sparse Attention 2":
+ * a pool of 2,048 eight-token blocks, a fresh Top-512 taken from it;
+ * Reindex rescores the Full layer's pool of the same query tokens), one
+ * workgroup per query.  For query q with n = n_visible[q] (T when NULL):
+ *   mode 0 (Full outputs): pool (may be NULL) holds exactly min(2048,
+ *          ceil(n/8)) block ids, strictly ascending, in [0, ceil(n/8)), then
+ *          -1; topk holds exactly min(512, n) positions, strictly ascending,
+ *          in [0, n) and inside pool blocks (when pool is given), then -1.
+ *   mode 1 (Reindex outputs, pool = its input): topk holds min(512, p)
+ *          positions (p = positions of the pool's blocks below n, the pool's
+ *          ids outside [0, ceil(n/8)) counting as empty), strictly
+ *          ascending, in [0, n) and inside pool blocks, then -1.
+ *   mode 2 (a Reindex input pool): ids >= 0 strictly ascending, then -1.
+ * pool, topk: device int32 [nq, 2048] / [nq, 512] as the calls above take
+ * them (topk unused in mode 2; pool required in modes 1 and 2).  bad: device
+ * uint32; the number of failing rows (a query counts once for its pool and
+ * once for its Top-K row) is added to *bad, which the caller zeroes.  args
+ * supplies nq, T and n_visible and must pass the same checks as the index
+ * calls.  All buffers stay the caller's; only *bad is written, on `stream`,
+ * with no wait.  Errors (nothing launched): CSA2_ERR_SHAPE for a mode outside
+ * 0..2 or arguments the index calls reject, CSA2_ERR_NULL for a missing
+ * buffer the mode needs, CSA2_ERR_ALIGN for a pointer not 4-byte aligned.
+ * No queries (batch x q_per_seq = 0): CSA2_OK, nothing launched.
+ */
+int csa2_check_index(const csa2_index_args* args, const int32_t* pool, const int32_t* topk, int32_t mode,
+                     uint32_t* bad, hipStream_t stream);
 
 /*
  * Sparse + sliding-window attention of one CSA2 layer.

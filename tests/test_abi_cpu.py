@@ -31,6 +31,17 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(lib, n), n
 
 
+def test_binding_declares_every_signature(lib):
+    """Every exported function that takes arguments has ctypes argtypes: without
+    them ctypes passes a Python int as a 32-bit C int, which truncates device
+    pointers."""
+    import fp4_kv_cache_e4m3_amd as m
+    for n in m.EXPORTS:
+        if n == "csa2_version":
+            continue
+        assert getattr(lib, n).argtypes is not None, n
+
+
 def test_status_strings(lib):
     import fp4_kv_cache_e4m3_amd as m
     for s in range(6):
@@ -85,6 +96,21 @@ def test_index_rejects(lib):
     up = lambda x, m: (x + m - 1) // m * m
     assert short == up(2 * (((1 << 19) - 16) + up(((1 << 19) - 16) // 8, 16)) * 4, 256)
     assert long_ == 2 * (1 << 16) * 4 + 2 * 2048 * 4
+
+
+def test_check_index_rejects(lib):
+    import fp4_kv_cache_e4m3_amd as m
+    a = m.IndexArgs(1, 2, 100, 8, 64, 16, 16, 16, None)
+    f = lib.csa2_check_index
+    assert f(ctypes.byref(a), 16, 16, 3, 16, None) == 2          # mode
+    assert f(ctypes.byref(a), 16, 16, 0, None, None) == 1        # no counter
+    assert f(ctypes.byref(a), 16, None, 0, 16, None) == 1        # no Top-K in mode 0
+    assert f(ctypes.byref(a), None, 16, 1, 16, None) == 1        # no pool in mode 1
+    assert f(ctypes.byref(a), None, None, 2, 16, None) == 1      # no pool in mode 2
+    assert f(ctypes.byref(a), 16, 16, 0, 18, None) == 3          # misaligned counter
+    assert f(ctypes.byref(m.IndexArgs(1, 1, 100, 3, 64, 16, 16, 16, None)), 16, 16, 0, 16, None) == 2
+    assert f(ctypes.byref(m.IndexArgs(0, 1, 100, 8, 64, 16, 16, 16, None)), None, None, 0, None, None) == 0
+    assert lib.csa2_status_string(7).startswith(b"CSA2_ERR_DEBUG")
 
 
 def test_index_fp8_rejects(lib):
