@@ -22,7 +22,8 @@ WINDOW = 128
 SCALE_GROUP = 16
 
 EXPORTS = (
-    "csa2_status_string", "csa2_version", "csa2_quantize_kv", "csa2_quantize_kv_paged", "csa2_quantize_swa_fp8",
+    "csa2_status_string", "csa2_version", "csa2_quantize_kv", "csa2_quantize_kv_bf16", "csa2_quantize_kv_paged",
+    "csa2_quantize_swa_fp8",
     "csa2_dequantize_kv",
     "csa2_index_workspace_size", "csa2_index_full", "csa2_index_scan", "csa2_index_select",
     "csa2_index_full_append", "csa2_index_select_append", "csa2_index_full_append_paged",
@@ -81,6 +82,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.csa2_version.restype = ctypes.c_int
     lib.csa2_quantize_kv.restype = ctypes.c_int
     lib.csa2_quantize_kv.argtypes = [vp, i64, i64, i32, vp, i64, vp, i64, vp]
+    lib.csa2_quantize_kv_bf16.restype = ctypes.c_int
+    lib.csa2_quantize_kv_bf16.argtypes = [vp, i64, i64, i32, vp, i64, vp, i64, vp]
     lib.csa2_quantize_kv_paged.restype = ctypes.c_int
     lib.csa2_quantize_kv_paged.argtypes = [vp, i64, i64, i32, vp, vp, vp, i32, i32, i32, vp, i64, vp, i64, i64, vp]
     for name in ("csa2_index_full_append_paged", "csa2_index_select_append_paged"):
@@ -142,11 +145,13 @@ def status_string(status: int) -> str:
 
 # ------------------------------------------------------------------ quantise
 def quantize_kv(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, stream=None) -> None:
-    """FP4-quantise fp32 rows x [rows, d] into codes [rows, >=d/2] / scales [rows, >=d/16]
-    (row strides taken from the tensors, so views into a larger cache work)."""
+    """FP4-quantise fp32 or bf16 rows x [rows, d] into codes [rows, >=d/2] / scales
+    [rows, >=d/16] (row strides taken from the tensors, so views into a larger
+    cache work); bf16 rows go to csa2_quantize_kv_bf16."""
     rows, dim = x.shape
-    _check(load().csa2_quantize_kv(_ptr(x), x.stride(0), rows, dim, _ptr(codes), codes.stride(0),
-                                   _ptr(scales), scales.stride(0), _stream(stream)))
+    fn = load().csa2_quantize_kv_bf16 if x.dtype == torch.bfloat16 else load().csa2_quantize_kv
+    _check(fn(_ptr(x), x.stride(0), rows, dim, _ptr(codes), codes.stride(0), _ptr(scales), scales.stride(0),
+              _stream(stream)))
 
 
 def quantize_kv_paged(x: torch.Tensor, row_seq: torch.Tensor, row_pos: torch.Tensor, block_table: torch.Tensor,

@@ -7,6 +7,7 @@
 #include "../../include/csa2.h"
 #include "common.h"
 #include "check.h"
+#include "quant.h"
 
 // Scratch of csa2_index_full_noalloc: one array per GPU, loaded with the
 // library's code object.  Host code never passes this name to a kernel (on
@@ -327,13 +328,25 @@ const char* csa2_status_string(int s) {
   }
 }
 
-int csa2_version(void) { return (1 << 16) | 1; }
+int csa2_version(void) { return (1 << 16) | 2; }
 
 int csa2_quantize_kv(const float* x, int64_t x_stride, int64_t rows, int32_t dim, uint8_t* codes,
                      int64_t codes_stride, uint8_t* scales, int64_t scales_stride, hipStream_t stream) {
   const int st = check_quantize(x, x_stride, rows, dim, codes, codes_stride, scales, scales_stride);
   if (st != CSA2_OK || rows == 0) return st;
   return hip_status(launch_quantize(x, x_stride, rows, dim, codes, codes_stride, scales, scales_stride, stream));
+}
+
+int csa2_quantize_kv_bf16(const uint16_t* x, int64_t x_stride, int64_t rows, int32_t dim, uint8_t* codes,
+                          int64_t codes_stride, uint8_t* scales, int64_t scales_stride, hipStream_t stream) {
+  // the fp32 checks, with the bf16 row alignment: 16 bytes at x and at every
+  // row start (x_stride a multiple of 8 elements)
+  if (rows < 0 || dim < 32 || dim > 4096 || dim % 32) return CSA2_ERR_SHAPE;
+  if (rows == 0) return CSA2_OK;
+  if (!x || !codes || !scales) return CSA2_ERR_NULL;
+  if (x_stride < dim || codes_stride < dim / 2 || scales_stride < dim / 16) return CSA2_ERR_SHAPE;
+  if (!aligned(x, 16) || x_stride % 8 || !aligned(codes, 8) || codes_stride % 8) return CSA2_ERR_ALIGN;
+  return hip_status(launch_quantize_bf16(x, x_stride, rows, dim, codes, codes_stride, scales, scales_stride, stream));
 }
 
 // arguments of new rows written through a block table; fills d on success

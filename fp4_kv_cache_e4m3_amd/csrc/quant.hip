@@ -18,22 +18,26 @@
 // 16-channel group there, 16 B of fp32 in and 2 code bytes out each.  Bulk
 // quantisation of a cache (a one-off) takes one thread per group.
 #include "quant_dev.h"
+#include "quant.h"
 
 namespace csa2 {
 
-__global__ __launch_bounds__(256) void k_quantize_group(const float* __restrict__ x, int64_t xs, int64_t rows,
+// T: float (fp32 rows) or uint16_t (bf16 rows, widened exactly to fp32)
+template <class T>
+__global__ __launch_bounds__(256) void k_quantize_group(const T* __restrict__ x, int64_t xs, int64_t rows,
                                                   int groups, uint8_t* __restrict__ codes, int64_t cs,
                                                   uint8_t* __restrict__ scales, int64_t ss) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= rows * groups) return;
   const int64_t r = gid / groups;
   const int g = (int)(gid - r * groups);
-  const float4* src = reinterpret_cast<const float4*>(x + r * xs + 16 * g);
+  const T* src = x + r * xs + 16 * g;
   float v[16];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float4 f = src[i];
-    v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
+    float f[4];
+    load4(src + 4 * i, f);
+    v[4 * i] = f[0]; v[4 * i + 1] = f[1]; v[4 * i + 2] = f[2]; v[4 * i + 3] = f[3];
   }
   float amax = 0.0f;
 #pragma unroll
@@ -56,7 +60,8 @@ __global__ __launch_bounds__(256) void k_quantize_group(const float* __restrict_
 // the group's amax over the lane quad by DPP (max is exact and ignores NaN in
 // any order), then each lane writes its 4 codes (2 bytes) and the quad's
 // first lane the scale.
-__global__ __launch_bounds__(256) void k_quantize_quad(const float* __restrict__ x, int64_t xs, int64_t rows,
+template <class T>
+__global__ __launch_bounds__(256) void k_quantize_quad(const T* __restrict__ x, int64_t xs, int64_t rows,
                                                   int groups, uint8_t* __restrict__ codes, int64_t cs,
                                                   uint8_t* __restrict__ scales, int64_t ss) {
   quantize_quad_thread(x, xs, rows, groups, codes, cs, scales, ss, (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
@@ -103,19 +108,30 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ 
 
 bool quantize_fits_quad(int64_t rows, int dim) { return rows * (dim / 16) <= kQuantQuadMaxGroups; }
 
-hipError_t launch_quantize(const float* x, int64_t xs, int64_t rows, int dim, uint8_t* codes,
-                           int64_t cs, uint8_t* scales, int64_t ss, hipStream_t st) {
+template <class T>
+static hipError_t launch_quantize_t(const T* x, int64_t xs, int64_t rows, int dim, uint8_t* codes,
+                                    int64_t cs, uint8_t* scales, int64_t ss, hipStream_t st) {
   const int groups = dim / 16;
   const int64_t n = rows * groups;
   if (n == 0) return hipSuccess;
   if (n <= kQuantQuadMaxGroups) {                 // four lanes per group
-    hipLaunchKernelGGL(k_quantize_quad, dim3((unsigned)((4 * n + 255) / 256)), dim3(256), 0, st, x, xs, rows, groups,
-                       codes, cs, scales, ss);
+    hipLaunchKernelGGL(k_quantize_quad<T>, dim3((unsigned)((4 * n + 255) / 256)), dim3(256), 0, st, x, xs, rows,
+                       groups, codes, cs, scales, ss);
   } else {
-    hipLaunchKernelGGL(k_quantize_group, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, x, xs, rows, groups,
-                       codes, cs, scales, ss);
+    hipLaunchKernelGGL(k_quantize_group<T>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, x, xs, rows,
+                       groups, codes, cs, scales, ss);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_quantize(const float* x, int64_t xs, int64_t rows, int dim, uint8_t* codes,
+                           int64_t cs, uint8_t* scales, int64_t ss, hipStream_t st) {
+  return launch_quantize_t(x, xs, rows, dim, codes, cs, scales, ss, st);
+}
+
+hipError_t launch_quantize_bf16(const uint16_t* x, int64_t xs, int64_t rows, int dim, uint8_t* codes,
+                                int64_t cs, uint8_t* scales, int64_t ss, hipStream_t st) {
+  return launch_quantize_t(x, xs, rows, dim, codes, cs, scales, ss, st);
 }
 
 // ---------------------------------------------------------------- 8-bit window rows

@@ -72,8 +72,20 @@ CSA2_DEV uint32_t element_code(float x, float s) {
 // kernel here and by the extra workgroups of the Full selection launch.
 // dst(r): the cache row that source row r is written to (-1: none); the four
 // lanes of a group share r, so they take the same branch.
-template <class Dst>
-CSA2_DEV void quantize_quad_thread_to(const float* __restrict__ x, int64_t xs, int64_t rows, int groups,
+// Four consecutive input values as fp32: fp32 rows, or bf16 rows (the bf16
+// bits shifted into the upper half of an fp32 word: exact).
+CSA2_DEV void load4(const float* p, float (&v)[4]) {
+  const float4 f = *reinterpret_cast<const float4*>(p);
+  v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+}
+CSA2_DEV void load4(const uint16_t* p, float (&v)[4]) {
+  const u2 w = *reinterpret_cast<const u2*>(p);
+  v[0] = __uint_as_float(w[0] << 16); v[1] = __uint_as_float(w[0] & 0xFFFF0000u);
+  v[2] = __uint_as_float(w[1] << 16); v[3] = __uint_as_float(w[1] & 0xFFFF0000u);
+}
+
+template <class T, class Dst>
+CSA2_DEV void quantize_quad_thread_to(const T* __restrict__ x, int64_t xs, int64_t rows, int groups,
                                       uint8_t* __restrict__ codes, int64_t cs, uint8_t* __restrict__ scales,
                                       int64_t ss, int64_t gid, Dst dst) {
   if (gid >= rows * groups * 4) return;            // whole quads: the count is a multiple of 4
@@ -83,8 +95,8 @@ CSA2_DEV void quantize_quad_thread_to(const float* __restrict__ x, int64_t xs, i
   const int g = (int)(grp - r * groups);
   const int64_t dr = dst(r);
   if (dr < 0) return;
-  const float4 f = *reinterpret_cast<const float4*>(x + r * xs + 16 * g + 4 * qtr);
-  const float v[4] = {f.x, f.y, f.z, f.w};
+  float v[4];
+  load4(x + r * xs + 16 * g + 4 * qtr, v);
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(v[i]));
@@ -102,7 +114,8 @@ CSA2_DEV void quantize_quad_thread_to(const float* __restrict__ x, int64_t xs, i
   if (qtr == 0) scales[dr * ss + g] = (uint8_t)sc;
 }
 
-CSA2_DEV void quantize_quad_thread(const float* __restrict__ x, int64_t xs, int64_t rows, int groups,
+template <class T>
+CSA2_DEV void quantize_quad_thread(const T* __restrict__ x, int64_t xs, int64_t rows, int groups,
                                    uint8_t* __restrict__ codes, int64_t cs, uint8_t* __restrict__ scales,
                                    int64_t ss, int64_t gid) {
   quantize_quad_thread_to(x, xs, rows, groups, codes, cs, scales, ss, gid, [](int64_t r) { return r; });

@@ -102,6 +102,21 @@ int csa2_quantize_kv(const float* x, int64_t x_stride, int64_t rows, int32_t dim
                      uint8_t* scales, int64_t scales_stride, hipStream_t stream);
 
 /*
+ * csa2_quantize_kv_bf16 -- csa2_quantize_kv for bf16 rows (the same passage:
+ * ai-maestro.online, "FP4 KV, Bounded Replay, and other extensions").
+ * Every bf16 value widens exactly to fp32, and the codes and scales are
+ * exactly those csa2_quantize_kv writes for the widened rows.
+ *
+ *   x           bf16 bit patterns, row r at x + r * x_stride (elements);
+ *               16-byte aligned, x_stride % 8 == 0.
+ *   rows, dim, codes, codes_stride, scales, scales_stride, stream: as above.
+ * Errors as csa2_quantize_kv (CSA2_ERR_ALIGN for the bf16 alignment above).
+ */
+int csa2_quantize_kv_bf16(const uint16_t* x, int64_t x_stride, int64_t rows, int32_t dim,
+                          uint8_t* codes, int64_t codes_stride, uint8_t* scales, int64_t scales_stride,
+                          hipStream_t stream);
+
+/*
  * csa2_quantize_kv_paged -- csa2_quantize_kv of new rows into a paged cache.
  * The quantisation happens where the row is written, as for the contiguous
  * cache (wpnews.pro TL;DR: the FP4 cache needs no separate quantisation

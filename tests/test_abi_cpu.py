@@ -113,6 +113,18 @@ def test_check_index_rejects(lib):
     assert lib.csa2_status_string(7).startswith(b"CSA2_ERR_DEBUG")
 
 
+def test_quantize_bf16_rejects(lib):
+    """bf16 rows: 16-byte aligned start and a row stride of a multiple of 8
+    elements; the other checks as for fp32 rows."""
+    f = lib.csa2_quantize_kv_bf16
+    assert f(16, 64, 2, 48, 16, 32, 16, 4, None) == 2             # dim % 32
+    assert f(None, 64, 2, 64, 16, 32, 16, 4, None) == 1           # no input
+    assert f(16, 60, 2, 64, 16, 32, 16, 4, None) == 2             # stride < dim
+    assert f(24, 64, 2, 64, 16, 32, 16, 4, None) == 3             # misaligned rows
+    assert f(16, 68, 2, 64, 16, 32, 16, 4, None) == 3             # stride not a multiple of 8
+    assert f(16, 64, 0, 64, None, 0, None, 0, None) == 0          # no rows: no-op
+
+
 def test_index_fp8_rejects(lib):
     """FP8 indexer arguments: the flag must be 0 or 1 and both scale arrays
     present and 4-byte aligned; int8 arguments ignore the scale pointers."""

@@ -128,3 +128,58 @@ def test_dequantize_every_code_and_scale():
     ref = formats.dequant_rows(c, s, d)
     np.testing.assert_array_equal(got, ref.astype(np.float32))
     np.testing.assert_array_equal(np.signbit(got), np.signbit(ref))
+
+
+def bf16_rows_every_finite_value() -> np.ndarray:
+    """Every finite bf16 bit pattern (both signs, subnormals, zeros) once, in
+    rows of 512: consecutive patterns share a group, so each value is coded
+    against the scale its neighbours set; plus the exhaustive fp32 groups
+    above, rounded to bf16 (scale midpoints and element midpoints at every
+    scale)."""
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    finite = (bits & 0x7F80) != 0x7F80
+    vals = (bits[finite] << 16).view(np.float32)
+    pad = (-len(vals)) % 512
+    vals = np.concatenate([vals, np.zeros(pad, np.float32)]).reshape(-1, 512)
+    ex = exhaustive_groups()
+    ex16 = ((ex.view(np.uint32) + 0x7FFF + ((ex.view(np.uint32) >> 16) & 1)) & 0xFFFF0000).view(np.float32)
+    ex16 = np.where(np.isfinite(ex16), ex16, np.float32(0))
+    return np.concatenate([vals, ex16])
+
+
+@pytest.mark.parametrize("copies", [1, 8])
+def test_quantize_bf16_every_value_bit_exact(copies):
+    """csa2_quantize_kv_bf16: bit-exact against the oracle on the widened
+    values, through both kernels (small launch and the bulk kernel past 8,192
+    groups)."""
+    x = np.concatenate([bf16_rows_every_finite_value()] * copies)
+    xb = torch.from_numpy(x).to("cuda").to(torch.bfloat16)
+    assert torch.equal(xb.float().cpu(), torch.from_numpy(x))       # the rows are bf16 values
+    n, d = x.shape
+    codes = torch.empty((n, d // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((n, d // 16), dtype=torch.uint8, device="cuda")
+    csa2.quantize_kv(xb, codes, scales)
+    rc, rs = quant.quantize_rows(x)
+    np.testing.assert_array_equal(host(scales), rs)
+    np.testing.assert_array_equal(host(codes), rc)
+
+
+@pytest.mark.parametrize("dim", [32, 512])
+def test_quantize_bf16_strided_rows_into_cache(dim):
+    """Strided bf16 source rows (a view) into strided cache rows, against the
+    oracle; the cache rows in between stay untouched."""
+    B, T = 7, 23
+    rng = np.random.default_rng(dim + 1)
+    src = torch.from_numpy((rng.standard_normal((B, dim + 64)) * 10.0 ** rng.uniform(-6, 5, (B, 1)))
+                           .astype(np.float32)).to("cuda").to(torch.bfloat16)
+    x = src[:, 8:8 + dim]                                             # row stride dim + 64, offset 16 bytes
+    codes = torch.full((B * T, dim // 2), 0xAB, dtype=torch.uint8, device="cuda")
+    scales = torch.full((B * T, dim // 16), 0xCD, dtype=torch.uint8, device="cuda")
+    csa2.quantize_kv(x, codes[T - 1::T], scales[T - 1::T])
+    hc, hs = host(codes), host(scales)
+    rc, rs = quant.quantize_rows(x.float().cpu().numpy())
+    np.testing.assert_array_equal(hc[T - 1::T], rc)
+    np.testing.assert_array_equal(hs[T - 1::T], rs)
+    mask = np.ones(B * T, bool)
+    mask[T - 1::T] = False
+    assert np.all(hc[mask] == 0xAB) and np.all(hs[mask] == 0xCD)
