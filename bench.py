@@ -292,7 +292,7 @@ def main() -> int:
     achieved = scan_bytes / (scan_ms / 1e3) / 1e9
     attn_achieved = nbytes["attn_layer"] / (attn_ms / 1e3) / 1e9
     # the library runs the one-workgroup-per-query kernel for many query tokens
-    wide = w.dim == 512 and not w.swa8 and w.nq * ((w.heads + 63) // 64) >= 512
+    wide = w.dim == 512 and not w.swa8 and w.nq * ((w.heads + 63) // 64) >= 96
     attn_kernel = "k_attn_wide" if wide else "k_attn"
     # matrix work of one attention layer: QK^T and PV over the Top-512 and window entries
     attn_tflop = 4.0 * w.nq * w.heads * (512 + w.window) * w.dim / 1e12

@@ -10,24 +10,30 @@
 // Design.  With thousands of queries the work is a dense contraction per
 // query (64 heads x 640 entries x 512 channels, twice), so this kernel is
 // laid out for the matrix cores: one workgroup per (query, group of 64
-// heads), eight waves (two per SIMD), 32-entry tiles.  Wave w = (hh, dq):
-// head half hh (32 heads), channel quarter dq (128 channels).
-//  * QK^T: wave (hh, dq) contracts its channel quarter for its 32 heads
-//    (MFMA 16x16x32, entries as A rows, heads as B columns, Q in registers).
-//    It decodes only that quarter of the tile's FP4 rows, so a row is
-//    decoded twice per query (once per head half).
-//  * The four quarters' partial logits meet in LDS: wave (hh, dq) adds the
-//    four partials (in quarter order) of one 16 x 16 block, entries of
-//    subtile dq / 2 and heads of tile dq % 2, and runs the online softmax
-//    on it; the two waves holding a head's two entry halves exchange their
-//    tile maxima, so both move the reference max together.  Every logit is
+// heads, head half hh of 32 heads), four waves (one per SIMD), 32-entry
+// tiles.  Wave dq takes channel quarter dq (128 channels).  The two head
+// halves of a query share nothing but their inputs, so they run as separate
+// workgroups, two of which share a CU: their barriers are independent, and
+// one workgroup's matrix work fills the SIMDs while the other waits at a
+// barrier or in its softmax (with both halves in one workgroup, every
+// barrier held all eight waves in the same phase).
+//  * QK^T: wave dq contracts its channel quarter for the 32 heads (MFMA
+//    16x16x32, entries as A rows, heads as B columns, Q in registers).  It
+//    decodes only that quarter of the tile's FP4 rows, so a row is decoded
+//    twice per query (once per head half).
+//  * The four quarters' partial logits meet in LDS: wave dq adds the four
+//    partials (in quarter order) of one 16 x 16 block, entries of subtile
+//    dq / 2 and heads of tile dq % 2, and runs the online softmax on it; the
+//    two waves holding a head's two entry halves exchange their tile
+//    maxima, so both move the reference max together.  Every logit is
 //    computed and exponentiated once.
-//  * PV: wave (hh, dq) owns output channels 128 dq + 64 hh .. + 63 for all
-//    64 heads.  Those lie in its own channel quarter, so it stages its own
-//    fp16 values in LDS and reads them back transposed (ds_read_b64_tr_b16)
-//    as the B operand; the probabilities of all four head tiles come from
-//    LDS in the A-operand layout of MFMA 16x16x32.
-//  * Per tile: three barriers (partial logits, tile maxima, probabilities).
+//  * PV: wave dq owns output channels 128 dq .. + 127 of the 32 heads.  Those
+//    are its own channel quarter, so it stages its own fp16 values in LDS
+//    and reads them back transposed (ds_read_b64_tr_b16) as the B operand;
+//    the probabilities of both head tiles come from LDS in the A-operand
+//    layout of MFMA 16x16x32.
+//  * Per tile: three barriers of four waves (partial logits, tile maxima,
+//    probabilities).
 // Precision as in attn.hip: FP4 values and bf16 Q are exact in fp16 (Q and
 // window rows inside fp16's range); window logits run on bf16 MFMA with the
 // bf16 Q; probabilities are fp16, normalised by the sum of the rounded values.
@@ -39,7 +45,7 @@ namespace {
 constexpr int kWD = 512;                // head dim
 constexpr int kWTE = 32;                // entries per tile
 constexpr int kWKQ = 4;                 // 32-channel k-steps per channel quarter
-constexpr int kWVP = 64 + 8;            // halves per staged V row (one channel eighth)
+constexpr int kWVP = 128 + 8;           // halves per staged V row (the wave's channel quarter)
 constexpr uint32_t kWOob = 0xFFFFF000u; // offset past every buffer
 constexpr int kWDepth = 1;              // FP4 tiles in flight per wave
 
@@ -65,32 +71,34 @@ CSA2_DEV v8bf half8_to_bf16(v8h x) {
 }  // namespace
 
 template <bool PG>
-__global__ __launch_bounds__(512, 1) void k_attn_wide(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) v4f xs[8][4 * 64];              // partial logits per wave
-  __shared__ __attribute__((aligned(16))) _Float16 vst[8][kWTE * kWVP];   // staged V per wave
-  __shared__ __attribute__((aligned(16))) v4h pg[2][2][2][64];            // probabilities [hh][et][ht][lane]
-  __shared__ float tmx[8][16];                                            // tile max per wave and head
-  __shared__ float alph[64];                                              // rescale factor per head
-  __shared__ int32_t rflag[4];                                            // per head tile: some head rescaled
-  __shared__ float lsum[8][16];                                           // softmax sums per wave and head
+__global__ __launch_bounds__(256, 2) void k_attn_wide(AttnParams p) {
+  __shared__ __attribute__((aligned(16))) v4f xs[4][4 * 64];              // partial logits per wave
+  __shared__ __attribute__((aligned(16))) _Float16 vst[4][kWTE * kWVP];   // staged V per wave
+  __shared__ __attribute__((aligned(16))) v4h pg[2][2][64];               // probabilities [et][ht][lane]
+  __shared__ float tmx[4][16];                                            // tile max per wave and head
+  __shared__ float alph[32];                                              // rescale factor per head
+  __shared__ int32_t rflag[2];                                            // per head tile: some head rescaled
+  __shared__ float lsum[4][16];                                           // softmax sums per wave and head
   __shared__ int32_t spos[kMaxTopK];                                      // rows of the Top-K slots, -1 empty
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
-  const int hh = wave >> 2, dq = wave & 3;
+  const int dq = wave;
   const int et_o = dq >> 1, ht_o = dq & 1;          // the logit block this wave reduces
-  const int partner = (hh << 2) | (dq ^ 2);         // the other entry half of the same heads
-  const bool stager = (g >> 1) == hh;               // this lane's channels lie in the wave's output eighth
-  const int cb = 128 * dq + 64 * hh;                // first output channel of the wave
+  const int partner = dq ^ 2;                       // the other entry half of the same heads
+  const int cb = 128 * dq;                          // first output channel of the wave
 
-  // workgroup -> (query, head group): consecutive queries on one XCD (the
-  // dispatcher deals workgroup ids round-robin to the 8 XCDs), so a query's
-  // neighbours, which share most of its window rows, share its L2
+  // workgroup -> (query, head group, head half): the two halves of a query
+  // are neighbours, and consecutive queries share an XCD (the dispatcher
+  // deals workgroup ids round-robin to the 8 XCDs), so a query's rows and
+  // its neighbours' window rows share its L2
   const int ngr = (p.heads + 63) >> 6;
-  const int64_t total = p.nq * ngr;
+  const int64_t total = p.nq * ngr * 2;
   const int64_t per_xcd = (total + 7) >> 3;
-  const int64_t u = (int64_t)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if (u >= total) return;
+  const int64_t uh = (int64_t)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (uh >= total) return;
+  const int hh = (int)(uh & 1);
+  const int64_t u = uh >> 1;
   const int q = (int)(u / ngr), grp = (int)(u - (int64_t)q * ngr);
   const int b = p.qn_shift >= 0 ? q >> p.qn_shift : q / p.qn;
   const int j = q - b * p.qn;
@@ -156,7 +164,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_wide(AttnParams p) {
     for (int et = 0; et < 2; ++et) row[et] = i < nft ? slot_row(kWTE * i + 16 * et + n) : -1;
     load_rows(row, raw[i]);
   }
-  for (int s = kWDepth * kWTE + threadIdx.x; s < nft * kWTE; s += 512) spos[s] = slot_row(s);
+  for (int s = kWDepth * kWTE + threadIdx.x; s < nft * kWTE; s += 256) spos[s] = slot_row(s);
   v8h qf[2][kWKQ];
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht)
@@ -197,20 +205,19 @@ __global__ __launch_bounds__(512, 1) void k_attn_wide(AttnParams p) {
     }
   };
 
-  // O: o[a][t] holds heads 16 a + 4 g + i (a = 2 hh' + ht'), channel
-  // cb + 16 t + n
-  v4f o[4][4];
+  // O: o[a][t] holds heads 32 hh + 16 a + 4 g + i, channel cb + 16 t + n
+  v4f o[2][8];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) o[a][t] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < 8; ++t) o[a][t] = v4f{0.f, 0.f, 0.f, 0.f};
   float m_run = -__builtin_inff(), l_run = 0.0f;   // head 32 hh + 16 ht_o + n over entry half et_o
 
   _Float16* const my = &vst[wave][0];
-  // V staging: lane (n, g) (stager) writes entry 16 et + n, channels
-  // 32 (g & 1) + 8 kk of the wave's eighth; transposing read: lane (n, g)
-  // gets entries 16 et + 4 g .. + 3 of eighth channel 16 t + n
-  _Float16* const vrow = my + n * kWVP + 32 * (g & 1);
+  // V staging: lane (n, g) writes entry 16 et + n, channels 32 g + 8 kk of
+  // the wave's quarter; transposing read: lane (n, g) gets entries
+  // 16 et + 4 g .. + 3 of quarter channel 16 t + n
+  _Float16* const vrow = my + n * kWVP + 32 * g;
   const _Float16* const vb = my + (4 * g + (n >> 2)) * kWVP + 4 * (n & 3);
 
   // the rest of a tile once the wave's partial logits acc[et][ht] (entries
@@ -222,9 +229,9 @@ __global__ __launch_bounds__(512, 1) void k_attn_wide(AttnParams p) {
       for (int ht = 0; ht < 2; ++ht) xs[wave][(2 * et + ht) * 64 + lane] = acc[et][ht];
     __syncthreads();
     // logits of block (et_o, ht_o): the four quarters, added in quarter order
-    v4f sfull = xs[hh << 2][dq * 64 + lane];
+    v4f sfull = xs[0][dq * 64 + lane];
 #pragma unroll
-    for (int d = 1; d < 4; ++d) sfull += xs[(hh << 2) | d][dq * 64 + lane];
+    for (int d = 1; d < 4; ++d) sfull += xs[d][dq * 64 + lane];
     float s[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -250,40 +257,40 @@ __global__ __launch_bounds__(512, 1) void k_attn_wide(AttnParams p) {
     const v2h one2 = {(_Float16)1.0f, (_Float16)1.0f};
     const float ps = __builtin_amdgcn_fdot2(v2h{pr[2], pr[3]}, one2, __builtin_amdgcn_fdot2(v2h{pr[0], pr[1]}, one2, 0.0f, false), false);
     l_run = l_run * alpha + ps;
-    pg[hh][et_o][ht_o][lane] = pr;
+    pg[et_o][ht_o][lane] = pr;
     if (et_o == 0) {
       const bool any_rs = __any(rs);
-      if (g == 0) alph[32 * hh + 16 * ht_o + n] = alpha;
-      if (lane == 0) rflag[2 * hh + ht_o] = any_rs ? 1 : 0;
+      if (g == 0) alph[16 * ht_o + n] = alpha;
+      if (lane == 0) rflag[ht_o] = any_rs ? 1 : 0;
     }
     __syncthreads();
     // rescale the O rows of every head tile that moved its max, then
     // O += P V over the 32 entries: k slot s of lane group g is entry
     // 4 g + s (s < 4) or 16 + 4 g + s - 4, in P and in V (two transposing
     // reads)
-    v8h pa[4];
+    v8h pa[2];
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const v4h p0 = pg[a >> 1][0][a & 1][lane];
-      const v4h p1 = pg[a >> 1][1][a & 1][lane];
+    for (int a = 0; a < 2; ++a) {
+      const v4h p0 = pg[0][a][lane];
+      const v4h p1 = pg[1][a][lane];
       pa[a] = v8h{p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
       if (rflag[a]) {
         float ai[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) ai[i] = alph[16 * a + 4 * g + i];
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < 8; ++t)
 #pragma unroll
           for (int i = 0; i < 4; ++i) o[a][t][i] *= ai[i];
       }
     }
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < 8; ++t) {
       const v4h v0 = lds_read_tr16(vb + 16 * t);
       const v4h v1 = lds_read_tr16(vb + 16 * kWVP + 16 * t);
       const v8h vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
 #pragma unroll
-      for (int a = 0; a < 4; ++a) o[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[a], vv, o[a][t], 0, 0, 0);
+      for (int a = 0; a < 2; ++a) o[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[a], vv, o[a][t], 0, 0, 0);
     }
   };
 
@@ -312,7 +319,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_wide(AttnParams p) {
             const v8h kf = fp4x8_to_half_s8(raw[uu].c[et][kk], sc[et][kk >> 1]);
             acc[et][0] = mfma_qk(kf, qf[0][kk], acc[et][0]);
             acc[et][1] = mfma_qk(kf, qf[1][kk], acc[et][1]);
-            if (stager) *reinterpret_cast<v8h*>(vrow + 16 * et * kWVP + 8 * kk) = kf;
+            *reinterpret_cast<v8h*>(vrow + 16 * et * kWVP + 8 * kk) = kf;
           }
         if (i + kWDepth < nft) load_fp4(i + kWDepth, raw[uu]);
         finish_tile(acc, vmask);
@@ -342,7 +349,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_wide(AttnParams p) {
           const v8bf kb = __builtin_bit_cast(v8bf, wr.w[et][kk]);
           acc[et][0] = mfma_qk(kb, qb[0][kk], acc[et][0]);
           acc[et][1] = mfma_qk(kb, qb[1][kk], acc[et][1]);
-          if (stager) *reinterpret_cast<v8h*>(vrow + 16 * et * kWVP + 8 * kk) = bf16x8_to_half(wr.w[et][kk]);
+          *reinterpret_cast<v8h*>(vrow + 16 * et * kWVP + 8 * kk) = bf16x8_to_half(wr.w[et][kk]);
         }
       if (i + 1 < nwt) load_swa(i + 1, wr);
       finish_tile(acc, vmask);
@@ -357,17 +364,17 @@ __global__ __launch_bounds__(512, 1) void k_attn_wide(AttnParams p) {
   }
   __syncthreads();
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int w0 = ((a >> 1) << 2) | (a & 1);       // et 0 owner of head tile a; et 1 owner is w0 + 2
+  for (int a = 0; a < 2; ++a) {
+    // wave a owns head tile a's entry half 0, wave a + 2 its entry half 1
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int hl = 16 * a + 4 * g + i;            // head within the group
-      const float l = lsum[w0][4 * g + i] + lsum[w0 + 2][4 * g + i];
+      const int hl = 32 * hh + 16 * a + 4 * g + i;  // head within the group
+      const float l = lsum[a][4 * g + i] + lsum[a + 2][4 * g + i];
       const float inv = l > 0.0f ? 1.0f / l : 0.0f;
       if (h0 + hl < p.heads) {
         float* const orow = p.out + ((int64_t)q * p.heads + h0 + hl) * kWD + cb + n;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) orow[16 * t] = o[a][t][i] * inv;
+        for (int t = 0; t < 8; ++t) orow[16 * t] = o[a][t][i] * inv;
       }
     }
   }
@@ -375,10 +382,10 @@ __global__ __launch_bounds__(512, 1) void k_attn_wide(AttnParams p) {
 
 hipError_t launch_attn_wide(const AttnParams& p, int nq, hipStream_t st) {
   if (nq == 0) return hipSuccess;
-  const int64_t total = (int64_t)nq * ((p.heads + 63) / 64);
+  const int64_t total = (int64_t)nq * ((p.heads + 63) / 64) * 2;
   const dim3 grid((unsigned)(8 * ((total + 7) / 8)));
-  if (p.block_table) hipLaunchKernelGGL(k_attn_wide<true>, grid, dim3(512), 0, st, p);
-  else hipLaunchKernelGGL(k_attn_wide<false>, grid, dim3(512), 0, st, p);
+  if (p.block_table) hipLaunchKernelGGL(k_attn_wide<true>, grid, dim3(256), 0, st, p);
+  else hipLaunchKernelGGL(k_attn_wide<false>, grid, dim3(256), 0, st, p);
   return hipGetLastError();
 }
 

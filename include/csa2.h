@@ -425,11 +425,12 @@ typedef struct {
   int32_t waves;
   int32_t splits;
   /* Kernel: 0 = the library's choice; 1 = workgroups of 16 heads (waves and
-     splits above apply); 2 = one workgroup per query and 64 heads, for many
-     query tokens at once (a prefill chunk): each FP4 row is decoded twice
-     per query instead of once per 16 heads, and the logits once; needs
-     dim = 512, swa_fp8 = 0 and waves = splits = 0.  The library's choice is
-     2 where that holds and nq * ceil(H / 64) >= 512, else 1.  The kernels
+     splits above apply); 2 = two workgroups per query and 64 heads (one per
+     32 heads), for many query tokens at once (a prefill chunk): each FP4 row
+     is decoded twice per query instead of once per 16 heads, and the logits
+     once; needs dim = 512, swa_fp8 = 0 and waves = splits = 0.  The
+     library's choice is 2 where that holds and nq * ceil(H / 64) >= 96,
+     else 1.  The kernels
      sum in different orders (results may differ in the last bits); each is
      deterministic.  Other values: CSA2_ERR_SHAPE.                            */
   int32_t kernel;
