@@ -38,7 +38,7 @@ PEAK_I8_TOPS = 5000.0          # MI355X dense int8 MFMA peak (AMD spec)
 # HBM bytes per k_index_scan launch measured with rocprofv3 FETCH_SIZE and
 # WRITE_SIZE (each scaled by what the counter reads for a plain 1 GiB copy) on
 # the workloads and kernel sources named here; reported only while they match.
-SCAN_TRAFFIC = {"source_sha256": "11f0c40eec2a0585876b84f60427d93bac556d6df12b596b2dc476cc96b8e665",   # csrc/index.hip + csrc/common.h
+SCAN_TRAFFIC = {"source_sha256": "064b41d96120484a58c187c1c6af5f5dda99c54757d6ddf5315a1f1acbdeb5de",   # csrc/index.hip + csrc/common.h
                 "bytes": {"decode_group_full_reuse3_b32_t65536": 268804505 + 9437286,
                           "decode_group_full_reuse3_b32_t65536_idx8": 278864076 + 9437900,
                           "verify_group_full_reuse3_b8_q6_t1m": 1074306662 + 25168281}}

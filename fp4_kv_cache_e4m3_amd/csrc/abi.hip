@@ -67,6 +67,7 @@ struct IndexLayout {
   int64_t nq, tk_stride, bk_stride, full_bytes, reindex_bytes, total;
   bool long_path;
   int64_t bk_off, pool_off;          // bytes: block keys; the pool (long path, when the caller passes none)
+  int64_t pkeys_off, pthr_off;       // bytes (long path): the pool blocks' keys, the Top-512 key floors
 };
 
 IndexLayout index_layout(const csa2_index_args* a) {
@@ -80,14 +81,16 @@ IndexLayout index_layout(const csa2_index_args* a) {
     L.full_bytes = L.nq * (L.tk_stride + L.bk_stride) * 4;
     L.bk_off = L.nq * L.tk_stride * 4;
     L.total = round_up(L.full_bytes > L.reindex_bytes ? L.full_bytes : L.reindex_bytes, 256);
-    L.pool_off = -1;
+    L.pool_off = L.pkeys_off = L.pthr_off = -1;
   } else {
     // block keys at the front (the Reindex keys reuse that space once the
     // pool is formed), then room for a pool
     L.full_bytes = L.nq * L.bk_stride * 4;
     L.bk_off = 0;
     L.pool_off = round_up(L.full_bytes > L.reindex_bytes ? L.full_bytes : L.reindex_bytes, 256);
-    L.total = round_up(L.pool_off + L.nq * kPoolBlocks * 4, 256);
+    L.pkeys_off = round_up(L.pool_off + L.nq * kPoolBlocks * 4, 256);
+    L.pthr_off = L.pkeys_off + L.nq * kPoolBlocks * 4;
+    L.total = round_up(L.pthr_off + L.nq * 4, 256);
   }
   return L;
 }
@@ -301,13 +304,20 @@ int select_impl(const csa2_index_args* a, int32_t* pool, int32_t* topk, const vo
   // long path: the pool (into the workspace when the caller takes none), then
   // the Top-512 of its positions rescored with this layer's own query
   int32_t* pl = pool ? pool : reinterpret_cast<int32_t*>(static_cast<char*>(const_cast<void*>(ws)) + L.pool_off);
+  char* const wsb = static_cast<char*>(const_cast<void*>(ws));
+  uint32_t* const pkeys = reinterpret_cast<uint32_t*>(wsb + L.pkeys_off);
+  uint32_t* const pthr = reinterpret_cast<uint32_t*>(wsb + L.pthr_off);
   SelectParams sel{nullptr, L.tk_stride, bkeys, L.bk_stride, a->n_visible, a->kv_len, pl, nullptr};
   sel.qj = qj;
+  sel.pkeys = pkeys;
+  sel.pthr = pthr;
   hipError_t e = launch_select_full(sel, (int)L.nq, (a->kv_len + kBlock - 1) / kBlock, stream);
   if (e != hipSuccess) return CSA2_ERR_HIP;
-  uint32_t* rk = static_cast<uint32_t*>(const_cast<void*>(ws));
+  // the rescoring gathers only the pool blocks at or above each query's
+  // Top-512 key floor (the others hold no Top-512 position)
+  uint32_t* rk = reinterpret_cast<uint32_t*>(wsb);
   ReindexParams rp{a->q, a->w, a->k, a->n_visible, q_scales(a), k_scales(a), pl, a->q_per_seq, a->kv_len,
-                   rk, topk, rk + L.nq * kPoolPositions};
+                   rk, topk, rk + L.nq * kPoolPositions, pkeys, pthr};
   return hip_status(launch_reindex(rp, (int)L.nq, a->heads, a->dim, stream));
 }
 

@@ -161,6 +161,8 @@ struct SelectParams {
   int32_t roles;                                         // workgroups per query (set by the launcher)
   int32_t sel_wgs;                                       // selection workgroups (set by the launcher)
   QuantJob qj;                                           // rows == 0: none
+  uint32_t* pkeys; uint32_t* pthr;                       // pool only: the pool blocks' keys [nq, 2048] and
+                                                         // the Top-512 key floor [nq], or NULL
 };
 struct ReindexParams {
   const int8_t* iq; const float* iw; const int8_t* ik; const int32_t* nvis;
@@ -169,6 +171,8 @@ struct ReindexParams {
   uint32_t* ckeys;                                       // [nq, 16384]
   int32_t* topk;
   uint32_t* bkeys;                                       // [nq, 2048]: max key of each pool block
+  const uint32_t* pkeys; const uint32_t* pthr;           // or NULL: pool blocks whose key is below the
+                                                         // floor are not rescored (long Full path)
 };
 struct AttnParams {
   const uint16_t* q; const uint8_t* codes; const uint8_t* scales;

@@ -40,6 +40,7 @@ struct SelShared {
   int32_t pool[kPoolBlocks];
   int32_t sbpool[kPoolBlocks];                   // chosen super-blocks (large pools only)
   int32_t cand[kSelThreads];                     // Top-512 candidate blocks (Full select, fast path)
+  uint32_t pkey[kPoolBlocks];                    // keys of the pool's blocks (pool-only select)
 };
 
 // inclusive prefix sum over the 64 lanes with DPP (row shifts inside 16-lane
@@ -489,14 +490,21 @@ __global__ __launch_bounds__(kSelThreads) void k_select_full(SelectParams p) {
     }
     {
       auto get = [&](int j) { return ckey[j]; };
-      uint32_t tau, need, kmin, kmax, cnt;
+      uint32_t tau, need, kmin, kmax, cnt, thr;
       key_stats<16>(get, sh, kmin, kmax, cnt);
-      radix_select<16>(get, K1, kmin, kmax, sh, &sh.hist[3], tau, need);
+      // the first pass also gives the first digit of the 512th block key:
+      // the Top-512 positions lie in the top 512 blocks, whose keys are at
+      // least its floor thr (the same argument as the candidates above)
+      const RadixState st = radix_first<16>(get, K1, kmin, kmax, sh, &sh.hist[3], min(K1, (uint32_t)kTopK), thr);
+      radix_rest<16>(get, st, sh, &sh.hist[3], tau, need);
       const int c0 = threadIdx.x * 16;
       compact_topk<16>(get, tau, need, sh, [&](uint32_t o, int j) {
         const int c = c0 + j;
         sh.pool[o] = sh.sbpool[c >> 3] * 8 + (c & 7);
+        sh.pkey[o] = get(j);
       });
+      // with fewer than 512 blocks every block counts (pool keys are nonzero)
+      if (p.pthr && threadIdx.x == 0) p.pthr[q] = K1 >= (uint32_t)kTopK ? thr : 1u;
     }
     // the position select below needs clean histograms
     __syncthreads();
@@ -513,6 +521,11 @@ __global__ __launch_bounds__(kSelThreads) void k_select_full(SelectParams p) {
   __syncthreads();
   if (p.pool && role != 1)
     for (int i = threadIdx.x; i < kPoolBlocks; i += kSelThreads) p.pool[q * kPoolBlocks + i] = sh.pool[i];
+  if (p.pkeys && !p.topk) {                  // pool only: its blocks' keys for the rescoring
+    for (int i = threadIdx.x; i < kPoolBlocks; i += kSelThreads)
+      p.pkeys[q * kPoolBlocks + i] = (uint32_t)i < K1 ? sh.pkey[i] : 0u;
+    if (K1 == 0 && threadIdx.x == 0) p.pthr[q] = 1u;
+  }
   if (role == 0 || !p.topk) return;
 
   // ---- step 2: Top-512 positions of the candidate blocks, or of the pool
@@ -561,8 +574,16 @@ __global__ __launch_bounds__(256) void k_reindex_score(ReindexParams p) {
   const int32_t* pool = p.pool + q * kPoolBlocks;
   const int slot0 = blockIdx.x * kRxSlotsPerWG + 2 * TPW * wave + (n >> 3);   // slot of tile u: slot0 + 2u
   int32_t blk[TPW];
+  // long Full path: blocks whose Full-layer key lies below the Top-512 floor
+  // hold no Top-512 position, and this query is that layer's own, so they
+  // are not gathered (their keys stay 0, not candidates)
+  uint32_t pk[TPW];
+  const uint32_t floor_q = p.pthr ? p.pthr[q] : 0u;
 #pragma unroll
-  for (int u = 0; u < TPW; ++u) blk[u] = pool[slot0 + 2 * u];
+  for (int u = 0; u < TPW; ++u) {
+    blk[u] = pool[slot0 + 2 * u];
+    pk[u] = p.pkeys ? p.pkeys[q * kPoolBlocks + slot0 + 2 * u] : 0u;
+  }
 
   v4i a[KK];
 #pragma unroll
@@ -585,7 +606,7 @@ __global__ __launch_bounds__(256) void k_reindex_score(ReindexParams p) {
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
     const int64_t pos = (int64_t)blk[u] * kBlock + (n & 7);
-    ok[u] = blk[u] >= 0 && (int64_t)blk[u] < nb && pos < nv;
+    ok[u] = blk[u] >= 0 && (int64_t)blk[u] < nb && pos < nv && pk[u] >= floor_q;
     skv[u] = 1.0f;
     if constexpr (F8) skv[u] = ok[u] ? p.iks[b * p.T + pos] : 0.0f;
 #pragma unroll

@@ -90,12 +90,13 @@ def test_index_rejects(lib):
     a = m.IndexArgs(1, 1, (1 << 20) + 1, 8, 64, 16, 16, 16, None)          # T too long
     assert lib.csa2_index_workspace_size(ctypes.byref(a)) == 0
     # from 2^19 positions on, the scan keeps only block maxima: the workspace
-    # shrinks from 4.5 B per query and position to 0.5 B (plus the pool)
+    # shrinks from 4.5 B per query and position to 0.5 B (plus the pool, its
+    # blocks' keys and a key floor per query)
     short = lib.csa2_index_workspace_size(ctypes.byref(m.IndexArgs(1, 2, (1 << 19) - 16, 8, 64, 16, 16, 16, None)))
     long_ = lib.csa2_index_workspace_size(ctypes.byref(m.IndexArgs(1, 2, 1 << 19, 8, 64, 16, 16, 16, None)))
     up = lambda x, m: (x + m - 1) // m * m
     assert short == up(2 * (((1 << 19) - 16) + up(((1 << 19) - 16) // 8, 16)) * 4, 256)
-    assert long_ == 2 * (1 << 16) * 4 + 2 * 2048 * 4
+    assert long_ == up(2 * (1 << 16) * 4 + 2 * 2048 * 4 + 2 * 2048 * 4 + 2 * 4, 256)
 
 
 def test_check_index_rejects(lib):
