@@ -103,6 +103,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_wide(AttnParams p) {
   const int b = p.qn_shift >= 0 ? q >> p.qn_shift : q / p.qn;
   const int j = q - b * p.qn;
   const int h0 = 64 * grp;
+  if (h0 + 32 * hh >= p.heads) return;             // a head half past H (H not a multiple of 64)
 
   // ---- Q: lane (n, g) holds, in k-step kk, channels 128 dq + 32 g + 8 kk ..
   // + 7 of head 32 hh + 16 ht + n (the k order inside an MFMA only has to
