@@ -285,6 +285,23 @@ def main() -> int:
         for i, (st, _) in enumerate(calls):
             stage_ms[st] = stage_ms.get(st, 0.0) + bev[k][i].elapsed_time(bev[k][i + 1]) / args.steps
 
+    # the device's achievable HBM read rate (every byte of 1 GiB read once by
+    # csa2_read_rate), the reference beside the 8 TB/s spec peak
+    del flush
+    rbuf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    rsink = torch.empty(csa2.READ_RATE_SINK_WORDS, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        csa2.read_rate(rbuf, rsink, stream)
+    rev = [pair() for _ in range(10)]
+    for a, b_ in rev:
+        a.record(stream)
+        csa2.read_rate(rbuf, rsink, stream)
+        b_.record(stream)
+    torch.cuda.synchronize()
+    read_ms = sorted(a.elapsed_time(b_) for a, b_ in rev)[len(rev) // 2]
+    read_gbs = (1 << 30) / (read_ms / 1e3) / 1e9
+    del rbuf, rsink
+
     nbytes = group_bytes(w)
     value = w.nq / (ms / 1e3)
     scan_bytes = nbytes["scan"] if full else nbytes["reindex"]
@@ -330,6 +347,9 @@ def main() -> int:
                           "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(attn_achieved / PEAK_HBM_GBS, 4),
                           "bytes_per_launch": nbytes["attn_layer"], "ms": round(attn_ms, 4)},
         "wall_s_timed": round(t_wall, 3),
+        "hbm_read_achievable": {"kernel": "k_read_rate", "gbs": round(read_gbs, 1),
+                                "frac_of_peak": round(read_gbs / PEAK_HBM_GBS, 4), "bytes": 1 << 30,
+                                "timing": "median of 10 event pairs, every byte read once"},
     }
     if w.encoder:
         # a prefill chunk is matrix work: the attention (the step's dominant

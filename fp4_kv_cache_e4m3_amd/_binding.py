@@ -29,7 +29,9 @@ EXPORTS = (
     "csa2_index_full_append", "csa2_index_select_append", "csa2_index_full_append_paged",
     "csa2_index_select_append_paged", "csa2_index_reindex",
     "csa2_attn_workspace_size", "csa2_sparse_attn", "csa2_index_full_noalloc", "csa2_check_index",
+    "csa2_read_rate",
 )
+READ_RATE_SINK_WORDS = 65536
 
 
 class CSA2Error(RuntimeError):
@@ -115,6 +117,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.csa2_sparse_attn.restype = ctypes.c_int
     lib.csa2_sparse_attn.argtypes = [ctypes.POINTER(AttnArgs), vp, sz, vp]
     lib.csa2_check_index.restype = ctypes.c_int
+    lib.csa2_read_rate.restype = ctypes.c_int
+    lib.csa2_read_rate.argtypes = [vp, sz, vp, vp]
     lib.csa2_check_index.argtypes = [ctypes.POINTER(IndexArgs), vp, vp, i32, vp, vp]
     _lib = lib
     return lib
@@ -267,6 +271,13 @@ def check_index(args: IndexArgs, pool, topk, mode: int, bad, stream=None) -> Non
     outputs against the given pool, 2 a Reindex input pool): the number of
     failing rows is added to bad (a device uint32 / int32 scalar tensor)."""
     _check(load().csa2_check_index(ctypes.byref(args), _ptr(pool), _ptr(topk), int(mode), _ptr(bad), _stream(stream)))
+
+
+def read_rate(buf, sink, stream=None) -> None:
+    """Read every byte of buf (a device tensor) once; timing it gives the
+    device's achievable HBM read rate.  sink: device int32/uint32 tensor of
+    READ_RATE_SINK_WORDS words."""
+    _check(load().csa2_read_rate(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)))
 
 
 def index_reindex(args: IndexArgs, pool, topk, ws, stream=None) -> None:

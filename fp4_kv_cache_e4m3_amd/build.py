@@ -16,7 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libcsa2.so")
-SOURCES = ["abi.hip", "quant.hip", "index.hip", "select.hip", "attn.hip", "attn_wide.hip", "check.hip"]
+SOURCES = ["abi.hip", "quant.hip", "index.hip", "select.hip", "attn.hip", "attn_wide.hip", "check.hip", "rate.hip"]
 ARCH = os.environ.get("CSA2_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

@@ -8,6 +8,7 @@
 #include "common.h"
 #include "check.h"
 #include "quant.h"
+#include "rate.h"
 
 // Scratch of csa2_index_full_noalloc: one array per GPU, loaded with the
 // library's code object.  Host code never passes this name to a kernel (on
@@ -348,6 +349,13 @@ int csa2_quantize_kv(const float* x, int64_t x_stride, int64_t rows, int32_t dim
   const int st = check_quantize(x, x_stride, rows, dim, codes, codes_stride, scales, scales_stride);
   if (st != CSA2_OK || rows == 0) return st;
   return hip_status(launch_quantize(x, x_stride, rows, dim, codes, codes_stride, scales, scales_stride, stream));
+}
+
+int csa2_read_rate(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  if (bytes == 0) return CSA2_OK;
+  if (!buf || !sink) return CSA2_ERR_NULL;
+  if (!aligned(buf, 16) || bytes % 16 || !aligned(sink, 4)) return CSA2_ERR_ALIGN;
+  return hip_status(launch_read_rate(buf, (int64_t)bytes, sink, kReadRateWorkgroups, stream));
 }
 
 int csa2_quantize_kv_bf16(const uint16_t* x, int64_t x_stride, int64_t rows, int32_t dim, uint8_t* codes,

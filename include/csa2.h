@@ -73,6 +73,20 @@ const char* csa2_status_string(int status);
 int csa2_version(void);
 
 /*
+ * csa2_read_rate -- reads every byte of buf once (16-byte non-temporal loads,
+ * one contiguous chunk per workgroup, 16,384 workgroups) and writes one word
+ * per wave to sink.  Not a step
+ * of the method: timing it with events gives the device's achievable HBM
+ * read rate, the reference beside the 8 TB/s peak for the streaming kernels.
+ *   buf    device, 16-byte aligned; bytes a multiple of 16 (0: no-op).
+ *   sink   device uint32 [CSA2_READ_RATE_SINK_WORDS], 4-byte aligned; its
+ *          contents are XORs of the data, with no meaning.
+ * Errors: CSA2_ERR_NULL (buf or sink NULL), CSA2_ERR_ALIGN; nothing launched.
+ */
+#define CSA2_READ_RATE_SINK_WORDS 65536
+int csa2_read_rate(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
+
+/*
  * csa2_quantize_kv -- FP4 quantisation of main-KV rows.
  * Source: ai-maestro.online, "FP4 KV, Bounded Replay, and other extensions".
  *

@@ -126,6 +126,19 @@ def test_quantize_bf16_rejects(lib):
     assert f(16, 64, 0, 64, None, 0, None, 0, None) == 0          # no rows: no-op
 
 
+def test_read_rate_rejects(lib):
+    """The read-rate probe: NULL buffer or sink, a misaligned buffer or sink, or
+    a size not a multiple of 16 is refused before any launch; 0 bytes is a
+    no-op."""
+    f = lib.csa2_read_rate
+    assert f(None, 64, 16, None) == 1
+    assert f(16, 64, None, None) == 1
+    assert f(24, 64, 16, None) == 3
+    assert f(16, 60, 16, None) == 3
+    assert f(16, 64, 18, None) == 3
+    assert f(None, 0, None, None) == 0
+
+
 def test_index_fp8_rejects(lib):
     """FP8 indexer arguments: the flag must be 0 or 1 and both scale arrays
     present and 4-byte aligned; int8 arguments ignore the scale pointers."""
