@@ -375,12 +375,15 @@ int csa2_check_index(const csa2_index_args* args, const int32_t* pool, const int
  *             { swa[b, r] : j <= r < j + window, r >= swa_rows - swa_len[b] },
  *   out[q, h] = sum_e softmax_e(sm_scale * Q[q,h] . e) * e   (key = value)
  * in one softmax; a query with no entry gets zeros.
- * Arithmetic: Q and SWA rows are converted bf16 -> fp16, exact for
- * magnitudes in [2^-14, 65504] (smaller ones lose at most 2^-25 absolute);
- * FP4 values are exact in fp16.  QK^T and PV run on fp16 MFMA with fp32
- * accumulation, sm_scale is applied to the fp32 logits, probabilities are
- * rounded to fp16 and normalised by the sum of the rounded values.
- * Requires |Q| and |SWA| below 65504.
+ * Arithmetic (fp32 accumulation throughout): the FP4 entries' logits run on
+ * fp16 MFMA (FP4 values are exact in fp16) against Q converted bf16 -> fp16,
+ * exact for magnitudes in [2^-14, 65504] (smaller ones lose at most 2^-25
+ * absolute); bf16 window entries' logits run on bf16 MFMA against Q and the
+ * rows as given (exact products), 8-bit ones on fp16 MFMA like the FP4
+ * entries.  sm_scale is applied to the fp32 logits,
+ * probabilities are rounded to fp16 and normalised by the sum of the rounded
+ * values, and PV runs on fp16 MFMA with the window rows converted to fp16 as
+ * Q is.  Requires |Q| and |SWA| below 65504.
  */
 typedef struct {
   int32_t batch;               /* B                                            */
