@@ -67,6 +67,7 @@ CASES = [  # (B, Qn, T, d, H, W, k)
     (1, 1, 6000, 512, 32, 128, 2048),   # longest Top-K row: many FP4 tile pairs per wave
     (2, 2, 3000, 512, 16, 64, 1000),    # odd number of FP4 tiles, shorter window
     (1, 3, 900, 128, 16, 128, 17),      # one full FP4 tile and a one-entry tail
+    (1, 2, 3000, 512, 16, 1024, 512),   # the longest window the header allows (64 window tiles)
 ]
 
 

@@ -27,6 +27,7 @@ WIDE_CASES = [  # (B, Qn, T, d, H, W, k)
     (2, 2, 64, 512, 8, 0, 64),          # no window at all
     (1, 1, 0, 512, 8, 128, 512),        # empty main cache: window only
     (1, 3, 900, 512, 64, 1, 17),        # one-row window
+    (1, 2, 3000, 512, 64, 1024, 512),   # the longest window the header allows (32 window tiles)
 ]
 
 
