@@ -208,3 +208,39 @@ def test_attn_large_window_values_and_tiny_q():
     ref = oracle_out(q, codes, scales, topk, swa, Qn, T, W)
     assert np.all(np.isfinite(got))
     assert rownorm_err(got, ref) <= ATTN_TOL
+
+
+@pytest.mark.parametrize("kernel", [1, 2])
+def test_attn_rows_at_the_top_of_the_offset_range(kernel):
+    """Top-K rows at both ends of a cache whose byte size comes within 8 KiB
+    of 4 GiB (T * codes_stride < 4 GiB - 8 KiB, the header's bound): the
+    32-bit row offsets of the last rows and the out-of-range offset that
+    empty slots read stay apart.  The oracle sees the 512 selected rows as a
+    512-row cache."""
+    d, H, W, k, Qn = 512, 64, 128, 512, 1
+    T = ((4 << 30) - (8 << 10)) // (d // 2) - 1              # the largest T under the bound
+    codes_s, scales_s, q, swa, _ = make_case(77, 1, Qn, k, d, H, W, k)
+    rng = np.random.default_rng(78)
+    ends = np.array([0, 1, T // 2, T - 2, T - 1], np.int64)
+    mid = rng.choice(np.arange(2, T - 2, 7919, dtype=np.int64), size=k - len(ends) - 1, replace=False)
+    pos = np.sort(np.concatenate([ends, mid]))                 # 511 rows and one empty slot
+    codes = torch.zeros((T, d // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.zeros((T, d // 16), dtype=torch.uint8, device="cuda")
+    idx = torch.from_numpy(pos).cuda()
+    codes[idx] = dev(codes_s[:len(pos)])
+    scales[idx] = dev(scales_s[:len(pos)])
+    topk = np.full((1, k), -1, np.int32)
+    topk[0, :len(pos)] = pos
+    out = torch.full((1, H, d), float("nan"), dtype=torch.float32, device="cuda")
+    args = csa2.attn_args(dev(q.view(np.int16)), codes, scales, dev(topk), dev(swa.view(np.int16)), out, Qn, T, W,
+                          kernel=kernel)
+    n = csa2.attn_workspace_size(args)
+    csa2.sparse_attn(args, torch.empty(max(n, 256), dtype=torch.uint8, device="cuda") if n else None)
+    got = host(out)
+    small = np.full((1, k), -1, np.int32)
+    small[0, :len(pos)] = np.arange(len(pos), dtype=np.int32)
+    ref = oracle_out(q, codes_s, scales_s, small, swa, Qn, k, W)
+    assert np.all(np.isfinite(got))
+    assert rownorm_err(got, ref) <= ATTN_TOL
+    del codes, scales
+    torch.cuda.empty_cache()
