@@ -78,6 +78,7 @@ PAGED_CASES = [  # (B, Qn, T, d, H, W, k, P)
     (2, 3, 700, 128, 8, 128, 100, 16),
     (1, 6, 5000, 512, 64, 128, 512, 1),       # one row per page
     (4, 1, 300, 128, 16, 128, 512, 4096),     # one page holds a whole sequence
+    (2, 1, 70000, 128, 8, 128, 512, 65536),   # the largest page size; two pages per sequence
 ]
 
 
