@@ -258,6 +258,10 @@ int check_attn(const csa2_attn_args* a) {
     if (!aligned(a->block_table, 4)) return CSA2_ERR_ALIGN;
   }
   if (!aligned(a->swa_start, 4)) return CSA2_ERR_ALIGN;
+  if (a->swa_new) {                                  // encoded by the attention launch itself
+    if (a->swa_fp8 != 1 || a->window < 1 || a->q_per_seq > kMaxSwaNew) return CSA2_ERR_SHAPE;
+    if (!aligned(a->swa_new, 16)) return CSA2_ERR_ALIGN;
+  }
   return CSA2_OK;
 }
 
@@ -342,7 +346,7 @@ const char* csa2_status_string(int s) {
   }
 }
 
-int csa2_version(void) { return (1 << 16) | 2; }
+int csa2_version(void) { return (1 << 16) | 3; }
 
 int csa2_quantize_kv(const float* x, int64_t x_stride, int64_t rows, int32_t dim, uint8_t* codes,
                      int64_t codes_stride, uint8_t* scales, int64_t scales_stride, hipStream_t stream) {
@@ -591,6 +595,7 @@ int csa2_sparse_attn(const csa2_attn_args* a, void* ws, size_t ws_size, hipStrea
     p.cache_rows = a->cache_rows;
   }
   p.swa_start = a->swa_start;
+  p.swa_new = a->swa_new;
   // With no tile at all the kernel still runs: every head ends with an empty
   // softmax and writes zeros (no memset node, so the call stays graph-safe).
   if (L.wide) return hip_status(launch_attn_wide(p, (int)L.nq, stream));

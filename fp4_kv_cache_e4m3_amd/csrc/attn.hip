@@ -44,6 +44,7 @@
 // accumulation.  sm_scale * log2(e) multiplies the fp32 logits and the
 // softmax uses exp2.
 #include "attn_dev.h"
+#include "quant_dev.h"
 
 namespace csa2 {
 
@@ -263,12 +264,17 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
   // one LDS arena: per-wave V half-tiles, Q of the 16 heads and this split's
   // Top-K positions while the tiles run; the NW partial outputs at the merge
   constexpr int VT_BYTES = NW * TILE_HALVES * 2, QS_BYTES = 16 * QPITCH * 2, SPOS_BYTES = kMaxTopK * 4;
-  constexpr int WORK_BYTES = VT_BYTES + 2 * QS_BYTES + SPOS_BYTES, FB_BYTES = NW * NT * 64 * 16;
+  // S8: the step's new window rows, encoded by the workgroup itself (codes
+  // [kMaxSwaNew][D], then their row scales)
+  constexpr int NEW_BYTES = S8 ? kMaxSwaNew * (D + 4) : 0;
+  constexpr int WORK_BYTES = VT_BYTES + 2 * QS_BYTES + SPOS_BYTES + NEW_BYTES, FB_BYTES = NW * NT * 64 * 16;
   __shared__ __attribute__((aligned(16))) unsigned char smem[WORK_BYTES > FB_BYTES ? WORK_BYTES : FB_BYTES];
   _Float16* const vt = reinterpret_cast<_Float16*>(smem);
   _Float16* const qs = reinterpret_cast<_Float16*>(smem + VT_BYTES);
   __bf16* const qsb = reinterpret_cast<__bf16*>(smem + VT_BYTES + QS_BYTES);      // the same Q as bf16
   int32_t* const spos = reinterpret_cast<int32_t*>(smem + VT_BYTES + 2 * QS_BYTES);   // -1 = empty slot
+  uint8_t* const nrc = smem + VT_BYTES + 2 * QS_BYTES + SPOS_BYTES;                   // S8 new rows' codes
+  float* const nrs = reinterpret_cast<float*>(nrc + kMaxSwaNew * D);                  // and their scales
   __shared__ __attribute__((aligned(8))) float ml[NW][16][2];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -356,6 +362,21 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
     const int c = threadIdx.x + 64 * NW * i;       // chunk c: head row c / (D / 8), 16 bytes each
     qraw[i] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(q_buf, c < QCH ? 16u * (uint32_t)c : kOob, 0, 0));
   }
+  // S8 with new window rows: wave w takes rows w, w + NW, ... of the
+  // sequence's Qn new rows (bf16, 16 bytes per lane; rows past Qn, or no new
+  // rows at all, read zeros)
+  constexpr int NRW = S8 ? kMaxSwaNew / NW : 1;
+  [[maybe_unused]] u4 nraw[NRW];
+  if constexpr (S8) {
+    const rsrc_t nb_buf = make_rsrc(p.swa_new ? p.swa_new + (int64_t)b * p.qn * D : nullptr,
+                                    p.swa_new ? (uint32_t)(p.qn * D * 2) : 0u);
+#pragma unroll
+    for (int i = 0; i < NRW; ++i) {
+      const int r = wave + NW * i;
+      nraw[i] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           nb_buf, lane < D / 8 ? 16u * (uint32_t)(r * (D / 8) + lane) : kOob, 0, 0));
+    }
+  }
   __builtin_amdgcn_sched_barrier(0);                // positions and Q go out before the gathers
 
   // ---- FP4 rows: the first two gathers go out as soon as their positions
@@ -397,6 +418,34 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
     const int sl = (int)threadIdx.x + 64 * NW * i;
     if (sl < n_slots) spos[sl] = slot0 + sl < p.topk_k ? to_row(sraw[i]) : -1;
   }
+  if constexpr (S8) {
+    if (p.swa_new) {
+      // window row swa_rows - Qn + r is the sequence's new row r: encoded as
+      // csa2_quantize_swa_fp8 encodes it, for this workgroup's window tiles
+      // (from LDS); the first workgroup of the sequence's first query also
+      // stores it in its slot of the window cache
+      const bool store = j == 0 && hg == 0 && c0 == 0 && split == 0;
+#pragma unroll
+      for (int i = 0; i < NRW; ++i) {
+        const int r = wave + NW * i;
+        if (r < p.qn) {
+          float sc;
+          const u2 c = swa8_encode_row(nraw[i], sc);
+          if (lane < D / 8) *reinterpret_cast<u2*>(nrc + r * D + 8 * lane) = c;
+          if (lane == 0) nrs[r] = sc;
+          if (store) {
+            int st = p.swa_start ? p.swa_start[b] : 0;   // ring slot of window row 0
+            st = st >= 0 && st < p.swa_rows ? st : 0;
+            const int wr = p.swa_rows - p.qn + r;
+            const int slot = wr + st >= p.swa_rows ? wr + st - p.swa_rows : wr + st;
+            const int64_t crow = (int64_t)b * p.swa_rows + slot;
+            if (lane < D / 8) *reinterpret_cast<u2*>(reinterpret_cast<uint8_t*>(const_cast<uint16_t*>(p.swa)) + crow * D + 8 * lane) = c;
+            if (lane == 0) const_cast<float*>(p.swa_scale)[crow] = sc;
+          }
+        }
+      }
+    }
+  }
   __syncthreads();
 
   v4f o[NT];
@@ -432,13 +481,17 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
   // ring buffer: window row r of the sequence sits in slot (r + start) mod rows
   int swa_st = p.swa_start ? p.swa_start[b] : 0;
   swa_st = swa_st >= 0 && swa_st < p.swa_rows ? swa_st : 0;
+  // S8 with new rows: rows swa_rows - Qn .. are not read from the cache (they
+  // come from the workgroup's own encoding in LDS)
+  const int first_new = S8 && p.swa_new ? p.swa_rows - p.qn : p.swa_rows;
   auto swa_rows = [&](int t) {                      // this lane's row offset of window tile t
     const int wr = (t - p.n_sparse_tiles) * 16 + n;
     const int r = j + wr;
     swa_valid = t < t_end && wr >= 0 && wr < p.window && r >= first_swa && r < p.swa_rows;
+    const bool cached = S8 ? swa_valid && r < first_new : swa_valid;
     const int rs = r + swa_st >= p.swa_rows ? r + swa_st - p.swa_rows : r + swa_st;
-    swa_so = swa_valid ? 4u * (uint32_t)rs : kOob;
-    return (swa_valid ? (uint32_t)rs * (kSwaBytes * D) : kOob) + swa_lane;
+    swa_so = cached ? 4u * (uint32_t)rs : kOob;
+    return (cached ? (uint32_t)rs * (kSwaBytes * D) : kOob) + swa_lane;
   };
   auto load_swa_half = [&](uint32_t ro, int hh) {
     if constexpr (S8) {
@@ -529,6 +582,16 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
       load_qf(Fp8Map<D>{});
       _Float16* wrow = my + n * PITCH + Fp8Map<D>::LANE * g;
       for (int t = swa_first; t < t_end; t += NW) {
+        // the step's new rows (read as zeros above) from the encoding in LDS
+        const int i_new = j + (t - p.n_sparse_tiles) * 16 + n - first_new;
+        if (i_new >= 0 && i_new < p.qn && swa_valid) {
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int i = 0; i < KH / 2; ++i)
+              w[hh][i] = *reinterpret_cast<const u4*>(nrc + i_new * D + swa_lane + gch(64 * i, 0) + HV::SUB * ch[hh]);
+          swa_sc = __float_as_uint(nrs[i_new]);
+        }
         const bool v = swa_valid;
         const float sc = __uint_as_float(swa_sc);
         attend_tile<D, Fp8Map<D>, v8h>(

@@ -18,6 +18,7 @@ namespace csa2 {
 
 constexpr int kTopK = 512;
 constexpr int kMaxTopK = 2048;                   // largest Top-K row the attention kernel takes
+constexpr int kMaxSwaNew = 16;                   // largest Qn whose new 8-bit window rows the attention encodes
 constexpr int kBlock = 8;
 constexpr int kPoolBlocks = 2048;
 constexpr int kPoolPositions = kPoolBlocks * kBlock;
@@ -188,6 +189,7 @@ struct AttnParams {
   int32_t max_pages, page_shift;
   int64_t cache_rows;                                    // physical rows of a paged cache
   const int32_t* swa_start;                              // ring slot of window row 0 per sequence, or NULL
+  const uint16_t* swa_new;                               // S8: the step's new window rows (bf16 [B * Qn, d]), or NULL
 };
 
 hipError_t launch_quantize(const float* x, int64_t xs, int64_t rows, int dim, uint8_t* codes,

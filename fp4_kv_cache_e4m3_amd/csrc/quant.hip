@@ -135,20 +135,8 @@ hipError_t launch_quantize_bf16(const uint16_t* x, int64_t xs, int64_t rows, int
 }
 
 // ---------------------------------------------------------------- 8-bit window rows
-// One wave per bf16 row of `dim` <= 512 channels, 8 channels per lane: the
-// row's power-of-two scale 2^k (the smallest k with max|x| <= 448 * 2^k),
-// then every |x| / 2^k (exact) rounded to the nearest E4M3 value, ties to
-// even, with the sign bit of x.  The rounding is exact: on the subnormal grid
-// y * 512 is an integer grid coordinate, on a binade y * 2^(3-e) lies in
-// [8, 16); both are exact scalings, and v_rndne_f32 rounds them half-even.
-CSA2_DEV uint32_t e4m3_rne_code(float y) {          // 0 <= y <= 448
-  if (y < 0x1p-6f) return (uint32_t)__builtin_rintf(y * 512.0f);      // codes 0..8 (8 = 2^-6)
-  int E;
-  (void)__builtin_frexpf(y, &E);                  // y = f * 2^E, f in [0.5, 1)
-  const int m = (int)__builtin_rintf(__builtin_ldexpf(y, 4 - E));     // 8 .. 16
-  return (uint32_t)((E + 6) * 8 + m - 8);
-}
-
+// One wave per bf16 row of `dim` <= 512 channels, 8 channels per lane (the
+// encoding is swa8_encode_row in quant_dev.h).
 __global__ __launch_bounds__(256) void k_quantize_swa8(const uint16_t* __restrict__ x, int64_t xs, int64_t rows,
                                                        int dim, uint8_t* __restrict__ out, int64_t os,
                                                        float* __restrict__ scales, int64_t ss) {
@@ -157,31 +145,10 @@ __global__ __launch_bounds__(256) void k_quantize_swa8(const uint16_t* __restric
   if (row >= rows) return;                         // whole waves
   const bool act = lane < dim / 8;
   const u4 w = act ? *reinterpret_cast<const u4*>(x + row * xs + 8 * lane) : u4{0u, 0u, 0u, 0u};
-  float v[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[2 * i] = __uint_as_float(w[i] << 16);
-    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-  }
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
-  int k = 0;
-  if (amax > 0.0f) {
-    int e;
-    const float f = __builtin_frexpf(amax, &e);    // amax = f * 2^e; 448 = 0.875 * 2^9
-    k = e - 9 + (f > 0.875f ? 1 : 0);
-  }
-  uint32_t word[2] = {0u, 0u};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t c = e4m3_rne_code(__builtin_ldexpf(fabsf(v[i]), -k)) | ((__float_as_uint(v[i]) >> 24) & 0x80u);
-    word[i / 4] |= c << (8 * (i % 4));
-  }
-  if (act) *reinterpret_cast<u2*>(out + row * os + 8 * lane) = u2{word[0], word[1]};
-  if (lane == 0) scales[row * ss] = __builtin_ldexpf(1.0f, k);
+  float sc;
+  const u2 c = swa8_encode_row(w, sc);
+  if (act) *reinterpret_cast<u2*>(out + row * os + 8 * lane) = c;
+  if (lane == 0) scales[row * ss] = sc;
 }
 
 hipError_t launch_quantize_swa8(const uint16_t* x, int64_t xs, int64_t rows, int dim, uint8_t* out, int64_t os,

@@ -8,6 +8,52 @@
 
 namespace csa2 {
 
+// ---------------------------------------------------------------- 8-bit window rows
+// A window row is stored as E4M3 codes with one power-of-two scale 2^k per
+// row: k is the smallest integer with max|x| <= 448 * 2^k (0 for an all-zero
+// row), and each |x| / 2^k (exact) is rounded to the nearest E4M3 value, ties
+// to even, with the sign bit of x.  The rounding is exact: on the subnormal
+// grid y * 512 is an integer grid coordinate, on a binade y * 2^(3-e) lies in
+// [8, 16); both are exact scalings, and v_rndne_f32 rounds them half-even.
+CSA2_DEV uint32_t e4m3_rne_code(float y) {          // 0 <= y <= 448
+  if (y < 0x1p-6f) return (uint32_t)__builtin_rintf(y * 512.0f);      // codes 0..8 (8 = 2^-6)
+  int E;
+  (void)__builtin_frexpf(y, &E);                  // y = f * 2^E, f in [0.5, 1)
+  const int m = (int)__builtin_rintf(__builtin_ldexpf(y, 4 - E));     // 8 .. 16
+  return (uint32_t)((E + 6) * 8 + m - 8);
+}
+
+// One row spread over a wave, eight bf16 channels per lane (w, channel order;
+// lanes past the row hold zeros): the lane's eight E4M3 codes as two words,
+// and the row scale 2^k in sc (every lane).
+CSA2_DEV u2 swa8_encode_row(u4 w, float& sc) {
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  int k = 0;
+  if (amax > 0.0f) {
+    int e;
+    const float f = __builtin_frexpf(amax, &e);    // amax = f * 2^e; 448 = 0.875 * 2^9
+    k = e - 9 + (f > 0.875f ? 1 : 0);
+  }
+  uint32_t word[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t c = e4m3_rne_code(__builtin_ldexpf(fabsf(v[i]), -k)) | ((__float_as_uint(v[i]) >> 24) & 0x80u);
+    word[i / 4] |= c << (8 * (i % 4));
+  }
+  sc = __builtin_ldexpf(1.0f, k);
+  return u2{word[0], word[1]};
+}
+
 // launches of at most this many 16-channel groups use four lanes per group
 constexpr int64_t kQuantQuadMaxGroups = 8192;
 

@@ -36,7 +36,7 @@ class DecodeGroup:
     is produced once at set-up (from the pool-source indexer Q) and is an
     input of every step."""
 
-    def __init__(self, w: synth.Workload, device: str = "cuda", kv_rows=None):
+    def __init__(self, w: synth.Workload, device: str = "cuda", kv_rows=None, fused_window: bool = True):
         self.w = w
         self.device = device
         dev = device
@@ -94,10 +94,13 @@ class DecodeGroup:
                 self.swa_start[l] = _dev(st, dev)
             self.swa.append(_dev(np.ascontiguousarray(rows).view(np.int16), dev))
         # 8-bit window rows: the older rows quantised once on the device from
-        # the bf16 rows; each step quantises its query tokens' new rows into
-        # the newest slots (rows swa_rows - Qn .. swa_rows - 1)
+        # the bf16 rows; each step encodes its query tokens' new rows into
+        # the newest slots (rows swa_rows - Qn .. swa_rows - 1): inside the
+        # attention call (fused_window), or by one strided quantise call per
+        # query slot before it
         self.swa_scale = [None] * nl
         self._swa_new = [[] for _ in range(nl)]
+        self._swa_rows_new = [None] * nl
         assert not (w.swa8 and w.swa_ring), "8-bit rings are not set up here"
         if w.swa8:
             for l in range(nl):
@@ -106,6 +109,9 @@ class DecodeGroup:
                 B.quantize_swa_fp8(self.swa[l].view(B_ * w.swa_rows, d), codes8.view(B_ * w.swa_rows, d), sc8.view(-1))
                 self.swa[l], self.swa_scale[l] = codes8, sc8
                 nb = _dev(synth.new_swa_rows(w, l).view(np.int16), dev).view(B_, w.q_per_seq, d)
+                if fused_window:
+                    self._swa_rows_new[l] = nb.view(B_ * w.q_per_seq, d)
+                    continue
                 for i in range(w.q_per_seq):          # one strided call per query slot
                     r = w.swa_rows - w.q_per_seq + i
                     self._swa_new[l].append((nb[:, i, :], codes8[:, r, :], sc8[:, r]))
@@ -127,7 +133,8 @@ class DecodeGroup:
             self._topk_of.append(self.topks[k])
         self.aargs = [B.attn_args(self.q[l], self.codes, self.scales, self._topk_of[l], self.swa[l], self.out[l],
                                   w.q_per_seq, T, w.window, swa_scale=self.swa_scale[l],
-                                  block_table=self.block_table, page_size=P, swa_start=self.swa_start[l])
+                                  block_table=self.block_table, page_size=P, swa_start=self.swa_start[l],
+                                  swa_new=self._swa_rows_new[l])
                       for l in range(nl)]
         aws = max(B.attn_workspace_size(a) for a in self.aargs)
         self.aws = torch.empty(max(256, aws), dtype=torch.uint8, device=dev) if aws > 0 else None

@@ -451,6 +451,17 @@ typedef struct {
      sum in different orders (results may differ in the last bits); each is
      deterministic.  Other values: CSA2_ERR_SHAPE.                            */
   int32_t kernel;
+  /* 8-bit windows (swa_fp8 = 1, window >= 1) only: NULL, or the step's new
+     window rows as bf16 [nq, d], 16-byte aligned, Qn <= 16.  Row b * Qn + i
+     is window row swa_rows - Qn + i of sequence b (the step's query
+     tokens).  The call encodes each exactly as csa2_quantize_swa_fp8 does,
+     attends over the encoded values, and stores the codes and the row scale
+     into swa and swa_scale at that row (its ring slot when swa_start is
+     given), so both must be writable; their previous contents at those rows
+     are not read.  This replaces a csa2_quantize_swa_fp8 launch per layer and
+     step.  Errors: CSA2_ERR_SHAPE (bf16 window, no window, Qn > 16),
+     CSA2_ERR_ALIGN.                                                        */
+  const uint16_t* swa_new;
 } csa2_attn_args;
 
 /* Bytes of workspace csa2_sparse_attn needs for these arguments (may be 0). */

@@ -259,6 +259,14 @@ def test_attn_rejects(lib):
     assert lib.csa2_attn_workspace_size(ctypes.byref(args(kernel=2))) == 0
     # the library's choice for a prefill chunk (4,096 queries): no workspace
     assert lib.csa2_attn_workspace_size(ctypes.byref(args(batch=1, q_per_seq=4096))) == 0
+    # new 8-bit window rows encoded by the call: 8-bit windows of at least one
+    # row, at most 16 query tokens per sequence, 16-byte aligned
+    s8 = dict(swa_fp8=1, swa_scale=256)
+    assert lib.csa2_attn_workspace_size(ctypes.byref(args(swa_new=256, **s8))) == need     # accepted
+    assert sa(ctypes.byref(args(swa_new=256)), None, 0, None) == 2                      # bf16 window
+    assert sa(ctypes.byref(args(swa_new=256, window=0, **s8)), None, 0, None) == 2      # no window
+    assert sa(ctypes.byref(args(swa_new=256, batch=1, q_per_seq=17, **s8)), None, 0, None) == 2
+    assert sa(ctypes.byref(args(swa_new=264, **s8)), None, 0, None) == 3
 
 
 def test_argument_structs_keep_their_tensors_alive():

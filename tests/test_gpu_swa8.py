@@ -122,3 +122,49 @@ def test_quantize_into_newest_window_slots():
     np.testing.assert_array_equal(got_c[:, R - 1], rc)
     np.testing.assert_array_equal(got_s[:, R - 1], rs.astype(np.float32))
     assert np.all(got_c[:, :R - 1] == 0xA5) and np.all(np.isnan(got_s[:, :R - 1]))
+
+
+@pytest.mark.parametrize("case", [
+    (3, 1, 1000, 512, 64, 128, 512, None),       # decode: one new row per sequence
+    (2, 6, 900, 512, 16, 128, 300, None),        # 1 + 5 draft queries: six new rows
+    (2, 3, 500, 128, 8, 64, 100, (2, 1)),        # d = 128, ring windows
+    (1, 16, 700, 512, 16, 32, 64, (5,)),         # the most new rows the call takes, ring
+], ids=lambda c: "B{}Q{}T{}d{}H{}W{}k{}ring{}".format(*c[:7], c[7] is not None))
+def test_attn_encodes_new_window_rows(case):
+    """swa_new: the attention call encodes the step's new window rows itself.
+    Its output is bit-identical to the same call over a window whose newest
+    rows already hold their 8-bit codes; afterwards the new rows' slots hold
+    the oracle's codes and scales and every other slot is unchanged."""
+    B, Qn, T, d, H, W, k, ring = case
+    codes, scales, q, swa, topk = make_case(sum(case[:7]) + 3, B, Qn, T, d, H, W, k)
+    R = swa.shape[1]                                    # W - 1 + Qn window rows
+    rc, rs = swa8.quantize_swa_rows(bf16_values(swa.reshape(-1, d)))
+    rc, rs = rc.reshape(B, R, d), rs.reshape(B, R).astype(np.float32)
+    start = np.zeros(B, np.int32) if ring is None else np.asarray(ring, np.int32)
+    full_c = np.stack([np.roll(rc[b], start[b], axis=0) for b in range(B)])     # row r in slot (r + start) % R
+    full_s = np.stack([np.roll(rs[b], start[b]) for b in range(B)])
+    new_slots = [(np.arange(R - Qn, R) + start[b]) % R for b in range(B)]
+    stale_c, stale_s = full_c.copy(), full_s.copy()
+    for b in range(B):
+        stale_c[b, new_slots[b]] = 0xA5                 # the new rows' slots before the call
+        stale_s[b, new_slots[b]] = np.nan
+    new_bits = np.ascontiguousarray(swa[:, R - Qn:].reshape(B * Qn, d))
+
+    def run(c8, s8, swa_new):
+        out = torch.full((B * Qn, H, d), float("nan"), dtype=torch.float32, device="cuda")
+        c_d, s_d = dev(c8), dev(s8)
+        args = csa2.attn_args(dev(q.view(np.int16)), dev(codes), dev(scales), dev(topk), c_d, out, Qn, T, W,
+                              swa_scale=s_d, swa_start=dev(start) if ring is not None else None,
+                              swa_new=None if swa_new is None else dev(swa_new.view(np.int16)))
+        n = csa2.attn_workspace_size(args)
+        csa2.sparse_attn(args, torch.empty(max(n, 256), dtype=torch.uint8, device="cuda") if n else None)
+        return host(out), host(c_d), host(s_d)
+
+    ref_out, _, _ = run(full_c, full_s, None)
+    got_out, got_c, got_s = run(stale_c, stale_s, new_bits)
+    np.testing.assert_array_equal(got_out, ref_out)
+    np.testing.assert_array_equal(got_c, full_c)
+    np.testing.assert_array_equal(got_s, full_s)
+    ref = oattn.sparse_attn(bf16_values(q), codes, scales, topk, swa8.swa_values(rc.reshape(-1, d), rs.reshape(-1))
+                            .reshape(swa.shape), Qn, T, window=W)
+    assert rownorm_err(got_out, ref) <= ATTN_TOL
