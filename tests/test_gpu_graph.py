@@ -1,7 +1,8 @@
 """A whole decode-group step captured in a HIP graph (torch.cuda.CUDAGraph):
 every library call enqueues kernels only (no allocation, no host sync, no
 memset node), so replays must reproduce the eager step bit for bit.  The
-outputs are clobbered eagerly before each replay, and eager work and
+outputs (and, with 8-bit windows, the new window rows the attention calls
+store) are clobbered eagerly before each replay, and eager work and
 synchronisations run between the replays."""
 import numpy as np
 import pytest
@@ -17,8 +18,12 @@ def snapshot(g):
     T, n = g.w.kv_len, g.w.new_per_seq
     new_rows = torch.from_numpy(np.concatenate([g.cache_rows(b, np.arange(T - n, T)) for b in range(g.w.batch)]))
     new_rows = new_rows.to(g.codes.device)
+    win = []
+    if g.w.swa8:                                          # the 8-bit windows the attention calls write into
+        for l in range(len(g.w.layers)):
+            win += [host(g.swa[l]), host(g.swa_scale[l])]
     return ([host(o) for o in g.out] + [host(t) for t in g.topks] + [host(g.pool)]
-            + [host(g.codes[new_rows]), host(g.scales[new_rows])])
+            + [host(g.codes[new_rows]), host(g.scales[new_rows])] + win)
 
 
 def clobber(g):
@@ -28,10 +33,16 @@ def clobber(g):
         t.fill_(-7)
     if "full" in g.w.layers:                              # otherwise the pool is an input
         g.pool.fill_(-7)
+    if g.w.swa8:                                          # the step's new window rows' slots
+        R, Qn = g.w.swa_rows, g.w.q_per_seq
+        for l in range(len(g.w.layers)):
+            g.swa[l][:, R - Qn:].fill_(0xA5)
+            g.swa_scale[l][:, R - Qn:].fill_(float("nan"))
 
 
 @pytest.mark.parametrize("name", ["decode_group_full_reuse3_b32_t65536", "decode_group_reindex_reuse3_b32_t65536",
-                                  "decode_group_full_reuse3_b32_t65536_paged"])
+                                  "decode_group_full_reuse3_b32_t65536_paged",
+                                  "decode_group_full_reuse3_b32_t65536_swa8"])
 def test_step_graph_replays_match_eager(name):
     w = synth.WORKLOADS[name]
     g = DecodeGroup(w)
