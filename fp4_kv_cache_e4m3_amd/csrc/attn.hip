@@ -254,7 +254,9 @@ CSA2_DEV void attend_tile(const AttnParams& p, KV kvf, QO qop, ST stage, AfterQK
 }
 
 // S8: the window rows are 8-bit (E4M3 codes + a power-of-two scale per row)
-// instead of bf16
+// instead of bf16; with p.swa_new the step's new rows arrive as bf16, are
+// encoded by every workgroup of the sequence into LDS (read from there, not
+// from the cache) and stored into the cache by one workgroup of the sequence
 template <int D, int NW, bool S8, bool PG>
 __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
   using G = Geo<D>;
