@@ -130,12 +130,16 @@ def test_quantize_into_newest_window_slots():
     (2, 3, 500, 128, 8, 64, 100, (2, 1)),        # d = 128, ring windows
     (1, 16, 700, 512, 16, 32, 64, (5,)),         # the most new rows the call takes, ring
 ], ids=lambda c: "B{}Q{}T{}d{}H{}W{}k{}ring{}".format(*c[:7], c[7] is not None))
-def test_attn_encodes_new_window_rows(case):
+@pytest.mark.parametrize("split", [(0, 0), (4, 1), (8, 3)], ids=["auto", "w4s1", "w8s3"])
+def test_attn_encodes_new_window_rows(case, split):
     """swa_new: the attention call encodes the step's new window rows itself.
     Its output is bit-identical to the same call over a window whose newest
     rows already hold their 8-bit codes; afterwards the new rows' slots hold
-    the oracle's codes and scales and every other slot is unchanged."""
+    the oracle's codes and scales and every other slot is unchanged.  Work
+    splits: the library's choice, 4-wave workgroups (four new rows per wave
+    to encode), and three tile-list splits (only the first stores)."""
     B, Qn, T, d, H, W, k, ring = case
+    waves, splits = split
     codes, scales, q, swa, topk = make_case(sum(case[:7]) + 3, B, Qn, T, d, H, W, k)
     R = swa.shape[1]                                    # W - 1 + Qn window rows
     rc, rs = swa8.quantize_swa_rows(bf16_values(swa.reshape(-1, d)))
@@ -155,7 +159,8 @@ def test_attn_encodes_new_window_rows(case):
         c_d, s_d = dev(c8), dev(s8)
         args = csa2.attn_args(dev(q.view(np.int16)), dev(codes), dev(scales), dev(topk), c_d, out, Qn, T, W,
                               swa_scale=s_d, swa_start=dev(start) if ring is not None else None,
-                              swa_new=None if swa_new is None else dev(swa_new.view(np.int16)))
+                              swa_new=None if swa_new is None else dev(swa_new.view(np.int16)),
+                              waves=waves, splits=splits)
         n = csa2.attn_workspace_size(args)
         csa2.sparse_attn(args, torch.empty(max(n, 256), dtype=torch.uint8, device="cuda") if n else None)
         return host(out), host(c_d), host(s_d)
