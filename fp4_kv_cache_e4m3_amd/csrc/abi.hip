@@ -200,7 +200,8 @@ AttnLayout attn_layout(const csa2_attn_args* a) {
   L.n_sparse_tiles = a->kv_len > 0 ? (a->topk_k + 15) / 16 : 0;
   L.swa_rows = a->window > 0 ? a->window - 1 + a->q_per_seq : 0;
   L.n_tiles = L.n_sparse_tiles + (a->window + 15) / 16;
-  const bool wide_ok = a->dim == 512 && a->swa_fp8 == 0 && a->waves == 0 && a->splits == 0;
+  const bool wide_ok = a->dim == 512 && a->swa_fp8 == 0 && a->waves == 0 && a->splits == 0 &&
+                       !a->topk_rows_out && !a->topk_is_rows;
   L.wide = a->kernel == 2 || (a->kernel == 0 && wide_ok && L.nq * ((a->heads + 63) / 64) >= kWideMinWorkgroups);
   if (L.wide) {
     L.waves = 4;
@@ -261,6 +262,17 @@ int check_attn(const csa2_attn_args* a) {
   if (a->swa_new) {                                  // encoded by the attention launch itself
     if (a->swa_fp8 != 1 || a->window < 1 || a->q_per_seq > kMaxSwaNew) return CSA2_ERR_SHAPE;
     if (!aligned(a->swa_new, 16)) return CSA2_ERR_ALIGN;
+  }
+  // the Top-K as cache rows: written by a paged call, read instead of positions
+  if (a->topk_is_rows != 0 && a->topk_is_rows != 1) return CSA2_ERR_SHAPE;
+  if ((a->topk_rows_out || a->topk_is_rows) && a->kernel == 2) return CSA2_ERR_SHAPE;
+  if (a->topk_rows_out && !a->block_table) return CSA2_ERR_SHAPE;
+  if (!aligned(a->topk_rows_out, 4)) return CSA2_ERR_ALIGN;
+  if (a->topk_is_rows) {
+    if (a->block_table) return CSA2_ERR_SHAPE;
+    if (a->cache_rows < 0 || a->cache_rows >= (1 << 24) || a->cache_rows * a->codes_stride > kBufMax ||
+        a->cache_rows * a->scales_stride > kBufMax)
+      return CSA2_ERR_SHAPE;
   }
   return CSA2_OK;
 }
@@ -346,7 +358,7 @@ const char* csa2_status_string(int s) {
   }
 }
 
-int csa2_version(void) { return (1 << 16) | 3; }
+int csa2_version(void) { return (1 << 16) | 4; }
 
 int csa2_quantize_kv(const float* x, int64_t x_stride, int64_t rows, int32_t dim, uint8_t* codes,
                      int64_t codes_stride, uint8_t* scales, int64_t scales_stride, hipStream_t stream) {
@@ -596,6 +608,9 @@ int csa2_sparse_attn(const csa2_attn_args* a, void* ws, size_t ws_size, hipStrea
   }
   p.swa_start = a->swa_start;
   p.swa_new = a->swa_new;
+  p.rows_out = a->topk_rows_out;
+  p.rows_in = a->topk_is_rows;
+  if (a->topk_is_rows) p.cache_rows = a->cache_rows;
   // With no tile at all the kernel still runs: every head ends with an empty
   // softmax and writes zeros (no memset node, so the call stays graph-safe).
   if (L.wide) return hip_status(launch_attn_wide(p, (int)L.nq, stream));

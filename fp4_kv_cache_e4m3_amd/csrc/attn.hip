@@ -256,8 +256,12 @@ CSA2_DEV void attend_tile(const AttnParams& p, KV kvf, QO qop, ST stage, AfterQK
 // S8: the window rows are 8-bit (E4M3 codes + a power-of-two scale per row)
 // instead of bf16; with p.swa_new the step's new rows arrive as bf16, are
 // encoded by every workgroup of the sequence into LDS (read from there, not
-// from the cache) and stored into the cache by one workgroup of the sequence
-template <int D, int NW, bool S8, bool PG>
+// from the cache) and stored into the cache by one workgroup of the sequence.
+// PG: 0 contiguous cache ([B, T] rows), 1 paged cache (Top-K positions go
+// through the block table; with p.rows_out one workgroup per query and
+// split also writes the rows it found), 2 the Top-K row already holds cache
+// rows (a paged call's rows_out)
+template <int D, int NW, bool S8, int PG>
 __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
   using G = Geo<D>;
   constexpr int KH = G::KH, NT = G::NT, PITCH = G::PITCH, HALF = G::HALF;
@@ -325,11 +329,13 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
   // block_table[b][t >> page_shift] * page_size + (t & (page_size - 1)) of the
   // whole cache; positions outside [0, T), negative page ids and rows past the
   // cache become -1 (empty).  Positions are translated where they are staged.
-  const rsrc_t bt_buf = make_rsrc(PG ? p.block_table + (int64_t)b * p.max_pages : nullptr,
-                                  PG ? (uint32_t)p.max_pages * 4u : 0u);
+  const rsrc_t bt_buf = make_rsrc(PG == 1 ? p.block_table + (int64_t)b * p.max_pages : nullptr,
+                                  PG == 1 ? (uint32_t)p.max_pages * 4u : 0u);
   auto to_row = [&](int32_t pos) -> int32_t {
-    if constexpr (!PG) {
+    if constexpr (PG == 0) {
       return pos;
+    } else if constexpr (PG == 2) {
+      return pos >= 0 && (int64_t)pos < p.cache_rows ? pos : -1;
     } else {
       const bool ok = pos >= 0 && (int64_t)pos < p.T;
       const int32_t page = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(
@@ -385,7 +391,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
   // are known
   Fp4Src src;
   // the sequence's rows, or (PG) the whole cache
-  const int64_t row0 = PG ? 0 : b * p.T, nrows = PG ? p.cache_rows : p.T;
+  const int64_t row0 = PG != 0 ? 0 : b * p.T, nrows = PG != 0 ? p.cache_rows : p.T;
   src.codes = make_rsrc(p.codes + row0 * p.codes_stride, (uint32_t)(nrows * p.codes_stride));
   src.scales = make_rsrc(p.scales + row0 * p.scales_stride, (uint32_t)(nrows * p.scales_stride));
   src.cstride = (uint32_t)p.codes_stride;
@@ -419,6 +425,17 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(AttnParams p) {
   for (int i = 0; i < SPT; ++i) {
     const int sl = (int)threadIdx.x + 64 * NW * i;
     if (sl < n_slots) spos[sl] = slot0 + sl < p.topk_k ? to_row(sraw[i]) : -1;
+  }
+  if constexpr (PG == 1) {
+    // the rows this split's slots name, for the later calls of the group
+    // (their Top-K as rows); one workgroup per (query, split) writes them
+    if (p.rows_out && hg == 0 && c0 == 0) {
+#pragma unroll
+      for (int i = 0; i < SPT; ++i) {
+        const int sl = (int)threadIdx.x + 64 * NW * i;
+        if (sl < n_slots && slot0 + sl < p.topk_k) p.rows_out[(int64_t)q * p.topk_k + slot0 + sl] = spos[sl];
+      }
+    }
   }
   if constexpr (S8) {
     if (p.swa_new) {
@@ -723,11 +740,14 @@ hipError_t launch_attn(const AttnParams& p, int nq, int dim, int waves, hipStrea
 #define CSA2_ATTN_CASE(D, NW)                                                                 \
   if (dim == D && waves == NW) {                                                              \
     if (p.block_table) {                                                                      \
-      if (p.swa_fp8) hipLaunchKernelGGL((k_attn<D, NW, true, true>), grid, dim3(64 * NW), 0, st, p); \
-      else hipLaunchKernelGGL((k_attn<D, NW, false, true>), grid, dim3(64 * NW), 0, st, p);        \
+      if (p.swa_fp8) hipLaunchKernelGGL((k_attn<D, NW, true, 1>), grid, dim3(64 * NW), 0, st, p); \
+      else hipLaunchKernelGGL((k_attn<D, NW, false, 1>), grid, dim3(64 * NW), 0, st, p);        \
+    } else if (p.rows_in) {                                                                   \
+      if (p.swa_fp8) hipLaunchKernelGGL((k_attn<D, NW, true, 2>), grid, dim3(64 * NW), 0, st, p); \
+      else hipLaunchKernelGGL((k_attn<D, NW, false, 2>), grid, dim3(64 * NW), 0, st, p);        \
     } else {                                                                                  \
-      if (p.swa_fp8) hipLaunchKernelGGL((k_attn<D, NW, true, false>), grid, dim3(64 * NW), 0, st, p); \
-      else hipLaunchKernelGGL((k_attn<D, NW, false, false>), grid, dim3(64 * NW), 0, st, p);        \
+      if (p.swa_fp8) hipLaunchKernelGGL((k_attn<D, NW, true, 0>), grid, dim3(64 * NW), 0, st, p); \
+      else hipLaunchKernelGGL((k_attn<D, NW, false, 0>), grid, dim3(64 * NW), 0, st, p);        \
     }                                                                                         \
     if (p.splits > 1) hipLaunchKernelGGL(k_attn_combine<D>, dim3(nq * p.heads), dim3(D / 4), 0, st, p); \
     return hipGetLastError();                                                                 \

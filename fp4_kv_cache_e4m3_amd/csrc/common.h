@@ -190,6 +190,8 @@ struct AttnParams {
   int64_t cache_rows;                                    // physical rows of a paged cache
   const int32_t* swa_start;                              // ring slot of window row 0 per sequence, or NULL
   const uint16_t* swa_new;                               // S8: the step's new window rows (bf16 [B * Qn, d]), or NULL
+  int32_t* rows_out;                                     // paged: the Top-K slots' cache rows [nq, topk_k], or NULL
+  int32_t rows_in;                                       // 1: topk holds cache rows (no block table)
 };
 
 hipError_t launch_quantize(const float* x, int64_t xs, int64_t rows, int dim, uint8_t* codes,

@@ -36,7 +36,8 @@ class DecodeGroup:
     is produced once at set-up (from the pool-source indexer Q) and is an
     input of every step."""
 
-    def __init__(self, w: synth.Workload, device: str = "cuda", kv_rows=None, fused_window: bool = True):
+    def __init__(self, w: synth.Workload, device: str = "cuda", kv_rows=None, fused_window: bool = True,
+                 rows_once: bool = True):
         self.w = w
         self.device = device
         dev = device
@@ -131,11 +132,24 @@ class DecodeGroup:
         for m in w.layers:
             k += m in ("full", "reindex")
             self._topk_of.append(self.topks[k])
-        self.aargs = [B.attn_args(self.q[l], self.codes, self.scales, self._topk_of[l], self.swa[l], self.out[l],
-                                  w.q_per_seq, T, w.window, swa_scale=self.swa_scale[l],
-                                  block_table=self.block_table, page_size=P, swa_start=self.swa_start[l],
-                                  swa_new=self._swa_rows_new[l])
-                      for l in range(nl)]
+        # Paged cache (rows_once): an indexing layer's attention call also
+        # writes its Top-K as cache rows, and the later layers that share
+        # that Top-K read the rows (no block-table reads of their own)
+        self.aargs = []
+        rows_of = {}
+        for l, m in enumerate(w.layers):
+            tk = self._topk_of[l]
+            kw = dict(swa_scale=self.swa_scale[l], swa_start=self.swa_start[l], swa_new=self._swa_rows_new[l])
+            if P and rows_once and m in ("full", "reindex"):
+                rows_of[id(tk)] = torch.full_like(tk, -1)
+                kw.update(block_table=self.block_table, page_size=P, topk_rows_out=rows_of[id(tk)])
+            elif P and rows_once and id(tk) in rows_of:
+                tk = rows_of[id(tk)]
+                kw.update(topk_is_rows=True)
+            else:
+                kw.update(block_table=self.block_table, page_size=P)
+            self.aargs.append(B.attn_args(self.q[l], self.codes, self.scales, tk, self.swa[l], self.out[l],
+                                          w.q_per_seq, T, w.window, **kw))
         aws = max(B.attn_workspace_size(a) for a in self.aargs)
         self.aws = torch.empty(max(256, aws), dtype=torch.uint8, device=dev) if aws > 0 else None
         # a step's new entries land in the last new_per_seq slots of each

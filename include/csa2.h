@@ -462,6 +462,18 @@ typedef struct {
      step.  Errors: CSA2_ERR_SHAPE (bf16 window, no window, Qn > 16),
      CSA2_ERR_ALIGN.                                                        */
   const uint16_t* swa_new;
+  /* Top-K as cache rows, for the later layers of a group over a paged cache:
+     topk_rows_out (block_table given): NULL, or int32 [nq, topk_k], 4-byte
+     aligned; the call also writes each Top-K slot's cache row there (-1 for
+     an empty slot, a position outside [0, T), a negative page id or a row at
+     or past cache_rows).  topk_is_rows = 1 (block_table NULL): topk holds
+     such rows, codes / scales span cache_rows rows as for a paged cache and
+     a row outside [0, cache_rows) leaves its slot empty; the result equals
+     the paged call that wrote them, without its block-table reads.  Both
+     need kernel 0 or 1 (the library then takes 1).  Errors: CSA2_ERR_SHAPE,
+     CSA2_ERR_ALIGN.                                                        */
+  int32_t* topk_rows_out;
+  int32_t topk_is_rows;
 } csa2_attn_args;
 
 /* Bytes of workspace csa2_sparse_attn needs for these arguments (may be 0). */

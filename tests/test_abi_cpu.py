@@ -267,6 +267,17 @@ def test_attn_rejects(lib):
     assert sa(ctypes.byref(args(swa_new=256, window=0, **s8)), None, 0, None) == 2      # no window
     assert sa(ctypes.byref(args(swa_new=256, batch=1, q_per_seq=17, **s8)), None, 0, None) == 2
     assert sa(ctypes.byref(args(swa_new=264, **s8)), None, 0, None) == 3
+    # the Top-K as cache rows: written by a paged call, read without a block table
+    pg = dict(block_table=256, max_pages=4, page_size=16, cache_rows=1024)
+    assert lib.csa2_attn_workspace_size(ctypes.byref(args(topk_rows_out=256, **pg))) == need   # accepted
+    assert lib.csa2_attn_workspace_size(ctypes.byref(args(topk_is_rows=1, cache_rows=1024))) == need
+    assert sa(ctypes.byref(args(topk_rows_out=256)), None, 0, None) == 2                 # no block table
+    assert sa(ctypes.byref(args(topk_rows_out=258, **pg)), None, 0, None) == 3
+    assert sa(ctypes.byref(args(topk_rows_out=256, kernel=2, **pg)), None, 0, None) == 2
+    assert sa(ctypes.byref(args(topk_is_rows=1, cache_rows=1024, block_table=256, max_pages=4, page_size=16)),
+              None, 0, None) == 2
+    assert sa(ctypes.byref(args(topk_is_rows=2, cache_rows=1024)), None, 0, None) == 2
+    assert sa(ctypes.byref(args(topk_is_rows=1, cache_rows=1 << 24)), None, 0, None) == 2
 
 
 def test_argument_structs_keep_their_tensors_alive():

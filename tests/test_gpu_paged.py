@@ -239,3 +239,45 @@ def test_index_append_paged_equals_separate_calls(rows, split):
     dst = bt[seq, pos // P].astype(np.int64) * P + pos % P
     np.testing.assert_array_equal(outs[0][2][dst], rc)
     np.testing.assert_array_equal(outs[0][3][dst], rs)
+
+
+@pytest.mark.parametrize("split", [(0, 0), (4, 1), (8, 3)], ids=["auto", "w4s1", "w8s3"])
+def test_attn_paged_rows_out_and_rows_in(split):
+    """A paged call with topk_rows_out writes every Top-K slot's cache row
+    (-1 for empty slots, positions past T and missing pages); a call given
+    those rows (topk_is_rows, no block table) is bit-identical to the paged
+    call, and both match the oracle."""
+    waves, splits = split
+    B, Qn, T, d, H, W, k, P = 3, 2, 3000, 512, 64, 128, 512, 64
+    codes, scales, q, swa, topk = make_case(41, B, Qn, T, d, H, W, k)
+    topk[0, -3:] = [-1, T, T + 5]
+    rng = np.random.default_rng(42)
+    bt, rows, n_rows = page_layout(rng, B, T, P)
+    pc, ps = paged_copy(codes, scales, rows, n_rows)
+    bt[2, 5] = -1                                         # a missing page
+    want_rows = np.full((B * Qn, k), -1, np.int32)
+    for i in range(B * Qn):
+        b = i // Qn
+        for s, t in enumerate(topk[i]):
+            if 0 <= t < T and bt[b, t // P] >= 0:
+                want_rows[i, s] = bt[b, t // P] * P + t % P
+    q_d, c_d, s_d, sw_d = dev(q.view(np.int16)), dev(pc), dev(ps), dev(swa.view(np.int16))
+
+    def run(tk, **kw):
+        out = torch.full((B * Qn, H, d), float("nan"), dtype=torch.float32, device="cuda")
+        args = csa2.attn_args(q_d, c_d, s_d, tk, sw_d, out, Qn, T, W, waves=waves, splits=splits, **kw)
+        n = csa2.attn_workspace_size(args)
+        csa2.sparse_attn(args, torch.empty(max(n, 256), dtype=torch.uint8, device="cuda") if n else None)
+        return host(out)
+
+    rows_d = torch.full((B * Qn, k), -7, dtype=torch.int32, device="cuda")
+    paged = run(dev(topk), block_table=dev(bt), page_size=P, topk_rows_out=rows_d)
+    np.testing.assert_array_equal(host(rows_d), want_rows)
+    plain = run(dev(topk), block_table=dev(bt), page_size=P)
+    np.testing.assert_array_equal(paged, plain)
+    from_rows = run(rows_d, topk_is_rows=True)
+    np.testing.assert_array_equal(from_rows, paged)
+    ref_topk = topk.copy()
+    ref_topk[4:6][(topk[4:6] // P) == 5] = -1             # sequence 2's missing page
+    want = oracle_out(q, codes, scales, ref_topk, swa, Qn, T, W)
+    assert rownorm_err(paged, want) <= ATTN_TOL
